@@ -1,0 +1,3 @@
+"""fp64 CPU oracle for the KDA forward. Test infrastructure only: see ``kda_oracle``."""
+from .kda_oracle import (DEFAULT_EPS, document_bounds, kda_document, kda_forward,  # noqa: F401
+                         kda_tasks, l2_normalise, default_workers)

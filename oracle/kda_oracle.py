@@ -1,0 +1,175 @@
+"""fp64 CPU oracle for the Kimi Delta Attention (KDA) forward.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+path; the only thing both sides share is the seeded input generator
+(``kda_workloads``), which holds none of the method's arithmetic.
+
+What it computes (page "nemo_automodel.components.models.kimi_k3.kda_fused",
+package docstring and the ``fused_chunk_kda`` / ``fused_kda_unsupported_reason``
+entries): the KDA delta rule, specialised to
+
+* one recurrent state ``S`` of shape K x V per (document, head), starting at
+  zero in every document ("no initial or final state"; "the recurrent state
+  resets at every document boundary" in the ``fused_chunk_kda`` docstring);
+* q and k l2-normalised inside the operator (``use_qk_l2norm_in_kernel``);
+* a log decay ``g`` per token, head and key channel (the "bounded log gate";
+  the K3 model page's ``KimiKDAFp32Params`` returns an fp32 ``[b, s, h, d]``
+  decay);
+* packed documents delimited by int32 ``cu_seqlens``.
+
+The pages print no formula for the recurrence.  The oracle takes the KDA
+delta rule in its plain token-by-token form:
+
+    S_t = (I - beta_t k_t k_t^T) Diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T
+    o_t = K**-0.5 * S_t^T q_t
+
+with k_t, q_t the l2-normalised vectors ``x / sqrt(sum(x*x) + eps)`` and
+``eps = 1e-6``.  The output uses the state *after* token t's write.  The
+second update line below is the same expression multiplied out:
+``(I - b k k^T) D S + b k v^T = D S + b k (v - (D S)^T k)^T``.
+
+Everything runs in fp64.  The caller passes the exact values the GPU path
+receives (bf16 q, k, v widened exactly; fp32 g, beta widened exactly).
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ProcessPoolExecutor
+
+import numpy as np
+
+DEFAULT_EPS = 1e-6
+
+
+def l2_normalise(x: np.ndarray, eps: float = DEFAULT_EPS) -> np.ndarray:
+    """``x / sqrt(sum(x**2) + eps)`` over the last axis (in-kernel q/k l2 norm)."""
+    x = np.asarray(x, np.float64)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+
+
+def kda_document(q, k, v, g, beta, scale: float | None = None,
+                 eps: float = DEFAULT_EPS) -> np.ndarray:
+    """Run one document from a zero state, all given heads at once.
+
+    q, k: [L, H, K]; v: [L, H, V]; g: [L, H, K]; beta: [L, H].
+    Returns o: [L, H, V] in fp64.  The final state is discarded.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    g = np.asarray(g, np.float64)
+    beta = np.asarray(beta, np.float64)
+    L, H, K = q.shape
+    V = v.shape[-1]
+    if scale is None:
+        scale = K ** -0.5
+    qn = l2_normalise(q, eps)
+    kn = l2_normalise(k, eps)
+    S = np.zeros((H, K, V))
+    o = np.empty((L, H, V))
+    for t in range(L):
+        # Diag(exp(g_t)) S_{t-1}: the decay scales the rows of S (key channels)
+        S *= np.exp(g[t])[:, :, None]
+        kt = kn[t]                                           # [H, K]
+        pred = np.matmul(kt[:, None, :], S)[:, 0, :]         # (D S)^T k  -> [H, V]
+        S += beta[t][:, None, None] * kt[:, :, None] * (v[t] - pred)[:, None, :]
+        o[t] = scale * np.matmul(qn[t][:, None, :], S)[:, 0, :]   # S_t^T q_t
+    return o
+
+
+def document_bounds(cu_seqlens, T: int) -> list[tuple[int, int]]:
+    """Documents ``[cu[i], cu[i+1])`` of a packed stream (``None`` = one document).
+
+    The list is read up to the first entry equal to T; zero-length documents
+    are kept (they produce nothing)."""
+    if cu_seqlens is None:
+        return [(0, T)]
+    cu = [int(x) for x in np.asarray(cu_seqlens).reshape(-1)]
+    if not cu or cu[0] != 0:
+        raise ValueError("cu_seqlens must start at 0")
+    out = []
+    for a, b in zip(cu[:-1], cu[1:]):
+        if b < a or b > T:
+            raise ValueError("cu_seqlens must be non-decreasing and end at T")
+        out.append((a, b))
+        if b == T:
+            break
+    if (out[-1][1] if out else 0) != T:
+        raise ValueError("cu_seqlens must reach T")
+    return out
+
+
+def kda_forward(q, k, v, g, beta, cu_seqlens=None, scale: float | None = None,
+                eps: float = DEFAULT_EPS) -> np.ndarray:
+    """Packed forward: q, k, g [T, H, K], v [T, H, V], beta [T, H] -> o [T, H, V] (fp64)."""
+    T = q.shape[0]
+    o = np.zeros((T,) + tuple(v.shape[1:]))
+    for a, b in document_bounds(cu_seqlens, T):
+        if b > a:
+            o[a:b] = kda_document(q[a:b], k[a:b], v[a:b], g[a:b], beta[a:b], scale, eps)
+    return o
+
+
+# ---------------------------------------------------------------------------
+# task-parallel driver: independent (document, head-range) tasks on a process
+# pool.  Inputs are inherited by the forked workers, not pickled.
+# ---------------------------------------------------------------------------
+
+_SHARED: dict = {}
+
+
+def _worker_init():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except ImportError:  # pragma: no cover
+        pass
+
+
+def _run_task(task):
+    a, b, h0, h1 = task
+    s = _SHARED
+    return task, kda_document(s["q"][a:b, h0:h1], s["k"][a:b, h0:h1], s["v"][a:b, h0:h1],
+                              s["g"][a:b, h0:h1], s["beta"][a:b, h0:h1],
+                              s["scale"], s["eps"])
+
+
+def default_workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def kda_tasks(q, k, v, g, beta, tasks, workers: int | None = None,
+              scale: float | None = None, eps: float = DEFAULT_EPS):
+    """Yield ``((a, b, h0, h1), o)`` for each task: tokens [a, b) of one document,
+    heads [h0, h1).  Tasks are run longest first on ``workers`` processes."""
+    import multiprocessing as mp
+    tasks = sorted(tasks, key=lambda t: -(t[1] - t[0]) * (t[3] - t[2]))
+    workers = workers or default_workers()
+    _SHARED.update(q=q, k=k, v=v, g=g, beta=beta, scale=scale, eps=eps)
+    try:
+        if workers <= 1 or len(tasks) <= 1:
+            for t in tasks:
+                yield _run_task(t)
+            return
+        env_keep = {x: os.environ.get(x) for x in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS")}
+        os.environ["OMP_NUM_THREADS"] = "1"
+        os.environ["OPENBLAS_NUM_THREADS"] = "1"
+        try:
+            ctx = mp.get_context("fork")
+            with ProcessPoolExecutor(workers, mp_context=ctx, initializer=_worker_init) as ex:
+                for r in ex.map(_run_task, tasks, chunksize=1):
+                    yield r
+        finally:
+            for key, val in env_keep.items():
+                if val is None:
+                    os.environ.pop(key, None)
+                else:
+                    os.environ[key] = val
+    finally:
+        _SHARED.clear()
