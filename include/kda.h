@@ -1,0 +1,119 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) forward pass of Kimi Delta Attention
+ * (KDA), chunked form, specialised to head dims K = V = 128 in packed layout.
+ *
+ * Operation (page "nemo_automodel.components.models.kimi_k3.kda_fused",
+ * package docstring, fused_chunk_kda and fused_kda_unsupported_reason):
+ * per document d and head h, a K x V fp32 state S starts at zero and, for
+ * every token t of the document in order,
+ *
+ *     S  <- (I - beta_t kh_t kh_t^T) Diag(exp(g_t)) S + beta_t kh_t v_t^T
+ *     o_t = 128**-0.5 * S^T qh_t
+ *
+ * where qh, kh are q, k scaled by 1/sqrt(sum(x*x) + 1e-6) (the in-kernel
+ * l2 norm), g_t is the per-key-channel log decay (the bounded log gate) and
+ * the state is dropped at the end of the document (no initial or final state).
+ * Documents are delimited by int32 cu_seqlens (the packed, batch-1 layout);
+ * a dense batch of B equal-length sequences is the same computation with
+ * cu_seqlens = [0, T, 2T, ..., BT].  The result does not depend on the chunk
+ * length; the library works in chunks of 64 tokens.
+ *
+ * All entry points are thread-safe.  Errors are returned, never hidden: there
+ * is no fallback path (the pages' contract: a call either runs the fused
+ * kernels or stops with the first violated condition).
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes of kda_chunk_fwd (0 = success). */
+enum kda_status {
+  KDA_OK = 0,
+  KDA_ERR_NULL_PTR = -1,    /* a required pointer is NULL                              */
+  KDA_ERR_BAD_SHAPE = -2,   /* T < 0, T > INT32_MAX, H < 1 or H > KDA_MAX_HEADS         */
+  KDA_ERR_UNSUPPORTED = -3, /* chunk != 64, or gate_bound not finite or outside [-5.5, 0) */
+  KDA_ERR_ALIGN = -4,       /* q, k, v, g, out not 16-byte aligned; beta, cu_seqlens not 4-byte aligned */
+  KDA_ERR_HIP = -5,         /* a HIP runtime call or kernel launch failed              */
+  KDA_ERR_ALLOC = -6        /* the stream-ordered workspace allocation failed          */
+};
+
+/* Bits of the sticky device status word (kda_device_status). */
+enum kda_device_flags {
+  KDA_DEV_BAD_CU_SEQLENS = 1, /* cu_seqlens broke its contract; out was filled with NaN  */
+  KDA_DEV_GATE_RANGE = 2      /* some g fell outside [gate_bound, 0] (or was NaN); the
+                                 result was still computed, without clamping             */
+};
+
+#define KDA_HEAD_DIM 128
+#define KDA_CHUNK 64
+#define KDA_MAX_HEADS 4096
+
+/*
+ * kda_chunk_fwd -- o = KDA(q, k, v, g, beta) over a packed token stream.
+ *
+ * Layouts (all contiguous, row-major, token-major "[1, T, H, D]" packed):
+ *   q, k, v     bf16  [T][H][128]   device memory, 16-byte aligned
+ *   g           fp32  [T][H][128]   device memory, 16-byte aligned; natural-log
+ *                                   decay per token, head and key channel; the
+ *                                   caller promises gate_bound <= g <= 0
+ *   beta        fp32  [T][H]        device memory, 4-byte aligned; any finite value
+ *   cu_seqlens  int32 [N+1]         device memory, 4-byte aligned, or NULL for a
+ *                                   single document [0, T).  cu[0] = 0, entries
+ *                                   non-decreasing, and the list ends at its first
+ *                                   entry equal to T, at index N <= T.  Zero-length
+ *                                   documents are allowed.  The library reads the
+ *                                   list in aligned 4 KiB blocks up to the block
+ *                                   that holds that entry (bytes past it in the same
+ *                                   page are read and ignored).
+ *   out         bf16  [T][H][128]   device memory, 16-byte aligned, fully
+ *                                   overwritten (round to nearest even)
+ *   T           tokens in the stream, 0 <= T <= INT32_MAX (T = 0 is a no-op)
+ *   H           heads, 1 <= H <= KDA_MAX_HEADS (same H for q, k and v)
+ *   chunk       must be 64
+ *   gate_bound  L with -5.5 <= L < 0: the lower bound of the bounded log gate.
+ *               It licenses the 16-token sub-block factorisation of the decay
+ *               inside a chunk (no exp() argument beyond +-88); it is never used
+ *               to clamp g.
+ *   stream      HIP stream on the current device; all work is enqueued on it.
+ *
+ * Ownership: the caller owns every buffer and keeps it alive until the stream
+ * has passed this call.  The library allocates a small stream-ordered
+ * workspace (hipMallocAsync / hipFreeAsync on `stream`), and never syncs the
+ * host.
+ *
+ * Errors: returns KDA_OK or the negative kda_status of the FIRST violated
+ * condition, checked in this order: shape (T, H), then (unless T = 0) NULL
+ * pointers, chunk and gate_bound, alignment.  kda_last_error() then names the
+ * condition.  Violations only visible on the device (cu_seqlens contents,
+ * g outside the promised range) are reported through kda_device_status().
+ */
+int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
+                  const float* beta, const int32_t* cu_seqlens, int64_t T, int32_t H,
+                  int32_t chunk, float gate_bound, void* out, hipStream_t stream);
+
+/*
+ * kda_last_error -- message for the last non-zero return of kda_chunk_fwd on
+ * the calling thread ("" if none).  The string is owned by the library and
+ * stays valid until the next call on the same thread.
+ */
+const char* kda_last_error(void);
+
+/*
+ * kda_device_status -- debug/test helper: synchronises `stream`, returns the
+ * sticky kda_device_flags word of the current device accumulated by all calls
+ * since the last kda_device_status, and clears it.  Returns KDA_ERR_HIP if a
+ * HIP call fails.  Not for the hot path (it blocks the host).
+ */
+int kda_device_status(hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,218 @@
+"""Kimi Delta Attention (KDA) chunked forward on MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/kda.h`` (``libkda.so``, built
+in-tree).  Torch is used only for device memory and streams: every step of
+the forward runs in the library's HIP kernels.  There is no CPU or PyTorch
+fallback: if the library is missing, importing works but every call raises.
+
+The tensor-level entry point mirrors the fused path of the K3 model
+(page "nemo_automodel.components.models.kimi_k3.kda_fused"):
+``chunk_fwd(q, k, v, g, beta, cu_seqlens)`` returns ``(o, None)`` like
+``fused_chunk_kda``; ``unsupported_reason`` names the first violated condition
+like ``fused_kda_unsupported_reason``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+HEAD_DIM = 128
+CHUNK = 64
+DEFAULT_GATE_BOUND = -5.0
+
+KDA_OK = 0
+KDA_ERR_NULL_PTR = -1
+KDA_ERR_BAD_SHAPE = -2
+KDA_ERR_UNSUPPORTED = -3
+KDA_ERR_ALIGN = -4
+KDA_ERR_HIP = -5
+KDA_ERR_ALLOC = -6
+KDA_DEV_BAD_CU_SEQLENS = 1
+KDA_DEV_GATE_RANGE = 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+_lib = None
+
+
+class KDAError(RuntimeError):
+    """A non-zero return of the C ABI."""
+
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"kda_chunk_fwd failed ({code}): {msg}")
+        self.code = code
+
+
+def load_library():
+    """Load ``libkda.so`` (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                "(there is no fallback implementation)")
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.kda_chunk_fwd.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+            ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
+        lib.kda_chunk_fwd.restype = ctypes.c_int
+        lib.kda_last_error.argtypes = []
+        lib.kda_last_error.restype = ctypes.c_char_p
+        lib.kda_device_status.argtypes = [ctypes.c_void_p]
+        lib.kda_device_status.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+# ---------------------------------------------------------------------------
+# same-name wrappers of the C entry points (argument marshalling only)
+# ---------------------------------------------------------------------------
+
+def kda_chunk_fwd(q, k, v, g, beta, cu_seqlens, T, H, chunk, gate_bound, out, stream) -> int:
+    """Call the C entry point with raw addresses (ints or None); returns its status."""
+    lib = load_library()
+    return lib.kda_chunk_fwd(q, k, v, g, beta, cu_seqlens, int(T), int(H), int(chunk),
+                             float(gate_bound), out, stream)
+
+
+def kda_last_error() -> str:
+    return load_library().kda_last_error().decode()
+
+
+def kda_device_status(stream=None) -> int:
+    return load_library().kda_device_status(stream)
+
+
+# ---------------------------------------------------------------------------
+# tensor-level API
+# ---------------------------------------------------------------------------
+
+def _layout(q):
+    """Return (B, T) of a [B, T, H, D] or [T, H, D] tensor."""
+    if q.dim() == 4:
+        return q.shape[0], q.shape[1]
+    if q.dim() == 3:
+        return 1, q.shape[0]
+    return None
+
+
+def unsupported_reason(q, k, v, g, beta, cu_seqlens=None, *, chunk: int = CHUNK,
+                       gate_bound: float = DEFAULT_GATE_BOUND, mode: str = "chunk",
+                       use_qk_l2norm_in_kernel: bool = True, safe_gate: bool = True,
+                       initial_state=None, output_final_state: bool = False,
+                       cp_context=None) -> str | None:
+    """Why this call cannot run on the library's kernels, or None when it can.
+
+    Checked in order: mode, l2 norm, safe gate, state, context parallelism,
+    chunk, gate bound, dtypes, devices, layout, shapes, contiguity, cu_seqlens."""
+    import torch
+    if mode != "chunk":
+        return f"kda_mode must be 'chunk' (got {mode!r})"
+    if not use_qk_l2norm_in_kernel:
+        return "q/k must be l2-normalised inside the kernel"
+    if not safe_gate:
+        return "the gate must be the bounded (safe) log gate"
+    if initial_state is not None or output_final_state:
+        return "initial / final state is not supported"
+    if cp_context is not None:
+        return "context parallelism is not supported"
+    if chunk != CHUNK:
+        return f"chunk must be {CHUNK}"
+    if not (isinstance(gate_bound, (int, float)) and math.isfinite(gate_bound)
+            and -5.5 <= gate_bound < 0):
+        return "gate_bound must be finite and in [-5.5, 0)"
+    for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16),
+                        ("v", v, torch.bfloat16), ("g", g, torch.float32),
+                        ("beta", beta, torch.float32)):
+        if not isinstance(t, torch.Tensor):
+            return f"{name} must be a tensor"
+        if t.dtype != dt:
+            return f"{name} must be {dt} (got {t.dtype})"
+        if t.device.type != "cuda":
+            return f"{name} must be on a GPU"
+        if t.device != q.device:
+            return f"{name} is on {t.device}, q on {q.device}"
+    lay = _layout(q)
+    if lay is None:
+        return "q must be [B, T, H, 128] or [T, H, 128]"
+    B, T = lay
+    if q.shape[-1] != HEAD_DIM:
+        return f"head dim must be {HEAD_DIM} (got {q.shape[-1]})"
+    H = q.shape[-2]
+    if k.shape != q.shape:
+        return f"k shape {tuple(k.shape)} != q shape {tuple(q.shape)}"
+    if g.shape != q.shape:
+        return f"g shape {tuple(g.shape)} != q shape {tuple(q.shape)}"
+    if v.shape != q.shape:
+        return f"v shape {tuple(v.shape)} must equal q shape {tuple(q.shape)} (V = K = 128)"
+    if tuple(beta.shape) != tuple(q.shape[:-1]):
+        return f"beta shape {tuple(beta.shape)} must be {tuple(q.shape[:-1])}"
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
+        if not t.is_contiguous():
+            return f"{name} must be contiguous"
+    if cu_seqlens is not None:
+        if B != 1:
+            return "packed input (cu_seqlens given) must have batch 1"
+        if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32:
+            return "cu_seqlens must be an int32 tensor"
+        if cu_seqlens.device != q.device:
+            return "cu_seqlens must be on the same GPU as q"
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            return "cu_seqlens must be 1-D with at least 2 entries"
+        if cu_seqlens.numel() > T + 1:
+            return "cu_seqlens has more than T + 1 entries"
+        if not cu_seqlens.is_contiguous():
+            return "cu_seqlens must be contiguous"
+    if B * T > 2**31 - 1:
+        return "too many tokens (T must be <= INT32_MAX)"
+    if H > 4096:
+        return "too many heads"
+    return None
+
+
+def chunk_fwd(q, k, v, g, beta, cu_seqlens=None, *, chunk: int = CHUNK,
+              gate_bound: float = DEFAULT_GATE_BOUND, out=None):
+    """KDA chunked forward.  Returns ``(o, None)``.
+
+    Packed input: ``q, k, v, g`` of shape [1, T, H, 128] (or [T, H, 128]),
+    ``beta`` [1, T, H], int32 ``cu_seqlens`` [N+1] on the same GPU.  Dense
+    input (``cu_seqlens=None``): [B, T, H, 128] is viewed as B packed
+    documents of T tokens (no copy).  Raises ValueError for an unsupported
+    call and KDAError if the library reports an error."""
+    import torch
+    reason = unsupported_reason(q, k, v, g, beta, cu_seqlens, chunk=chunk, gate_bound=gate_bound)
+    if reason is not None:
+        raise ValueError(reason)
+    B, T = _layout(q)
+    H = q.shape[-2]
+    n_tok = B * T
+    if out is None:
+        out = torch.empty_like(v)
+    elif out.shape != v.shape or out.dtype != torch.bfloat16 or not out.is_contiguous() \
+            or out.device != q.device:
+        raise ValueError("out must be a contiguous bf16 tensor shaped like v on q's device")
+    if n_tok == 0:
+        return out, None
+    cu = cu_seqlens
+    if cu is None and B > 1:
+        cu = torch.arange(0, n_tok + 1, T, dtype=torch.int32, device=q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = kda_chunk_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(),
+                           None if cu is None else cu.data_ptr(), n_tok, H, chunk, gate_bound,
+                           out.data_ptr(), stream)
+    if rc != KDA_OK:
+        raise KDAError(rc, kda_last_error())
+    return out, None
+
+
+def device_status(device=None) -> int:
+    """Synchronise the current stream and return / clear the sticky device flags."""
+    import torch
+    with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+        rc = kda_device_status(torch.cuda.current_stream().cuda_stream)
+    if rc < 0:
+        raise KDAError(rc, "kda_device_status failed")
+    return rc

@@ -1,0 +1,101 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point that include/kda.h declares, and rejects bad arguments with
+the documented status codes before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_sequence_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "kda.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert _declared_functions() == ["kda_chunk_fwd", "kda_device_status", "kda_last_error"]
+
+
+def test_library_exports_every_declared_symbol():
+    if not os.path.exists(kda.LIB_PATH):
+        pytest.skip("libkda.so not built")
+    lib = ctypes.CDLL(kda.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+# a plausible, 16-byte aligned fake address: never dereferenced because every
+# call below fails validation first
+P = 1 << 20
+
+
+def _call(**kw):
+    args = dict(q=P, k=P, v=P, g=P, beta=P, cu=None, T=128, H=2, chunk=64, gate_bound=-5.0,
+                out=P, stream=None)
+    args.update(kw)
+    rc = kda.kda_chunk_fwd(args["q"], args["k"], args["v"], args["g"], args["beta"], args["cu"],
+                           args["T"], args["H"], args["chunk"], args["gate_bound"], args["out"],
+                           args["stream"])
+    return rc, kda.kda_last_error()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(T=-1), kda.KDA_ERR_BAD_SHAPE, "T must be >= 0"),
+    (dict(T=2**31), kda.KDA_ERR_BAD_SHAPE, "INT32_MAX"),
+    (dict(H=0), kda.KDA_ERR_BAD_SHAPE, "H must be >= 1"),
+    (dict(H=5000), kda.KDA_ERR_BAD_SHAPE, "KDA_MAX_HEADS"),
+    (dict(q=None), kda.KDA_ERR_NULL_PTR, "q is NULL"),
+    (dict(k=None), kda.KDA_ERR_NULL_PTR, "k is NULL"),
+    (dict(v=None), kda.KDA_ERR_NULL_PTR, "v is NULL"),
+    (dict(g=None), kda.KDA_ERR_NULL_PTR, "g is NULL"),
+    (dict(beta=None), kda.KDA_ERR_NULL_PTR, "beta is NULL"),
+    (dict(out=None), kda.KDA_ERR_NULL_PTR, "out is NULL"),
+    (dict(chunk=32), kda.KDA_ERR_UNSUPPORTED, "chunk must be 64"),
+    (dict(gate_bound=0.0), kda.KDA_ERR_UNSUPPORTED, "gate_bound"),
+    (dict(gate_bound=-6.0), kda.KDA_ERR_UNSUPPORTED, "gate_bound"),
+    (dict(gate_bound=float("nan")), kda.KDA_ERR_UNSUPPORTED, "gate_bound"),
+    (dict(q=P + 8), kda.KDA_ERR_ALIGN, "q is not 16-byte aligned"),
+    (dict(g=P + 4), kda.KDA_ERR_ALIGN, "g is not 16-byte aligned"),
+    (dict(out=P + 2), kda.KDA_ERR_ALIGN, "out is not 16-byte aligned"),
+    (dict(beta=P + 2), kda.KDA_ERR_ALIGN, "beta is not 4-byte aligned"),
+    (dict(cu=P + 2), kda.KDA_ERR_ALIGN, "cu_seqlens is not 4-byte aligned"),
+])
+def test_argument_validation(kw, code, msg):
+    if not os.path.exists(kda.LIB_PATH):
+        pytest.skip("libkda.so not built")
+    rc, err = _call(**kw)
+    assert rc == code
+    assert msg in err
+
+
+def test_first_violated_condition_is_reported():
+    if not os.path.exists(kda.LIB_PATH):
+        pytest.skip("libkda.so not built")
+    rc, err = _call(q=None, chunk=32, H=0)
+    assert rc == kda.KDA_ERR_BAD_SHAPE and "H must be" in err
+    rc, err = _call(q=None, chunk=32)
+    assert rc == kda.KDA_ERR_NULL_PTR and "q is NULL" in err
+
+
+def test_empty_stream_is_a_noop():
+    if not os.path.exists(kda.LIB_PATH):
+        pytest.skip("libkda.so not built")
+    rc, err = _call(T=0, q=None, k=None, v=None, g=None, beta=None, out=None)
+    assert rc == kda.KDA_OK and err == ""
+
+
+def test_unsupported_reason_on_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 8, 2, 128, dtype=torch.bfloat16)
+    r = kda.unsupported_reason(q, q, q, q.float(), torch.zeros(1, 8, 2), None)
+    assert "must be on a GPU" in r
+    assert "kda_mode" in kda.unsupported_reason(q, q, q, q.float(), None, mode="recurrent")
+    assert "initial / final state" in kda.unsupported_reason(q, q, q, q.float(), None,
+                                                             initial_state=q)
+    assert "chunk must be 64" in kda.unsupported_reason(q, q, q, q.float(), None, chunk=16)

@@ -1,0 +1,218 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bar: relative L2 error <= 5e-3 and max absolute error <= 3e-2 on the same
+seeded inputs.  Small cases compare every output; the full-size packed
+streams compare sampled (document, head) tasks, each of which the oracle
+computes in full, in the same launch configuration the benchmark times."""
+import numpy as np
+import pytest
+
+import oracle
+from kda_gpu_util import check, doc_tasks, log, run_gpu, to_device
+from kda_workloads import (Inputs, cu_from_lengths, make_inputs, one_hot_keys, with_gate_scale,
+                           workload, workload_inputs)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import linear_attention_sequence_amd as kda
+    kda.load_library()
+
+
+def _small(T, H, seed, lengths, **kw):
+    return make_inputs(T, H, seed, cu_from_lengths(lengths), **kw)
+
+
+# ---------------------------------------------------------------- workloads
+
+def test_workload1_single_doc_T256():
+    w, inp = workload_inputs(1)
+    log(f"[case] workload 1 {w.name}")
+    o = run_gpu(inp)
+    check(inp, o, doc_tasks(inp.cu_seqlens, w.H), w.name)
+
+
+def test_workload2_single_doc_T4096():
+    w, inp = workload_inputs(2)
+    log(f"[case] workload 2 {w.name}")
+    o = run_gpu(inp)
+    check(inp, o, doc_tasks(inp.cu_seqlens, w.H), w.name)
+
+
+def test_workload3_packed_lognormal_sampled_heads():
+    w, inp = workload_inputs(3)
+    log(f"[case] workload 3 {w.name} docs={len(w.lengths)}")
+    o = run_gpu(inp)
+    check(inp, o, doc_tasks(inp.cu_seqlens, w.H, heads=[0, 7, 13, 22, 31]), w.name)
+
+
+def test_workload4_dense_batch_sampled():
+    w, inp = workload_inputs(4)
+    log(f"[case] workload 4 {w.name}")
+    o = run_gpu(inp)
+    cu = inp.cu_seqlens
+    tasks = [(int(cu[i]), int(cu[i + 1]), h, h + 1) for i, h in ((0, 0), (3, 17), (7, 31))]
+    check(inp, o, tasks, w.name)
+
+
+def test_workload5_long_plus_short_sampled():
+    w, inp = workload_inputs(5)
+    log(f"[case] workload 5 {w.name} docs={len(w.lengths)}")
+    o = run_gpu(inp)
+    cu = inp.cu_seqlens
+    tasks = [(0, int(cu[1]), 5, 6)] + doc_tasks(cu[1:], w.H, heads=[2, 29])
+    check(inp, o, tasks, w.name)
+
+
+# ---------------------------------------------------------------- special inputs
+
+def test_beta_zero_gives_exact_zeros():
+    inp = _small(300, 3, 21, [100, 200])
+    inp.beta[:] = 0.0
+    o = run_gpu(inp)
+    assert int((o != 0).sum()) == 0
+
+
+def test_all_length_one_documents():
+    T, H = 4096, 4
+    inp = _small(T, H, 22, [1] * T)
+    o = run_gpu(inp)
+    check(inp, o, doc_tasks(inp.cu_seqlens, H, heads=[0, 3])[:600], "all length-1 documents")
+    # closed form at T = 1: o = scale * beta * (qh . kh) v
+    qn = oracle.l2_normalise(inp.q)
+    kn = oracle.l2_normalise(inp.k)
+    ref = 128 ** -0.5 * inp.beta[..., None] * (qn * kn).sum(-1, keepdims=True) * inp.v
+    got = o.float().cpu().numpy()
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    log(f"[parity] length-1 closed form relL2={rel:.3e}")
+    assert rel <= 5e-3
+
+
+@pytest.mark.parametrize("gate_scale,T", [(-0.05, 2048), (0.0, 512)])
+def test_slow_decay_exercises_the_state(gate_scale, T):
+    H = 4
+    inp = with_gate_scale(_small(T, H, 23, [T]), 23, gate_scale)
+    o = run_gpu(inp)
+    check(inp, o, doc_tasks(inp.cu_seqlens, H), f"gate {gate_scale}*sigmoid T={T}")
+
+
+def test_one_hot_keys():
+    T, H = 1024, 4
+    inp = _small(T, H, 24, [300, 724])
+    inp.k[:] = one_hot_keys(T, H, 24)
+    inp = with_gate_scale(inp, 24, -0.3)
+    o = run_gpu(inp)
+    check(inp, o, doc_tasks(inp.cu_seqlens, H), "one-hot keys")
+
+
+def test_ragged_document_lengths():
+    lengths = [1, 2, 15, 16, 17, 63, 64, 65, 0, 127, 128, 129, 200, 31]
+    T, H = sum(lengths), 3
+    inp = _small(T, H, 25, lengths)
+    o = run_gpu(inp)
+    check(inp, o, doc_tasks(inp.cu_seqlens, H), "ragged lengths")
+
+
+def test_gate_at_the_bound():
+    T, H = 300, 2
+    inp = _small(T, H, 26, [T])
+    inp.g[:] = -5.0
+    inp.g[::7] = -0.001
+    o = run_gpu(inp)
+    check(inp, o, doc_tasks(inp.cu_seqlens, H), "gate at the bound")
+
+
+# ---------------------------------------------------------------- layouts
+
+def test_cu_none_is_one_document():
+    T, H = 333, 2
+    inp = _small(T, H, 27, [T])
+    a = run_gpu(inp, cu=True)
+    b = run_gpu(inp, cu=False)
+    assert bool((a == b).all())
+    check(inp, b, doc_tasks(inp.cu_seqlens, H), "cu_seqlens=None")
+
+
+def test_dense_batch_is_packed_documents():
+    import torch
+    import linear_attention_sequence_amd as kda
+    B, T, H = 3, 100, 2
+    inp = _small(B * T, H, 28, [T] * B)
+    d = to_device(inp)
+    packed, _ = kda.chunk_fwd(d["q"][None], d["k"][None], d["v"][None], d["g"][None],
+                              d["beta"][None], d["cu"])
+    dense, _ = kda.chunk_fwd(d["q"].view(B, T, H, 128), d["k"].view(B, T, H, 128),
+                             d["v"].view(B, T, H, 128), d["g"].view(B, T, H, 128),
+                             d["beta"].view(B, T, H))
+    torch.cuda.synchronize()
+    assert bool((packed.view(B, T, H, 128) == dense).all())
+
+
+def test_deterministic():
+    import torch
+    import linear_attention_sequence_amd as kda
+    w, inp = workload_inputs(3)
+    d = to_device(inp)
+    a, _ = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"])
+    b, _ = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"])
+    torch.cuda.synchronize()
+    assert bool((a.view(torch.int16) == b.view(torch.int16)).all())
+
+
+def test_empty_stream():
+    import torch
+    import linear_attention_sequence_amd as kda
+    z = torch.zeros(0, 2, 128, dtype=torch.bfloat16, device="cuda")
+    o, none = kda.chunk_fwd(z, z, z, z.float(), torch.zeros(0, 2, device="cuda"), None)
+    assert o.numel() == 0 and none is None
+
+
+# ---------------------------------------------------------------- device-side errors
+
+def test_bad_cu_seqlens_sets_status_and_nan():
+    import torch
+    import linear_attention_sequence_amd as kda
+    T, H = 128, 2
+    inp = _small(T, H, 29, [T])
+    d = to_device(inp)
+    assert kda.device_status() == 0
+    for bad in ([0, 100, 90, 128], [1, 128], [0, 130, 128]):
+        cu = torch.tensor(bad, dtype=torch.int32, device="cuda")
+        o, _ = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], cu)
+        st = kda.device_status()
+        assert st & kda.KDA_DEV_BAD_CU_SEQLENS, bad
+        assert bool(torch.isnan(o.float()).all()), bad
+    assert kda.device_status() == 0
+
+
+def test_gate_out_of_range_is_flagged():
+    import linear_attention_sequence_amd as kda
+    T, H = 64, 1
+    inp = _small(T, H, 30, [T])
+    d = to_device(inp)
+    assert kda.device_status() == 0
+    kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"])
+    assert kda.device_status() == 0
+    d["g"][5, 0, 3] = 0.5
+    kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"])
+    assert kda.device_status() & kda.KDA_DEV_GATE_RANGE
+
+
+def test_binding_rejects_bad_tensors():
+    import torch
+    import linear_attention_sequence_amd as kda
+    q = torch.zeros(1, 64, 2, 128, dtype=torch.bfloat16, device="cuda")
+    g = torch.zeros(1, 64, 2, 128, device="cuda")
+    beta = torch.zeros(1, 64, 2, device="cuda")
+    with pytest.raises(ValueError, match="k must be"):
+        kda.chunk_fwd(q, q.float(), q, g, beta)
+    with pytest.raises(ValueError, match="head dim"):
+        kda.chunk_fwd(q[..., :64].contiguous(), q[..., :64].contiguous(), q[..., :64].contiguous(),
+                      g[..., :64].contiguous(), beta)
+    with pytest.raises(ValueError, match="cu_seqlens must be an int32"):
+        kda.chunk_fwd(q, q, q, g, beta, torch.tensor([0, 64], device="cuda"))
