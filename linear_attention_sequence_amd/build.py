@@ -15,6 +15,8 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # packed fp32 VALU ops are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep small private arrays in registers (never moved into LDS)
+    "-mllvm", "-disable-promote-alloca-to-lds",
     "-I" + os.path.join(ROOT, "include"),
 ]
 

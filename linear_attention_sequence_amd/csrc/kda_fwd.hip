@@ -32,10 +32,15 @@
 // registers; its bf16 copy feeds the MFMAs.
 //
 // Decay factors inside a chunk can reach exp(+-64*5.5).  A and M are therefore
-// built from 16-token sub-blocks: for a diagonal sub-block both factors are
-// taken relative to the sub-block's 8th token (each factor <= exp(8|L|)); for
-// an off-diagonal pair (a > b) the left factor is exp(G_r - G_end(b)) <= 1
-// and the right exp(G_end(b) - G_i) <= 1.  With |L| <= 5.5 nothing overflows.
+// built from 16-token sub-blocks, with the decay split at G_end(b), the
+// cumulative decay at the last token of the column sub-block b: the right
+// factor exp(G_end(b) - G_i) is <= 1; the left factor exp(G_r - G_end(b)) is
+// <= 1 for an off-diagonal pair (a > b) and at most exp(15|L|) inside a
+// diagonal sub-block, where the masked upper triangle stays below
+// exp(15|L|) as well (sum_c |qh_c kh_c| <= 1).  With |L| <= 5.5 nothing
+// overflows fp32 or bf16.  Off-diagonal operands are all in [0, 1] and use
+// fp16 (11-bit mantissa, one MFMA); diagonal operands use the bf16 hi + lo
+// split.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -58,6 +63,8 @@ constexpr float L2_EPS = 1e-6f;
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -94,6 +101,15 @@ __device__ __forceinline__ int swap23(int m) {
     (LO) = (bf16)(x_ - (float)h_);     \
   } while (0)
 
+// lane i of each 16-lane row receives x from lane i - N of the same row (0 if none)
+template <int N>
+__device__ __forceinline__ float dpp_row_shr(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ f32x4 mfma16h(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -102,7 +118,8 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 }
 
 // ---------------------------------------------------------------------------
-// LDS layout of the main kernel (one chunk in flight)
+// LDS layout of the main kernel (one chunk in flight, ~122 KB: one workgroup
+// per CU)
 // ---------------------------------------------------------------------------
 struct alignas(16) Smem {
   bf16 Qt[CH][DK + 8];       // qh * e^G                      (A operand of Qt S)
@@ -110,20 +127,54 @@ struct alignas(16) Smem {
   bf16 KbT[DK][CH + 8];      // (kh * e^{G_c - G})^T          (A operand of the state update)
   bf16 Mhi[CH][CH + 8];      // M split into hi + lo
   bf16 Mlo[CH][CH + 8];
-  bf16 Tbhi[CH][CH + 8];     // Tb split into hi + lo
-  bf16 Tblo[CH][CH + 8];
   union {
-    bf16x8 R[3][4][2][64];   // right operands of off-diagonal sub-blocks, lane order
-    float A[CH][CH + 4];     // beta-scaled strictly lower A (fp32) for the solve
+    struct {
+      bf16 hi[CH][CH + 8];   // Tb split into hi + lo (written after the solve)
+      bf16 lo[CH][CH + 8];
+    } tb;
+    float A[CH][CH + 4];     // beta-scaled strictly lower A (fp32), input of the solve
   } u;
-  float T[CH][CH + 4];       // (I + A)^-1
-  float D[DK];               // e^{G_c}
+  union {
+    f16x8 R[3][4][64];       // right operands of off-diagonal sub-blocks (fp16), lane order
+    float T[CH][CH + 4];     // (I + A)^-1 (fp32)
+    struct {
+      union {
+        unsigned short vt[32][CH + 8];  // this chunk's V, transposed (its 32 columns)
+        unsigned short o[CH][32];       // then the bf16 O rows of those columns
+      };
+    } ws[4];                 // per-wave staging slices
+  } u2;
+  float etab[10][DK];        // per-channel decay factors of the chunk (see fill_tables)
   float tot[4][DK];          // per sub-block total decay
   float beta[CH];
-  float Y[4][16][17];        // per-wave scratch of the block solve
   int unit;
   int gate_bad;
 };
+
+// Store the 16x16 block (a, b) of M (lower incl., split hi + lo) and of A
+// (beta-scaled, strictly lower, fp32).  C layout of a 16x16 MFMA tile: lane l
+// holds column l % 16 and rows 4 (l / 16) + 0..3.  beta_mine is beta of the
+// token this lane holds in the prologue layout (token r = l % 16 of block a).
+__device__ __forceinline__ void store_block(Smem& sm, const f32x4& accM, const f32x4& accA,
+                                            int a, int b, int l, bool diag, float beta_mine) {
+  const int col = l & 15;
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) {
+    const int row = 4 * (l >> 4) + qq;
+    const int R = 16 * a + row, C = 16 * b + col;
+    float mm = accM[qq], aa = accA[qq];
+    if (diag) {
+      if (col > row) mm = 0.f;
+      if (col >= row) aa = 0.f;
+    }
+    aa *= __shfl(beta_mine, row);
+    sm.u.A[R][C] = aa;
+    bf16 hi, lo;
+    SPLIT_BF16(mm, hi, lo);
+    sm.Mhi[R][C] = hi;
+    sm.Mlo[R][C] = lo;
+  }
+}
 
 // ---------------------------------------------------------------------------
 // scheduler: validate cu_seqlens, emit non-empty documents longest first
@@ -273,6 +324,66 @@ __device__ __forceinline__ void load_raw(RawChunk& rc, const bf16* __restrict__ 
   }
 }
 
+// V of one chunk, the 32 value columns of wave w: load i, lane l holds 16 bytes
+// of row 16 i + l / 4 (columns 32 w + 8 (l % 4) ..).  Rows past the end re-read
+// the last valid row; they are zeroed when used.
+struct VChunk {
+  uint4 r[4];
+};
+
+__device__ __forceinline__ VChunk load_v(const bf16* __restrict__ v, int64_t c0, int n, int H,
+                                         int h, int w, int l) {
+  VChunk vc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = min(16 * i + (l >> 2), n - 1);
+    vc.r[i] = *reinterpret_cast<const uint4*>(v + ((size_t)(c0 + row) * H + h) * DV + 32 * w + 8 * (l & 3));
+  }
+  return vc;
+}
+
+// lane i of each 16-lane row receives lane N of the same row
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + N, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ f32x4 mfma16k16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// Per-channel decay factors of a chunk from the sub-block totals t_w:
+//   rows 0..3: e^{P_1} .. e^{P_4}   (P_a = t_0 + ... + t_{a-1}; row 3 = e^{G_c} = D)
+//   rows 4..6: e^{P_4 - P_a}, a = 1..3
+//   rows 7..9: e^{t_1}, e^{t_2}, e^{t_1 + t_2}  (left factors of the pairs (2,0), (3,1), (3,0))
+__device__ __forceinline__ void fill_tables(Smem& sm, int tid) {
+#pragma unroll
+  for (int e = tid; e < 10 * DK; e += NTHR) {
+    const int row = e >> 7, c = e & (DK - 1);
+    const float t0 = sm.tot[0][c], t1 = sm.tot[1][c], t2 = sm.tot[2][c], t3 = sm.tot[3][c];
+    float x;
+    switch (row) {
+      case 0: x = t0; break;
+      case 1: x = t0 + t1; break;
+      case 2: x = (t0 + t1) + t2; break;
+      case 3: x = ((t0 + t1) + t2) + t3; break;
+      case 4: x = (t1 + t2) + t3; break;
+      case 5: x = t2 + t3; break;
+      case 6: x = t3; break;
+      case 7: x = t1; break;
+      case 8: x = t2; break;
+      default: x = t1 + t2; break;
+    }
+    sm.etab[row][c] = __expf(x);
+  }
+}
+
 __global__ __launch_bounds__(NTHR, 1) void kda_chunk_fwd_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, bf16* __restrict__ out,
@@ -280,12 +391,13 @@ __global__ __launch_bounds__(NTHR, 1) void kda_chunk_fwd_kernel(
     float gate_bound) {
   __shared__ Smem sm;
   const int tid = threadIdx.x;
-  const int w = tid >> 6;      // wave
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave (scalar)
   const int l = tid & 63;      // lane
   const int r = l & 15;        // prologue: token inside the 16-token sub-block
   const int cg = l >> 4;       // prologue: channel group (32 channels)
-  const int m = l & 31;        // recurrence: MFMA row / column lane index
-  const int hg = l >> 5;       // recurrence: lane half
+  const int m = l & 31;        // chain: MFMA row / column lane index
+  const int hg = l >> 5;       // chain: lane half
+  const int tok = 16 * w + r;  // prologue: token of this lane inside the chunk
   const float scale = 0.08838834764831845f;  // 128^-1/2
 
   if (hdr->status != 0) {
@@ -317,30 +429,22 @@ __global__ __launch_bounds__(NTHR, 1) void kda_chunk_fwd_kernel(
       for (int i = 0; i < 16; ++i) S[kt][i] = 0.f;
 
     RawChunk cur;
+    VChunk vcur;
     {
       const int n0 = (int)min<int64_t>(CH, eos - bos);
-      load_raw(cur, q, k, g, beta, bos + 16 * w + r, 16 * w + r < n0, H, h, cg);
+      load_raw(cur, q, k, g, beta, bos + tok, tok < n0, H, h, cg);
+      vcur = load_v(v, bos, n0, H, h, w, l);
     }
 
     for (int64_t c0 = bos; c0 < eos; c0 += CH) {
       const int n = (int)min<int64_t>(CH, eos - c0);
-      const int tok = 16 * w + r;
-
-      // ---- V of this chunk in the C layout of the X tiles (see swap23)
-      unsigned short vreg[2][16];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int t = 32 * mt + 16 * (i >> 3) + 8 * hg + (i & 7);
-          vreg[mt][i] = (t < n)
-              ? reinterpret_cast<const unsigned short*>(v)[((size_t)(c0 + t) * H + h) * DV + 32 * w + m]
-              : (unsigned short)0;
-        }
 
       // ================= prologue: l2 norm, cumulative decay =================
-      float qh[32], kh[32], loc[32];
+      // lane (w, r, cg): token 16w + r of the chunk, channels 32cg .. 32cg + 31
+      float qe[32], ke[32], kr[32];  // qh e^{G - P_w}, kh e^{G - P_w}, kh e^{G_end(w) - G}
+      const float beta_mine = cur.beta;
       {
+        float qh[32], kh[32], loc[32];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint32_t qa[4] = {cur.q[i].x, cur.q[i].y, cur.q[i].z, cur.q[i].w};
@@ -353,6 +457,18 @@ __global__ __launch_bounds__(NTHR, 1) void kda_chunk_fwd_kernel(
             kh[8 * i + 2 * j + 1] = bf16_hi_to_f32(ka[j]);
           }
         }
+        bool gbad = false;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float ga[4] = {cur.g[i].x, cur.g[i].y, cur.g[i].z, cur.g[i].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            loc[4 * i + j] = ga[j];
+            gbad |= !(ga[j] >= gate_bound && ga[j] <= 0.f);
+          }
+        }
+        if (gbad && tok < n) sm.gate_bad = 1;
+        if (cg == 0) sm.beta[tok] = cur.beta;
         float sq = 0.f, sk = 0.f;
 #pragma unroll
         for (int j = 0; j < 32; ++j) { sq += qh[j] * qh[j]; sk += kh[j] * kh[j]; }
@@ -364,26 +480,15 @@ __global__ __launch_bounds__(NTHR, 1) void kda_chunk_fwd_kernel(
         const float rk = 1.0f / sqrtf(sk + L2_EPS);
 #pragma unroll
         for (int j = 0; j < 32; ++j) { qh[j] *= rq; kh[j] *= rk; }
-
-        bool gbad = false;
+        // inclusive scan over the 16 tokens of the sub-block (one 16-lane row)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float ga[4] = {cur.g[i].x, cur.g[i].y, cur.g[i].z, cur.g[i].w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            loc[4 * i + j] = ga[j];
-            gbad |= !(ga[j] >= gate_bound && ga[j] <= 0.f) && (tok < n);
-          }
-        }
-        if (gbad) sm.gate_bad = 1;
-        // inclusive scan over the 16 tokens of the sub-block (one DPP row)
-#pragma unroll
-        for (int d = 1; d < 16; d <<= 1) {
-#pragma unroll
-          for (int j = 0; j < 32; ++j) {
-            const float y = __shfl_up(loc[j], d, 16);
-            loc[j] += (r >= d) ? y : 0.f;
-          }
+        for (int j = 0; j < 32; ++j) {
+          float x = loc[j];
+          x += dpp_row_shr<1>(x);
+          x += dpp_row_shr<2>(x);
+          x += dpp_row_shr<4>(x);
+          x += dpp_row_shr<8>(x);
+          loc[j] = x;
         }
         if (r == 15) {
 #pragma unroll
@@ -391,237 +496,253 @@ __global__ __launch_bounds__(NTHR, 1) void kda_chunk_fwd_kernel(
             *reinterpret_cast<float4*>(&sm.tot[w][32 * cg + j]) =
                 make_float4(loc[j], loc[j + 1], loc[j + 2], loc[j + 3]);
         }
-        if (cg == 0) sm.beta[tok] = cur.beta;
-      }
-      __syncthreads();  // tot, beta visible
 
-      // next chunk's raw inputs: issue the loads now, consume next iteration
-      {
-        const int64_t c1 = c0 + CH;
-        const int n1 = (int)min<int64_t>(CH, eos - c1);
-        load_raw(cur, q, k, g, beta, c1 + tok, c1 < eos && tok < n1, H, h, cg);
-      }
-
-      // ---- prefix decays, operand tiles of the chain, right operands of A / M
-      float ref[32];
-      {
-        float P[32], P4[32];
+        // diagonal block (w, w) of A and M, decay split at the sub-block's last
+        // token: right kh_i e^{G_end - G_i} <= 1, left x_r e^{G_r - G_end} >= 1
+        f32x4 accM = {0.f, 0.f, 0.f, 0.f}, accA = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 32; j += 4) {
-          float4 p = make_float4(0.f, 0.f, 0.f, 0.f), a = p;
-#pragma unroll
-          for (int ww = 0; ww < 4; ++ww) {
-            const float4 t4 = *reinterpret_cast<const float4*>(&sm.tot[ww][32 * cg + j]);
-            if (ww < w) { p.x += t4.x; p.y += t4.y; p.z += t4.z; p.w += t4.w; }
-            a.x += t4.x; a.y += t4.y; a.z += t4.z; a.w += t4.w;
-          }
-          P[j] = p.x; P[j + 1] = p.y; P[j + 2] = p.z; P[j + 3] = p.w;
-          P4[j] = a.x; P4[j + 1] = a.y; P4[j + 2] = a.z; P4[j + 3] = a.w;
-        }
-#pragma unroll
-        for (int j0 = 0; j0 < 32; j0 += 8) {
-          bf16x8 qt, kt;
+        for (int s = 0; s < 4; ++s) {
+          bf16x8 lqh, lql, lkh, lkl, rh, rl;
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            const float G = P[j0 + j] + loc[j0 + j];
-            const float e = __expf(G);
-            qt[j] = (bf16)(qh[j0 + j] * e);
-            kt[j] = (bf16)(-kh[j0 + j] * e);
-            sm.KbT[32 * cg + j0 + j][tok] = (bf16)(kh[j0 + j] * __expf(P4[j0 + j] - G));
+            const int jj = 8 * s + j;
+            const float tw = row_bcast<15>(loc[jj]);
+            const float ert = __expf(tw - loc[jj]);    // e^{G_end - G_r} <= 1
+            const float elt = __builtin_amdgcn_rcpf(ert);  // e^{G_r - G_end} >= 1 (v_rcp_f32)
+            const float eg = __expf(loc[jj]);          // e^{G_r - P_w} <= 1
+            kr[jj] = kh[jj] * ert;
+            qe[jj] = qh[jj] * eg;
+            ke[jj] = kh[jj] * eg;
+            SPLIT_BF16(qh[jj] * elt, lqh[j], lql[j]);
+            SPLIT_BF16(kh[jj] * elt, lkh[j], lkl[j]);
+            SPLIT_BF16(kr[jj], rh[j], rl[j]);
           }
-          *reinterpret_cast<bf16x8*>(&sm.Qt[tok][32 * cg + j0]) = qt;
-          *reinterpret_cast<bf16x8*>(&sm.Kt[tok][32 * cg + j0]) = kt;
+          accM = mfma16(lqh, rh, accM);
+          accM = mfma16(lql, rh, accM);
+          accM = mfma16(lqh, rl, accM);
+          accA = mfma16(lkh, rh, accA);
+          accA = mfma16(lkl, rh, accA);
+          accA = mfma16(lkh, rl, accA);
         }
-        if (w == 0 && r == 0) {
-#pragma unroll
-          for (int j = 0; j < 32; ++j) sm.D[32 * cg + j] = __expf(P4[j]);
-        }
-        // reference of the diagonal sub-block: G at its 8th token
-#pragma unroll
-        for (int j = 0; j < 32; ++j) ref[j] = __shfl(loc[j], (l & ~15) | 7);
-        if (w < 3) {
-          // kh_i * e^{G_end(w) - G_i} <= 1 (right operand of pairs (a > w, w))
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            bf16x8 hi, lo;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const int jj = 8 * s + j;
-              const float tw = __shfl(loc[jj], (l & ~15) | 15);
-              SPLIT_BF16(kh[jj] * __expf(tw - loc[jj]), hi[j], lo[j]);
-            }
-            sm.u.R[w][s][0][l] = hi;
-            sm.u.R[w][s][1][l] = lo;
-          }
-        }
-      }
-
-      // ================= intra-chunk A and M (16x16 sub-blocks) =================
-      // accMd / accAd: diagonal block (w, w); accMo[b] / accAo[b]: block (w, b), b < w
-      f32x4 accMd, accAd, accMo[4], accAo[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        accMd[i] = 0.f;
-        accAd[i] = 0.f;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) { accMo[b][i] = 0.f; accAo[b][i] = 0.f; }
-      }
-      // diagonal block (w, w) from registers
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        bf16x8 lqh, lql, lkh, lkl, rh, rl;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int jj = 8 * s + j;
-          const float el = __expf(loc[jj] - ref[jj]);
-          const float er = __expf(ref[jj] - loc[jj]);
-          SPLIT_BF16(qh[jj] * el, lqh[j], lql[j]);
-          SPLIT_BF16(kh[jj] * el, lkh[j], lkl[j]);
-          SPLIT_BF16(kh[jj] * er, rh[j], rl[j]);
-        }
-        accMd = mfma16(lqh, rh, accMd);
-        accMd = mfma16(lql, rh, accMd);
-        accMd = mfma16(lqh, rl, accMd);
-        accAd = mfma16(lkh, rh, accAd);
-        accAd = mfma16(lkl, rh, accAd);
-        accAd = mfma16(lkh, rl, accAd);
-      }
-      __syncthreads();  // right operands R visible
-      // off-diagonal blocks (w, b), b < w
-#pragma unroll
-      for (int b = 0; b < 3; ++b) {
-        if (b < w) {
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const bf16x8 rh = sm.u.R[b][s][0][l];
-            const bf16x8 rl = sm.u.R[b][s][1][l];
-            bf16x8 lqh, lql, lkh, lkl;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const int jj = 8 * s + j;
-              float e = loc[jj];  // G_r - P_w
-              for (int ww = b + 1; ww < w; ++ww) e += sm.tot[ww][32 * cg + jj];
-              const float f = __expf(e);   // e^{G_r - G_end(b)} <= 1
-              SPLIT_BF16(qh[jj] * f, lqh[j], lql[j]);
-              SPLIT_BF16(kh[jj] * f, lkh[j], lkl[j]);
-            }
-            accMo[b] = mfma16(lqh, rh, accMo[b]);
-            accMo[b] = mfma16(lql, rh, accMo[b]);
-            accMo[b] = mfma16(lqh, rl, accMo[b]);
-            accAo[b] = mfma16(lkh, rh, accAo[b]);
-            accAo[b] = mfma16(lkl, rh, accAo[b]);
-            accAo[b] = mfma16(lkh, rl, accAo[b]);
-          }
-        }
-      }
-      __syncthreads();  // all reads of R done (A aliases R)
-      // write A (beta-scaled, strictly lower) and M (lower incl.) of row block w
-      {
-        const int col = l & 15;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
+        store_block(sm, accM, accA, w, w, l, true, beta_mine);
+        // blocks above the diagonal are read by the chain's MFMAs: zero them
+        const bf16 z = (bf16)0.f;
+#pragma unroll 1
+        for (int bb = w + 1; bb < 4; ++bb)
 #pragma unroll
           for (int qq = 0; qq < 4; ++qq) {
-            const int row = 4 * (l >> 4) + qq;
-            const int R = 16 * w + row, C = 16 * b + col;
-            float a = 0.f, mm = 0.f;
-            if (b < w) {
-              a = accAo[b][qq];
-              mm = accMo[b][qq];
-            } else if (b == w) {
-              a = (col < row) ? accAd[qq] : 0.f;
-              mm = (col <= row) ? accMd[qq] : 0.f;
-            }
-            a *= sm.beta[R];
-            sm.u.A[R][C] = a;
-            bf16 hi, lo;
-            SPLIT_BF16(mm, hi, lo);
-            sm.Mhi[R][C] = hi;
-            sm.Mlo[R][C] = lo;
+            sm.Mhi[16 * w + 4 * (l >> 4) + qq][16 * bb + (l & 15)] = z;
+            sm.Mlo[16 * w + 4 * (l >> 4) + qq][16 * bb + (l & 15)] = z;
+          }
+        if (w < 3) {
+          // right operand of the pairs (a > w, w): kh_i e^{G_end(w) - G_i} <= 1
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            f16x8 rv;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) rv[j] = (_Float16)kr[8 * s + j];
+            sm.u2.R[w][s][l] = rv;
           }
         }
       }
-      __syncthreads();
+      __syncthreads();  // B1: tot, beta, R, diagonal A / M visible
+      fill_tables(sm, tid);
+      __syncthreads();  // B2: decay tables visible
 
-      // ================= (I + A)^-1 by 16x16 blocks =================
+      // ---- operand tiles of the chain
+#pragma unroll
+      for (int j0 = 0; j0 < 32; j0 += 8) {
+        float fq[8], fk[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) { fq[j] = 1.f; fk[j] = 1.f; }
+        if (w > 0) {  // e^{P_w}
+          const float4 a = *reinterpret_cast<const float4*>(&sm.etab[w - 1][32 * cg + j0]);
+          const float4 b = *reinterpret_cast<const float4*>(&sm.etab[w - 1][32 * cg + j0 + 4]);
+          fq[0] = a.x; fq[1] = a.y; fq[2] = a.z; fq[3] = a.w;
+          fq[4] = b.x; fq[5] = b.y; fq[6] = b.z; fq[7] = b.w;
+        }
+        if (w < 3) {  // e^{P_4 - P_{w+1}}
+          const float4 a = *reinterpret_cast<const float4*>(&sm.etab[4 + w][32 * cg + j0]);
+          const float4 b = *reinterpret_cast<const float4*>(&sm.etab[4 + w][32 * cg + j0 + 4]);
+          fk[0] = a.x; fk[1] = a.y; fk[2] = a.z; fk[3] = a.w;
+          fk[4] = b.x; fk[5] = b.y; fk[6] = b.z; fk[7] = b.w;
+        }
+        bf16x8 qt, kt;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          qt[j] = (bf16)(qe[j0 + j] * fq[j]);
+          kt[j] = (bf16)(-ke[j0 + j] * fq[j]);
+          sm.KbT[32 * cg + j0 + j][tok] = (bf16)(kr[j0 + j] * fk[j]);
+        }
+        *reinterpret_cast<bf16x8*>(&sm.Qt[tok][32 * cg + j0]) = qt;
+        *reinterpret_cast<bf16x8*>(&sm.Kt[tok][32 * cg + j0]) = kt;
+      }
+
+      // ---- off-diagonal blocks (w, b), b < w: left factor e^{G_r - G_end(b)} <= 1
+#pragma unroll 1
+      for (int b = 0; b < w; ++b) {
+        const int frow = (b == w - 1) ? -1 : (w == 2 ? 7 : (b == 1 ? 8 : 9));
+        f32x4 accM = {0.f, 0.f, 0.f, 0.f}, accA = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const f16x8 rv = sm.u2.R[b][s][l];
+          float f[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) f[j] = 1.f;
+          if (frow >= 0) {
+            const float4 a = *reinterpret_cast<const float4*>(&sm.etab[frow][32 * cg + 8 * s]);
+            const float4 c = *reinterpret_cast<const float4*>(&sm.etab[frow][32 * cg + 8 * s + 4]);
+            f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+            f[4] = c.x; f[5] = c.y; f[6] = c.z; f[7] = c.w;
+          }
+          f16x8 lq, lk;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            lq[j] = (_Float16)(qe[8 * s + j] * f[j]);
+            lk[j] = (_Float16)(ke[8 * s + j] * f[j]);
+          }
+          accM = mfma16h(lq, rv, accM);
+          accA = mfma16h(lk, rv, accA);
+        }
+        store_block(sm, accM, accA, w, b, l, false, beta_mine);
+      }
+      __syncthreads();  // B3: A and M complete, R dead
+
+      // ================= T = (I + A)^-1 by 16x16 blocks =================
+      // diagonal blocks: forward substitution, lane j < 16 of wave w owns column j
       if (l < 16) {
         const int j = l;
+        float a4[16][16];
+#pragma unroll
+        for (int rr = 1; rr < 16; ++rr)
+#pragma unroll
+          for (int i0 = 0; i0 < rr; i0 += 4) {
+            const float4 av = *reinterpret_cast<const float4*>(&sm.u.A[16 * w + rr][16 * w + i0]);
+            a4[rr][i0] = av.x; a4[rr][i0 + 1] = av.y; a4[rr][i0 + 2] = av.z; a4[rr][i0 + 3] = av.w;
+          }
         float x[16];
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
           float acc = (rr == j) ? 1.f : 0.f;
 #pragma unroll
-          for (int i = 0; i < rr; ++i) acc -= sm.u.A[16 * w + rr][16 * w + i] * x[i];
+          for (int i = 0; i < rr; ++i) acc -= a4[rr][i] * x[i];
           x[rr] = acc;
         }
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
+        for (int rr = 0; rr < 16; ++rr) sm.u2.T[16 * w + rr][16 * w + j] = x[rr];
+#pragma unroll 1
+        for (int bb = w + 1; bb < 4; ++bb)
 #pragma unroll
-          for (int b = 0; b < 4; ++b)
-            sm.T[16 * w + rr][16 * b + j] = (b == w) ? x[rr] : 0.f;
-        }
+          for (int rr = 0; rr < 16; ++rr) sm.u2.T[16 * w + rr][16 * bb + j] = 0.f;
       }
-      __syncthreads();
-#pragma unroll
-      for (int dlev = 1; dlev < 4; ++dlev) {
-        const int a = w, b = w - dlev;
-        const int j = l & 15, gq = l >> 4;
-        if (b >= 0) {
-          float y[4] = {0.f, 0.f, 0.f, 0.f};
+      __syncthreads();  // B4: diagonal blocks of T visible
+      // off-diagonal blocks: wave b walks column block b downwards,
+      // T_ab = -T_aa sum_{k=b}^{a-1} A_ak T_kb, on 16x16x16 MFMAs with hi + lo operands
+      if (w < 3) {
+        const int b = w;
+        const int c = l & 15, g4 = 4 * (l >> 4);
+#pragma unroll 1
+        for (int a = b + 1; a < 4; ++a) {
+          f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
           for (int kb = b; kb < a; ++kb) {
+            const float4 av = *reinterpret_cast<const float4*>(&sm.u.A[16 * a + c][16 * kb + g4]);
+            const float tv[4] = {sm.u2.T[16 * kb + g4][16 * b + c], sm.u2.T[16 * kb + g4 + 1][16 * b + c],
+                                 sm.u2.T[16 * kb + g4 + 2][16 * b + c], sm.u2.T[16 * kb + g4 + 3][16 * b + c]};
+            const float aa[4] = {av.x, av.y, av.z, av.w};
+            bf16x4 ah, al, bh, bl;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const float tv = sm.T[16 * kb + i][16 * b + j];
-#pragma unroll
-              for (int qq = 0; qq < 4; ++qq) y[qq] += sm.u.A[16 * a + 4 * gq + qq][16 * kb + i] * tv;
+            for (int i = 0; i < 4; ++i) {
+              SPLIT_BF16(aa[i], ah[i], al[i]);
+              SPLIT_BF16(tv[i], bh[i], bl[i]);
             }
+            Y = mfma16k16(ah, bh, Y);
+            Y = mfma16k16(al, bh, Y);
+            Y = mfma16k16(ah, bl, Y);
           }
+          const float4 tv4 = *reinterpret_cast<const float4*>(&sm.u2.T[16 * a + c][16 * a + g4]);
+          const float ta[4] = {tv4.x, tv4.y, tv4.z, tv4.w};
+          bf16x4 th, tl, yh, yl;
 #pragma unroll
-          for (int qq = 0; qq < 4; ++qq) sm.Y[w][4 * gq + qq][j] = y[qq];
-        }
-        __syncthreads();
-        if (b >= 0) {
-          float t[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float yv = sm.Y[w][i][j];
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) t[qq] -= sm.T[16 * a + 4 * gq + qq][16 * a + i] * yv;
+          for (int i = 0; i < 4; ++i) {
+            SPLIT_BF16(ta[i], th[i], tl[i]);
+            SPLIT_BF16(Y[i], yh[i], yl[i]);
           }
+          f32x4 Z = {0.f, 0.f, 0.f, 0.f};
+          Z = mfma16k16(th, yh, Z);
+          Z = mfma16k16(tl, yh, Z);
+          Z = mfma16k16(th, yl, Z);
 #pragma unroll
-          for (int qq = 0; qq < 4; ++qq) sm.T[16 * a + 4 * gq + qq][16 * b + j] = t[qq];
+          for (int i = 0; i < 4; ++i) sm.u2.T[16 * a + g4 + i][16 * b + c] = -Z[i];
         }
-        __syncthreads();
       }
-      // Tb = T Diag(beta), split into hi + lo
-      for (int e = tid; e < CH * CH; e += NTHR) {
-        const int rr = e >> 6, cc = e & 63;
+      __syncthreads();  // B5: T complete
+      // Tb = T Diag(beta), split into hi + lo (overwrites A)
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int rr = 4 * it + (tid >> 6), cc = tid & 63;
         bf16 hi, lo;
-        SPLIT_BF16(sm.T[rr][cc] * sm.beta[cc], hi, lo);
-        sm.Tbhi[rr][cc] = hi;
-        sm.Tblo[rr][cc] = lo;
+        SPLIT_BF16(sm.u2.T[rr][cc] * sm.beta[cc], hi, lo);
+        sm.u.tb.hi[rr][cc] = hi;
+        sm.u.tb.lo[rr][cc] = lo;
       }
-      __syncthreads();
+      __syncthreads();  // B6: Tb visible, T dead (its space stages O)
 
       // ================= the chain: X, U, O, S (wave w owns V columns 32w..) ====
       {
+        // this chunk's V, transposed into the wave's staging slice (rows past
+        // the end are zero)
+        unsigned short (*vt)[CH + 8] = sm.u2.ws[w].vt;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * i + (l >> 2);
+          const uint4 u = (t < n) ? vcur.r[i] : make_uint4(0, 0, 0, 0);
+          const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            vt[8 * (l & 3) + 2 * j][t] = (unsigned short)(uu[j] & 0xFFFFu);
+            vt[8 * (l & 3) + 2 * j + 1][t] = (unsigned short)(uu[j] >> 16);
+          }
+        }
+        wave_sync_lds();
         const int rowsel = swap23(m);
+        f32x16 X[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const uint4 u = *reinterpret_cast<const uint4*>(&vt[m][32 * mt + 16 * hh + 8 * hg]);
+            const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              X[mt][8 * hh + 2 * j] = bf16_lo_to_f32(uu[j]);
+              X[mt][8 * hh + 2 * j + 1] = bf16_hi_to_f32(uu[j]);
+            }
+          }
+        wave_sync_lds();  // V read out before the slice stages O
+
         bf16x8 Sb[8];
 #pragma unroll
         for (int s = 0; s < 8; ++s)
 #pragma unroll
           for (int j = 0; j < 8; ++j) Sb[s][j] = (bf16)S[s >> 1][8 * (s & 1) + j];
 
-        // X = V - kh e^G S
-        f32x16 X[2];
+        // X = V - kh e^G S (A operands loaded two k-steps ahead)
+        {
+          bf16x8 ka[2][2];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
+          for (int s = 0; s < 2; ++s)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) X[mt][i] = __uint_as_float((uint32_t)vreg[mt][i] << 16);
+            for (int mt = 0; mt < 2; ++mt)
+              ka[mt][s] = *reinterpret_cast<const bf16x8*>(&sm.Kt[32 * mt + rowsel][16 * s + 8 * hg]);
 #pragma unroll
           for (int s = 0; s < 8; ++s) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.Kt[32 * mt + rowsel][16 * s + 8 * hg]);
-            X[mt] = mfma32(a, Sb[s], X[mt]);
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+              X[mt] = mfma32(ka[mt][s & 1], Sb[s], X[mt]);
+              if (s + 2 < 8)
+                ka[mt][s & 1] = *reinterpret_cast<const bf16x8*>(&sm.Kt[32 * mt + rowsel][16 * (s + 2) + 8 * hg]);
+            }
           }
         }
         bf16x8 Xb[4];
@@ -630,20 +751,25 @@ __global__ __launch_bounds__(NTHR, 1) void kda_chunk_fwd_kernel(
 #pragma unroll
           for (int j = 0; j < 8; ++j) Xb[s][j] = (bf16)X[s >> 1][8 * (s & 1) + j];
 
-        // U = Tb X
+        // U = Tb X: the six lower-triangular (row tile, k-step) pairs
+        constexpr int PMT[6] = {0, 0, 1, 1, 1, 1};
+        constexpr int PS[6] = {0, 1, 0, 1, 2, 3};
         f32x16 U[2];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int i = 0; i < 16; ++i) U[mt][i] = 0.f;
+        {
+          bf16x8 th[6], tl[6];
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            if (s < 2 * (mt + 1)) {
-              const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&sm.Tbhi[32 * mt + rowsel][16 * s + 8 * hg]);
-              const bf16x8 al = *reinterpret_cast<const bf16x8*>(&sm.Tblo[32 * mt + rowsel][16 * s + 8 * hg]);
-              U[mt] = mfma32(ah, Xb[s], U[mt]);
-              U[mt] = mfma32(al, Xb[s], U[mt]);
-            }
+          for (int p = 0; p < 6; ++p) {
+            th[p] = *reinterpret_cast<const bf16x8*>(&sm.u.tb.hi[32 * PMT[p] + rowsel][16 * PS[p] + 8 * hg]);
+            tl[p] = *reinterpret_cast<const bf16x8*>(&sm.u.tb.lo[32 * PMT[p] + rowsel][16 * PS[p] + 8 * hg]);
+          }
+#pragma unroll
+          for (int p = 0; p < 6; ++p) {
+            U[PMT[p]] = mfma32(th[p], Xb[PS[p]], U[PMT[p]]);
+            U[PMT[p]] = mfma32(tl[p], Xb[PS[p]], U[PMT[p]]);
           }
         }
         bf16x8 Ubh[4], Ubl[4];
@@ -652,45 +778,92 @@ __global__ __launch_bounds__(NTHR, 1) void kda_chunk_fwd_kernel(
 #pragma unroll
           for (int j = 0; j < 8; ++j) SPLIT_BF16(U[s >> 1][8 * (s & 1) + j], Ubh[s][j], Ubl[s][j]);
 
-        // O = scale (qh e^G S + M U)
+        // the next chunk's inputs land during the rest of this chunk and the
+        // next chunk's prologue
+        {
+          const int64_t c1 = c0 + CH;
+          const int n1 = (int)min<int64_t>(CH, eos - c1);
+          load_raw(cur, q, k, g, beta, c1 + tok, c1 < eos && tok < n1, H, h, cg);
+          if (c1 < eos) vcur = load_v(v, c1, n1, H, h, w, l);
+        }
+
+        // O = scale (qh e^G S + M U), staged through LDS for 16-byte stores
+        unsigned short (*ost)[32] = sm.u2.ws[w].o;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
           f32x16 O;
 #pragma unroll
           for (int i = 0; i < 16; ++i) O[i] = 0.f;
+          {
+            bf16x8 qa[2];
+            qa[0] = *reinterpret_cast<const bf16x8*>(&sm.Qt[32 * mt + rowsel][8 * hg]);
+            qa[1] = *reinterpret_cast<const bf16x8*>(&sm.Qt[32 * mt + rowsel][16 + 8 * hg]);
 #pragma unroll
-          for (int s = 0; s < 8; ++s) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.Qt[32 * mt + rowsel][16 * s + 8 * hg]);
-            O = mfma32(a, Sb[s], O);
+            for (int s = 0; s < 8; ++s) {
+              O = mfma32(qa[s & 1], Sb[s], O);
+              if (s + 2 < 8) qa[s & 1] = *reinterpret_cast<const bf16x8*>(&sm.Qt[32 * mt + rowsel][16 * (s + 2) + 8 * hg]);
+            }
           }
+          {
+            bf16x8 mh[4], ml[4];
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            if (s < 2 * (mt + 1)) {
-              const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&sm.Mhi[32 * mt + rowsel][16 * s + 8 * hg]);
-              const bf16x8 al = *reinterpret_cast<const bf16x8*>(&sm.Mlo[32 * mt + rowsel][16 * s + 8 * hg]);
-              O = mfma32(ah, Ubh[s], O);
-              O = mfma32(al, Ubh[s], O);
-              O = mfma32(ah, Ubl[s], O);
+            for (int s = 0; s < 4; ++s) {
+              if (s < 2 * (mt + 1)) {
+                mh[s] = *reinterpret_cast<const bf16x8*>(&sm.Mhi[32 * mt + rowsel][16 * s + 8 * hg]);
+                ml[s] = *reinterpret_cast<const bf16x8*>(&sm.Mlo[32 * mt + rowsel][16 * s + 8 * hg]);
+              }
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              if (s < 2 * (mt + 1)) {
+                O = mfma32(mh[s], Ubh[s], O);
+                O = mfma32(ml[s], Ubh[s], O);
+                O = mfma32(mh[s], Ubl[s], O);
+              }
             }
           }
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int t = 32 * mt + 16 * (i >> 3) + 8 * hg + (i & 7);
-            if (t < n) out[((size_t)(c0 + t) * H + h) * DV + 32 * w + m] = (bf16)(O[i] * scale);
+            const bf16 ob = (bf16)(O[i] * scale);
+            ost[t][m] = __builtin_bit_cast(unsigned short, ob);
           }
         }
 
         // S <- e^{G_c} S + (kh e^{G_c - G})^T U
+        {
+          bf16x8 kb[2];
+          kb[0] = *reinterpret_cast<const bf16x8*>(&sm.KbT[rowsel][8 * hg]);
+          kb[1] = *reinterpret_cast<const bf16x8*>(&sm.KbT[rowsel][16 + 8 * hg]);
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
+          for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            S[kt][i] *= sm.D[32 * kt + 16 * (i >> 3) + 8 * hg + (i & 7)];
+            for (int i0 = 0; i0 < 16; i0 += 8) {
+              const float* dp = &sm.etab[3][32 * kt + 16 * (i0 >> 3) + 8 * hg];
+              const float4 d0 = *reinterpret_cast<const float4*>(dp);
+              const float4 d1 = *reinterpret_cast<const float4*>(dp + 4);
+              S[kt][i0 + 0] *= d0.x; S[kt][i0 + 1] *= d0.y; S[kt][i0 + 2] *= d0.z; S[kt][i0 + 3] *= d0.w;
+              S[kt][i0 + 4] *= d1.x; S[kt][i0 + 5] *= d1.y; S[kt][i0 + 6] *= d1.z; S[kt][i0 + 7] *= d1.w;
+            }
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.KbT[32 * kt + rowsel][16 * s + 8 * hg]);
-            S[kt] = mfma32(a, Ubh[s], S[kt]);
+            for (int s = 0; s < 4; ++s) {
+              const int idx = 4 * kt + s;
+              S[kt] = mfma32(kb[idx & 1], Ubh[s], S[kt]);
+              const int nx = idx + 2;
+              if (nx < 16)
+                kb[idx & 1] = *reinterpret_cast<const bf16x8*>(&sm.KbT[32 * (nx >> 2) + rowsel][16 * (nx & 3) + 8 * hg]);
+            }
           }
+        }
+
+        // O rows: lane l writes 16 bytes of row 16 it + l / 4
+        wave_sync_lds();
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int t = 16 * it + (l >> 2);
+          const uint4 val = *reinterpret_cast<const uint4*>(&ost[t][8 * (l & 3)]);
+          if (t < n)
+            *reinterpret_cast<uint4*>(out + ((size_t)(c0 + t) * H + h) * DV + 32 * w + 8 * (l & 3)) = val;
         }
       }
       __syncthreads();  // the next chunk overwrites every LDS tile
