@@ -107,6 +107,9 @@ __device__ __forceinline__ float dpp_row_shr(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xF, 0xF, false));
 }
 
+__device__ __forceinline__ f32x4 mfma16f(float a, float b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 __device__ __forceinline__ f32x4 mfma16h(const f16x8& a, const f16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -144,8 +147,8 @@ struct alignas(16) Smem {
       };
     } ws[4];                 // per-wave staging slices
   } u2;
-  float etab[10][DK];        // per-channel decay factors of the chunk (see fill_tables)
-  float tot[4][DK];          // per sub-block total decay
+  float etab[13][DK];        // per-channel decay factors of the chunk (see fill_tables)
+  float tot[4][DK];          // per sub-block total decay (log2 domain)
   float beta[CH];
   int unit;
   int gate_bad;
@@ -295,9 +298,9 @@ __global__ __launch_bounds__(SCHED_THREADS) void kda_schedule_kernel(
 // main kernel
 // ---------------------------------------------------------------------------
 struct RawChunk {
-  uint4 q[4];    // 32 bf16 channels of one token
+  uint4 q[4];    // 32 bf16 channels of one token (element 8 s + j = channel 32 s + 8 cg + j)
   uint4 k[4];
-  float4 g[8];   // 32 fp32 channels
+  float4 g[8];   // the same 32 channels, fp32
   float beta;
 };
 
@@ -306,14 +309,16 @@ __device__ __forceinline__ void load_raw(RawChunk& rc, const bf16* __restrict__ 
                                          const float* __restrict__ beta, int64_t tok_global,
                                          bool valid, int H, int h, int cg) {
   if (valid) {
-    const size_t off = ((size_t)tok_global * H + h) * DK + 32 * cg;
-    const uint4* qp = reinterpret_cast<const uint4*>(q + off);
-    const uint4* kp = reinterpret_cast<const uint4*>(k + off);
-    const float4* gp = reinterpret_cast<const float4*>(g + off);
+    // element 8 s + j of this lane is channel 32 s + 8 cg + j: the four lanes of
+    // a token read one contiguous 64-byte (q, k) or 128-byte (g) span per load
+    const size_t off = ((size_t)tok_global * H + h) * DK + 8 * cg;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { rc.q[i] = qp[i]; rc.k[i] = kp[i]; }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) rc.g[i] = gp[i];
+    for (int i = 0; i < 4; ++i) {
+      rc.q[i] = *reinterpret_cast<const uint4*>(q + off + 32 * i);
+      rc.k[i] = *reinterpret_cast<const uint4*>(k + off + 32 * i);
+      rc.g[2 * i] = *reinterpret_cast<const float4*>(g + off + 32 * i);
+      rc.g[2 * i + 1] = *reinterpret_cast<const float4*>(g + off + 32 * i + 4);
+    }
     rc.beta = beta[(size_t)tok_global * H + h];
   } else {
 #pragma unroll
@@ -358,13 +363,15 @@ __device__ __forceinline__ f32x4 mfma16k16(const bf16x4& a, const bf16x4& b, con
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
-// Per-channel decay factors of a chunk from the sub-block totals t_w:
-//   rows 0..3: e^{P_1} .. e^{P_4}   (P_a = t_0 + ... + t_{a-1}; row 3 = e^{G_c} = D)
-//   rows 4..6: e^{P_4 - P_a}, a = 1..3
-//   rows 7..9: e^{t_1}, e^{t_2}, e^{t_1 + t_2}  (left factors of the pairs (2,0), (3,1), (3,0))
+// Per-channel decay factors of a chunk from the sub-block totals t_w (log2
+// domain, so every factor is a bare exp2):
+//   rows 0..3:  e^{G_end(w)}          = 2^{t_0 + .. + t_w}      (row 3 = e^{G_c} = D)
+//   rows 4..6:  e^{G_c - G_end(w)}    = 2^{t_{w+1} + .. + t_3}, w = 0..2
+//   rows 7..12: e^{G_end(w) - G_end(b)} = 2^{t_{b+1} + .. + t_w}, pair (w, b), b < w,
+//               at row 7 + w (w - 1) / 2 + b
 __device__ __forceinline__ void fill_tables(Smem& sm, int tid) {
 #pragma unroll
-  for (int e = tid; e < 10 * DK; e += NTHR) {
+  for (int e = tid; e < 13 * DK; e += NTHR) {
     const int row = e >> 7, c = e & (DK - 1);
     const float t0 = sm.tot[0][c], t1 = sm.tot[1][c], t2 = sm.tot[2][c], t3 = sm.tot[3][c];
     float x;
@@ -376,11 +383,14 @@ __device__ __forceinline__ void fill_tables(Smem& sm, int tid) {
       case 4: x = (t1 + t2) + t3; break;
       case 5: x = t2 + t3; break;
       case 6: x = t3; break;
-      case 7: x = t1; break;
-      case 8: x = t2; break;
-      default: x = t1 + t2; break;
+      case 7: x = t1; break;         // (1, 0)
+      case 8: x = t1 + t2; break;    // (2, 0)
+      case 9: x = t2; break;         // (2, 1)
+      case 10: x = (t1 + t2) + t3; break;  // (3, 0)
+      case 11: x = t2 + t3; break;   // (3, 1)
+      default: x = t3; break;        // (3, 2)
     }
-    sm.etab[row][c] = __expf(x);
+    sm.etab[row][c] = __builtin_amdgcn_exp2f(x);
   }
 }
 
@@ -440,11 +450,14 @@ __global__ __launch_bounds__(NTHR, 1) void kda_chunk_fwd_kernel(
       const int n = (int)min<int64_t>(CH, eos - c0);
 
       // ================= prologue: l2 norm, cumulative decay =================
-      // lane (w, r, cg): token 16w + r of the chunk, channels 32cg .. 32cg + 31
-      float qe[32], ke[32], kr[32];  // qh e^{G - P_w}, kh e^{G - P_w}, kh e^{G_end(w) - G}
+      // lane (w, r, cg): token 16w + r of the chunk; element 8 s + j is channel
+      // 32 s + 8 cg + j (k-step s of the 16x16x32 MFMAs takes elements 8 s .. 8 s + 7).
+      // lq, lk: qh, kh times e^{G - G_end(w)} (>= 1); kr: kh e^{G_end(w) - G} (<= 1),
+      // where G_end(w) is the cumulative decay at the last token of sub-block w.
+      float lq[32], lk[32], kr[32];
       const float beta_mine = cur.beta;
       {
-        float qh[32], kh[32], loc[32];
+        float qh[32], kh[32], lg[32];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint32_t qa[4] = {cur.q[i].x, cur.q[i].y, cur.q[i].z, cur.q[i].w};
@@ -457,17 +470,18 @@ __global__ __launch_bounds__(NTHR, 1) void kda_chunk_fwd_kernel(
             kh[8 * i + 2 * j + 1] = bf16_hi_to_f32(ka[j]);
           }
         }
-        bool gbad = false;
+        float gmin = 0.f, gmax = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const float ga[4] = {cur.g[i].x, cur.g[i].y, cur.g[i].z, cur.g[i].w};
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            loc[4 * i + j] = ga[j];
-            gbad |= !(ga[j] >= gate_bound && ga[j] <= 0.f);
+            gmin = fminf(gmin, ga[j]);
+            gmax = fmaxf(gmax, ga[j]);
+            lg[4 * i + j] = ga[j] * 1.4426950408889634f;  // log2 domain
           }
         }
-        if (gbad && tok < n) sm.gate_bad = 1;
+        if (tok < n && !(gmin >= gate_bound && gmax <= 0.f)) sm.gate_bad = 1;
         if (cg == 0) sm.beta[tok] = cur.beta;
         float sq = 0.f, sk = 0.f;
 #pragma unroll
@@ -478,53 +492,44 @@ __global__ __launch_bounds__(NTHR, 1) void kda_chunk_fwd_kernel(
         sk += __shfl_xor(sk, 32);
         const float rq = 1.0f / sqrtf(sq + L2_EPS);
         const float rk = 1.0f / sqrtf(sk + L2_EPS);
-#pragma unroll
-        for (int j = 0; j < 32; ++j) { qh[j] *= rq; kh[j] *= rk; }
         // inclusive scan over the 16 tokens of the sub-block (one 16-lane row)
 #pragma unroll
         for (int j = 0; j < 32; ++j) {
-          float x = loc[j];
+          float x = lg[j];
           x += dpp_row_shr<1>(x);
           x += dpp_row_shr<2>(x);
           x += dpp_row_shr<4>(x);
           x += dpp_row_shr<8>(x);
-          loc[j] = x;
+          lg[j] = x;
         }
         if (r == 15) {
 #pragma unroll
           for (int j = 0; j < 32; j += 4)
-            *reinterpret_cast<float4*>(&sm.tot[w][32 * cg + j]) =
-                make_float4(loc[j], loc[j + 1], loc[j + 2], loc[j + 3]);
+            *reinterpret_cast<float4*>(&sm.tot[w][32 * (j >> 3) + 8 * cg + (j & 7)]) =
+                make_float4(lg[j], lg[j + 1], lg[j + 2], lg[j + 3]);
         }
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          const float ert = __builtin_amdgcn_exp2f(row_bcast<15>(lg[j]) - lg[j]);  // <= 1
+          const float elt = __builtin_amdgcn_rcpf(ert);                             // >= 1
+          const float qn = qh[j] * rq, kn = kh[j] * rk;
+          lq[j] = qn * elt;
+          lk[j] = kn * elt;
+          kr[j] = kn * ert;
+        }
+      }
 
-        // diagonal block (w, w) of A and M, decay split at the sub-block's last
-        // token: right kh_i e^{G_end - G_i} <= 1, left x_r e^{G_r - G_end} >= 1
-        f32x4 accM = {0.f, 0.f, 0.f, 0.f}, accA = {0.f, 0.f, 0.f, 0.f};
+      // diagonal block (w, w) of M and A on fp32 MFMA: k-step s takes element s
+      // from every lane (the same channel on both operands)
+      {
+        f32x4 accM[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        f32x4 accA[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          bf16x8 lqh, lql, lkh, lkl, rh, rl;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int jj = 8 * s + j;
-            const float tw = row_bcast<15>(loc[jj]);
-            const float ert = __expf(tw - loc[jj]);    // e^{G_end - G_r} <= 1
-            const float elt = __builtin_amdgcn_rcpf(ert);  // e^{G_r - G_end} >= 1 (v_rcp_f32)
-            const float eg = __expf(loc[jj]);          // e^{G_r - P_w} <= 1
-            kr[jj] = kh[jj] * ert;
-            qe[jj] = qh[jj] * eg;
-            ke[jj] = kh[jj] * eg;
-            SPLIT_BF16(qh[jj] * elt, lqh[j], lql[j]);
-            SPLIT_BF16(kh[jj] * elt, lkh[j], lkl[j]);
-            SPLIT_BF16(kr[jj], rh[j], rl[j]);
-          }
-          accM = mfma16(lqh, rh, accM);
-          accM = mfma16(lql, rh, accM);
-          accM = mfma16(lqh, rl, accM);
-          accA = mfma16(lkh, rh, accA);
-          accA = mfma16(lkl, rh, accA);
-          accA = mfma16(lkh, rl, accA);
+        for (int s = 0; s < 32; ++s) {
+          accM[s & 1] = mfma16f(lq[s], kr[s], accM[s & 1]);
+          accA[s & 1] = mfma16f(lk[s], kr[s], accA[s & 1]);
         }
-        store_block(sm, accM, accA, w, w, l, true, beta_mine);
+        store_block(sm, accM[0] + accM[1], accA[0] + accA[1], w, w, l, true, beta_mine);
         // blocks above the diagonal are read by the chain's MFMAs: zero them
         const bf16 z = (bf16)0.f;
 #pragma unroll 1
@@ -549,63 +554,61 @@ __global__ __launch_bounds__(NTHR, 1) void kda_chunk_fwd_kernel(
       fill_tables(sm, tid);
       __syncthreads();  // B2: decay tables visible
 
-      // ---- operand tiles of the chain
+      // ---- operand tiles of the chain: Qt = lq e^{G_end(w)}, Kt = -lk e^{G_end(w)},
+      //      KbT = kr e^{G_c - G_end(w)}
 #pragma unroll
       for (int j0 = 0; j0 < 32; j0 += 8) {
         float fq[8], fk[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) { fq[j] = 1.f; fk[j] = 1.f; }
-        if (w > 0) {  // e^{P_w}
-          const float4 a = *reinterpret_cast<const float4*>(&sm.etab[w - 1][32 * cg + j0]);
-          const float4 b = *reinterpret_cast<const float4*>(&sm.etab[w - 1][32 * cg + j0 + 4]);
+        {
+          const float4 a = *reinterpret_cast<const float4*>(&sm.etab[w][4 * j0 + 8 * cg]);
+          const float4 b = *reinterpret_cast<const float4*>(&sm.etab[w][4 * j0 + 8 * cg + 4]);
           fq[0] = a.x; fq[1] = a.y; fq[2] = a.z; fq[3] = a.w;
           fq[4] = b.x; fq[5] = b.y; fq[6] = b.z; fq[7] = b.w;
         }
-        if (w < 3) {  // e^{P_4 - P_{w+1}}
-          const float4 a = *reinterpret_cast<const float4*>(&sm.etab[4 + w][32 * cg + j0]);
-          const float4 b = *reinterpret_cast<const float4*>(&sm.etab[4 + w][32 * cg + j0 + 4]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) fk[j] = 1.f;
+        if (w < 3) {
+          const float4 a = *reinterpret_cast<const float4*>(&sm.etab[4 + w][4 * j0 + 8 * cg]);
+          const float4 b = *reinterpret_cast<const float4*>(&sm.etab[4 + w][4 * j0 + 8 * cg + 4]);
           fk[0] = a.x; fk[1] = a.y; fk[2] = a.z; fk[3] = a.w;
           fk[4] = b.x; fk[5] = b.y; fk[6] = b.z; fk[7] = b.w;
         }
         bf16x8 qt, kt;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          qt[j] = (bf16)(qe[j0 + j] * fq[j]);
-          kt[j] = (bf16)(-ke[j0 + j] * fq[j]);
-          sm.KbT[32 * cg + j0 + j][tok] = (bf16)(kr[j0 + j] * fk[j]);
+          qt[j] = (bf16)(lq[j0 + j] * fq[j]);
+          kt[j] = (bf16)(-lk[j0 + j] * fq[j]);
+          sm.KbT[4 * j0 + 8 * cg + j][tok] = (bf16)(kr[j0 + j] * fk[j]);
         }
-        *reinterpret_cast<bf16x8*>(&sm.Qt[tok][32 * cg + j0]) = qt;
-        *reinterpret_cast<bf16x8*>(&sm.Kt[tok][32 * cg + j0]) = kt;
+        *reinterpret_cast<bf16x8*>(&sm.Qt[tok][4 * j0 + 8 * cg]) = qt;
+        *reinterpret_cast<bf16x8*>(&sm.Kt[tok][4 * j0 + 8 * cg]) = kt;
       }
 
-      // ---- off-diagonal blocks (w, b), b < w: left factor e^{G_r - G_end(b)} <= 1
+      // ---- off-diagonal blocks (w, b), b < w, on fp16 MFMA:
+      //      left x_r e^{G_r - G_end(b)} = l{q,k} e^{G_end(w) - G_end(b)} <= 1
 #pragma unroll 1
       for (int b = 0; b < w; ++b) {
-        const int frow = (b == w - 1) ? -1 : (w == 2 ? 7 : (b == 1 ? 8 : 9));
-        f32x4 accM = {0.f, 0.f, 0.f, 0.f}, accA = {0.f, 0.f, 0.f, 0.f};
+        const float* fr = sm.etab[7 + (w * (w - 1)) / 2 + b];
+        f32x4 accM[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        f32x4 accA[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const f16x8 rv = sm.u2.R[b][s][l];
-          float f[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) f[j] = 1.f;
-          if (frow >= 0) {
-            const float4 a = *reinterpret_cast<const float4*>(&sm.etab[frow][32 * cg + 8 * s]);
-            const float4 c = *reinterpret_cast<const float4*>(&sm.etab[frow][32 * cg + 8 * s + 4]);
-            f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-            f[4] = c.x; f[5] = c.y; f[6] = c.z; f[7] = c.w;
-          }
-          f16x8 lq, lk;
+          const float4 fa = *reinterpret_cast<const float4*>(&fr[32 * s + 8 * cg]);
+          const float4 fb = *reinterpret_cast<const float4*>(&fr[32 * s + 8 * cg + 4]);
+          const float f[8] = {fa.x, fa.y, fa.z, fa.w, fb.x, fb.y, fb.z, fb.w};
+          f16x8 lqv, lkv;
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            lq[j] = (_Float16)(qe[8 * s + j] * f[j]);
-            lk[j] = (_Float16)(ke[8 * s + j] * f[j]);
+            lqv[j] = (_Float16)(lq[8 * s + j] * f[j]);
+            lkv[j] = (_Float16)(lk[8 * s + j] * f[j]);
           }
-          accM = mfma16h(lq, rv, accM);
-          accA = mfma16h(lk, rv, accA);
+          accM[s & 1] = mfma16h(lqv, rv, accM[s & 1]);
+          accA[s & 1] = mfma16h(lkv, rv, accA[s & 1]);
         }
-        store_block(sm, accM, accA, w, b, l, false, beta_mine);
+        store_block(sm, accM[0] + accM[1], accA[0] + accA[1], w, b, l, false, beta_mine);
       }
+
       __syncthreads();  // B3: A and M complete, R dead
 
       // ================= T = (I + A)^-1 by 16x16 blocks =================
@@ -754,11 +757,11 @@ __global__ __launch_bounds__(NTHR, 1) void kda_chunk_fwd_kernel(
         // U = Tb X: the six lower-triangular (row tile, k-step) pairs
         constexpr int PMT[6] = {0, 0, 1, 1, 1, 1};
         constexpr int PS[6] = {0, 1, 0, 1, 2, 3};
-        f32x16 U[2];
+        f32x16 U[2], U2[2];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) U[mt][i] = 0.f;
+          for (int i = 0; i < 16; ++i) { U[mt][i] = 0.f; U2[mt][i] = 0.f; }
         {
           bf16x8 th[6], tl[6];
 #pragma unroll
@@ -766,11 +769,16 @@ __global__ __launch_bounds__(NTHR, 1) void kda_chunk_fwd_kernel(
             th[p] = *reinterpret_cast<const bf16x8*>(&sm.u.tb.hi[32 * PMT[p] + rowsel][16 * PS[p] + 8 * hg]);
             tl[p] = *reinterpret_cast<const bf16x8*>(&sm.u.tb.lo[32 * PMT[p] + rowsel][16 * PS[p] + 8 * hg]);
           }
+          // order (1,0) (0,0) (1,1) (0,1) (1,2) (1,3): the two row tiles alternate
+          constexpr int ORD[6] = {2, 0, 3, 1, 4, 5};
 #pragma unroll
-          for (int p = 0; p < 6; ++p) {
+          for (int o = 0; o < 6; ++o) {
+            const int p = ORD[o];
             U[PMT[p]] = mfma32(th[p], Xb[PS[p]], U[PMT[p]]);
-            U[PMT[p]] = mfma32(tl[p], Xb[PS[p]], U[PMT[p]]);
+            U2[PMT[p]] = mfma32(tl[p], Xb[PS[p]], U2[PMT[p]]);
           }
+          U[0] += U2[0];
+          U[1] += U2[1];
         }
         bf16x8 Ubh[4], Ubl[4];
 #pragma unroll
@@ -787,56 +795,56 @@ __global__ __launch_bounds__(NTHR, 1) void kda_chunk_fwd_kernel(
           if (c1 < eos) vcur = load_v(v, c1, n1, H, h, w, l);
         }
 
-        // O = scale (qh e^G S + M U), staged through LDS for 16-byte stores
+        // O = scale (qh e^G S + M U), staged through LDS for 16-byte stores;
+        // four independent accumulators (row tile x {Qt S, M U})
         unsigned short (*ost)[32] = sm.u2.ws[w].o;
+        {
+          f32x16 OQ[2], OM[2];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          f32x16 O;
+          for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) O[i] = 0.f;
-          {
-            bf16x8 qa[2];
-            qa[0] = *reinterpret_cast<const bf16x8*>(&sm.Qt[32 * mt + rowsel][8 * hg]);
-            qa[1] = *reinterpret_cast<const bf16x8*>(&sm.Qt[32 * mt + rowsel][16 + 8 * hg]);
+            for (int i = 0; i < 16; ++i) { OQ[mt][i] = 0.f; OM[mt][i] = 0.f; }
+          bf16x8 qa[2][2];
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-              O = mfma32(qa[s & 1], Sb[s], O);
-              if (s + 2 < 8) qa[s & 1] = *reinterpret_cast<const bf16x8*>(&sm.Qt[32 * mt + rowsel][16 * (s + 2) + 8 * hg]);
-            }
-          }
-          {
-            bf16x8 mh[4], ml[4];
+          for (int s = 0; s < 2; ++s)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              if (s < 2 * (mt + 1)) {
-                mh[s] = *reinterpret_cast<const bf16x8*>(&sm.Mhi[32 * mt + rowsel][16 * s + 8 * hg]);
-                ml[s] = *reinterpret_cast<const bf16x8*>(&sm.Mlo[32 * mt + rowsel][16 * s + 8 * hg]);
-              }
-            }
+            for (int mt = 0; mt < 2; ++mt)
+              qa[mt][s] = *reinterpret_cast<const bf16x8*>(&sm.Qt[32 * mt + rowsel][16 * s + 8 * hg]);
+          bf16x8 mh[6], ml[6];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              if (s < 2 * (mt + 1)) {
-                O = mfma32(mh[s], Ubh[s], O);
-                O = mfma32(ml[s], Ubh[s], O);
-                O = mfma32(mh[s], Ubl[s], O);
-              }
-            }
+          for (int p = 0; p < 6; ++p) {
+            mh[p] = *reinterpret_cast<const bf16x8*>(&sm.Mhi[32 * PMT[p] + rowsel][16 * PS[p] + 8 * hg]);
+            ml[p] = *reinterpret_cast<const bf16x8*>(&sm.Mlo[32 * PMT[p] + rowsel][16 * PS[p] + 8 * hg]);
           }
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int t = 32 * mt + 16 * (i >> 3) + 8 * hg + (i & 7);
-            const bf16 ob = (bf16)(O[i] * scale);
-            ost[t][m] = __builtin_bit_cast(unsigned short, ob);
+          for (int s = 0; s < 8; ++s) {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+              OQ[mt] = mfma32(qa[mt][s & 1], Sb[s], OQ[mt]);
+              if (s + 2 < 8)
+                qa[mt][s & 1] = *reinterpret_cast<const bf16x8*>(&sm.Qt[32 * mt + rowsel][16 * (s + 2) + 8 * hg]);
+            }
+            if (s < 6) {
+              const int p = s;
+              OM[PMT[p]] = mfma32(mh[p], Ubh[PS[p]], OM[PMT[p]]);
+              OM[PMT[p]] = mfma32(ml[p], Ubh[PS[p]], OM[PMT[p]]);
+              OM[PMT[p]] = mfma32(mh[p], Ubl[PS[p]], OM[PMT[p]]);
+            }
           }
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int t = 32 * mt + 16 * (i >> 3) + 8 * hg + (i & 7);
+              const bf16 ob = (bf16)((OQ[mt][i] + OM[mt][i]) * scale);
+              ost[t][m] = __builtin_bit_cast(unsigned short, ob);
+            }
         }
 
-        // S <- e^{G_c} S + (kh e^{G_c - G})^T U
+        // S <- e^{G_c} S + (kh e^{G_c - G})^T U  (the four row tiles interleaved)
         {
-          bf16x8 kb[2];
-          kb[0] = *reinterpret_cast<const bf16x8*>(&sm.KbT[rowsel][8 * hg]);
-          kb[1] = *reinterpret_cast<const bf16x8*>(&sm.KbT[rowsel][16 + 8 * hg]);
 #pragma unroll
-          for (int kt = 0; kt < 4; ++kt) {
+          for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
             for (int i0 = 0; i0 < 16; i0 += 8) {
               const float* dp = &sm.etab[3][32 * kt + 16 * (i0 >> 3) + 8 * hg];
@@ -845,13 +853,17 @@ __global__ __launch_bounds__(NTHR, 1) void kda_chunk_fwd_kernel(
               S[kt][i0 + 0] *= d0.x; S[kt][i0 + 1] *= d0.y; S[kt][i0 + 2] *= d0.z; S[kt][i0 + 3] *= d0.w;
               S[kt][i0 + 4] *= d1.x; S[kt][i0 + 5] *= d1.y; S[kt][i0 + 6] *= d1.z; S[kt][i0 + 7] *= d1.w;
             }
+          bf16x8 kb[2][4];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              const int idx = 4 * kt + s;
-              S[kt] = mfma32(kb[idx & 1], Ubh[s], S[kt]);
-              const int nx = idx + 2;
-              if (nx < 16)
-                kb[idx & 1] = *reinterpret_cast<const bf16x8*>(&sm.KbT[32 * (nx >> 2) + rowsel][16 * (nx & 3) + 8 * hg]);
+          for (int kt = 0; kt < 4; ++kt)
+            kb[0][kt] = *reinterpret_cast<const bf16x8*>(&sm.KbT[32 * kt + rowsel][8 * hg]);
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+              if (s + 1 < 4)
+                kb[(s + 1) & 1][kt] = *reinterpret_cast<const bf16x8*>(&sm.KbT[32 * kt + rowsel][16 * (s + 1) + 8 * hg]);
+              S[kt] = mfma32(kb[s & 1][kt], Ubh[s], S[kt]);
             }
           }
         }
