@@ -5,11 +5,16 @@ packed 32768-token stream with H = 32, K = V = 128 and lognormal document
 lengths (median 1024, clipped to [17, 8192]).  Inputs are resident in HBM
 before the timed region.  Prints ONE JSON line on stdout.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-probe]
+
+``--copy-probe`` adds, after the timed region, two plain device-to-device
+copies of 1 GiB: under ``rocprofv3 --pmc FETCH_SIZE`` / ``WRITE_SIZE`` their
+counter readings calibrate the chunk kernel's readings to bytes.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -27,6 +32,21 @@ BYTES_PER_TOKEN_HEAD = 2 * DK + 2 * DK + 2 * DV + 4 * DK + 4 + 2 * DV  # q k v g
 PEAK_BF16_TFLOPS = 2516.6   # dense bf16 MFMA, 256 CU x 2.4 GHz x 4096 flop/clk/CU
 PEAK_HBM_GBS = 8000.0       # HBM3E
 METRIC_WORKLOAD = 3
+KERNEL_SOURCE = os.path.join(ROOT, "linear_attention_sequence_amd", "csrc", "kda_fwd.hip")
+COPY_PROBE_BYTES = 1 << 30
+
+# HBM traffic of one chunk-kernel launch on the packed 32768-token stream, from
+# two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) scaled by
+# the same counters' reading for a 1 GiB device copy.  Valid only for the kernel
+# source with this sha256; otherwise the traffic is reported as null.
+TRAFFIC = {
+    "workload": "packed_lognormal_T32768_H32",
+    "kernel_sha256": "25c01b4d0664ac1c8f953eee0bf2c178dcdb95285f414b2dfe4c73e05fb47aa1",
+    "fetch_kib": 665029.1,     # mean of 3 dispatches
+    "write_kib": 262173.3,
+    "fetch_scale": 2.0,        # 1 GiB copy: FETCH_SIZE 524303 KiB for 1048576 KiB read
+    "write_scale": 1.0,        # 1 GiB copy: WRITE_SIZE 1048576 KiB
+}
 
 
 def chunk_flops(c: int, K: int = DK, V: int = DV) -> int:
@@ -42,6 +62,20 @@ def algorithmic_flops(lengths, heads: int) -> int:
         full, tail = divmod(int(L), CHUNK)
         f += full * chunk_flops(CHUNK) + (chunk_flops(tail) if tail else 0)
     return f * heads
+
+
+def kernel_source_sha256() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload_name: str):
+    """HBM bytes per launch from the stored counter readings, or None when they
+    were taken on another kernel source or workload."""
+    t = TRAFFIC
+    if t is None or t["workload"] != workload_name or t["kernel_sha256"] != kernel_source_sha256():
+        return None
+    return (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024.0
 
 
 def log(msg):
@@ -80,6 +114,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", type=int, default=METRIC_WORKLOAD)
+    ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the KDA forward here is a single-GPU "
@@ -120,6 +155,15 @@ def main():
     ms = ev0.elapsed_time(ev1) / args.steps
     status = kda.device_status()
 
+    if args.copy_probe:
+        src = torch.ones(COPY_PROBE_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: 2 x {COPY_PROBE_BYTES} B read + {COPY_PROBE_BYTES} B written")
+        del src, dst
+
     sec = ms / 1e3
     tokens_per_s = T / sec
     flops = algorithmic_flops(w.lengths, H)
@@ -159,7 +203,10 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": gbs / PEAK_HBM_GBS,
-            "traffic": None,
+            "traffic": measured_traffic(w.name),
+            "algorithmic_bytes": bytes_alg,
+            "kernel": "kda_chunk_fwd_kernel",
+            "timing": "HIP events on the launch stream around each call (scheduler + chunk kernel)",
         },
         "device_status": status,
     }
