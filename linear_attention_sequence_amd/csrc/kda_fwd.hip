@@ -46,6 +46,9 @@
 #include <stdint.h>
 #include <math.h>
 #include <string.h>
+#include <stdlib.h>
+#include <stddef.h>
+#include <algorithm>
 #include <stdio.h>
 #include <string>
 #include <mutex>
@@ -67,18 +70,6 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-// ---------------------------------------------------------------------------
-// workspace written by the scheduler, read by the main kernel
-// ---------------------------------------------------------------------------
-struct WorkHeader {
-  int counter;   // next unit to hand out
-  int status;    // non-zero: cu_seqlens broke its contract
-  int n_units;   // documents * heads
-  int n_docs;    // non-empty documents
-};
-
-__device__ int g_kda_status;  // sticky kda_device_flags of this device
 
 // ---------------------------------------------------------------------------
 // small helpers
@@ -121,8 +112,13 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 }
 
 // ---------------------------------------------------------------------------
-// LDS layout of the main kernel (one chunk in flight, ~122 KB: one workgroup
-// per CU)
+// LDS layout (one chunk in flight, ~117 KB: one workgroup per CU)
+//
+// The leading part, Qt .. u.tb, is the chunk's "image": everything the chain
+// reads that does not depend on the state.  For a split document the pre
+// kernel builds it and copies it to global memory byte for byte; the main
+// kernel copies it back instead of building it.  The per-channel state decay
+// e^{G_c} travels in the row padding of Kt (see dvec).
 // ---------------------------------------------------------------------------
 struct alignas(16) Smem {
   bf16 Qt[CH][DK + 8];       // qh * e^G                      (A operand of Qt S)
@@ -137,6 +133,7 @@ struct alignas(16) Smem {
     } tb;
     float A[CH][CH + 4];     // beta-scaled strictly lower A (fp32), input of the solve
   } u;
+  // ---- end of the image
   union {
     f16x8 R[3][4][64];       // right operands of off-diagonal sub-blocks (fp16), lane order
     float T[CH][CH + 4];     // (I + A)^-1 (fp32)
@@ -151,8 +148,20 @@ struct alignas(16) Smem {
   float tot[4][DK];          // per sub-block total decay (log2 domain)
   float beta[CH];
   int unit;
+  int next_unit;
   int gate_bad;
 };
+
+constexpr int IMG_BYTES = (int)offsetof(Smem, u2);
+constexpr int IMG_VEC = IMG_BYTES / 16;         // 16-byte pieces of an image
+constexpr int IMG_PER_THREAD = IMG_VEC / NTHR;  // pieces per thread
+static_assert(IMG_VEC % NTHR == 0, "image must split evenly over the workgroup");
+static_assert(offsetof(Smem, u) + sizeof(((Smem*)nullptr)->u.tb) == IMG_BYTES, "image layout");
+
+// e^{G_c} of channels c .. c + 3 (c a multiple of 4): the padding of Kt row c / 4
+__device__ __forceinline__ float* dvec(Smem& sm, int c) {
+  return reinterpret_cast<float*>(&sm.Kt[c >> 2][DK]);
+}
 
 // Store the 16x16 block (a, b) of M (lower incl., split hi + lo) and of A
 // (beta-scaled, strictly lower, fp32).  C layout of a 16x16 MFMA tile: lane l
@@ -180,89 +189,118 @@ __device__ __forceinline__ void store_block(Smem& sm, const f32x4& accM, const f
 }
 
 // ---------------------------------------------------------------------------
-// scheduler: validate cu_seqlens, emit non-empty documents longest first
+// scheduler: validate cu_seqlens, order documents longest first, and choose
+// the documents whose chunks are prepared in parallel ("split" documents)
 // ---------------------------------------------------------------------------
 constexpr int SCHED_THREADS = 1024;
 constexpr int NBUCKET = 1024;
+constexpr int MIN_SPLIT_CHUNKS = 8;   // shorter documents are never split
+constexpr int MAX_SPLIT_DOCS = 4096;  // split candidates examined
+// relative cost of one chunk of one head: fused (prepare + chain on one
+// workgroup), prepare only (pre kernel), chain only (main kernel)
+constexpr int COST_FUSED = 37, COST_PRE = 27, COST_CHAIN = 14;
 
+enum SplitPolicy { SPLIT_NEVER = 0, SPLIT_AUTO = 1, SPLIT_ALWAYS = 2 };
+
+struct WorkHeader {
+  int counter;      // next unit of the main kernel
+  int status;       // non-zero: cu_seqlens broke its contract
+  int n_units;      // documents * heads
+  int n_docs;       // non-empty documents
+  int pre_counter;  // next unit of the pre kernel
+  int n_pre_units;  // split chunks * heads
+  int n_split;      // split documents (the first n_split entries of the list)
+  int pad;
+};
+
+__device__ int g_kda_status;  // sticky kda_device_flags of this device
+
+// docs[i] = (first token, length) for a fused document, (-(j + 1), length) for
+// split document j; split[j] = (first token, index of its first chunk in
+// pre_chunks); pre_chunks[p] = (first token, length) of split chunk p.
 __global__ __launch_bounds__(SCHED_THREADS) void kda_schedule_kernel(
-    const int32_t* __restrict__ cu, int T, int H, WorkHeader* __restrict__ hdr,
-    int2* __restrict__ docs) {
+    const int32_t* __restrict__ cu, int T, int H, int n_cu, int cap_chunks, int policy,
+    WorkHeader* __restrict__ hdr, int2* __restrict__ docs, int2* __restrict__ split,
+    int2* __restrict__ pre_chunks) {
   __shared__ int s_vals[SCHED_THREADS];
   __shared__ int s_term;
   __shared__ int s_bad;
   __shared__ int s_carry;
   __shared__ int s_hist[NBUCKET];
   __shared__ int s_count;
+  __shared__ unsigned long long s_total;
+  __shared__ int s_nsplit;
+  __shared__ int s_split_chunks;
   const int tid = threadIdx.x;
 
+  int n;  // number of documents (entries 0..n of cu are valid)
   if (cu == nullptr) {
-    if (tid == 0) {
-      docs[0] = make_int2(0, T);
-      hdr->counter = 0;
-      hdr->status = 0;
-      hdr->n_docs = 1;
-      hdr->n_units = H;
+    n = 1;
+  } else {
+    // ---- 1. find the terminating entry (first entry equal to T) and validate
+    if (tid == 0) { s_term = INT32_MAX; s_bad = 0; s_carry = 0; }
+    __syncthreads();
+    const int32_t* page = reinterpret_cast<const int32_t*>(reinterpret_cast<uintptr_t>(cu) & ~uintptr_t(4095));
+    const int64_t first_idx = page - cu;  // index of page[0] relative to cu (<= 0)
+    for (int64_t step = 0;; ++step) {
+      const int64_t idx = first_idx + step * SCHED_THREADS + tid;  // entry index of this thread
+      const bool mine = idx >= 0 && idx <= (int64_t)T;
+      int val = 0;
+      if (mine) val = page[step * SCHED_THREADS + tid];
+      s_vals[tid] = val;
+      __syncthreads();
+      if (mine) {
+        if (val == T) atomicMin(&s_term, (int)idx);
+      }
+      __syncthreads();
+      const int term = s_term;
+      if (mine && idx <= (int64_t)term) {
+        int prev = (tid > 0) ? s_vals[tid - 1] : s_carry;
+        bool bad = false;
+        if (idx == 0) bad = (val != 0);
+        else bad = (val < prev) || (val > T) || (val < 0);
+        if (bad) atomicOr(&s_bad, 1);
+      }
+      __syncthreads();
+      if (s_bad || term != INT32_MAX) break;
+      // no terminator in this block: continue only if entries remain allowed
+      const int64_t last_idx = first_idx + (step + 1) * SCHED_THREADS - 1;
+      if (last_idx >= (int64_t)T) { if (tid == 0) s_bad = 1; __syncthreads(); break; }
+      if (tid == 0) s_carry = s_vals[SCHED_THREADS - 1];
+      __syncthreads();
     }
-    return;
+    if (s_bad) {
+      if (tid == 0) {
+        hdr->counter = 0;
+        hdr->status = 1;
+        hdr->n_docs = 0;
+        hdr->n_units = 0;
+        hdr->pre_counter = 0;
+        hdr->n_pre_units = 0;
+        hdr->n_split = 0;
+        atomicOr(&g_kda_status, KDA_DEV_BAD_CU_SEQLENS);
+      }
+      return;
+    }
+    n = s_term;
   }
-
-  // ---- 1. find the terminating entry (first entry equal to T) and validate
-  if (tid == 0) { s_term = INT32_MAX; s_bad = 0; s_carry = 0; }
-  __syncthreads();
-  const int32_t* page = reinterpret_cast<const int32_t*>(reinterpret_cast<uintptr_t>(cu) & ~uintptr_t(4095));
-  const int64_t first_idx = page - cu;  // index of page[0] relative to cu (<= 0)
-  for (int64_t step = 0;; ++step) {
-    const int64_t idx = first_idx + step * SCHED_THREADS + tid;  // entry index of this thread
-    const bool mine = idx >= 0 && idx <= (int64_t)T;
-    int val = 0;
-    if (mine) val = page[step * SCHED_THREADS + tid];
-    s_vals[tid] = val;
-    __syncthreads();
-    if (mine) {
-      if (val == T) atomicMin(&s_term, (int)idx);
-    }
-    __syncthreads();
-    const int term = s_term;
-    if (mine && idx <= (int64_t)term) {
-      int prev = (tid > 0) ? s_vals[tid - 1] : s_carry;
-      bool bad = false;
-      if (idx == 0) bad = (val != 0);
-      else bad = (val < prev) || (val > T) || (val < 0);
-      if (bad) atomicOr(&s_bad, 1);
-    }
-    __syncthreads();
-    if (s_bad || term != INT32_MAX) break;
-    // no terminator in this block: continue only if entries remain allowed
-    const int64_t last_idx = first_idx + (step + 1) * SCHED_THREADS - 1;
-    if (last_idx >= (int64_t)T) { if (tid == 0) s_bad = 1; __syncthreads(); break; }
-    if (tid == 0) s_carry = s_vals[SCHED_THREADS - 1];
-    __syncthreads();
-  }
-  if (s_bad) {
-    if (tid == 0) {
-      hdr->counter = 0;
-      hdr->status = 1;
-      hdr->n_docs = 0;
-      hdr->n_units = 0;
-      atomicOr(&g_kda_status, KDA_DEV_BAD_CU_SEQLENS);
-    }
-    return;
-  }
-  const int n = s_term;  // number of documents (entries 0..n are valid)
+  auto cu_at = [&](int i) -> int { return cu ? cu[i] : (i == 0 ? 0 : T); };
 
   // ---- 2. histogram of chunk counts (descending order = longest first)
   for (int b = tid; b < NBUCKET; b += SCHED_THREADS) s_hist[b] = 0;
-  if (tid == 0) s_count = 0;
+  if (tid == 0) { s_count = 0; s_total = 0; }
   __syncthreads();
+  unsigned long long my_chunks = 0;
   for (int i = tid; i < n; i += SCHED_THREADS) {
-    const int a = cu[i], len = cu[i + 1] - a;
+    const int a = cu_at(i), len = cu_at(i + 1) - a;
     if (len > 0) {
-      const int nch = min((len + CH - 1) / CH, NBUCKET - 1);
-      atomicAdd(&s_hist[NBUCKET - 1 - nch], 1);
+      const int nch = (len + CH - 1) / CH;
+      my_chunks += nch;
+      atomicAdd(&s_hist[NBUCKET - 1 - min(nch, NBUCKET - 1)], 1);
       atomicAdd(&s_count, 1);
     }
   }
+  atomicAdd(&s_total, my_chunks);
   __syncthreads();
   // exclusive prefix sum over buckets (Hillis-Steele on s_vals)
   {
@@ -279,72 +317,186 @@ __global__ __launch_bounds__(SCHED_THREADS) void kda_schedule_kernel(
   }
   __syncthreads();
   for (int i = tid; i < n; i += SCHED_THREADS) {
-    const int a = cu[i], len = cu[i + 1] - a;
+    const int a = cu_at(i), len = cu_at(i + 1) - a;
     if (len > 0) {
-      const int nch = min((len + CH - 1) / CH, NBUCKET - 1);
-      const int pos = atomicAdd(&s_hist[NBUCKET - 1 - nch], 1);
+      const int nch = (len + CH - 1) / CH;
+      const int pos = atomicAdd(&s_hist[NBUCKET - 1 - min(nch, NBUCKET - 1)], 1);
       docs[pos] = make_int2(a, len);
     }
+  }
+  __threadfence_block();
+  __syncthreads();
+
+  // ---- 3. split decision.  Documents of 1024+ chunks share the top bucket in
+  // arbitrary order; the decision only needs the list to be roughly sorted.
+  if (tid == 0) {
+    const int nd = s_count;
+    const long long Hc = H, ncu = max(n_cu, 1);
+    const long long total = (long long)s_total;
+    auto nch_of = [&](int i) -> long long { return (docs[i].y + CH - 1) / CH; };
+    int best_s = 0;
+    long long best_sum = 0;
+    if (policy != SPLIT_NEVER && nd > 0) {
+      long long best = nd > 0 ? max(nch_of(0) * COST_FUSED, (total * Hc * COST_FUSED + ncu - 1) / ncu) : 0;
+      long long sum = 0, longest_split = 0;
+      for (int s = 1; s <= min(nd, MAX_SPLIT_DOCS); ++s) {
+        const long long c = nch_of(s - 1);
+        if (c < MIN_SPLIT_CHUNKS || sum + c > cap_chunks) break;
+        sum += c;
+        longest_split = max(longest_split, c);
+        const long long pre = (sum * Hc + ncu - 1) / ncu * COST_PRE;
+        const long long rest = (s < nd) ? nch_of(s) * COST_FUSED : 0;
+        const long long avg = ((sum * COST_CHAIN + (total - sum) * COST_FUSED) * Hc + ncu - 1) / ncu;
+        const long long est = pre + max(max(longest_split * COST_CHAIN, rest), avg);
+        if (policy == SPLIT_ALWAYS || est < best) { best = est; best_s = s; best_sum = sum; }
+      }
+    }
+    long long base = 0;
+    for (int j = 0; j < best_s; ++j) {
+      const int2 d = docs[j];
+      split[j] = make_int2(d.x, (int)base);
+      docs[j] = make_int2(-(j + 1), d.y);
+      base += (d.y + CH - 1) / CH;
+    }
+    s_nsplit = best_s;
+    s_split_chunks = (int)best_sum;
+  }
+  __threadfence_block();
+  __syncthreads();
+  const int ns = s_nsplit;
+  for (int j = 0; j < ns; ++j) {
+    const int2 sp = split[j];
+    const int len = docs[j].y;
+    const int nch = (len + CH - 1) / CH;
+    for (int c = tid; c < nch; c += SCHED_THREADS)
+      pre_chunks[sp.y + c] = make_int2(sp.x + CH * c, min(CH, len - CH * c));
   }
   if (tid == 0) {
     hdr->counter = 0;
     hdr->status = 0;
     hdr->n_docs = s_count;
     hdr->n_units = s_count * H;
+    hdr->pre_counter = 0;
+    hdr->n_pre_units = s_split_chunks * H;
+    hdr->n_split = ns;
   }
 }
 
 // ---------------------------------------------------------------------------
-// main kernel
+// per-chunk stages shared by the kernels
 // ---------------------------------------------------------------------------
+// ---- global memory through buffer descriptors.  A descriptor covers the
+// rows of one chunk of one head; per-lane byte offsets (always in the VGPR
+// offset, which the hardware range-checks) select token rows.  Rows at or past
+// the end of the chunk are out of range: loads return 0, stores are dropped.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+// bytes of the first n token rows of one head when a token row holds row_bytes
+// for each of H heads (n <= 0: nothing)
+__device__ __forceinline__ uint32_t chunk_bytes(int n, int H, uint32_t row_bytes) {
+  return n > 0 ? ((uint32_t)(n - 1) * (uint32_t)H + 1u) * row_bytes : 0u;
+}
+__device__ __forceinline__ u32x4 bload(Rsrc r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void bstore(u32x4 x, Rsrc r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b128(x, r, (int)off, 0, 0);
+}
+
 struct RawChunk {
-  uint4 q[4];    // 32 bf16 channels of one token (element 8 s + j = channel 32 s + 8 cg + j)
-  uint4 k[4];
-  float4 g[8];   // the same 32 channels, fp32
+  u32x4 q[4];    // 32 bf16 channels of one token (element 8 s + j = channel 32 s + 8 cg + j)
+  u32x4 k[4];
+  u32x4 g[8];    // the same 32 channels, fp32 bits
   float beta;
 };
 
+// per-lane byte offsets, fixed for the whole kernel
+struct Offsets {
+  uint32_t qk;    // token row of the prologue layout in q / k (g: twice this)
+  uint32_t b;     // the same token in beta
+  uint32_t v[4];  // V / O layout: row 16 i + l / 4, columns 32 w + 8 (l % 4) ..
+};
+
+__device__ __forceinline__ Offsets make_offsets(int H, int tok, int cg, int w, int l) {
+  Offsets o;
+  o.qk = (uint32_t)tok * (uint32_t)H * 256u + 16u * cg;
+  o.b = (uint32_t)tok * (uint32_t)H * 4u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o.v[i] = (uint32_t)(16 * i + (l >> 2)) * (uint32_t)H * 256u + 64u * w + 16u * (l & 3);
+  return o;
+}
+
+// q, k, g, beta of the chunk of n tokens at token c0 (head h); tokens at or
+// past n read as zero.  Element 8 s + j of this lane is channel 32 s + 8 cg + j:
+// the four lanes of a token read one contiguous 64-byte (q, k) or 128-byte (g)
+// span per load.
 __device__ __forceinline__ void load_raw(RawChunk& rc, const bf16* __restrict__ q,
                                          const bf16* __restrict__ k, const float* __restrict__ g,
-                                         const float* __restrict__ beta, int64_t tok_global,
-                                         bool valid, int H, int h, int cg) {
-  if (valid) {
-    // element 8 s + j of this lane is channel 32 s + 8 cg + j: the four lanes of
-    // a token read one contiguous 64-byte (q, k) or 128-byte (g) span per load
-    const size_t off = ((size_t)tok_global * H + h) * DK + 8 * cg;
+                                         const float* __restrict__ beta, int64_t c0, int n, int H,
+                                         int h, const Offsets& of) {
+  const size_t row = (size_t)c0 * H + h;
+  const uint32_t nb = chunk_bytes(n, H, 256u);
+  const Rsrc rq = make_rsrc(q + row * DK, nb);
+  const Rsrc rk = make_rsrc(k + row * DK, nb);
+  const Rsrc rg = make_rsrc(g + row * DK, 2u * nb);
+  const Rsrc rb = make_rsrc(beta + row, chunk_bytes(n, H, 4u));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      rc.q[i] = *reinterpret_cast<const uint4*>(q + off + 32 * i);
-      rc.k[i] = *reinterpret_cast<const uint4*>(k + off + 32 * i);
-      rc.g[2 * i] = *reinterpret_cast<const float4*>(g + off + 32 * i);
-      rc.g[2 * i + 1] = *reinterpret_cast<const float4*>(g + off + 32 * i + 4);
-    }
-    rc.beta = beta[(size_t)tok_global * H + h];
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { rc.q[i] = make_uint4(0, 0, 0, 0); rc.k[i] = make_uint4(0, 0, 0, 0); }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) rc.g[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    rc.beta = 0.f;
+  for (int i = 0; i < 4; ++i) {
+    rc.q[i] = bload(rq, of.qk + 64u * i);
+    rc.k[i] = bload(rk, of.qk + 64u * i);
+    rc.g[2 * i] = bload(rg, 2u * of.qk + 128u * i);
+    rc.g[2 * i + 1] = bload(rg, 2u * of.qk + 128u * i + 16u);
   }
+  rc.beta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, (int)of.b, 0, 0));
 }
 
 // V of one chunk, the 32 value columns of wave w: load i, lane l holds 16 bytes
-// of row 16 i + l / 4 (columns 32 w + 8 (l % 4) ..).  Rows past the end re-read
-// the last valid row; they are zeroed when used.
+// of row 16 i + l / 4 (columns 32 w + 8 (l % 4) ..); rows past the end read 0.
 struct VChunk {
-  uint4 r[4];
+  u32x4 r[4];
 };
 
 __device__ __forceinline__ VChunk load_v(const bf16* __restrict__ v, int64_t c0, int n, int H,
-                                         int h, int w, int l) {
+                                         int h, const Offsets& of) {
+  const Rsrc rv = make_rsrc(v + ((size_t)c0 * H + h) * DV, chunk_bytes(n, H, 256u));
   VChunk vc;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = min(16 * i + (l >> 2), n - 1);
-    vc.r[i] = *reinterpret_cast<const uint4*>(v + ((size_t)(c0 + row) * H + h) * DV + 32 * w + 8 * (l & 3));
-  }
+  for (int i = 0; i < 4; ++i) vc.r[i] = bload(rv, of.v[i]);
   return vc;
+}
+
+// a chunk image in registers: thread tid holds pieces tid + NTHR i
+struct Image {
+  u32x4 p[IMG_PER_THREAD];
+};
+
+__device__ __forceinline__ void load_image(Image& im, const uint8_t* __restrict__ src, int tid) {
+  const Rsrc r = make_rsrc(src, IMG_BYTES);
+#pragma unroll
+  for (int i = 0; i < IMG_PER_THREAD; ++i)
+    im.p[i] = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * tid, 16 * NTHR * i, 0);
+}
+
+__device__ __forceinline__ void image_to_lds(Smem& sm, const Image& im, int tid) {
+  uint8_t* dst = reinterpret_cast<uint8_t*>(&sm);
+#pragma unroll
+  for (int i = 0; i < IMG_PER_THREAD; ++i)
+    *reinterpret_cast<u32x4*>(dst + 16 * (tid + NTHR * i)) = im.p[i];
+}
+
+__device__ __forceinline__ void lds_to_global_image(uint8_t* __restrict__ dst, const Smem& sm, int tid) {
+  const Rsrc r = make_rsrc(dst, IMG_BYTES);
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(&sm);
+#pragma unroll
+  for (int i = 0; i < IMG_PER_THREAD; ++i)
+    __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(src + 16 * (tid + NTHR * i)),
+                                           r, 16 * tid, 16 * NTHR * i, 0);
 }
 
 // lane i of each 16-lane row receives lane N of the same row
@@ -369,6 +521,7 @@ __device__ __forceinline__ f32x4 mfma16k16(const bf16x4& a, const bf16x4& b, con
 //   rows 4..6:  e^{G_c - G_end(w)}    = 2^{t_{w+1} + .. + t_3}, w = 0..2
 //   rows 7..12: e^{G_end(w) - G_end(b)} = 2^{t_{b+1} + .. + t_w}, pair (w, b), b < w,
 //               at row 7 + w (w - 1) / 2 + b
+// D is also written to the image (dvec).
 __device__ __forceinline__ void fill_tables(Smem& sm, int tid) {
 #pragma unroll
   for (int e = tid; e < 13 * DK; e += NTHR) {
@@ -390,25 +543,537 @@ __device__ __forceinline__ void fill_tables(Smem& sm, int tid) {
       case 11: x = t2 + t3; break;   // (3, 1)
       default: x = t3; break;        // (3, 2)
     }
-    sm.etab[row][c] = __builtin_amdgcn_exp2f(x);
+    const float f = __builtin_amdgcn_exp2f(x);
+    sm.etab[row][c] = f;
+    if (row == 3) dvec(sm, c)[c & 3] = f;
   }
 }
 
+// lane coordinates inside the workgroup
+struct Lane {
+  int tid;
+  int w;    // wave (scalar)
+  int l;    // lane
+  int r;    // prologue: token inside the 16-token sub-block
+  int cg;   // prologue: channel group
+  int m;    // chain: MFMA row / column lane index
+  int hg;   // chain: lane half
+  int tok;  // prologue: token of this lane inside the chunk
+};
+
+__device__ __forceinline__ Lane make_lane() {
+  Lane ln;
+  ln.tid = threadIdx.x;
+  ln.w = __builtin_amdgcn_readfirstlane(ln.tid >> 6);
+  ln.l = ln.tid & 63;
+  ln.r = ln.l & 15;
+  ln.cg = ln.l >> 4;
+  ln.m = ln.l & 31;
+  ln.hg = ln.l >> 5;
+  ln.tok = 16 * ln.w + ln.r;
+  return ln;
+}
+
+// Everything of a chunk that does not depend on the state: from the raw
+// inputs `cur` (n valid tokens) to the image in LDS (Qt, Kt, KbT, M, Tb, D).
+// after_prologue() runs once `cur` has been consumed (it may refill it).
+// Ends with a workgroup barrier after which the image is complete.
+template <class AfterPrologue>
+__device__ __forceinline__ void prepare_chunk(Smem& sm, const RawChunk& cur, int n, float gate_bound,
+                                              const Lane& ln, AfterPrologue after_prologue) {
+  const int tid = ln.tid, w = ln.w, l = ln.l, r = ln.r, cg = ln.cg, tok = ln.tok;
+
+  // ================= prologue: l2 norm, cumulative decay =================
+  // lane (w, r, cg): token 16w + r of the chunk; element 8 s + j is channel
+  // 32 s + 8 cg + j (k-step s of the 16x16x32 MFMAs takes elements 8 s .. 8 s + 7).
+  // lq, lk: qh, kh times e^{G - G_end(w)} (>= 1); kr: kh e^{G_end(w) - G} (<= 1),
+  // where G_end(w) is the cumulative decay at the last token of sub-block w.
+  float lq[32], lk[32], kr[32];
+  const float beta_mine = cur.beta;
+  {
+    float qh[32], kh[32], lg[32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t qa[4] = {cur.q[i][0], cur.q[i][1], cur.q[i][2], cur.q[i][3]};
+      const uint32_t ka[4] = {cur.k[i][0], cur.k[i][1], cur.k[i][2], cur.k[i][3]};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        qh[8 * i + 2 * j] = bf16_lo_to_f32(qa[j]);
+        qh[8 * i + 2 * j + 1] = bf16_hi_to_f32(qa[j]);
+        kh[8 * i + 2 * j] = bf16_lo_to_f32(ka[j]);
+        kh[8 * i + 2 * j + 1] = bf16_hi_to_f32(ka[j]);
+      }
+    }
+    float gmin = 0.f, gmax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float ga[4] = {__uint_as_float(cur.g[i][0]), __uint_as_float(cur.g[i][1]),
+                           __uint_as_float(cur.g[i][2]), __uint_as_float(cur.g[i][3])};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        gmin = fminf(gmin, ga[j]);
+        gmax = fmaxf(gmax, ga[j]);
+        lg[4 * i + j] = ga[j] * 1.4426950408889634f;  // log2 domain
+      }
+    }
+    if (tok < n && !(gmin >= gate_bound && gmax <= 0.f)) sm.gate_bad = 1;
+    if (cg == 0) sm.beta[tok] = cur.beta;
+    after_prologue();
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) { sq += qh[j] * qh[j]; sk += kh[j] * kh[j]; }
+    sq += __shfl_xor(sq, 16);
+    sq += __shfl_xor(sq, 32);
+    sk += __shfl_xor(sk, 16);
+    sk += __shfl_xor(sk, 32);
+    const float rq = 1.0f / sqrtf(sq + L2_EPS);
+    const float rk = 1.0f / sqrtf(sk + L2_EPS);
+    // inclusive scan over the 16 tokens of the sub-block (one 16-lane row)
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      float x = lg[j];
+      x += dpp_row_shr<1>(x);
+      x += dpp_row_shr<2>(x);
+      x += dpp_row_shr<4>(x);
+      x += dpp_row_shr<8>(x);
+      lg[j] = x;
+    }
+    if (r == 15) {
+#pragma unroll
+      for (int j = 0; j < 32; j += 4)
+        *reinterpret_cast<float4*>(&sm.tot[w][32 * (j >> 3) + 8 * cg + (j & 7)]) =
+            make_float4(lg[j], lg[j + 1], lg[j + 2], lg[j + 3]);
+    }
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const float ert = __builtin_amdgcn_exp2f(row_bcast<15>(lg[j]) - lg[j]);  // <= 1
+      const float elt = __builtin_amdgcn_rcpf(ert);                             // >= 1
+      const float qn = qh[j] * rq, kn = kh[j] * rk;
+      lq[j] = qn * elt;
+      lk[j] = kn * elt;
+      kr[j] = kn * ert;
+    }
+  }
+
+  // diagonal block (w, w) of M and A on fp32 MFMA: k-step s takes element s
+  // from every lane (the same channel on both operands)
+  {
+    f32x4 accM[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    f32x4 accA[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int s = 0; s < 32; ++s) {
+      accM[s & 1] = mfma16f(lq[s], kr[s], accM[s & 1]);
+      accA[s & 1] = mfma16f(lk[s], kr[s], accA[s & 1]);
+    }
+    store_block(sm, accM[0] + accM[1], accA[0] + accA[1], w, w, l, true, beta_mine);
+    // blocks above the diagonal are read by the chain's MFMAs: zero them
+    const bf16 z = (bf16)0.f;
+#pragma unroll 1
+    for (int bb = w + 1; bb < 4; ++bb)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        sm.Mhi[16 * w + 4 * (l >> 4) + qq][16 * bb + (l & 15)] = z;
+        sm.Mlo[16 * w + 4 * (l >> 4) + qq][16 * bb + (l & 15)] = z;
+      }
+    if (w < 3) {
+      // right operand of the pairs (a > w, w): kh_i e^{G_end(w) - G_i} <= 1
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        f16x8 rv;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) rv[j] = (_Float16)kr[8 * s + j];
+        sm.u2.R[w][s][l] = rv;
+      }
+    }
+  }
+  __syncthreads();  // B1: tot, beta, R, diagonal A / M visible
+  fill_tables(sm, tid);
+  __syncthreads();  // B2: decay tables visible
+
+  // ---- operand tiles of the chain: Qt = lq e^{G_end(w)}, Kt = -lk e^{G_end(w)},
+  //      KbT = kr e^{G_c - G_end(w)}
+#pragma unroll
+  for (int j0 = 0; j0 < 32; j0 += 8) {
+    float fq[8], fk[8];
+    {
+      const float4 a = *reinterpret_cast<const float4*>(&sm.etab[w][4 * j0 + 8 * cg]);
+      const float4 b = *reinterpret_cast<const float4*>(&sm.etab[w][4 * j0 + 8 * cg + 4]);
+      fq[0] = a.x; fq[1] = a.y; fq[2] = a.z; fq[3] = a.w;
+      fq[4] = b.x; fq[5] = b.y; fq[6] = b.z; fq[7] = b.w;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) fk[j] = 1.f;
+    if (w < 3) {
+      const float4 a = *reinterpret_cast<const float4*>(&sm.etab[4 + w][4 * j0 + 8 * cg]);
+      const float4 b = *reinterpret_cast<const float4*>(&sm.etab[4 + w][4 * j0 + 8 * cg + 4]);
+      fk[0] = a.x; fk[1] = a.y; fk[2] = a.z; fk[3] = a.w;
+      fk[4] = b.x; fk[5] = b.y; fk[6] = b.z; fk[7] = b.w;
+    }
+    bf16x8 qt, kt;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      qt[j] = (bf16)(lq[j0 + j] * fq[j]);
+      kt[j] = (bf16)(-lk[j0 + j] * fq[j]);
+      sm.KbT[4 * j0 + 8 * cg + j][tok] = (bf16)(kr[j0 + j] * fk[j]);
+    }
+    *reinterpret_cast<bf16x8*>(&sm.Qt[tok][4 * j0 + 8 * cg]) = qt;
+    *reinterpret_cast<bf16x8*>(&sm.Kt[tok][4 * j0 + 8 * cg]) = kt;
+  }
+
+  // ---- off-diagonal blocks (w, b), b < w, on fp16 MFMA:
+  //      left x_r e^{G_r - G_end(b)} = l{q,k} e^{G_end(w) - G_end(b)} <= 1
+#pragma unroll 1
+  for (int b = 0; b < w; ++b) {
+    const float* fr = sm.etab[7 + (w * (w - 1)) / 2 + b];
+    f32x4 accM[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    f32x4 accA[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const f16x8 rv = sm.u2.R[b][s][l];
+      const float4 fa = *reinterpret_cast<const float4*>(&fr[32 * s + 8 * cg]);
+      const float4 fb = *reinterpret_cast<const float4*>(&fr[32 * s + 8 * cg + 4]);
+      const float f[8] = {fa.x, fa.y, fa.z, fa.w, fb.x, fb.y, fb.z, fb.w};
+      f16x8 lqv, lkv;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        lqv[j] = (_Float16)(lq[8 * s + j] * f[j]);
+        lkv[j] = (_Float16)(lk[8 * s + j] * f[j]);
+      }
+      accM[s & 1] = mfma16h(lqv, rv, accM[s & 1]);
+      accA[s & 1] = mfma16h(lkv, rv, accA[s & 1]);
+    }
+    store_block(sm, accM[0] + accM[1], accA[0] + accA[1], w, b, l, false, beta_mine);
+  }
+
+  __syncthreads();  // B3: A and M complete, R dead
+
+  // ================= T = (I + A)^-1 by 16x16 blocks =================
+  // diagonal blocks: forward substitution, lane j < 16 of wave w owns column j
+  if (l < 16) {
+    const int j = l;
+    float a4[16][16];
+#pragma unroll
+    for (int rr = 1; rr < 16; ++rr)
+#pragma unroll
+      for (int i0 = 0; i0 < rr; i0 += 4) {
+        const float4 av = *reinterpret_cast<const float4*>(&sm.u.A[16 * w + rr][16 * w + i0]);
+        a4[rr][i0] = av.x; a4[rr][i0 + 1] = av.y; a4[rr][i0 + 2] = av.z; a4[rr][i0 + 3] = av.w;
+      }
+    float x[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      float acc = (rr == j) ? 1.f : 0.f;
+#pragma unroll
+      for (int i = 0; i < rr; ++i) acc -= a4[rr][i] * x[i];
+      x[rr] = acc;
+    }
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) sm.u2.T[16 * w + rr][16 * w + j] = x[rr];
+#pragma unroll 1
+    for (int bb = w + 1; bb < 4; ++bb)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) sm.u2.T[16 * w + rr][16 * bb + j] = 0.f;
+  }
+  __syncthreads();  // B4: diagonal blocks of T visible
+  // off-diagonal blocks: wave b walks column block b downwards,
+  // T_ab = -T_aa sum_{k=b}^{a-1} A_ak T_kb, on 16x16x16 MFMAs with hi + lo operands
+  if (w < 3) {
+    const int b = w;
+    const int c = l & 15, g4 = 4 * (l >> 4);
+#pragma unroll 1
+    for (int a = b + 1; a < 4; ++a) {
+      f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+      for (int kb = b; kb < a; ++kb) {
+        const float4 av = *reinterpret_cast<const float4*>(&sm.u.A[16 * a + c][16 * kb + g4]);
+        const float tv[4] = {sm.u2.T[16 * kb + g4][16 * b + c], sm.u2.T[16 * kb + g4 + 1][16 * b + c],
+                             sm.u2.T[16 * kb + g4 + 2][16 * b + c], sm.u2.T[16 * kb + g4 + 3][16 * b + c]};
+        const float aa[4] = {av.x, av.y, av.z, av.w};
+        bf16x4 ah, al, bh, bl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          SPLIT_BF16(aa[i], ah[i], al[i]);
+          SPLIT_BF16(tv[i], bh[i], bl[i]);
+        }
+        Y = mfma16k16(ah, bh, Y);
+        Y = mfma16k16(al, bh, Y);
+        Y = mfma16k16(ah, bl, Y);
+      }
+      const float4 tv4 = *reinterpret_cast<const float4*>(&sm.u2.T[16 * a + c][16 * a + g4]);
+      const float ta[4] = {tv4.x, tv4.y, tv4.z, tv4.w};
+      bf16x4 th, tl, yh, yl;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        SPLIT_BF16(ta[i], th[i], tl[i]);
+        SPLIT_BF16(Y[i], yh[i], yl[i]);
+      }
+      f32x4 Z = {0.f, 0.f, 0.f, 0.f};
+      Z = mfma16k16(th, yh, Z);
+      Z = mfma16k16(tl, yh, Z);
+      Z = mfma16k16(th, yl, Z);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.u2.T[16 * a + g4 + i][16 * b + c] = -Z[i];
+    }
+  }
+  __syncthreads();  // B5: T complete
+  // Tb = T Diag(beta), split into hi + lo (overwrites A)
+#pragma unroll
+  for (int it = 0; it < 16; ++it) {
+    const int rr = 4 * it + (tid >> 6), cc = tid & 63;
+    bf16 hi, lo;
+    SPLIT_BF16(sm.u2.T[rr][cc] * sm.beta[cc], hi, lo);
+    sm.u.tb.hi[rr][cc] = hi;
+    sm.u.tb.lo[rr][cc] = lo;
+  }
+  __syncthreads();  // B6: the image is complete, T dead (its space stages O)
+}
+
+// The state-dependent part of a chunk of n tokens starting at token c0, from
+// the image in LDS and this chunk's V (wave w owns value columns 32 w ..):
+//   X = V - Kt S,  U = Tb X,  O = scale (Qt S + M U),  S <- D S + KbT U.
+// mid() runs once V has been consumed (it may refill vcur).
+template <class Mid>
+__device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChunk& vcur, int n,
+                                            int64_t c0, int H, int h, bf16* __restrict__ out,
+                                            const Lane& ln, const Offsets& of, Mid mid) {
+  const int w = ln.w, l = ln.l, m = ln.m, hg = ln.hg;
+  const float scale = 0.08838834764831845f;  // 128^-1/2
+
+  // this chunk's V, transposed into the wave's staging slice (rows past
+  // the end were read as zero)
+  unsigned short (*vt)[CH + 8] = sm.u2.ws[w].vt;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = 16 * i + (l >> 2);
+    const u32x4 u = vcur.r[i];
+    const uint32_t uu[4] = {u[0], u[1], u[2], u[3]};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      vt[8 * (l & 3) + 2 * j][t] = (unsigned short)(uu[j] & 0xFFFFu);
+      vt[8 * (l & 3) + 2 * j + 1][t] = (unsigned short)(uu[j] >> 16);
+    }
+  }
+  wave_sync_lds();
+  const int rowsel = swap23(m);
+  f32x16 X[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const uint4 u = *reinterpret_cast<const uint4*>(&vt[m][32 * mt + 16 * hh + 8 * hg]);
+      const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        X[mt][8 * hh + 2 * j] = bf16_lo_to_f32(uu[j]);
+        X[mt][8 * hh + 2 * j + 1] = bf16_hi_to_f32(uu[j]);
+      }
+    }
+  wave_sync_lds();  // V read out before the slice stages O
+
+  bf16x8 Sb[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) Sb[s][j] = (bf16)S[s >> 1][8 * (s & 1) + j];
+
+  // X = V - kh e^G S (A operands loaded two k-steps ahead)
+  {
+    bf16x8 ka[2][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        ka[mt][s] = *reinterpret_cast<const bf16x8*>(&sm.Kt[32 * mt + rowsel][16 * s + 8 * hg]);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        X[mt] = mfma32(ka[mt][s & 1], Sb[s], X[mt]);
+        if (s + 2 < 8)
+          ka[mt][s & 1] = *reinterpret_cast<const bf16x8*>(&sm.Kt[32 * mt + rowsel][16 * (s + 2) + 8 * hg]);
+      }
+    }
+  }
+  bf16x8 Xb[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) Xb[s][j] = (bf16)X[s >> 1][8 * (s & 1) + j];
+
+  // U = Tb X: the six lower-triangular (row tile, k-step) pairs
+  constexpr int PMT[6] = {0, 0, 1, 1, 1, 1};
+  constexpr int PS[6] = {0, 1, 0, 1, 2, 3};
+  f32x16 U[2], U2[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { U[mt][i] = 0.f; U2[mt][i] = 0.f; }
+  {
+    bf16x8 th[6], tl[6];
+#pragma unroll
+    for (int p = 0; p < 6; ++p) {
+      th[p] = *reinterpret_cast<const bf16x8*>(&sm.u.tb.hi[32 * PMT[p] + rowsel][16 * PS[p] + 8 * hg]);
+      tl[p] = *reinterpret_cast<const bf16x8*>(&sm.u.tb.lo[32 * PMT[p] + rowsel][16 * PS[p] + 8 * hg]);
+    }
+    // order (1,0) (0,0) (1,1) (0,1) (1,2) (1,3): the two row tiles alternate
+    constexpr int ORD[6] = {2, 0, 3, 1, 4, 5};
+#pragma unroll
+    for (int o = 0; o < 6; ++o) {
+      const int p = ORD[o];
+      U[PMT[p]] = mfma32(th[p], Xb[PS[p]], U[PMT[p]]);
+      U2[PMT[p]] = mfma32(tl[p], Xb[PS[p]], U2[PMT[p]]);
+    }
+    U[0] += U2[0];
+    U[1] += U2[1];
+  }
+  bf16x8 Ubh[4], Ubl[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) SPLIT_BF16(U[s >> 1][8 * (s & 1) + j], Ubh[s][j], Ubl[s][j]);
+
+  mid();
+
+  // O = scale (qh e^G S + M U), staged through LDS for 16-byte stores;
+  // four independent accumulators (row tile x {Qt S, M U})
+  unsigned short (*ost)[32] = sm.u2.ws[w].o;
+  {
+    f32x16 OQ[2], OM[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) { OQ[mt][i] = 0.f; OM[mt][i] = 0.f; }
+    bf16x8 qa[2][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        qa[mt][s] = *reinterpret_cast<const bf16x8*>(&sm.Qt[32 * mt + rowsel][16 * s + 8 * hg]);
+    bf16x8 mh[6], ml[6];
+#pragma unroll
+    for (int p = 0; p < 6; ++p) {
+      mh[p] = *reinterpret_cast<const bf16x8*>(&sm.Mhi[32 * PMT[p] + rowsel][16 * PS[p] + 8 * hg]);
+      ml[p] = *reinterpret_cast<const bf16x8*>(&sm.Mlo[32 * PMT[p] + rowsel][16 * PS[p] + 8 * hg]);
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        OQ[mt] = mfma32(qa[mt][s & 1], Sb[s], OQ[mt]);
+        if (s + 2 < 8)
+          qa[mt][s & 1] = *reinterpret_cast<const bf16x8*>(&sm.Qt[32 * mt + rowsel][16 * (s + 2) + 8 * hg]);
+      }
+      if (s < 6) {
+        const int p = s;
+        OM[PMT[p]] = mfma32(mh[p], Ubh[PS[p]], OM[PMT[p]]);
+        OM[PMT[p]] = mfma32(ml[p], Ubh[PS[p]], OM[PMT[p]]);
+        OM[PMT[p]] = mfma32(mh[p], Ubl[PS[p]], OM[PMT[p]]);
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int t = 32 * mt + 16 * (i >> 3) + 8 * hg + (i & 7);
+        const bf16 ob = (bf16)((OQ[mt][i] + OM[mt][i]) * scale);
+        ost[t][m] = __builtin_bit_cast(unsigned short, ob);
+      }
+  }
+
+  // S <- e^{G_c} S + (kh e^{G_c - G})^T U  (the four row tiles interleaved)
+  {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i0 = 0; i0 < 16; i0 += 8) {
+        const int c = 32 * kt + 16 * (i0 >> 3) + 8 * hg;
+        const float4 d0 = *reinterpret_cast<const float4*>(dvec(sm, c));
+        const float4 d1 = *reinterpret_cast<const float4*>(dvec(sm, c + 4));
+        S[kt][i0 + 0] *= d0.x; S[kt][i0 + 1] *= d0.y; S[kt][i0 + 2] *= d0.z; S[kt][i0 + 3] *= d0.w;
+        S[kt][i0 + 4] *= d1.x; S[kt][i0 + 5] *= d1.y; S[kt][i0 + 6] *= d1.z; S[kt][i0 + 7] *= d1.w;
+      }
+    bf16x8 kb[2][4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+      kb[0][kt] = *reinterpret_cast<const bf16x8*>(&sm.KbT[32 * kt + rowsel][8 * hg]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        if (s + 1 < 4)
+          kb[(s + 1) & 1][kt] = *reinterpret_cast<const bf16x8*>(&sm.KbT[32 * kt + rowsel][16 * (s + 1) + 8 * hg]);
+        S[kt] = mfma32(kb[s & 1][kt], Ubh[s], S[kt]);
+      }
+    }
+  }
+
+  // O rows: lane l writes 16 bytes of row 16 it + l / 4 (rows past the end
+  // are dropped by the descriptor's range)
+  wave_sync_lds();
+  const Rsrc ro = make_rsrc(out + ((size_t)c0 * H + h) * DV, chunk_bytes(n, H, 256u));
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int t = 16 * it + (l >> 2);
+    bstore(*reinterpret_cast<const u32x4*>(&ost[t][8 * (l & 3)]), ro, of.v[it]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// pre kernel: the state-independent part of every chunk of the split
+// documents, in parallel, written out as images
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(NTHR, 1) void kda_pre_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
+    const float* __restrict__ beta, WorkHeader* __restrict__ hdr,
+    const int2* __restrict__ pre_chunks, uint8_t* __restrict__ images, int H, float gate_bound) {
+  __shared__ Smem sm;
+  const Lane ln = make_lane();
+  if (hdr->status != 0) return;
+  const int n_units = hdr->n_pre_units;
+  if (n_units == 0) return;
+  const Offsets of = make_offsets(H, ln.tok, ln.cg, ln.w, ln.l);
+  if (ln.tid == 0) {
+    sm.gate_bad = 0;
+    sm.next_unit = atomicAdd(&hdr->pre_counter, 1);
+  }
+  __syncthreads();
+  int unit = __builtin_amdgcn_readfirstlane(sm.next_unit);
+  RawChunk cur;
+  int2 ch = make_int2(0, 0);
+  if (unit < n_units) {
+    ch = pre_chunks[unit / H];
+    load_raw(cur, q, k, g, beta, ch.x, ch.y, H, unit % H, of);
+  }
+  while (unit < n_units) {
+    __syncthreads();  // every lane has read next_unit
+    if (ln.tid == 0) sm.next_unit = atomicAdd(&hdr->pre_counter, 1);
+    __syncthreads();
+    const int next = __builtin_amdgcn_readfirstlane(sm.next_unit);
+    const int h = unit % H;
+    const int2 nch = (next < n_units) ? pre_chunks[next / H] : make_int2(0, 0);
+    prepare_chunk(sm, cur, ch.y, gate_bound, ln, [&] {
+      load_raw(cur, q, k, g, beta, nch.x, (next < n_units) ? nch.y : 0, H, next % H, of);
+    });
+    lds_to_global_image(images + ((size_t)(unit / H) * H + h) * IMG_BYTES, sm, ln.tid);
+    unit = next;
+    ch = nch;
+  }
+  __syncthreads();
+  if (ln.tid == 0 && sm.gate_bad) atomicOr(&g_kda_status, KDA_DEV_GATE_RANGE);
+}
+
+// ---------------------------------------------------------------------------
+// main kernel: one (document, head) unit at a time; fused documents prepare
+// and chain each chunk, split documents chain precomputed images
+// ---------------------------------------------------------------------------
 __global__ __launch_bounds__(NTHR, 1) void kda_chunk_fwd_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, bf16* __restrict__ out,
-    WorkHeader* __restrict__ hdr, const int2* __restrict__ docs, int64_t T, int H,
-    float gate_bound) {
+    WorkHeader* __restrict__ hdr, const int2* __restrict__ docs, const int2* __restrict__ split,
+    const uint8_t* __restrict__ images, int64_t T, int H, float gate_bound) {
   __shared__ Smem sm;
-  const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave (scalar)
-  const int l = tid & 63;      // lane
-  const int r = l & 15;        // prologue: token inside the 16-token sub-block
-  const int cg = l >> 4;       // prologue: channel group (32 channels)
-  const int m = l & 31;        // chain: MFMA row / column lane index
-  const int hg = l >> 5;       // chain: lane half
-  const int tok = 16 * w + r;  // prologue: token of this lane inside the chunk
-  const float scale = 0.08838834764831845f;  // 128^-1/2
+  const Lane ln = make_lane();
+  const int tid = ln.tid, w = ln.w, l = ln.l;
 
   if (hdr->status != 0) {
     // cu_seqlens was rejected on the device: make the failure visible
@@ -419,18 +1084,18 @@ __global__ __launch_bounds__(NTHR, 1) void kda_chunk_fwd_kernel(
     return;
   }
   const int n_units = hdr->n_units;
+  const Offsets of = make_offsets(H, ln.tok, ln.cg, w, l);
   if (tid == 0) sm.gate_bad = 0;
 
   for (;;) {
     __syncthreads();
     if (tid == 0) sm.unit = atomicAdd(&hdr->counter, 1);
     __syncthreads();
-    const int unit = sm.unit;
+    const int unit = __builtin_amdgcn_readfirstlane(sm.unit);
     if (unit >= n_units) break;
     const int di = unit / H;
     const int h = unit - di * H;
     const int2 doc = docs[di];
-    const int64_t bos = doc.x, eos = (int64_t)doc.x + doc.y;
 
     f32x16 S[4];
 #pragma unroll
@@ -438,447 +1103,50 @@ __global__ __launch_bounds__(NTHR, 1) void kda_chunk_fwd_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) S[kt][i] = 0.f;
 
-    RawChunk cur;
-    VChunk vcur;
-    {
-      const int n0 = (int)min<int64_t>(CH, eos - bos);
-      load_raw(cur, q, k, g, beta, bos + tok, tok < n0, H, h, cg);
-      vcur = load_v(v, bos, n0, H, h, w, l);
-    }
-
-    for (int64_t c0 = bos; c0 < eos; c0 += CH) {
-      const int n = (int)min<int64_t>(CH, eos - c0);
-
-      // ================= prologue: l2 norm, cumulative decay =================
-      // lane (w, r, cg): token 16w + r of the chunk; element 8 s + j is channel
-      // 32 s + 8 cg + j (k-step s of the 16x16x32 MFMAs takes elements 8 s .. 8 s + 7).
-      // lq, lk: qh, kh times e^{G - G_end(w)} (>= 1); kr: kh e^{G_end(w) - G} (<= 1),
-      // where G_end(w) is the cumulative decay at the last token of sub-block w.
-      float lq[32], lk[32], kr[32];
-      const float beta_mine = cur.beta;
+    if (doc.x < 0) {
+      // ---- split document: chain over precomputed images
+      const int2 sp = split[-doc.x - 1];
+      const int64_t bos = sp.x, eos = (int64_t)sp.x + doc.y;
+      const uint8_t* img = images + ((size_t)sp.y * H + h) * IMG_BYTES;
+      const size_t img_stride = (size_t)H * IMG_BYTES;
+      Image im;
+      load_image(im, img, tid);
+      VChunk vcur = load_v(v, bos, (int)min<int64_t>(CH, eos - bos), H, h, of);
+      for (int64_t c0 = bos; c0 < eos; c0 += CH) {
+        const int n = (int)min<int64_t>(CH, eos - c0);
+        image_to_lds(sm, im, tid);
+        __syncthreads();  // the image is in LDS
+        img += img_stride;
+        const int64_t c1 = c0 + CH;
+        const int n1 = (int)min<int64_t>(CH, eos - c1);
+        if (c1 < eos) load_image(im, img, tid);
+        chain_chunk(sm, S, vcur, n, c0, H, h, out, ln, of, [&] {
+          vcur = load_v(v, c1, n1, H, h, of);
+        });
+        __syncthreads();  // the next chunk overwrites the image
+      }
+    } else {
+      // ---- fused document: prepare and chain each chunk here
+      const int64_t bos = doc.x, eos = (int64_t)doc.x + doc.y;
+      RawChunk cur;
+      VChunk vcur;
       {
-        float qh[32], kh[32], lg[32];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t qa[4] = {cur.q[i].x, cur.q[i].y, cur.q[i].z, cur.q[i].w};
-          const uint32_t ka[4] = {cur.k[i].x, cur.k[i].y, cur.k[i].z, cur.k[i].w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            qh[8 * i + 2 * j] = bf16_lo_to_f32(qa[j]);
-            qh[8 * i + 2 * j + 1] = bf16_hi_to_f32(qa[j]);
-            kh[8 * i + 2 * j] = bf16_lo_to_f32(ka[j]);
-            kh[8 * i + 2 * j + 1] = bf16_hi_to_f32(ka[j]);
-          }
-        }
-        float gmin = 0.f, gmax = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float ga[4] = {cur.g[i].x, cur.g[i].y, cur.g[i].z, cur.g[i].w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            gmin = fminf(gmin, ga[j]);
-            gmax = fmaxf(gmax, ga[j]);
-            lg[4 * i + j] = ga[j] * 1.4426950408889634f;  // log2 domain
-          }
-        }
-        if (tok < n && !(gmin >= gate_bound && gmax <= 0.f)) sm.gate_bad = 1;
-        if (cg == 0) sm.beta[tok] = cur.beta;
-        float sq = 0.f, sk = 0.f;
-#pragma unroll
-        for (int j = 0; j < 32; ++j) { sq += qh[j] * qh[j]; sk += kh[j] * kh[j]; }
-        sq += __shfl_xor(sq, 16);
-        sq += __shfl_xor(sq, 32);
-        sk += __shfl_xor(sk, 16);
-        sk += __shfl_xor(sk, 32);
-        const float rq = 1.0f / sqrtf(sq + L2_EPS);
-        const float rk = 1.0f / sqrtf(sk + L2_EPS);
-        // inclusive scan over the 16 tokens of the sub-block (one 16-lane row)
-#pragma unroll
-        for (int j = 0; j < 32; ++j) {
-          float x = lg[j];
-          x += dpp_row_shr<1>(x);
-          x += dpp_row_shr<2>(x);
-          x += dpp_row_shr<4>(x);
-          x += dpp_row_shr<8>(x);
-          lg[j] = x;
-        }
-        if (r == 15) {
-#pragma unroll
-          for (int j = 0; j < 32; j += 4)
-            *reinterpret_cast<float4*>(&sm.tot[w][32 * (j >> 3) + 8 * cg + (j & 7)]) =
-                make_float4(lg[j], lg[j + 1], lg[j + 2], lg[j + 3]);
-        }
-#pragma unroll
-        for (int j = 0; j < 32; ++j) {
-          const float ert = __builtin_amdgcn_exp2f(row_bcast<15>(lg[j]) - lg[j]);  // <= 1
-          const float elt = __builtin_amdgcn_rcpf(ert);                             // >= 1
-          const float qn = qh[j] * rq, kn = kh[j] * rk;
-          lq[j] = qn * elt;
-          lk[j] = kn * elt;
-          kr[j] = kn * ert;
-        }
+        const int n0 = (int)min<int64_t>(CH, eos - bos);
+        load_raw(cur, q, k, g, beta, bos, n0, H, h, of);
+        vcur = load_v(v, bos, n0, H, h, of);
       }
-
-      // diagonal block (w, w) of M and A on fp32 MFMA: k-step s takes element s
-      // from every lane (the same channel on both operands)
-      {
-        f32x4 accM[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-        f32x4 accA[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int s = 0; s < 32; ++s) {
-          accM[s & 1] = mfma16f(lq[s], kr[s], accM[s & 1]);
-          accA[s & 1] = mfma16f(lk[s], kr[s], accA[s & 1]);
-        }
-        store_block(sm, accM[0] + accM[1], accA[0] + accA[1], w, w, l, true, beta_mine);
-        // blocks above the diagonal are read by the chain's MFMAs: zero them
-        const bf16 z = (bf16)0.f;
-#pragma unroll 1
-        for (int bb = w + 1; bb < 4; ++bb)
-#pragma unroll
-          for (int qq = 0; qq < 4; ++qq) {
-            sm.Mhi[16 * w + 4 * (l >> 4) + qq][16 * bb + (l & 15)] = z;
-            sm.Mlo[16 * w + 4 * (l >> 4) + qq][16 * bb + (l & 15)] = z;
-          }
-        if (w < 3) {
-          // right operand of the pairs (a > w, w): kh_i e^{G_end(w) - G_i} <= 1
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            f16x8 rv;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) rv[j] = (_Float16)kr[8 * s + j];
-            sm.u2.R[w][s][l] = rv;
-          }
-        }
+      for (int64_t c0 = bos; c0 < eos; c0 += CH) {
+        const int n = (int)min<int64_t>(CH, eos - c0);
+        const int64_t c1 = c0 + CH;
+        const int n1 = (int)min<int64_t>(CH, eos - c1);
+        prepare_chunk(sm, cur, n, gate_bound, ln, [&] {
+          load_raw(cur, q, k, g, beta, c1, n1, H, h, of);
+        });
+        chain_chunk(sm, S, vcur, n, c0, H, h, out, ln, of, [&] {
+          vcur = load_v(v, c1, n1, H, h, of);
+        });
+        __syncthreads();  // the next chunk overwrites every LDS tile
       }
-      __syncthreads();  // B1: tot, beta, R, diagonal A / M visible
-      fill_tables(sm, tid);
-      __syncthreads();  // B2: decay tables visible
-
-      // ---- operand tiles of the chain: Qt = lq e^{G_end(w)}, Kt = -lk e^{G_end(w)},
-      //      KbT = kr e^{G_c - G_end(w)}
-#pragma unroll
-      for (int j0 = 0; j0 < 32; j0 += 8) {
-        float fq[8], fk[8];
-        {
-          const float4 a = *reinterpret_cast<const float4*>(&sm.etab[w][4 * j0 + 8 * cg]);
-          const float4 b = *reinterpret_cast<const float4*>(&sm.etab[w][4 * j0 + 8 * cg + 4]);
-          fq[0] = a.x; fq[1] = a.y; fq[2] = a.z; fq[3] = a.w;
-          fq[4] = b.x; fq[5] = b.y; fq[6] = b.z; fq[7] = b.w;
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) fk[j] = 1.f;
-        if (w < 3) {
-          const float4 a = *reinterpret_cast<const float4*>(&sm.etab[4 + w][4 * j0 + 8 * cg]);
-          const float4 b = *reinterpret_cast<const float4*>(&sm.etab[4 + w][4 * j0 + 8 * cg + 4]);
-          fk[0] = a.x; fk[1] = a.y; fk[2] = a.z; fk[3] = a.w;
-          fk[4] = b.x; fk[5] = b.y; fk[6] = b.z; fk[7] = b.w;
-        }
-        bf16x8 qt, kt;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          qt[j] = (bf16)(lq[j0 + j] * fq[j]);
-          kt[j] = (bf16)(-lk[j0 + j] * fq[j]);
-          sm.KbT[4 * j0 + 8 * cg + j][tok] = (bf16)(kr[j0 + j] * fk[j]);
-        }
-        *reinterpret_cast<bf16x8*>(&sm.Qt[tok][4 * j0 + 8 * cg]) = qt;
-        *reinterpret_cast<bf16x8*>(&sm.Kt[tok][4 * j0 + 8 * cg]) = kt;
-      }
-
-      // ---- off-diagonal blocks (w, b), b < w, on fp16 MFMA:
-      //      left x_r e^{G_r - G_end(b)} = l{q,k} e^{G_end(w) - G_end(b)} <= 1
-#pragma unroll 1
-      for (int b = 0; b < w; ++b) {
-        const float* fr = sm.etab[7 + (w * (w - 1)) / 2 + b];
-        f32x4 accM[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-        f32x4 accA[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const f16x8 rv = sm.u2.R[b][s][l];
-          const float4 fa = *reinterpret_cast<const float4*>(&fr[32 * s + 8 * cg]);
-          const float4 fb = *reinterpret_cast<const float4*>(&fr[32 * s + 8 * cg + 4]);
-          const float f[8] = {fa.x, fa.y, fa.z, fa.w, fb.x, fb.y, fb.z, fb.w};
-          f16x8 lqv, lkv;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            lqv[j] = (_Float16)(lq[8 * s + j] * f[j]);
-            lkv[j] = (_Float16)(lk[8 * s + j] * f[j]);
-          }
-          accM[s & 1] = mfma16h(lqv, rv, accM[s & 1]);
-          accA[s & 1] = mfma16h(lkv, rv, accA[s & 1]);
-        }
-        store_block(sm, accM[0] + accM[1], accA[0] + accA[1], w, b, l, false, beta_mine);
-      }
-
-      __syncthreads();  // B3: A and M complete, R dead
-
-      // ================= T = (I + A)^-1 by 16x16 blocks =================
-      // diagonal blocks: forward substitution, lane j < 16 of wave w owns column j
-      if (l < 16) {
-        const int j = l;
-        float a4[16][16];
-#pragma unroll
-        for (int rr = 1; rr < 16; ++rr)
-#pragma unroll
-          for (int i0 = 0; i0 < rr; i0 += 4) {
-            const float4 av = *reinterpret_cast<const float4*>(&sm.u.A[16 * w + rr][16 * w + i0]);
-            a4[rr][i0] = av.x; a4[rr][i0 + 1] = av.y; a4[rr][i0 + 2] = av.z; a4[rr][i0 + 3] = av.w;
-          }
-        float x[16];
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          float acc = (rr == j) ? 1.f : 0.f;
-#pragma unroll
-          for (int i = 0; i < rr; ++i) acc -= a4[rr][i] * x[i];
-          x[rr] = acc;
-        }
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) sm.u2.T[16 * w + rr][16 * w + j] = x[rr];
-#pragma unroll 1
-        for (int bb = w + 1; bb < 4; ++bb)
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) sm.u2.T[16 * w + rr][16 * bb + j] = 0.f;
-      }
-      __syncthreads();  // B4: diagonal blocks of T visible
-      // off-diagonal blocks: wave b walks column block b downwards,
-      // T_ab = -T_aa sum_{k=b}^{a-1} A_ak T_kb, on 16x16x16 MFMAs with hi + lo operands
-      if (w < 3) {
-        const int b = w;
-        const int c = l & 15, g4 = 4 * (l >> 4);
-#pragma unroll 1
-        for (int a = b + 1; a < 4; ++a) {
-          f32x4 Y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1
-          for (int kb = b; kb < a; ++kb) {
-            const float4 av = *reinterpret_cast<const float4*>(&sm.u.A[16 * a + c][16 * kb + g4]);
-            const float tv[4] = {sm.u2.T[16 * kb + g4][16 * b + c], sm.u2.T[16 * kb + g4 + 1][16 * b + c],
-                                 sm.u2.T[16 * kb + g4 + 2][16 * b + c], sm.u2.T[16 * kb + g4 + 3][16 * b + c]};
-            const float aa[4] = {av.x, av.y, av.z, av.w};
-            bf16x4 ah, al, bh, bl;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              SPLIT_BF16(aa[i], ah[i], al[i]);
-              SPLIT_BF16(tv[i], bh[i], bl[i]);
-            }
-            Y = mfma16k16(ah, bh, Y);
-            Y = mfma16k16(al, bh, Y);
-            Y = mfma16k16(ah, bl, Y);
-          }
-          const float4 tv4 = *reinterpret_cast<const float4*>(&sm.u2.T[16 * a + c][16 * a + g4]);
-          const float ta[4] = {tv4.x, tv4.y, tv4.z, tv4.w};
-          bf16x4 th, tl, yh, yl;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            SPLIT_BF16(ta[i], th[i], tl[i]);
-            SPLIT_BF16(Y[i], yh[i], yl[i]);
-          }
-          f32x4 Z = {0.f, 0.f, 0.f, 0.f};
-          Z = mfma16k16(th, yh, Z);
-          Z = mfma16k16(tl, yh, Z);
-          Z = mfma16k16(th, yl, Z);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sm.u2.T[16 * a + g4 + i][16 * b + c] = -Z[i];
-        }
-      }
-      __syncthreads();  // B5: T complete
-      // Tb = T Diag(beta), split into hi + lo (overwrites A)
-#pragma unroll
-      for (int it = 0; it < 16; ++it) {
-        const int rr = 4 * it + (tid >> 6), cc = tid & 63;
-        bf16 hi, lo;
-        SPLIT_BF16(sm.u2.T[rr][cc] * sm.beta[cc], hi, lo);
-        sm.u.tb.hi[rr][cc] = hi;
-        sm.u.tb.lo[rr][cc] = lo;
-      }
-      __syncthreads();  // B6: Tb visible, T dead (its space stages O)
-
-      // ================= the chain: X, U, O, S (wave w owns V columns 32w..) ====
-      {
-        // this chunk's V, transposed into the wave's staging slice (rows past
-        // the end are zero)
-        unsigned short (*vt)[CH + 8] = sm.u2.ws[w].vt;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = 16 * i + (l >> 2);
-          const uint4 u = (t < n) ? vcur.r[i] : make_uint4(0, 0, 0, 0);
-          const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            vt[8 * (l & 3) + 2 * j][t] = (unsigned short)(uu[j] & 0xFFFFu);
-            vt[8 * (l & 3) + 2 * j + 1][t] = (unsigned short)(uu[j] >> 16);
-          }
-        }
-        wave_sync_lds();
-        const int rowsel = swap23(m);
-        f32x16 X[2];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const uint4 u = *reinterpret_cast<const uint4*>(&vt[m][32 * mt + 16 * hh + 8 * hg]);
-            const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              X[mt][8 * hh + 2 * j] = bf16_lo_to_f32(uu[j]);
-              X[mt][8 * hh + 2 * j + 1] = bf16_hi_to_f32(uu[j]);
-            }
-          }
-        wave_sync_lds();  // V read out before the slice stages O
-
-        bf16x8 Sb[8];
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) Sb[s][j] = (bf16)S[s >> 1][8 * (s & 1) + j];
-
-        // X = V - kh e^G S (A operands loaded two k-steps ahead)
-        {
-          bf16x8 ka[2][2];
-#pragma unroll
-          for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-              ka[mt][s] = *reinterpret_cast<const bf16x8*>(&sm.Kt[32 * mt + rowsel][16 * s + 8 * hg]);
-#pragma unroll
-          for (int s = 0; s < 8; ++s) {
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-              X[mt] = mfma32(ka[mt][s & 1], Sb[s], X[mt]);
-              if (s + 2 < 8)
-                ka[mt][s & 1] = *reinterpret_cast<const bf16x8*>(&sm.Kt[32 * mt + rowsel][16 * (s + 2) + 8 * hg]);
-            }
-          }
-        }
-        bf16x8 Xb[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) Xb[s][j] = (bf16)X[s >> 1][8 * (s & 1) + j];
-
-        // U = Tb X: the six lower-triangular (row tile, k-step) pairs
-        constexpr int PMT[6] = {0, 0, 1, 1, 1, 1};
-        constexpr int PS[6] = {0, 1, 0, 1, 2, 3};
-        f32x16 U[2], U2[2];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) { U[mt][i] = 0.f; U2[mt][i] = 0.f; }
-        {
-          bf16x8 th[6], tl[6];
-#pragma unroll
-          for (int p = 0; p < 6; ++p) {
-            th[p] = *reinterpret_cast<const bf16x8*>(&sm.u.tb.hi[32 * PMT[p] + rowsel][16 * PS[p] + 8 * hg]);
-            tl[p] = *reinterpret_cast<const bf16x8*>(&sm.u.tb.lo[32 * PMT[p] + rowsel][16 * PS[p] + 8 * hg]);
-          }
-          // order (1,0) (0,0) (1,1) (0,1) (1,2) (1,3): the two row tiles alternate
-          constexpr int ORD[6] = {2, 0, 3, 1, 4, 5};
-#pragma unroll
-          for (int o = 0; o < 6; ++o) {
-            const int p = ORD[o];
-            U[PMT[p]] = mfma32(th[p], Xb[PS[p]], U[PMT[p]]);
-            U2[PMT[p]] = mfma32(tl[p], Xb[PS[p]], U2[PMT[p]]);
-          }
-          U[0] += U2[0];
-          U[1] += U2[1];
-        }
-        bf16x8 Ubh[4], Ubl[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) SPLIT_BF16(U[s >> 1][8 * (s & 1) + j], Ubh[s][j], Ubl[s][j]);
-
-        // the next chunk's inputs land during the rest of this chunk and the
-        // next chunk's prologue
-        {
-          const int64_t c1 = c0 + CH;
-          const int n1 = (int)min<int64_t>(CH, eos - c1);
-          load_raw(cur, q, k, g, beta, c1 + tok, c1 < eos && tok < n1, H, h, cg);
-          if (c1 < eos) vcur = load_v(v, c1, n1, H, h, w, l);
-        }
-
-        // O = scale (qh e^G S + M U), staged through LDS for 16-byte stores;
-        // four independent accumulators (row tile x {Qt S, M U})
-        unsigned short (*ost)[32] = sm.u2.ws[w].o;
-        {
-          f32x16 OQ[2], OM[2];
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) { OQ[mt][i] = 0.f; OM[mt][i] = 0.f; }
-          bf16x8 qa[2][2];
-#pragma unroll
-          for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-              qa[mt][s] = *reinterpret_cast<const bf16x8*>(&sm.Qt[32 * mt + rowsel][16 * s + 8 * hg]);
-          bf16x8 mh[6], ml[6];
-#pragma unroll
-          for (int p = 0; p < 6; ++p) {
-            mh[p] = *reinterpret_cast<const bf16x8*>(&sm.Mhi[32 * PMT[p] + rowsel][16 * PS[p] + 8 * hg]);
-            ml[p] = *reinterpret_cast<const bf16x8*>(&sm.Mlo[32 * PMT[p] + rowsel][16 * PS[p] + 8 * hg]);
-          }
-#pragma unroll
-          for (int s = 0; s < 8; ++s) {
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-              OQ[mt] = mfma32(qa[mt][s & 1], Sb[s], OQ[mt]);
-              if (s + 2 < 8)
-                qa[mt][s & 1] = *reinterpret_cast<const bf16x8*>(&sm.Qt[32 * mt + rowsel][16 * (s + 2) + 8 * hg]);
-            }
-            if (s < 6) {
-              const int p = s;
-              OM[PMT[p]] = mfma32(mh[p], Ubh[PS[p]], OM[PMT[p]]);
-              OM[PMT[p]] = mfma32(ml[p], Ubh[PS[p]], OM[PMT[p]]);
-              OM[PMT[p]] = mfma32(mh[p], Ubl[PS[p]], OM[PMT[p]]);
-            }
-          }
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int t = 32 * mt + 16 * (i >> 3) + 8 * hg + (i & 7);
-              const bf16 ob = (bf16)((OQ[mt][i] + OM[mt][i]) * scale);
-              ost[t][m] = __builtin_bit_cast(unsigned short, ob);
-            }
-        }
-
-        // S <- e^{G_c} S + (kh e^{G_c - G})^T U  (the four row tiles interleaved)
-        {
-#pragma unroll
-          for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int i0 = 0; i0 < 16; i0 += 8) {
-              const float* dp = &sm.etab[3][32 * kt + 16 * (i0 >> 3) + 8 * hg];
-              const float4 d0 = *reinterpret_cast<const float4*>(dp);
-              const float4 d1 = *reinterpret_cast<const float4*>(dp + 4);
-              S[kt][i0 + 0] *= d0.x; S[kt][i0 + 1] *= d0.y; S[kt][i0 + 2] *= d0.z; S[kt][i0 + 3] *= d0.w;
-              S[kt][i0 + 4] *= d1.x; S[kt][i0 + 5] *= d1.y; S[kt][i0 + 6] *= d1.z; S[kt][i0 + 7] *= d1.w;
-            }
-          bf16x8 kb[2][4];
-#pragma unroll
-          for (int kt = 0; kt < 4; ++kt)
-            kb[0][kt] = *reinterpret_cast<const bf16x8*>(&sm.KbT[32 * kt + rowsel][8 * hg]);
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
-              if (s + 1 < 4)
-                kb[(s + 1) & 1][kt] = *reinterpret_cast<const bf16x8*>(&sm.KbT[32 * kt + rowsel][16 * (s + 1) + 8 * hg]);
-              S[kt] = mfma32(kb[s & 1][kt], Ubh[s], S[kt]);
-            }
-          }
-        }
-
-        // O rows: lane l writes 16 bytes of row 16 it + l / 4
-        wave_sync_lds();
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-          const int t = 16 * it + (l >> 2);
-          const uint4 val = *reinterpret_cast<const uint4*>(&ost[t][8 * (l & 3)]);
-          if (t < n)
-            *reinterpret_cast<uint4*>(out + ((size_t)(c0 + t) * H + h) * DV + 32 * w + 8 * (l & 3)) = val;
-        }
-      }
-      __syncthreads();  // the next chunk overwrites every LDS tile
     }
   }
   __syncthreads();
@@ -926,6 +1194,19 @@ int device_info(int dev, DeviceInfo** out) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// Upper bound of the chunk images of split documents in the workspace.
+constexpr size_t IMAGE_BUDGET_BYTES = size_t(16) << 30;
+
+// KDA_SPLIT=never|always overrides the automatic choice of split documents
+// (for tests; both settings give bit-identical results).
+int split_policy() {
+  const char* s = getenv("KDA_SPLIT");
+  if (s == nullptr) return SPLIT_AUTO;
+  if (strcmp(s, "never") == 0) return SPLIT_NEVER;
+  if (strcmp(s, "always") == 0) return SPLIT_ALWAYS;
+  return SPLIT_AUTO;
+}
+
 }  // namespace
 
 extern "C" int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
@@ -959,21 +1240,45 @@ extern "C" int kda_chunk_fwd(const void* q, const void* k, const void* v, const 
   DeviceInfo* di = nullptr;
   if (device_info(dev, &di) != 0) return fail(KDA_ERR_HIP, "hipDeviceGetAttribute failed");
 
-  const size_t ws_bytes = sizeof(WorkHeader) + sizeof(int2) * (size_t)T;
-  void* ws = nullptr;
-  if (hipMallocAsync(&ws, ws_bytes, stream) != hipSuccess || !ws)
+  // workspace: header | docs[T] | split[max_split] | pre_chunks[cap] | images[cap][H]
+  const int policy = split_policy();
+  const size_t max_split = std::min<size_t>((size_t)T / (CH * (MIN_SPLIT_CHUNKS - 1) + 1) + 1,
+                                            MAX_SPLIT_DOCS);
+  size_t cap_chunks = 0;
+  if (policy != SPLIT_NEVER) {
+    cap_chunks = ((size_t)T + CH - 1) / CH + max_split;
+    cap_chunks = std::min(cap_chunks, IMAGE_BUDGET_BYTES / ((size_t)H * IMG_BYTES));
+    if (cap_chunks < (size_t)MIN_SPLIT_CHUNKS) cap_chunks = 0;
+  }
+  const size_t off_docs = 256;
+  const size_t off_split = off_docs + sizeof(int2) * (size_t)T;
+  const size_t off_pre = off_split + sizeof(int2) * max_split;
+  const size_t off_img = (off_pre + sizeof(int2) * cap_chunks + 255) & ~size_t(255);
+  const size_t ws_bytes = off_img + cap_chunks * (size_t)H * IMG_BYTES;
+  uint8_t* ws = nullptr;
+  if (hipMallocAsync(reinterpret_cast<void**>(&ws), ws_bytes, stream) != hipSuccess || !ws)
     return fail(KDA_ERR_ALLOC, "hipMallocAsync of the workspace failed");
-  WorkHeader* hdr = static_cast<WorkHeader*>(ws);
-  int2* docs = reinterpret_cast<int2*>(hdr + 1);
+  WorkHeader* hdr = reinterpret_cast<WorkHeader*>(ws);
+  int2* docs = reinterpret_cast<int2*>(ws + off_docs);
+  int2* split = reinterpret_cast<int2*>(ws + off_split);
+  int2* pre_chunks = reinterpret_cast<int2*>(ws + off_pre);
+  uint8_t* images = ws + off_img;
 
   hipLaunchKernelGGL(kda_schedule_kernel, dim3(1), dim3(SCHED_THREADS), 0, stream, cu_seqlens,
-                     (int)T, (int)H, hdr, docs);
+                     (int)T, (int)H, di->num_cu, (int)cap_chunks, policy, hdr, docs, split,
+                     pre_chunks);
   hipError_t e = hipGetLastError();
+  if (e == hipSuccess && cap_chunks > 0) {
+    hipLaunchKernelGGL(kda_pre_kernel, dim3(di->num_cu), dim3(NTHR), 0, stream,
+                       static_cast<const bf16*>(q), static_cast<const bf16*>(k), g, beta, hdr,
+                       pre_chunks, images, (int)H, gate_bound);
+    e = hipGetLastError();
+  }
   if (e == hipSuccess) {
     hipLaunchKernelGGL(kda_chunk_fwd_kernel, dim3(di->num_cu), dim3(NTHR), 0, stream,
                        static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                        static_cast<const bf16*>(v), g, beta, static_cast<bf16*>(out), hdr, docs,
-                       T, (int)H, gate_bound);
+                       split, images, T, (int)H, gate_bound);
     e = hipGetLastError();
   }
   const hipError_t ef = hipFreeAsync(ws, stream);

@@ -127,6 +127,40 @@ def test_gate_at_the_bound():
     check(inp, o, doc_tasks(inp.cu_seqlens, H), "gate at the bound")
 
 
+# ---------------------------------------------------------------- split documents
+# Long documents may be "split": their chunks' state-independent part runs on
+# all CUs first and only the sequential chain stays per (document, head).
+# KDA_SPLIT forces the choice; both paths must give identical bits.
+
+def _bits(o):
+    import torch
+    return o.view(torch.int16)
+
+
+def test_split_path_is_bit_identical_to_fused(monkeypatch):
+    lengths = [513, 64 * 8, 1000, 37, 700, 2000, 1, 450]
+    T, H = sum(lengths), 3
+    inp = _small(T, H, 31, lengths)
+    monkeypatch.setenv("KDA_SPLIT", "never")
+    a = run_gpu(inp)
+    monkeypatch.setenv("KDA_SPLIT", "always")
+    b = run_gpu(inp)
+    assert bool((_bits(a) == _bits(b)).all())
+    check(inp, b, doc_tasks(inp.cu_seqlens, H), "split documents")
+
+
+@pytest.mark.parametrize("cu", [True, False])
+def test_split_long_document_carries_the_state(monkeypatch, cu):
+    T, H = 2048 + 37, 4
+    inp = with_gate_scale(_small(T, H, 32, [T]), 32, -0.05)
+    monkeypatch.setenv("KDA_SPLIT", "never")
+    a = run_gpu(inp, cu=cu)
+    monkeypatch.setenv("KDA_SPLIT", "always")
+    b = run_gpu(inp, cu=cu)
+    assert bool((_bits(a) == _bits(b)).all())
+    check(inp, b, doc_tasks(inp.cu_seqlens, H), "split, slow decay")
+
+
 # ---------------------------------------------------------------- layouts
 
 def test_cu_none_is_one_document():
