@@ -148,7 +148,6 @@ struct alignas(16) Smem {
   float tot[4][DK];          // per sub-block total decay (log2 domain)
   float beta[CH];
   int unit;
-  int next_unit;
   int gate_bad;
 };
 
@@ -163,11 +162,46 @@ __device__ __forceinline__ float* dvec(Smem& sm, int c) {
   return reinterpret_cast<float*>(&sm.Kt[c >> 2][DK]);
 }
 
+// byte offsets of the image parts
+constexpr int OFF_QT = (int)offsetof(Smem, Qt);
+constexpr int OFF_KT = (int)offsetof(Smem, Kt);
+constexpr int OFF_KBT = (int)offsetof(Smem, KbT);
+constexpr int OFF_TB = (int)offsetof(Smem, u);
+constexpr int ROW_QK = (DK + 8) * 2;   // bytes per Qt / Kt row
+constexpr int ROW_CC = (CH + 8) * 2;   // bytes per M / Tb row
+static_assert(offsetof(Smem, Mhi) == OFF_KBT + DK * ROW_CC, "KbT, Mhi, Mlo are contiguous");
+static_assert(offsetof(Smem, Mlo) == offsetof(Smem, Mhi) + CH * ROW_CC, "KbT, Mhi, Mlo are contiguous");
+static_assert(OFF_TB == (int)offsetof(Smem, Mlo) + CH * ROW_CC, "Tb follows M");
+
+// LDS of the pre kernel (~79 KB: two workgroups per CU).  KbT and M are
+// staged here in the image's own layout; Qt, Kt, Tb and D go straight from
+// registers to the image in global memory.
+struct alignas(16) PreSmem {
+  bf16 KbT[DK][CH + 8];
+  bf16 Mhi[CH][CH + 8];
+  bf16 Mlo[CH][CH + 8];
+  struct {
+    float A[CH][CH + 4];
+  } u;
+  union {
+    f16x8 R[3][4][64];
+    float T[CH][CH + 4];
+  } u2;
+  float etab[13][DK];
+  float tot[4][DK];
+  float beta[CH];
+  int gate_bad;
+};
+constexpr int PRE_STAGED = (int)(sizeof(((PreSmem*)nullptr)->KbT) + sizeof(((PreSmem*)nullptr)->Mhi) +
+                                 sizeof(((PreSmem*)nullptr)->Mlo));
+static_assert(PRE_STAGED % (16 * NTHR) == 0, "staged image parts split evenly");
+
 // Store the 16x16 block (a, b) of M (lower incl., split hi + lo) and of A
 // (beta-scaled, strictly lower, fp32).  C layout of a 16x16 MFMA tile: lane l
 // holds column l % 16 and rows 4 (l / 16) + 0..3.  beta_mine is beta of the
 // token this lane holds in the prologue layout (token r = l % 16 of block a).
-__device__ __forceinline__ void store_block(Smem& sm, const f32x4& accM, const f32x4& accA,
+template <class Sm>
+__device__ __forceinline__ void store_block(Sm& sm, const f32x4& accM, const f32x4& accA,
                                             int a, int b, int l, bool diag, float beta_mine) {
   const int col = l & 15;
 #pragma unroll
@@ -195,10 +229,10 @@ __device__ __forceinline__ void store_block(Smem& sm, const f32x4& accM, const f
 constexpr int SCHED_THREADS = 1024;
 constexpr int NBUCKET = 1024;
 constexpr int MIN_SPLIT_CHUNKS = 8;   // shorter documents are never split
-constexpr int MAX_SPLIT_DOCS = 4096;  // split candidates examined
+constexpr int MAX_SPLIT_DOCS = 1024;  // split candidates examined (the longest documents)
 // relative cost of one chunk of one head: fused (prepare + chain on one
 // workgroup), prepare only (pre kernel), chain only (main kernel)
-constexpr int COST_FUSED = 37, COST_PRE = 27, COST_CHAIN = 14;
+constexpr int COST_FUSED = 29, COST_PRE = 22, COST_CHAIN = 11;
 
 enum SplitPolicy { SPLIT_NEVER = 0, SPLIT_AUTO = 1, SPLIT_ALWAYS = 2 };
 
@@ -207,10 +241,9 @@ struct WorkHeader {
   int status;       // non-zero: cu_seqlens broke its contract
   int n_units;      // documents * heads
   int n_docs;       // non-empty documents
-  int pre_counter;  // next unit of the pre kernel
   int n_pre_units;  // split chunks * heads
   int n_split;      // split documents (the first n_split entries of the list)
-  int pad;
+  int pad[2];
 };
 
 __device__ int g_kda_status;  // sticky kda_device_flags of this device
@@ -231,6 +264,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void kda_schedule_kernel(
   __shared__ unsigned long long s_total;
   __shared__ int s_nsplit;
   __shared__ int s_split_chunks;
+  __shared__ int s_base[MAX_SPLIT_DOCS];
   const int tid = threadIdx.x;
 
   int n;  // number of documents (entries 0..n of cu are valid)
@@ -275,7 +309,6 @@ __global__ __launch_bounds__(SCHED_THREADS) void kda_schedule_kernel(
         hdr->status = 1;
         hdr->n_docs = 0;
         hdr->n_units = 0;
-        hdr->pre_counter = 0;
         hdr->n_pre_units = 0;
         hdr->n_split = 0;
         atomicOr(&g_kda_status, KDA_DEV_BAD_CU_SEQLENS);
@@ -327,56 +360,66 @@ __global__ __launch_bounds__(SCHED_THREADS) void kda_schedule_kernel(
   __threadfence_block();
   __syncthreads();
 
-  // ---- 3. split decision.  Documents of 1024+ chunks share the top bucket in
-  // arbitrary order; the decision only needs the list to be roughly sorted.
+  // ---- 3. split decision over the longest MAX_SPLIT_DOCS documents, staged
+  // in LDS (starts in s_hist, lengths in s_vals).  Documents of 1024+ chunks
+  // share the top bucket in arbitrary order; the decision only needs the list
+  // to be roughly sorted.
+  const int n_cand = min(s_count, MAX_SPLIT_DOCS);
+  for (int i = tid; i < n_cand; i += SCHED_THREADS) {
+    const int2 d = docs[i];
+    s_hist[i] = d.x;
+    s_vals[i] = d.y;
+  }
+  __syncthreads();
   if (tid == 0) {
     const int nd = s_count;
     const long long Hc = H, ncu = max(n_cu, 1);
     const long long total = (long long)s_total;
-    auto nch_of = [&](int i) -> long long { return (docs[i].y + CH - 1) / CH; };
+    auto nch_of = [&](int i) -> long long { return (s_vals[i] + CH - 1) / CH; };
     int best_s = 0;
     long long best_sum = 0;
     if (policy != SPLIT_NEVER && nd > 0) {
       long long best = nd > 0 ? max(nch_of(0) * COST_FUSED, (total * Hc * COST_FUSED + ncu - 1) / ncu) : 0;
       long long sum = 0, longest_split = 0;
-      for (int s = 1; s <= min(nd, MAX_SPLIT_DOCS); ++s) {
+      for (int s = 1; s <= n_cand; ++s) {
         const long long c = nch_of(s - 1);
         if (c < MIN_SPLIT_CHUNKS || sum + c > cap_chunks) break;
         sum += c;
         longest_split = max(longest_split, c);
         const long long pre = (sum * Hc + ncu - 1) / ncu * COST_PRE;
-        const long long rest = (s < nd) ? nch_of(s) * COST_FUSED : 0;
+        // longest fused document (beyond the candidates: at most the last one's length)
+        const long long rest = (s < nd) ? nch_of(min(s, n_cand - 1)) * COST_FUSED : 0;
         const long long avg = ((sum * COST_CHAIN + (total - sum) * COST_FUSED) * Hc + ncu - 1) / ncu;
         const long long est = pre + max(max(longest_split * COST_CHAIN, rest), avg);
         if (policy == SPLIT_ALWAYS || est < best) { best = est; best_s = s; best_sum = sum; }
       }
     }
-    long long base = 0;
+    // first chunk of each split document in pre_chunks (exclusive prefix sum)
+    int base = 0;
     for (int j = 0; j < best_s; ++j) {
-      const int2 d = docs[j];
-      split[j] = make_int2(d.x, (int)base);
-      docs[j] = make_int2(-(j + 1), d.y);
-      base += (d.y + CH - 1) / CH;
+      s_base[j] = base;
+      base += (int)nch_of(j);
     }
     s_nsplit = best_s;
     s_split_chunks = (int)best_sum;
   }
-  __threadfence_block();
   __syncthreads();
   const int ns = s_nsplit;
+  for (int j = tid; j < ns; j += SCHED_THREADS) {
+    split[j] = make_int2(s_hist[j], s_base[j]);
+    docs[j] = make_int2(-(j + 1), s_vals[j]);
+  }
   for (int j = 0; j < ns; ++j) {
-    const int2 sp = split[j];
-    const int len = docs[j].y;
+    const int start = s_hist[j], len = s_vals[j], b = s_base[j];
     const int nch = (len + CH - 1) / CH;
     for (int c = tid; c < nch; c += SCHED_THREADS)
-      pre_chunks[sp.y + c] = make_int2(sp.x + CH * c, min(CH, len - CH * c));
+      pre_chunks[b + c] = make_int2(start + CH * c, min(CH, len - CH * c));
   }
   if (tid == 0) {
     hdr->counter = 0;
     hdr->status = 0;
     hdr->n_docs = s_count;
     hdr->n_units = s_count * H;
-    hdr->pre_counter = 0;
     hdr->n_pre_units = s_split_chunks * H;
     hdr->n_split = ns;
   }
@@ -435,25 +478,53 @@ __device__ __forceinline__ Offsets make_offsets(int H, int tok, int cg, int w, i
 // q, k, g, beta of the chunk of n tokens at token c0 (head h); tokens at or
 // past n read as zero.  Element 8 s + j of this lane is channel 32 s + 8 cg + j:
 // the four lanes of a token read one contiguous 64-byte (q, k) or 128-byte (g)
-// span per load.
-__device__ __forceinline__ void load_raw(RawChunk& rc, const bf16* __restrict__ q,
-                                         const bf16* __restrict__ k, const float* __restrict__ g,
-                                         const float* __restrict__ beta, int64_t c0, int n, int H,
-                                         int h, const Offsets& of) {
+// span per load.  The loads are issued in three parts (q and k; the first and
+// the second half of g, and beta) so that they can be spread over a chunk.
+struct RawSrc {
+  Rsrc q, k, g, b;
+};
+
+__device__ __forceinline__ RawSrc raw_src(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                          const float* __restrict__ g, const float* __restrict__ beta,
+                                          int64_t c0, int n, int H, int h) {
   const size_t row = (size_t)c0 * H + h;
   const uint32_t nb = chunk_bytes(n, H, 256u);
-  const Rsrc rq = make_rsrc(q + row * DK, nb);
-  const Rsrc rk = make_rsrc(k + row * DK, nb);
-  const Rsrc rg = make_rsrc(g + row * DK, 2u * nb);
-  const Rsrc rb = make_rsrc(beta + row, chunk_bytes(n, H, 4u));
+  RawSrc src;
+  src.q = make_rsrc(q + row * DK, nb);
+  src.k = make_rsrc(k + row * DK, nb);
+  src.g = make_rsrc(g + row * DK, 2u * nb);
+  src.b = make_rsrc(beta + row, chunk_bytes(n, H, 4u));
+  return src;
+}
+
+__device__ __forceinline__ void load_raw_part(RawChunk& rc, const RawSrc& src, const Offsets& of,
+                                              int part) {
+  if (part == 0) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    rc.q[i] = bload(rq, of.qk + 64u * i);
-    rc.k[i] = bload(rk, of.qk + 64u * i);
-    rc.g[2 * i] = bload(rg, 2u * of.qk + 128u * i);
-    rc.g[2 * i + 1] = bload(rg, 2u * of.qk + 128u * i + 16u);
+    for (int i = 0; i < 4; ++i) {
+      rc.q[i] = bload(src.q, of.qk + 64u * i);
+      rc.k[i] = bload(src.k, of.qk + 64u * i);
+    }
+  } else if (part == 1) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      rc.g[2 * i] = bload(src.g, 2u * of.qk + 128u * i);
+      rc.g[2 * i + 1] = bload(src.g, 2u * of.qk + 128u * i + 16u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 2; i < 4; ++i) {
+      rc.g[2 * i] = bload(src.g, 2u * of.qk + 128u * i);
+      rc.g[2 * i + 1] = bload(src.g, 2u * of.qk + 128u * i + 16u);
+    }
+    rc.beta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(src.b, (int)of.b, 0, 0));
   }
-  rc.beta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, (int)of.b, 0, 0));
+}
+
+__device__ __forceinline__ void load_raw(RawChunk& rc, const RawSrc& src, const Offsets& of) {
+  load_raw_part(rc, src, of, 0);
+  load_raw_part(rc, src, of, 1);
+  load_raw_part(rc, src, of, 2);
 }
 
 // V of one chunk, the 32 value columns of wave w: load i, lane l holds 16 bytes
@@ -476,11 +547,15 @@ struct Image {
   u32x4 p[IMG_PER_THREAD];
 };
 
-__device__ __forceinline__ void load_image(Image& im, const uint8_t* __restrict__ src, int tid) {
-  const Rsrc r = make_rsrc(src, IMG_BYTES);
+// pieces [i0, i1) of an image
+__device__ __forceinline__ void load_image_part(Image& im, Rsrc r, int tid, int i0, int i1) {
 #pragma unroll
   for (int i = 0; i < IMG_PER_THREAD; ++i)
-    im.p[i] = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * tid, 16 * NTHR * i, 0);
+    if (i >= i0 && i < i1) im.p[i] = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * tid, 16 * NTHR * i, 0);
+}
+
+__device__ __forceinline__ void load_image(Image& im, const uint8_t* __restrict__ src, int tid) {
+  load_image_part(im, make_rsrc(src, IMG_BYTES), tid, 0, IMG_PER_THREAD);
 }
 
 __device__ __forceinline__ void image_to_lds(Smem& sm, const Image& im, int tid) {
@@ -490,14 +565,38 @@ __device__ __forceinline__ void image_to_lds(Smem& sm, const Image& im, int tid)
     *reinterpret_cast<u32x4*>(dst + 16 * (tid + NTHR * i)) = im.p[i];
 }
 
-__device__ __forceinline__ void lds_to_global_image(uint8_t* __restrict__ dst, const Smem& sm, int tid) {
-  const Rsrc r = make_rsrc(dst, IMG_BYTES);
-  const uint8_t* src = reinterpret_cast<const uint8_t*>(&sm);
-#pragma unroll
-  for (int i = 0; i < IMG_PER_THREAD; ++i)
-    __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(src + 16 * (tid + NTHR * i)),
-                                           r, 16 * tid, 16 * NTHR * i, 0);
-}
+
+// Where prepare_chunk puts the image parts it holds in registers (Qt, Kt, Tb
+// and D): the LDS image of the main kernel, or the global image.
+struct LdsSink {
+  Smem* sm;
+  __device__ __forceinline__ void qk(int tok, int col, const bf16x8& qt, const bf16x8& kt) const {
+    *reinterpret_cast<bf16x8*>(&sm->Qt[tok][col]) = qt;
+    *reinterpret_cast<bf16x8*>(&sm->Kt[tok][col]) = kt;
+  }
+  __device__ __forceinline__ void dv(int c, float f) const { dvec(*sm, c)[c & 3] = f; }
+  __device__ __forceinline__ void tb(int row, int col, const bf16x8& hi, const bf16x8& lo) const {
+    *reinterpret_cast<bf16x8*>(&sm->u.tb.hi[row][col]) = hi;
+    *reinterpret_cast<bf16x8*>(&sm->u.tb.lo[row][col]) = lo;
+  }
+};
+
+struct GlobalSink {
+  Rsrc r;  // one image, IMG_BYTES
+  __device__ __forceinline__ void qk(int tok, int col, const bf16x8& qt, const bf16x8& kt) const {
+    const uint32_t o = (uint32_t)(tok * ROW_QK + 2 * col);
+    bstore(__builtin_bit_cast(u32x4, qt), r, OFF_QT + o);
+    bstore(__builtin_bit_cast(u32x4, kt), r, OFF_KT + o);
+  }
+  __device__ __forceinline__ void dv(int c, float f) const {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f), r, OFF_KT + (c >> 2) * ROW_QK + 2 * DK + 4 * (c & 3), 0, 0);
+  }
+  __device__ __forceinline__ void tb(int row, int col, const bf16x8& hi, const bf16x8& lo) const {
+    const uint32_t o = (uint32_t)(row * ROW_CC + 2 * col);
+    bstore(__builtin_bit_cast(u32x4, hi), r, OFF_TB + o);
+    bstore(__builtin_bit_cast(u32x4, lo), r, OFF_TB + CH * ROW_CC + o);
+  }
+};
 
 // lane i of each 16-lane row receives lane N of the same row
 template <int N>
@@ -521,8 +620,9 @@ __device__ __forceinline__ f32x4 mfma16k16(const bf16x4& a, const bf16x4& b, con
 //   rows 4..6:  e^{G_c - G_end(w)}    = 2^{t_{w+1} + .. + t_3}, w = 0..2
 //   rows 7..12: e^{G_end(w) - G_end(b)} = 2^{t_{b+1} + .. + t_w}, pair (w, b), b < w,
 //               at row 7 + w (w - 1) / 2 + b
-// D is also written to the image (dvec).
-__device__ __forceinline__ void fill_tables(Smem& sm, int tid) {
+// D is also written to the image (sink.dv).
+template <class Sm, class Sink>
+__device__ __forceinline__ void fill_tables(Sm& sm, const Sink& sink, int tid) {
 #pragma unroll
   for (int e = tid; e < 13 * DK; e += NTHR) {
     const int row = e >> 7, c = e & (DK - 1);
@@ -545,7 +645,7 @@ __device__ __forceinline__ void fill_tables(Smem& sm, int tid) {
     }
     const float f = __builtin_amdgcn_exp2f(x);
     sm.etab[row][c] = f;
-    if (row == 3) dvec(sm, c)[c & 3] = f;
+    if (row == 3) sink.dv(c, f);
   }
 }
 
@@ -576,11 +676,12 @@ __device__ __forceinline__ Lane make_lane() {
 
 // Everything of a chunk that does not depend on the state: from the raw
 // inputs `cur` (n valid tokens) to the image in LDS (Qt, Kt, KbT, M, Tb, D).
-// after_prologue() runs once `cur` has been consumed (it may refill it).
+// hook(0..2) run at fixed points once `cur` has been consumed (they may
+// refill it); the scheduling barriers keep the loads they issue spread out.
 // Ends with a workgroup barrier after which the image is complete.
-template <class AfterPrologue>
-__device__ __forceinline__ void prepare_chunk(Smem& sm, const RawChunk& cur, int n, float gate_bound,
-                                              const Lane& ln, AfterPrologue after_prologue) {
+template <class Sm, class Sink, class Hook>
+__device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const RawChunk& cur, int n,
+                                              float gate_bound, const Lane& ln, Hook hook) {
   const int tid = ln.tid, w = ln.w, l = ln.l, r = ln.r, cg = ln.cg, tok = ln.tok;
 
   // ================= prologue: l2 norm, cumulative decay =================
@@ -618,7 +719,9 @@ __device__ __forceinline__ void prepare_chunk(Smem& sm, const RawChunk& cur, int
     }
     if (tok < n && !(gmin >= gate_bound && gmax <= 0.f)) sm.gate_bad = 1;
     if (cg == 0) sm.beta[tok] = cur.beta;
-    after_prologue();
+    __builtin_amdgcn_sched_barrier(0);
+    hook(0);
+    __builtin_amdgcn_sched_barrier(0);
     float sq = 0.f, sk = 0.f;
 #pragma unroll
     for (int j = 0; j < 32; ++j) { sq += qh[j] * qh[j]; sk += kh[j] * kh[j]; }
@@ -665,6 +768,9 @@ __device__ __forceinline__ void prepare_chunk(Smem& sm, const RawChunk& cur, int
       accM[s & 1] = mfma16f(lq[s], kr[s], accM[s & 1]);
       accA[s & 1] = mfma16f(lk[s], kr[s], accA[s & 1]);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    hook(1);
+    __builtin_amdgcn_sched_barrier(0);
     store_block(sm, accM[0] + accM[1], accA[0] + accA[1], w, w, l, true, beta_mine);
     // blocks above the diagonal are read by the chain's MFMAs: zero them
     const bf16 z = (bf16)0.f;
@@ -687,7 +793,7 @@ __device__ __forceinline__ void prepare_chunk(Smem& sm, const RawChunk& cur, int
     }
   }
   __syncthreads();  // B1: tot, beta, R, diagonal A / M visible
-  fill_tables(sm, tid);
+  fill_tables(sm, sink, tid);
   __syncthreads();  // B2: decay tables visible
 
   // ---- operand tiles of the chain: Qt = lq e^{G_end(w)}, Kt = -lk e^{G_end(w)},
@@ -716,10 +822,12 @@ __device__ __forceinline__ void prepare_chunk(Smem& sm, const RawChunk& cur, int
       kt[j] = (bf16)(-lk[j0 + j] * fq[j]);
       sm.KbT[4 * j0 + 8 * cg + j][tok] = (bf16)(kr[j0 + j] * fk[j]);
     }
-    *reinterpret_cast<bf16x8*>(&sm.Qt[tok][4 * j0 + 8 * cg]) = qt;
-    *reinterpret_cast<bf16x8*>(&sm.Kt[tok][4 * j0 + 8 * cg]) = kt;
+    sink.qk(tok, 4 * j0 + 8 * cg, qt, kt);
   }
 
+  __builtin_amdgcn_sched_barrier(0);
+  hook(2);
+  __builtin_amdgcn_sched_barrier(0);
   // ---- off-diagonal blocks (w, b), b < w, on fp16 MFMA:
   //      left x_r e^{G_r - G_end(b)} = l{q,k} e^{G_end(w) - G_end(b)} <= 1
 #pragma unroll 1
@@ -816,14 +924,24 @@ __device__ __forceinline__ void prepare_chunk(Smem& sm, const RawChunk& cur, int
     }
   }
   __syncthreads();  // B5: T complete
-  // Tb = T Diag(beta), split into hi + lo (overwrites A)
+  // Tb = T Diag(beta), split into hi + lo (in LDS it overwrites A): thread
+  // tid converts row tid / 4, columns 16 (tid % 4) .. + 15
+  {
+    const int rr = tid >> 2;
 #pragma unroll
-  for (int it = 0; it < 16; ++it) {
-    const int rr = 4 * it + (tid >> 6), cc = tid & 63;
-    bf16 hi, lo;
-    SPLIT_BF16(sm.u2.T[rr][cc] * sm.beta[cc], hi, lo);
-    sm.u.tb.hi[rr][cc] = hi;
-    sm.u.tb.lo[rr][cc] = lo;
+    for (int half = 0; half < 2; ++half) {
+      const int cc = 16 * (tid & 3) + 8 * half;
+      const float4 t0 = *reinterpret_cast<const float4*>(&sm.u2.T[rr][cc]);
+      const float4 t1 = *reinterpret_cast<const float4*>(&sm.u2.T[rr][cc + 4]);
+      const float4 b0 = *reinterpret_cast<const float4*>(&sm.beta[cc]);
+      const float4 b1 = *reinterpret_cast<const float4*>(&sm.beta[cc + 4]);
+      const float x[8] = {t0.x * b0.x, t0.y * b0.y, t0.z * b0.z, t0.w * b0.w,
+                          t1.x * b1.x, t1.y * b1.y, t1.z * b1.z, t1.w * b1.w};
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) SPLIT_BF16(x[j], hi[j], lo[j]);
+      sink.tb(rr, cc, hi, lo);
+    }
   }
   __syncthreads();  // B6: the image is complete, T dead (its space stages O)
 }
@@ -831,11 +949,12 @@ __device__ __forceinline__ void prepare_chunk(Smem& sm, const RawChunk& cur, int
 // The state-dependent part of a chunk of n tokens starting at token c0, from
 // the image in LDS and this chunk's V (wave w owns value columns 32 w ..):
 //   X = V - Kt S,  U = Tb X,  O = scale (Qt S + M U),  S <- D S + KbT U.
-// mid() runs once V has been consumed (it may refill vcur).
-template <class Mid>
+// hook(0..3) run at fixed points after V has been consumed (they may refill
+// vcur): after the V staging, after X, after U and after O.
+template <class Hook>
 __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChunk& vcur, int n,
                                             int64_t c0, int H, int h, bf16* __restrict__ out,
-                                            const Lane& ln, const Offsets& of, Mid mid) {
+                                            const Lane& ln, const Offsets& of, Hook hook) {
   const int w = ln.w, l = ln.l, m = ln.m, hg = ln.hg;
   const float scale = 0.08838834764831845f;  // 128^-1/2
 
@@ -869,6 +988,9 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
       }
     }
   wave_sync_lds();  // V read out before the slice stages O
+  __builtin_amdgcn_sched_barrier(0);
+  hook(0);
+  __builtin_amdgcn_sched_barrier(0);
 
   bf16x8 Sb[8];
 #pragma unroll
@@ -899,6 +1021,9 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
   for (int s = 0; s < 4; ++s)
 #pragma unroll
     for (int j = 0; j < 8; ++j) Xb[s][j] = (bf16)X[s >> 1][8 * (s & 1) + j];
+  __builtin_amdgcn_sched_barrier(0);
+  hook(1);
+  __builtin_amdgcn_sched_barrier(0);
 
   // U = Tb X: the six lower-triangular (row tile, k-step) pairs
   constexpr int PMT[6] = {0, 0, 1, 1, 1, 1};
@@ -931,8 +1056,9 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
   for (int s = 0; s < 4; ++s)
 #pragma unroll
     for (int j = 0; j < 8; ++j) SPLIT_BF16(U[s >> 1][8 * (s & 1) + j], Ubh[s][j], Ubl[s][j]);
-
-  mid();
+  __builtin_amdgcn_sched_barrier(0);
+  hook(2);
+  __builtin_amdgcn_sched_barrier(0);
 
   // O = scale (qh e^G S + M U), staged through LDS for 16-byte stores;
   // four independent accumulators (row tile x {Qt S, M U})
@@ -980,6 +1106,9 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
       }
   }
 
+  __builtin_amdgcn_sched_barrier(0);
+  hook(3);
+  __builtin_amdgcn_sched_barrier(0);
   // S <- e^{G_c} S + (kh e^{G_c - G})^T U  (the four row tiles interleaved)
   {
 #pragma unroll
@@ -1020,43 +1149,36 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
 
 // ---------------------------------------------------------------------------
 // pre kernel: the state-independent part of every chunk of the split
-// documents, in parallel, written out as images
+// documents, in parallel (two workgroups per CU), written out as images
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(NTHR, 1) void kda_pre_kernel(
+__global__ __launch_bounds__(NTHR, 2) void kda_pre_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, WorkHeader* __restrict__ hdr,
     const int2* __restrict__ pre_chunks, uint8_t* __restrict__ images, int H, float gate_bound) {
-  __shared__ Smem sm;
+  __shared__ PreSmem sm;
   const Lane ln = make_lane();
   if (hdr->status != 0) return;
   const int n_units = hdr->n_pre_units;
   if (n_units == 0) return;
   const Offsets of = make_offsets(H, ln.tok, ln.cg, ln.w, ln.l);
-  if (ln.tid == 0) {
-    sm.gate_bad = 0;
-    sm.next_unit = atomicAdd(&hdr->pre_counter, 1);
-  }
-  __syncthreads();
-  int unit = __builtin_amdgcn_readfirstlane(sm.next_unit);
-  RawChunk cur;
-  int2 ch = make_int2(0, 0);
-  if (unit < n_units) {
-    ch = pre_chunks[unit / H];
-    load_raw(cur, q, k, g, beta, ch.x, ch.y, H, unit % H, of);
-  }
-  while (unit < n_units) {
-    __syncthreads();  // every lane has read next_unit
-    if (ln.tid == 0) sm.next_unit = atomicAdd(&hdr->pre_counter, 1);
-    __syncthreads();
-    const int next = __builtin_amdgcn_readfirstlane(sm.next_unit);
+  if (ln.tid == 0) sm.gate_bad = 0;
+  // every unit costs the same: workgroup b takes units b, b + grid, ...
+  for (int unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
+    const int2 ch = pre_chunks[unit / H];
     const int h = unit % H;
-    const int2 nch = (next < n_units) ? pre_chunks[next / H] : make_int2(0, 0);
-    prepare_chunk(sm, cur, ch.y, gate_bound, ln, [&] {
-      load_raw(cur, q, k, g, beta, nch.x, (next < n_units) ? nch.y : 0, H, next % H, of);
-    });
-    lds_to_global_image(images + ((size_t)(unit / H) * H + h) * IMG_BYTES, sm, ln.tid);
-    unit = next;
-    ch = nch;
+    RawChunk cur;
+    load_raw(cur, raw_src(q, k, g, beta, ch.x, ch.y, H, h), of);
+    uint8_t* img = images + ((size_t)(unit / H) * H + h) * IMG_BYTES;
+    const GlobalSink sink{make_rsrc(img, IMG_BYTES)};
+    prepare_chunk(sm, sink, cur, ch.y, gate_bound, ln, [&](int) {});
+    // KbT, Mhi, Mlo: LDS staging -> image
+    const uint8_t* st = reinterpret_cast<const uint8_t*>(&sm.KbT[0][0]);
+#pragma unroll
+    for (int i = 0; i < PRE_STAGED / (16 * NTHR); ++i) {
+      const int o = 16 * (ln.tid + NTHR * i);
+      bstore(*reinterpret_cast<const u32x4*>(st + o), sink.r, OFF_KBT + o);
+    }
+    __syncthreads();  // the staging is read out before the next unit rewrites it
   }
   __syncthreads();
   if (ln.tid == 0 && sm.gate_bad) atomicOr(&g_kda_status, KDA_DEV_GATE_RANGE);
@@ -1119,9 +1241,18 @@ __global__ __launch_bounds__(NTHR, 1) void kda_chunk_fwd_kernel(
         img += img_stride;
         const int64_t c1 = c0 + CH;
         const int n1 = (int)min<int64_t>(CH, eos - c1);
-        if (c1 < eos) load_image(im, img, tid);
-        chain_chunk(sm, S, vcur, n, c0, H, h, out, ln, of, [&] {
-          vcur = load_v(v, c1, n1, H, h, of);
+        const Rsrc rimg = make_rsrc(img, c1 < eos ? IMG_BYTES : 0);
+        chain_chunk(sm, S, vcur, n, c0, H, h, out, ln, of, [&](int stage) {
+          if (stage == 0) {
+            vcur = load_v(v, c1, n1, H, h, of);
+            load_image_part(im, rimg, tid, 0, 6);
+          } else if (stage == 1) {
+            load_image_part(im, rimg, tid, 6, 12);
+          } else if (stage == 2) {
+            load_image_part(im, rimg, tid, 12, 17);
+          } else {
+            load_image_part(im, rimg, tid, 17, IMG_PER_THREAD);
+          }
         });
         __syncthreads();  // the next chunk overwrites the image
       }
@@ -1132,18 +1263,18 @@ __global__ __launch_bounds__(NTHR, 1) void kda_chunk_fwd_kernel(
       VChunk vcur;
       {
         const int n0 = (int)min<int64_t>(CH, eos - bos);
-        load_raw(cur, q, k, g, beta, bos, n0, H, h, of);
+        load_raw(cur, raw_src(q, k, g, beta, bos, n0, H, h), of);
         vcur = load_v(v, bos, n0, H, h, of);
       }
       for (int64_t c0 = bos; c0 < eos; c0 += CH) {
         const int n = (int)min<int64_t>(CH, eos - c0);
         const int64_t c1 = c0 + CH;
         const int n1 = (int)min<int64_t>(CH, eos - c1);
-        prepare_chunk(sm, cur, n, gate_bound, ln, [&] {
-          load_raw(cur, q, k, g, beta, c1, n1, H, h, of);
-        });
-        chain_chunk(sm, S, vcur, n, c0, H, h, out, ln, of, [&] {
-          vcur = load_v(v, c1, n1, H, h, of);
+        const RawSrc src = raw_src(q, k, g, beta, c1, n1, H, h);
+        prepare_chunk(sm, LdsSink{&sm}, cur, n, gate_bound, ln,
+                      [&](int part) { load_raw_part(cur, src, of, part); });
+        chain_chunk(sm, S, vcur, n, c0, H, h, out, ln, of, [&](int stage) {
+          if (stage == 0) vcur = load_v(v, c1, n1, H, h, of);
         });
         __syncthreads();  // the next chunk overwrites every LDS tile
       }
@@ -1269,7 +1400,7 @@ extern "C" int kda_chunk_fwd(const void* q, const void* k, const void* v, const 
                      pre_chunks);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && cap_chunks > 0) {
-    hipLaunchKernelGGL(kda_pre_kernel, dim3(di->num_cu), dim3(NTHR), 0, stream,
+    hipLaunchKernelGGL(kda_pre_kernel, dim3(2 * di->num_cu), dim3(NTHR), 0, stream,
                        static_cast<const bf16*>(q), static_cast<const bf16*>(k), g, beta, hdr,
                        pre_chunks, images, (int)H, gate_bound);
     e = hipGetLastError();
