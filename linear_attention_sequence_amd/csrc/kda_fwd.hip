@@ -974,19 +974,13 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
   }
   wave_sync_lds();
   const int rowsel = swap23(m);
-  f32x16 X[2];
+  // V in the C layout of the X tiles (packed bf16; added after the product)
+  u32x4 vx[2][2];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const uint4 u = *reinterpret_cast<const uint4*>(&vt[m][32 * mt + 16 * hh + 8 * hg]);
-      const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        X[mt][8 * hh + 2 * j] = bf16_lo_to_f32(uu[j]);
-        X[mt][8 * hh + 2 * j + 1] = bf16_hi_to_f32(uu[j]);
-      }
-    }
+    for (int hh = 0; hh < 2; ++hh)
+      vx[mt][hh] = *reinterpret_cast<const u32x4*>(&vt[m][32 * mt + 16 * hh + 8 * hg]);
   wave_sync_lds();  // V read out before the slice stages O
   __builtin_amdgcn_sched_barrier(0);
   hook(0);
@@ -998,7 +992,12 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
 #pragma unroll
     for (int j = 0; j < 8; ++j) Sb[s][j] = (bf16)S[s >> 1][8 * (s & 1) + j];
 
-  // X = V - kh e^G S (A operands loaded two k-steps ahead)
+  // X = V - kh e^G S (A operands loaded two k-steps ahead; Kt holds -kh e^G)
+  f32x16 X[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) X[mt][i] = 0.f;
   {
     bf16x8 ka[2][2];
 #pragma unroll
@@ -1020,7 +1019,11 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) Xb[s][j] = (bf16)X[s >> 1][8 * (s & 1) + j];
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t vv = vx[s >> 1][s & 1][j];
+      Xb[s][2 * j] = (bf16)(X[s >> 1][8 * (s & 1) + 2 * j] + bf16_lo_to_f32(vv));
+      Xb[s][2 * j + 1] = (bf16)(X[s >> 1][8 * (s & 1) + 2 * j + 1] + bf16_hi_to_f32(vv));
+    }
   __builtin_amdgcn_sched_barrier(0);
   hook(1);
   __builtin_amdgcn_sched_barrier(0);
@@ -1028,28 +1031,33 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
   // U = Tb X: the six lower-triangular (row tile, k-step) pairs
   constexpr int PMT[6] = {0, 0, 1, 1, 1, 1};
   constexpr int PS[6] = {0, 1, 0, 1, 2, 3};
-  f32x16 U[2], U2[2];
+  f32x16 U[2];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) { U[mt][i] = 0.f; U2[mt][i] = 0.f; }
+    for (int i = 0; i < 16; ++i) U[mt][i] = 0.f;
   {
-    bf16x8 th[6], tl[6];
-#pragma unroll
-    for (int p = 0; p < 6; ++p) {
-      th[p] = *reinterpret_cast<const bf16x8*>(&sm.u.tb.hi[32 * PMT[p] + rowsel][16 * PS[p] + 8 * hg]);
-      tl[p] = *reinterpret_cast<const bf16x8*>(&sm.u.tb.lo[32 * PMT[p] + rowsel][16 * PS[p] + 8 * hg]);
-    }
-    // order (1,0) (0,0) (1,1) (0,1) (1,2) (1,3): the two row tiles alternate
+    // order (1,0) (0,0) (1,1) (0,1) (1,2) (1,3): the two row tiles alternate;
+    // operands are loaded two pairs ahead
     constexpr int ORD[6] = {2, 0, 3, 1, 4, 5};
+    bf16x8 th[2], tl[2];
+#pragma unroll
+    for (int o = 0; o < 2; ++o) {
+      const int p = ORD[o];
+      th[o] = *reinterpret_cast<const bf16x8*>(&sm.u.tb.hi[32 * PMT[p] + rowsel][16 * PS[p] + 8 * hg]);
+      tl[o] = *reinterpret_cast<const bf16x8*>(&sm.u.tb.lo[32 * PMT[p] + rowsel][16 * PS[p] + 8 * hg]);
+    }
 #pragma unroll
     for (int o = 0; o < 6; ++o) {
       const int p = ORD[o];
-      U[PMT[p]] = mfma32(th[p], Xb[PS[p]], U[PMT[p]]);
-      U2[PMT[p]] = mfma32(tl[p], Xb[PS[p]], U2[PMT[p]]);
+      U[PMT[p]] = mfma32(th[o & 1], Xb[PS[p]], U[PMT[p]]);
+      U[PMT[p]] = mfma32(tl[o & 1], Xb[PS[p]], U[PMT[p]]);
+      if (o + 2 < 6) {
+        const int pn = ORD[o + 2];
+        th[o & 1] = *reinterpret_cast<const bf16x8*>(&sm.u.tb.hi[32 * PMT[pn] + rowsel][16 * PS[pn] + 8 * hg]);
+        tl[o & 1] = *reinterpret_cast<const bf16x8*>(&sm.u.tb.lo[32 * PMT[pn] + rowsel][16 * PS[pn] + 8 * hg]);
+      }
     }
-    U[0] += U2[0];
-    U[1] += U2[1];
   }
   bf16x8 Ubh[4], Ubl[4];
 #pragma unroll
@@ -1061,23 +1069,24 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
   __builtin_amdgcn_sched_barrier(0);
 
   // O = scale (qh e^G S + M U), staged through LDS for 16-byte stores;
-  // four independent accumulators (row tile x {Qt S, M U})
+  // one accumulator per row tile
   unsigned short (*ost)[32] = sm.u2.ws[w].o;
   {
-    f32x16 OQ[2], OM[2];
+    f32x16 O[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) { OQ[mt][i] = 0.f; OM[mt][i] = 0.f; }
+      for (int i = 0; i < 16; ++i) O[mt][i] = 0.f;
     bf16x8 qa[2][2];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
         qa[mt][s] = *reinterpret_cast<const bf16x8*>(&sm.Qt[32 * mt + rowsel][16 * s + 8 * hg]);
-    bf16x8 mh[6], ml[6];
+    // M operands loaded two pairs ahead
+    bf16x8 mh[2], ml[2];
 #pragma unroll
-    for (int p = 0; p < 6; ++p) {
+    for (int p = 0; p < 2; ++p) {
       mh[p] = *reinterpret_cast<const bf16x8*>(&sm.Mhi[32 * PMT[p] + rowsel][16 * PS[p] + 8 * hg]);
       ml[p] = *reinterpret_cast<const bf16x8*>(&sm.Mlo[32 * PMT[p] + rowsel][16 * PS[p] + 8 * hg]);
     }
@@ -1085,15 +1094,19 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
     for (int s = 0; s < 8; ++s) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        OQ[mt] = mfma32(qa[mt][s & 1], Sb[s], OQ[mt]);
+        O[mt] = mfma32(qa[mt][s & 1], Sb[s], O[mt]);
         if (s + 2 < 8)
           qa[mt][s & 1] = *reinterpret_cast<const bf16x8*>(&sm.Qt[32 * mt + rowsel][16 * (s + 2) + 8 * hg]);
       }
       if (s < 6) {
         const int p = s;
-        OM[PMT[p]] = mfma32(mh[p], Ubh[PS[p]], OM[PMT[p]]);
-        OM[PMT[p]] = mfma32(ml[p], Ubh[PS[p]], OM[PMT[p]]);
-        OM[PMT[p]] = mfma32(mh[p], Ubl[PS[p]], OM[PMT[p]]);
+        O[PMT[p]] = mfma32(mh[p & 1], Ubh[PS[p]], O[PMT[p]]);
+        O[PMT[p]] = mfma32(ml[p & 1], Ubh[PS[p]], O[PMT[p]]);
+        O[PMT[p]] = mfma32(mh[p & 1], Ubl[PS[p]], O[PMT[p]]);
+        if (p + 2 < 6) {
+          mh[p & 1] = *reinterpret_cast<const bf16x8*>(&sm.Mhi[32 * PMT[p + 2] + rowsel][16 * PS[p + 2] + 8 * hg]);
+          ml[p & 1] = *reinterpret_cast<const bf16x8*>(&sm.Mlo[32 * PMT[p + 2] + rowsel][16 * PS[p + 2] + 8 * hg]);
+        }
       }
     }
 #pragma unroll
@@ -1101,7 +1114,7 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int t = 32 * mt + 16 * (i >> 3) + 8 * hg + (i & 7);
-        const bf16 ob = (bf16)((OQ[mt][i] + OM[mt][i]) * scale);
+        const bf16 ob = (bf16)(O[mt][i] * scale);
         ost[t][m] = __builtin_bit_cast(unsigned short, ob);
       }
   }
