@@ -110,6 +110,9 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x16 mfma32h(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
 
 // ---------------------------------------------------------------------------
 // LDS layout (one chunk in flight, ~117 KB: one workgroup per CU)
@@ -124,13 +127,9 @@ struct alignas(16) Smem {
   bf16 Qt[CH][DK + 8];       // qh * e^G                      (A operand of Qt S)
   bf16 Kt[CH][DK + 8];       // -kh * e^G                     (A operand of X = V - Kt S)
   bf16 KbT[DK][CH + 8];      // (kh * e^{G_c - G})^T          (A operand of the state update)
-  bf16 Mhi[CH][CH + 8];      // M split into hi + lo
-  bf16 Mlo[CH][CH + 8];
+  _Float16 M[CH][CH + 8];    // M (|M| <= 1), lower incl.
   union {
-    struct {
-      bf16 hi[CH][CH + 8];   // Tb split into hi + lo (written after the solve)
-      bf16 lo[CH][CH + 8];
-    } tb;
+    _Float16 tb[CH][CH + 8];  // Tb 2^-e (written after the solve; 2^e in tbscale)
     float A[CH][CH + 4];     // beta-scaled strictly lower A (fp32), input of the solve
   } u;
   // ---- end of the image
@@ -147,19 +146,23 @@ struct alignas(16) Smem {
   float etab[13][DK];        // per-channel decay factors of the chunk (see fill_tables)
   float tot[4][DK];          // per sub-block total decay (log2 domain)
   float beta[CH];
+  float tbmax[8];            // per wave: largest |Tb| of the blocks it solved
   int unit;
   int gate_bad;
 };
 
-constexpr int IMG_BYTES = (int)offsetof(Smem, u2);
-constexpr int IMG_VEC = IMG_BYTES / 16;         // 16-byte pieces of an image
-constexpr int IMG_PER_THREAD = IMG_VEC / NTHR;  // pieces per thread
-static_assert(IMG_VEC % NTHR == 0, "image must split evenly over the workgroup");
-static_assert(offsetof(Smem, u) + sizeof(((Smem*)nullptr)->u.tb) == IMG_BYTES, "image layout");
+constexpr int IMG_BYTES = (int)(offsetof(Smem, u) + sizeof(((Smem*)nullptr)->u.tb));
+constexpr int IMG_VEC = IMG_BYTES / 16;                         // 16-byte pieces of an image
+constexpr int IMG_PER_THREAD = (IMG_VEC + NTHR - 1) / NTHR;     // pieces per thread (the last partial)
+static_assert(IMG_BYTES % 16 == 0 && (IMG_VEC % NTHR) % 64 == 0, "the last piece round is whole waves");
 
 // e^{G_c} of channels c .. c + 3 (c a multiple of 4): the padding of Kt row c / 4
 __device__ __forceinline__ float* dvec(Smem& sm, int c) {
   return reinterpret_cast<float*>(&sm.Kt[c >> 2][DK]);
+}
+// the power of two Tb was divided by: the padding of Kt row 32
+__device__ __forceinline__ float* tbscale(Smem& sm) {
+  return reinterpret_cast<float*>(&sm.Kt[32][DK]);
 }
 
 // byte offsets of the image parts
@@ -169,17 +172,15 @@ constexpr int OFF_KBT = (int)offsetof(Smem, KbT);
 constexpr int OFF_TB = (int)offsetof(Smem, u);
 constexpr int ROW_QK = (DK + 8) * 2;   // bytes per Qt / Kt row
 constexpr int ROW_CC = (CH + 8) * 2;   // bytes per M / Tb row
-static_assert(offsetof(Smem, Mhi) == OFF_KBT + DK * ROW_CC, "KbT, Mhi, Mlo are contiguous");
-static_assert(offsetof(Smem, Mlo) == offsetof(Smem, Mhi) + CH * ROW_CC, "KbT, Mhi, Mlo are contiguous");
-static_assert(OFF_TB == (int)offsetof(Smem, Mlo) + CH * ROW_CC, "Tb follows M");
+static_assert(offsetof(Smem, M) == OFF_KBT + DK * ROW_CC, "KbT and M are contiguous");
+static_assert(OFF_TB == (int)offsetof(Smem, M) + CH * ROW_CC, "Tb follows M");
 
-// LDS of the pre kernel (~79 KB: two workgroups per CU).  KbT and M are
+// LDS of the pre kernel (~70 KB: two workgroups per CU).  KbT and M are
 // staged here in the image's own layout; Qt, Kt, Tb and D go straight from
 // registers to the image in global memory.
 struct alignas(16) PreSmem {
   bf16 KbT[DK][CH + 8];
-  bf16 Mhi[CH][CH + 8];
-  bf16 Mlo[CH][CH + 8];
+  _Float16 M[CH][CH + 8];
   struct {
     float A[CH][CH + 4];
   } u;
@@ -190,13 +191,14 @@ struct alignas(16) PreSmem {
   float etab[13][DK];
   float tot[4][DK];
   float beta[CH];
+  float tbmax[8];
   int gate_bad;
 };
-constexpr int PRE_STAGED = (int)(sizeof(((PreSmem*)nullptr)->KbT) + sizeof(((PreSmem*)nullptr)->Mhi) +
-                                 sizeof(((PreSmem*)nullptr)->Mlo));
-static_assert(PRE_STAGED % (16 * NTHR) == 0, "staged image parts split evenly");
+constexpr int PRE_STAGED = (int)(sizeof(((PreSmem*)nullptr)->KbT) + sizeof(((PreSmem*)nullptr)->M));
+constexpr int PRE_STAGED_VEC = PRE_STAGED / 16;
+static_assert(PRE_STAGED % 16 == 0 && (PRE_STAGED_VEC % NTHR) % 64 == 0, "staged parts: whole waves");
 
-// Store the 16x16 block (a, b) of M (lower incl., split hi + lo) and of A
+// Store the 16x16 block (a, b) of M (lower incl., fp16) and of A
 // (beta-scaled, strictly lower, fp32).  C layout of a 16x16 MFMA tile: lane l
 // holds column l % 16 and rows 4 (l / 16) + 0..3.  beta_mine is beta of the
 // token this lane holds in the prologue layout (token r = l % 16 of block a).
@@ -215,10 +217,7 @@ __device__ __forceinline__ void store_block(Sm& sm, const f32x4& accM, const f32
     }
     aa *= __shfl(beta_mine, row);
     sm.u.A[R][C] = aa;
-    bf16 hi, lo;
-    SPLIT_BF16(mm, hi, lo);
-    sm.Mhi[R][C] = hi;
-    sm.Mlo[R][C] = lo;
+    sm.M[R][C] = (_Float16)mm;
   }
 }
 
@@ -372,25 +371,26 @@ __global__ __launch_bounds__(SCHED_THREADS) void kda_schedule_kernel(
   }
   __syncthreads();
   if (tid == 0) {
+    // estimates in float: only their order matters
     const int nd = s_count;
-    const long long Hc = H, ncu = max(n_cu, 1);
-    const long long total = (long long)s_total;
-    auto nch_of = [&](int i) -> long long { return (s_vals[i] + CH - 1) / CH; };
+    const float per_cu = (float)H / (float)max(n_cu, 1);
+    const float total = (float)s_total;
+    auto nch_of = [&](int i) -> int { return (s_vals[i] + CH - 1) / CH; };
     int best_s = 0;
-    long long best_sum = 0;
+    int best_sum = 0;
     if (policy != SPLIT_NEVER && nd > 0) {
-      long long best = nd > 0 ? max(nch_of(0) * COST_FUSED, (total * Hc * COST_FUSED + ncu - 1) / ncu) : 0;
-      long long sum = 0, longest_split = 0;
+      float best = fmaxf((float)nch_of(0) * COST_FUSED, total * per_cu * COST_FUSED);
+      int sum = 0, longest_split = 0;
       for (int s = 1; s <= n_cand; ++s) {
-        const long long c = nch_of(s - 1);
+        const int c = nch_of(s - 1);
         if (c < MIN_SPLIT_CHUNKS || sum + c > cap_chunks) break;
         sum += c;
         longest_split = max(longest_split, c);
-        const long long pre = (sum * Hc + ncu - 1) / ncu * COST_PRE;
+        const float pre = ceilf((float)sum * per_cu) * COST_PRE;
         // longest fused document (beyond the candidates: at most the last one's length)
-        const long long rest = (s < nd) ? nch_of(min(s, n_cand - 1)) * COST_FUSED : 0;
-        const long long avg = ((sum * COST_CHAIN + (total - sum) * COST_FUSED) * Hc + ncu - 1) / ncu;
-        const long long est = pre + max(max(longest_split * COST_CHAIN, rest), avg);
+        const float rest = (s < nd) ? (float)nch_of(min(s, n_cand - 1)) * COST_FUSED : 0.f;
+        const float avg = ((float)sum * COST_CHAIN + (total - (float)sum) * COST_FUSED) * per_cu;
+        const float est = pre + fmaxf(fmaxf((float)longest_split * COST_CHAIN, rest), avg);
         if (policy == SPLIT_ALWAYS || est < best) { best = est; best_s = s; best_sum = sum; }
       }
     }
@@ -401,7 +401,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void kda_schedule_kernel(
       base += (int)nch_of(j);
     }
     s_nsplit = best_s;
-    s_split_chunks = (int)best_sum;
+    s_split_chunks = best_sum;
   }
   __syncthreads();
   const int ns = s_nsplit;
@@ -547,11 +547,12 @@ struct Image {
   u32x4 p[IMG_PER_THREAD];
 };
 
-// pieces [i0, i1) of an image
+// pieces [i0, i1) of an image (the last round only covers the first waves)
 __device__ __forceinline__ void load_image_part(Image& im, Rsrc r, int tid, int i0, int i1) {
 #pragma unroll
   for (int i = 0; i < IMG_PER_THREAD; ++i)
-    if (i >= i0 && i < i1) im.p[i] = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * tid, 16 * NTHR * i, 0);
+    if (i >= i0 && i < i1 && tid + NTHR * i < IMG_VEC)
+      im.p[i] = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * tid, 16 * NTHR * i, 0);
 }
 
 __device__ __forceinline__ void load_image(Image& im, const uint8_t* __restrict__ src, int tid) {
@@ -562,7 +563,7 @@ __device__ __forceinline__ void image_to_lds(Smem& sm, const Image& im, int tid)
   uint8_t* dst = reinterpret_cast<uint8_t*>(&sm);
 #pragma unroll
   for (int i = 0; i < IMG_PER_THREAD; ++i)
-    *reinterpret_cast<u32x4*>(dst + 16 * (tid + NTHR * i)) = im.p[i];
+    if (tid + NTHR * i < IMG_VEC) *reinterpret_cast<u32x4*>(dst + 16 * (tid + NTHR * i)) = im.p[i];
 }
 
 
@@ -575,10 +576,10 @@ struct LdsSink {
     *reinterpret_cast<bf16x8*>(&sm->Kt[tok][col]) = kt;
   }
   __device__ __forceinline__ void dv(int c, float f) const { dvec(*sm, c)[c & 3] = f; }
-  __device__ __forceinline__ void tb(int row, int col, const bf16x8& hi, const bf16x8& lo) const {
-    *reinterpret_cast<bf16x8*>(&sm->u.tb.hi[row][col]) = hi;
-    *reinterpret_cast<bf16x8*>(&sm->u.tb.lo[row][col]) = lo;
+  __device__ __forceinline__ void tb(int row, int col, const f16x8& x) const {
+    *reinterpret_cast<f16x8*>(&sm->u.tb[row][col]) = x;
   }
+  __device__ __forceinline__ void tbs(float f) const { *tbscale(*sm) = f; }
 };
 
 struct GlobalSink {
@@ -591,10 +592,11 @@ struct GlobalSink {
   __device__ __forceinline__ void dv(int c, float f) const {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f), r, OFF_KT + (c >> 2) * ROW_QK + 2 * DK + 4 * (c & 3), 0, 0);
   }
-  __device__ __forceinline__ void tb(int row, int col, const bf16x8& hi, const bf16x8& lo) const {
-    const uint32_t o = (uint32_t)(row * ROW_CC + 2 * col);
-    bstore(__builtin_bit_cast(u32x4, hi), r, OFF_TB + o);
-    bstore(__builtin_bit_cast(u32x4, lo), r, OFF_TB + CH * ROW_CC + o);
+  __device__ __forceinline__ void tb(int row, int col, const f16x8& x) const {
+    bstore(__builtin_bit_cast(u32x4, x), r, OFF_TB + (uint32_t)(row * ROW_CC + 2 * col));
+  }
+  __device__ __forceinline__ void tbs(float f) const {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f), r, OFF_KT + 32 * ROW_QK + 2 * DK, 0, 0);
   }
 };
 
@@ -609,6 +611,27 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
+
+// largest value of a non-negative x over the wave (uniform result)
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_row_shr<1>(x));
+  x = fmaxf(x, dpp_row_shr<2>(x));
+  x = fmaxf(x, dpp_row_shr<4>(x));
+  x = fmaxf(x, dpp_row_shr<8>(x));
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 47));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+// fp16 operands: the power of two e >= 0 that brings a largest magnitude m
+// below 2^14 (e = 0 for m < 2^14), as the biased-exponent bits of 2^-e and 2^e
+__device__ __forceinline__ int f16_exponent(float m) {
+  const int ex = (__float_as_int(m) >> 23) & 0xFF;
+  return max(0, ex - (127 + 13));
+}
+__device__ __forceinline__ float pow2i(int e) { return __int_as_float((127 + e) << 23); }
 
 __device__ __forceinline__ f32x4 mfma16k16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
@@ -773,14 +796,10 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
     __builtin_amdgcn_sched_barrier(0);
     store_block(sm, accM[0] + accM[1], accA[0] + accA[1], w, w, l, true, beta_mine);
     // blocks above the diagonal are read by the chain's MFMAs: zero them
-    const bf16 z = (bf16)0.f;
 #pragma unroll 1
     for (int bb = w + 1; bb < 4; ++bb)
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        sm.Mhi[16 * w + 4 * (l >> 4) + qq][16 * bb + (l & 15)] = z;
-        sm.Mlo[16 * w + 4 * (l >> 4) + qq][16 * bb + (l & 15)] = z;
-      }
+      for (int qq = 0; qq < 4; ++qq) sm.M[16 * w + 4 * (l >> 4) + qq][16 * bb + (l & 15)] = (_Float16)0.f;
     if (w < 3) {
       // right operand of the pairs (a > w, w): kh_i e^{G_end(w) - G_i} <= 1
 #pragma unroll
@@ -856,7 +875,9 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
   __syncthreads();  // B3: A and M complete, R dead
 
   // ================= T = (I + A)^-1 by 16x16 blocks =================
-  // diagonal blocks: forward substitution, lane j < 16 of wave w owns column j
+  // diagonal blocks: forward substitution, lane j < 16 of wave w owns column j;
+  // tmax tracks the largest |Tb| = |T_ij beta_j| this wave produces
+  float tmax = 0.f;
   if (l < 16) {
     const int j = l;
     float a4[16][16];
@@ -875,8 +896,12 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
       for (int i = 0; i < rr; ++i) acc -= a4[rr][i] * x[i];
       x[rr] = acc;
     }
+    const float bj = fabsf(sm.beta[16 * w + j]);
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) sm.u2.T[16 * w + rr][16 * w + j] = x[rr];
+    for (int rr = 0; rr < 16; ++rr) {
+      sm.u2.T[16 * w + rr][16 * w + j] = x[rr];
+      tmax = fmaxf(tmax, fabsf(x[rr]) * bj);
+    }
 #pragma unroll 1
     for (int bb = w + 1; bb < 4; ++bb)
 #pragma unroll
@@ -919,14 +944,24 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
       Z = mfma16k16(th, yh, Z);
       Z = mfma16k16(tl, yh, Z);
       Z = mfma16k16(th, yl, Z);
+      const float bc = fabsf(sm.beta[16 * b + c]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm.u2.T[16 * a + g4 + i][16 * b + c] = -Z[i];
+      for (int i = 0; i < 4; ++i) {
+        sm.u2.T[16 * a + g4 + i][16 * b + c] = -Z[i];
+        tmax = fmaxf(tmax, fabsf(Z[i]) * bc);
+      }
     }
   }
+  tmax = wave_max(tmax);
+  if (l == 0) sm.tbmax[w] = tmax;
   __syncthreads();  // B5: T complete
-  // Tb = T Diag(beta), split into hi + lo (in LDS it overwrites A): thread
-  // tid converts row tid / 4, columns 16 (tid % 4) .. + 15
+  // Tb = T Diag(beta) 2^-e in fp16 (in LDS it overwrites A), e chosen so
+  // that |Tb 2^-e| < 2^14 (e = 0 unless Tb is huge): thread tid converts row
+  // tid / 4, columns 16 (tid % 4) .. + 15
   {
+    const int e = f16_exponent(fmaxf(fmaxf(sm.tbmax[0], sm.tbmax[1]), fmaxf(sm.tbmax[2], sm.tbmax[3])));
+    const float down = pow2i(-e);
+    if (tid == 0) sink.tbs(pow2i(e));
     const int rr = tid >> 2;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -937,10 +972,10 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
       const float4 b1 = *reinterpret_cast<const float4*>(&sm.beta[cc + 4]);
       const float x[8] = {t0.x * b0.x, t0.y * b0.y, t0.z * b0.z, t0.w * b0.w,
                           t1.x * b1.x, t1.y * b1.y, t1.z * b1.z, t1.w * b1.w};
-      bf16x8 hi, lo;
+      f16x8 th;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) SPLIT_BF16(x[j], hi[j], lo[j]);
-      sink.tb(rr, cc, hi, lo);
+      for (int j = 0; j < 8; ++j) th[j] = (_Float16)(x[j] * down);
+      sink.tb(rr, cc, th);
     }
   }
   __syncthreads();  // B6: the image is complete, T dead (its space stages O)
@@ -1015,20 +1050,34 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
       }
     }
   }
-  bf16x8 Xb[4];
+  // X in fp16, divided by 2^eX when |X| would not fit (eX = 0 almost always)
+  float xv[32];
+  float xmax = 0.f;
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t vv = vx[s >> 1][s & 1][j];
-      Xb[s][2 * j] = (bf16)(X[s >> 1][8 * (s & 1) + 2 * j] + bf16_lo_to_f32(vv));
-      Xb[s][2 * j + 1] = (bf16)(X[s >> 1][8 * (s & 1) + 2 * j + 1] + bf16_hi_to_f32(vv));
+      xv[8 * s + 2 * j] = X[s >> 1][8 * (s & 1) + 2 * j] + bf16_lo_to_f32(vv);
+      xv[8 * s + 2 * j + 1] = X[s >> 1][8 * (s & 1) + 2 * j + 1] + bf16_hi_to_f32(vv);
+      xmax = fmaxf(xmax, fmaxf(fabsf(xv[8 * s + 2 * j]), fabsf(xv[8 * s + 2 * j + 1])));
     }
+  const int ex = f16_exponent(wave_max(xmax));
+  if (ex != 0) {
+    const float down = pow2i(-ex);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) xv[i] *= down;
+  }
+  f16x8 Xh[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) Xh[s][j] = (_Float16)xv[8 * s + j];
   __builtin_amdgcn_sched_barrier(0);
   hook(1);
   __builtin_amdgcn_sched_barrier(0);
 
-  // U = Tb X: the six lower-triangular (row tile, k-step) pairs
+  // U = Tb X: the six lower-triangular (row tile, k-step) pairs, fp16 operands
   constexpr int PMT[6] = {0, 0, 1, 1, 1, 1};
   constexpr int PS[6] = {0, 1, 0, 1, 2, 3};
   f32x16 U[2];
@@ -1040,30 +1089,56 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
     // order (1,0) (0,0) (1,1) (0,1) (1,2) (1,3): the two row tiles alternate;
     // operands are loaded two pairs ahead
     constexpr int ORD[6] = {2, 0, 3, 1, 4, 5};
-    bf16x8 th[2], tl[2];
+    f16x8 th[2];
 #pragma unroll
     for (int o = 0; o < 2; ++o) {
       const int p = ORD[o];
-      th[o] = *reinterpret_cast<const bf16x8*>(&sm.u.tb.hi[32 * PMT[p] + rowsel][16 * PS[p] + 8 * hg]);
-      tl[o] = *reinterpret_cast<const bf16x8*>(&sm.u.tb.lo[32 * PMT[p] + rowsel][16 * PS[p] + 8 * hg]);
+      th[o] = *reinterpret_cast<const f16x8*>(&sm.u.tb[32 * PMT[p] + rowsel][16 * PS[p] + 8 * hg]);
     }
 #pragma unroll
     for (int o = 0; o < 6; ++o) {
       const int p = ORD[o];
-      U[PMT[p]] = mfma32(th[o & 1], Xb[PS[p]], U[PMT[p]]);
-      U[PMT[p]] = mfma32(tl[o & 1], Xb[PS[p]], U[PMT[p]]);
+      U[PMT[p]] = mfma32h(th[o & 1], Xh[PS[p]], U[PMT[p]]);
       if (o + 2 < 6) {
         const int pn = ORD[o + 2];
-        th[o & 1] = *reinterpret_cast<const bf16x8*>(&sm.u.tb.hi[32 * PMT[pn] + rowsel][16 * PS[pn] + 8 * hg]);
-        tl[o & 1] = *reinterpret_cast<const bf16x8*>(&sm.u.tb.lo[32 * PMT[pn] + rowsel][16 * PS[pn] + 8 * hg]);
+        th[o & 1] = *reinterpret_cast<const f16x8*>(&sm.u.tb[32 * PMT[pn] + rowsel][16 * PS[pn] + 8 * hg]);
       }
     }
   }
-  bf16x8 Ubh[4], Ubl[4];
+  // undo the scalings of Tb and X (powers of two, exact)
+  {
+    const float up = *tbscale(sm) * pow2i(ex);
+    if (up != 1.f) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) U[mt][i] *= up;
+    }
+  }
+  // U in bf16 for the state update; in fp16 (divided by 2^eu when needed) for M U
+  bf16x8 Ubh[4];
+  f16x8 Uh[4];
+  float umax = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) umax = fmaxf(umax, fabsf(U[mt][i]));
+  const int eu = f16_exponent(wave_max(umax));
+  const float udown = pow2i(-eu);
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) SPLIT_BF16(U[s >> 1][8 * (s & 1) + j], Ubh[s][j], Ubl[s][j]);
+    for (int j = 0; j < 8; ++j) {
+      Ubh[s][j] = (bf16)U[s >> 1][8 * (s & 1) + j];
+      Uh[s][j] = (_Float16)(U[s >> 1][8 * (s & 1) + j] * udown);
+    }
+  if (eu != 0) {
+    // M U is computed as M (U 2^-eu): bring Qt S to the same scale
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) Sb[s][j] = (bf16)(S[s >> 1][8 * (s & 1) + j] * udown);
+  }
   __builtin_amdgcn_sched_barrier(0);
   hook(2);
   __builtin_amdgcn_sched_barrier(0);
@@ -1072,6 +1147,7 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
   // one accumulator per row tile
   unsigned short (*ost)[32] = sm.u2.ws[w].o;
   {
+    const float oscale = scale * pow2i(eu);
     f32x16 O[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -1084,12 +1160,10 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
       for (int mt = 0; mt < 2; ++mt)
         qa[mt][s] = *reinterpret_cast<const bf16x8*>(&sm.Qt[32 * mt + rowsel][16 * s + 8 * hg]);
     // M operands loaded two pairs ahead
-    bf16x8 mh[2], ml[2];
+    f16x8 mh[2];
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      mh[p] = *reinterpret_cast<const bf16x8*>(&sm.Mhi[32 * PMT[p] + rowsel][16 * PS[p] + 8 * hg]);
-      ml[p] = *reinterpret_cast<const bf16x8*>(&sm.Mlo[32 * PMT[p] + rowsel][16 * PS[p] + 8 * hg]);
-    }
+    for (int p = 0; p < 2; ++p)
+      mh[p] = *reinterpret_cast<const f16x8*>(&sm.M[32 * PMT[p] + rowsel][16 * PS[p] + 8 * hg]);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
 #pragma unroll
@@ -1100,13 +1174,9 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
       }
       if (s < 6) {
         const int p = s;
-        O[PMT[p]] = mfma32(mh[p & 1], Ubh[PS[p]], O[PMT[p]]);
-        O[PMT[p]] = mfma32(ml[p & 1], Ubh[PS[p]], O[PMT[p]]);
-        O[PMT[p]] = mfma32(mh[p & 1], Ubl[PS[p]], O[PMT[p]]);
-        if (p + 2 < 6) {
-          mh[p & 1] = *reinterpret_cast<const bf16x8*>(&sm.Mhi[32 * PMT[p + 2] + rowsel][16 * PS[p + 2] + 8 * hg]);
-          ml[p & 1] = *reinterpret_cast<const bf16x8*>(&sm.Mlo[32 * PMT[p + 2] + rowsel][16 * PS[p + 2] + 8 * hg]);
-        }
+        O[PMT[p]] = mfma32h(mh[p & 1], Uh[PS[p]], O[PMT[p]]);
+        if (p + 2 < 6)
+          mh[p & 1] = *reinterpret_cast<const f16x8*>(&sm.M[32 * PMT[p + 2] + rowsel][16 * PS[p + 2] + 8 * hg]);
       }
     }
 #pragma unroll
@@ -1114,7 +1184,7 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int t = 32 * mt + 16 * (i >> 3) + 8 * hg + (i & 7);
-        const bf16 ob = (bf16)(O[mt][i] * scale);
+        const bf16 ob = (bf16)(O[mt][i] * oscale);
         ost[t][m] = __builtin_bit_cast(unsigned short, ob);
       }
   }
@@ -1184,12 +1254,13 @@ __global__ __launch_bounds__(NTHR, 2) void kda_pre_kernel(
     uint8_t* img = images + ((size_t)(unit / H) * H + h) * IMG_BYTES;
     const GlobalSink sink{make_rsrc(img, IMG_BYTES)};
     prepare_chunk(sm, sink, cur, ch.y, gate_bound, ln, [&](int) {});
-    // KbT, Mhi, Mlo: LDS staging -> image
+    // KbT and M: LDS staging -> image
     const uint8_t* st = reinterpret_cast<const uint8_t*>(&sm.KbT[0][0]);
 #pragma unroll
-    for (int i = 0; i < PRE_STAGED / (16 * NTHR); ++i) {
-      const int o = 16 * (ln.tid + NTHR * i);
-      bstore(*reinterpret_cast<const u32x4*>(st + o), sink.r, OFF_KBT + o);
+    for (int i = 0; i < (PRE_STAGED_VEC + NTHR - 1) / NTHR; ++i) {
+      const int pc = ln.tid + NTHR * i;
+      if (pc < PRE_STAGED_VEC)
+        bstore(*reinterpret_cast<const u32x4*>(st + 16 * pc), sink.r, OFF_KBT + 16 * pc);
     }
     __syncthreads();  // the staging is read out before the next unit rewrites it
   }

@@ -161,6 +161,39 @@ def test_split_long_document_carries_the_state(monkeypatch, cu):
     check(inp, b, doc_tasks(inp.cu_seqlens, H), "split, slow decay")
 
 
+# ---------------------------------------------------------------- value range
+# Tb X and M U run on fp16 operands; values that would not fit are brought in
+# range by exact powers of two.  Large v exercise those paths: the output is
+# linear in v, so GPU(2^k v) / 2^k must match the oracle on v.
+
+def _scaled_v(inp, k):
+    import dataclasses
+    return dataclasses.replace(inp, v=inp.v * np.float32(2.0 ** k))
+
+
+@pytest.mark.parametrize("k", [12, 20, 40])
+def test_large_values_stay_in_range(monkeypatch, k):
+    import torch
+    T, H = 700, 2
+    base = with_gate_scale(_small(T, H, 33, [300, 400]), 33, -0.05)
+    for policy in ("never", "always"):
+        monkeypatch.setenv("KDA_SPLIT", policy)
+        o = run_gpu(_scaled_v(base, k))
+        assert bool(torch.isfinite(o.float()).all())
+        o1 = (o.float() * 2.0 ** -k).to(torch.bfloat16)
+        check(base, o1, doc_tasks(base.cu_seqlens, H), f"v * 2^{k} ({policy})")
+
+
+def test_large_beta(monkeypatch):
+    T, H = 640, 2
+    inp = with_gate_scale(_small(T, H, 34, [T]), 34, -0.3)
+    inp.beta[:] = 1.9
+    for policy in ("never", "always"):
+        monkeypatch.setenv("KDA_SPLIT", policy)
+        o = run_gpu(inp)
+        check(inp, o, doc_tasks(inp.cu_seqlens, H), f"beta 1.9 ({policy})")
+
+
 # ---------------------------------------------------------------- layouts
 
 def test_cu_none_is_one_document():
