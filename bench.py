@@ -1,6 +1,6 @@
 """Benchmark of the KDA chunked forward on one MI355X.
 
-One step = one kda_chunk_fwd call (scheduler + fused chunk kernel) over the
+One step = one kda_chunk_fwd call (scheduler, pre and main kernels) over the
 packed 32768-token stream with H = 32, K = V = 128 and lognormal document
 lengths (median 1024, clipped to [17, 8192]).  Inputs are resident in HBM
 before the timed region.  Prints ONE JSON line on stdout.
@@ -35,17 +35,18 @@ METRIC_WORKLOAD = 3
 KERNEL_SOURCE = os.path.join(ROOT, "linear_attention_sequence_amd", "csrc", "kda_fwd.hip")
 COPY_PROBE_BYTES = 1 << 30
 
-# HBM traffic of one chunk-kernel launch on the packed 32768-token stream, from
-# two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) scaled by
-# the same counters' reading for a 1 GiB device copy.  Valid only for the kernel
-# source with this sha256; otherwise the traffic is reported as null.
+# HBM traffic of one call on the packed 32768-token stream, from two rocprofv3
+# --pmc passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch, mean of 3 calls) per
+# kernel of the call, scaled by the same counters' reading for a 1 GiB device
+# copy (FETCH_SIZE reads half the bytes a copy moves, WRITE_SIZE all of them).
+# Valid only for the kernel source with this sha256; otherwise null.
 TRAFFIC = {
     "workload": "packed_lognormal_T32768_H32",
-    "kernel_sha256": "25c01b4d0664ac1c8f953eee0bf2c178dcdb95285f414b2dfe4c73e05fb47aa1",
-    "fetch_kib": 665029.1,     # mean of 3 dispatches
-    "write_kib": 262173.3,
-    "fetch_scale": 2.0,        # 1 GiB copy: FETCH_SIZE 524303 KiB for 1048576 KiB read
-    "write_scale": 1.0,        # 1 GiB copy: WRITE_SIZE 1048576 KiB
+    "kernel_sha256": "f422c17c0a25f1630df9bacdc326d1ab97808d78aaa83e93e55c557cc3c114a5",
+    "fetch_kib": {"kda_schedule_kernel": 7.2, "kda_pre_kernel": 267304.5, "kda_chunk_fwd_kernel": 686102.2},
+    "write_kib": {"kda_schedule_kernel": 2.2, "kda_pre_kernel": 571134.4, "kda_chunk_fwd_kernel": 262173.8},
+    "fetch_scale": 2.0,
+    "write_scale": 1.0,
 }
 
 
@@ -75,7 +76,8 @@ def measured_traffic(workload_name: str):
     t = TRAFFIC
     if t is None or t["workload"] != workload_name or t["kernel_sha256"] != kernel_source_sha256():
         return None
-    return (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024.0
+    return (sum(t["fetch_kib"].values()) * t["fetch_scale"] +
+            sum(t["write_kib"].values()) * t["write_scale"]) * 1024.0
 
 
 def log(msg):
@@ -205,13 +207,13 @@ def main():
             "frac": gbs / PEAK_HBM_GBS,
             "traffic": measured_traffic(w.name),
             "algorithmic_bytes": bytes_alg,
-            "kernel": "kda_chunk_fwd_kernel",
-            "timing": "HIP events on the launch stream around each call (scheduler + chunk kernel)",
+            "kernel": "kda_chunk_fwd call (kda_schedule_kernel + kda_pre_kernel + kda_chunk_fwd_kernel)",
+            "timing": "HIP events on the launch stream around each call",
         },
         "device_status": status,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(inp, w.lengths, sample_heads=list(range(0, H, 4)))
+        result["cpu_baseline"] = cpu_baseline(inp, w.lengths, sample_heads=list(range(0, H, 2)))
     print(json.dumps(result), flush=True)
 
 

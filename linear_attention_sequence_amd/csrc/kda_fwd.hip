@@ -632,6 +632,12 @@ __device__ __forceinline__ int f16_exponent(float m) {
   return max(0, ex - (127 + 13));
 }
 __device__ __forceinline__ float pow2i(int e) { return __int_as_float((127 + e) << 23); }
+// the exponent for the wave's largest lane value m: 0 unless some lane has
+// m >= 2^14 (the common case costs one compare and a ballot)
+__device__ __forceinline__ int wave_f16_exponent(float m) {
+  if (__builtin_amdgcn_ballot_w64(m >= 16384.f) == 0) return 0;
+  return f16_exponent(wave_max(m));
+}
 
 __device__ __forceinline__ f32x4 mfma16k16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
@@ -1062,7 +1068,7 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
       xv[8 * s + 2 * j + 1] = X[s >> 1][8 * (s & 1) + 2 * j + 1] + bf16_hi_to_f32(vv);
       xmax = fmaxf(xmax, fmaxf(fabsf(xv[8 * s + 2 * j]), fabsf(xv[8 * s + 2 * j + 1])));
     }
-  const int ex = f16_exponent(wave_max(xmax));
+  const int ex = wave_f16_exponent(xmax);
   if (ex != 0) {
     const float down = pow2i(-ex);
 #pragma unroll
@@ -1123,7 +1129,7 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) umax = fmaxf(umax, fabsf(U[mt][i]));
-  const int eu = f16_exponent(wave_max(umax));
+  const int eu = wave_f16_exponent(umax);
   const float udown = pow2i(-eu);
 #pragma unroll
   for (int s = 0; s < 4; ++s)
