@@ -83,9 +83,15 @@ enum kda_device_flags {
  *   stream      HIP stream on the current device; all work is enqueued on it.
  *
  * Ownership: the caller owns every buffer and keeps it alive until the stream
- * has passed this call.  The library allocates a small stream-ordered
- * workspace (hipMallocAsync / hipFreeAsync on `stream`), and never syncs the
- * host.
+ * has passed this call.  The library allocates one stream-ordered workspace
+ * per call (hipMallocAsync / hipFreeAsync on `stream`) and never syncs the
+ * host: a document list (8 B per token) and room for the intermediate chunk
+ * images of long documents (up to about 1.2 KB per token and head, at most
+ * 16 GiB; the device's default memory pool keeps it between calls).
+ *
+ * Environment: KDA_SPLIT=never|always overrides the automatic choice of the
+ * documents whose chunks are prepared in parallel (for tests; the output is
+ * the same bit for bit).
  *
  * Errors: returns KDA_OK or the negative kda_status of the FIRST violated
  * condition, checked in this order: shape (T, H), then (unless T = 0) NULL

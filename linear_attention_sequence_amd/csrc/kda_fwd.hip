@@ -18,18 +18,27 @@
 //
 // Only the last four lines depend on S; they form the sequential chain of a
 // (document, head) unit.  Everything above them depends only on the chunk's
-// own q, k, g, beta.
+// own q, k, g, beta: call it the chunk's image (Qt, Kt, KbT, M, Tb, D).
 //
-// Work decomposition: one workgroup of 4 waves owns a (document, head) unit at
-// a time and walks its chunks in order.  A persistent grid pulls units from a
-// counter; a one-workgroup scheduler kernel orders units longest-document
-// first so the long sequential chains start early.
+// Work decomposition (three launches on the caller's stream):
+//   kda_schedule_kernel  validates cu_seqlens, orders the (document, head)
+//                        units longest document first and decides which long
+//                        documents to split (a cost model over chunk counts);
+//   kda_pre_kernel       builds the images of every chunk of the split
+//                        documents in parallel (two workgroups per CU) and
+//                        writes them to the workspace;
+//   kda_chunk_fwd_kernel one workgroup of 4 waves per CU pulls units from a
+//                        counter: a fused unit prepares and chains each chunk
+//                        itself, a split unit only chains precomputed images,
+//                        so a long document's sequential chain is short.
 //
-// Matrix products run on bf16 MFMA with fp32 accumulation.  Products whose
-// rounding dominates the error (the intra-chunk A and M blocks, Tb X, M U) use
-// a two-term bf16 split x = hi + lo on the operands (three MFMAs: hi*hi +
-// lo*hi + hi*lo), which keeps ~16 significant bits.  The state S stays fp32 in
-// registers; its bf16 copy feeds the MFMAs.
+// Precision: Qt, Kt, KbT and the state's MFMA copy are bf16; S stays fp32 in
+// registers.  M (|M| <= 1) and Tb are fp16, and so are X and U where they meet
+// them (Tb X, M U): fp16 carries three more mantissa bits than bf16 and those
+// two products dominate the error.  Values that would not fit fp16 are scaled
+// by exact powers of two (Tb per chunk, X and U per wave; almost never taken).
+// The diagonal 16x16 blocks of A and M run on fp32 MFMA; the triangular
+// solve's block levels use a two-term bf16 split (hi + lo, ~16 bits).
 //
 // Decay factors inside a chunk can reach exp(+-64*5.5).  A and M are therefore
 // built from 16-token sub-blocks, with the decay split at G_end(b), the
@@ -38,9 +47,7 @@
 // <= 1 for an off-diagonal pair (a > b) and at most exp(15|L|) inside a
 // diagonal sub-block, where the masked upper triangle stays below
 // exp(15|L|) as well (sum_c |qh_c kh_c| <= 1).  With |L| <= 5.5 nothing
-// overflows fp32 or bf16.  Off-diagonal operands are all in [0, 1] and use
-// fp16 (11-bit mantissa, one MFMA); diagonal operands use the bf16 hi + lo
-// split.
+// overflows fp32; off-diagonal operands are all in [0, 1] and use fp16.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
