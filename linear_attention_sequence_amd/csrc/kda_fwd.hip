@@ -659,29 +659,29 @@ __device__ __forceinline__ f32x4 mfma16k16(const bf16x4& a, const bf16x4& b, con
 // D is also written to the image (sink.dv).
 template <class Sm, class Sink>
 __device__ __forceinline__ void fill_tables(Sm& sm, const Sink& sink, int tid) {
-#pragma unroll
-  for (int e = tid; e < 13 * DK; e += NTHR) {
-    const int row = e >> 7, c = e & (DK - 1);
-    const float t0 = sm.tot[0][c], t1 = sm.tot[1][c], t2 = sm.tot[2][c], t3 = sm.tot[3][c];
-    float x;
-    switch (row) {
-      case 0: x = t0; break;
-      case 1: x = t0 + t1; break;
-      case 2: x = (t0 + t1) + t2; break;
-      case 3: x = ((t0 + t1) + t2) + t3; break;
-      case 4: x = (t1 + t2) + t3; break;
-      case 5: x = t2 + t3; break;
-      case 6: x = t3; break;
-      case 7: x = t1; break;         // (1, 0)
-      case 8: x = t1 + t2; break;    // (2, 0)
-      case 9: x = t2; break;         // (2, 1)
-      case 10: x = (t1 + t2) + t3; break;  // (3, 0)
-      case 11: x = t2 + t3; break;   // (3, 1)
-      default: x = t3; break;        // (3, 2)
-    }
-    const float f = __builtin_amdgcn_exp2f(x);
-    sm.etab[row][c] = f;
-    if (row == 3) sink.dv(c, f);
+  // thread pair (c, half): channel c reads its four totals once; half 0 writes
+  // rows 0..6, half 1 rows 7..12
+  const int c = tid & (DK - 1);
+  const float t0 = sm.tot[0][c], t1 = sm.tot[1][c], t2 = sm.tot[2][c], t3 = sm.tot[3][c];
+  const float t12 = t1 + t2, t23 = t2 + t3, t123 = t12 + t3;
+  if (tid < DK) {
+    const float t01 = t0 + t1, t012 = t01 + t2;
+    const float d = __builtin_amdgcn_exp2f(t012 + t3);
+    sm.etab[0][c] = __builtin_amdgcn_exp2f(t0);
+    sm.etab[1][c] = __builtin_amdgcn_exp2f(t01);
+    sm.etab[2][c] = __builtin_amdgcn_exp2f(t012);
+    sm.etab[3][c] = d;
+    sink.dv(c, d);
+    sm.etab[4][c] = __builtin_amdgcn_exp2f(t123);
+    sm.etab[5][c] = __builtin_amdgcn_exp2f(t23);
+    sm.etab[6][c] = __builtin_amdgcn_exp2f(t3);
+  } else {
+    sm.etab[7][c] = __builtin_amdgcn_exp2f(t1);     // (1, 0)
+    sm.etab[8][c] = __builtin_amdgcn_exp2f(t12);    // (2, 0)
+    sm.etab[9][c] = __builtin_amdgcn_exp2f(t2);     // (2, 1)
+    sm.etab[10][c] = __builtin_amdgcn_exp2f(t123);  // (3, 0)
+    sm.etab[11][c] = __builtin_amdgcn_exp2f(t23);   // (3, 1)
+    sm.etab[12][c] = __builtin_amdgcn_exp2f(t3);    // (3, 2)
   }
 }
 
