@@ -685,6 +685,45 @@ __device__ __forceinline__ void fill_tables(Sm& sm, const Sink& sink, int tid) {
   }
 }
 
+// Column block B of T = (I + A)^-1 below the diagonal, on fp32 16x16x4 MFMA
+// (the diagonal blocks T_aa are in LDS).  k-step s of lane group g = l / 16
+// takes k = 4 g + s on both operands, so the C layout of one product (lane l:
+// rows 4 g .. 4 g + 3 of column l % 16) is the B operand of the next: the
+// blocks T_kB stay in registers.  Returns tmax updated with |T_aB beta_col|.
+template <int B, class Sm>
+__device__ __forceinline__ float levels_column(Sm& sm, int l, float tmax) {
+  const int c = l & 15, g4 = 4 * (l >> 4);
+  f32x4 tcol[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) tcol[B][i] = sm.u2.T[16 * B + g4 + i][16 * B + c];
+  const float bc = fabsf(sm.beta[16 * B + c]);
+#pragma unroll
+  for (int a = B + 1; a < 4; ++a) {
+    f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = B; kb < a; ++kb) {
+      const float4 av = *reinterpret_cast<const float4*>(&sm.u.A[16 * a + c][16 * kb + g4]);
+      Y = mfma16f(av.x, tcol[kb][0], Y);
+      Y = mfma16f(av.y, tcol[kb][1], Y);
+      Y = mfma16f(av.z, tcol[kb][2], Y);
+      Y = mfma16f(av.w, tcol[kb][3], Y);
+    }
+    const float4 tv = *reinterpret_cast<const float4*>(&sm.u2.T[16 * a + c][16 * a + g4]);
+    f32x4 Z = {0.f, 0.f, 0.f, 0.f};
+    Z = mfma16f(tv.x, Y[0], Z);
+    Z = mfma16f(tv.y, Y[1], Z);
+    Z = mfma16f(tv.z, Y[2], Z);
+    Z = mfma16f(tv.w, Y[3], Z);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      tcol[a][i] = -Z[i];
+      sm.u2.T[16 * a + g4 + i][16 * B + c] = -Z[i];
+      tmax = fmaxf(tmax, fabsf(Z[i]) * bc);
+    }
+  }
+  return tmax;
+}
+
 // lane coordinates inside the workgroup
 struct Lane {
   int tid;
@@ -901,14 +940,15 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
         const float4 av = *reinterpret_cast<const float4*>(&sm.u.A[16 * w + rr][16 * w + i0]);
         a4[rr][i0] = av.x; a4[rr][i0 + 1] = av.y; a4[rr][i0 + 2] = av.z; a4[rr][i0 + 3] = av.w;
       }
+    // column-oriented: once x_i is final, subtract its share from every later
+    // row (dependency depth 16 instead of the 120 terms of row dot products)
     float x[16];
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      float acc = (rr == j) ? 1.f : 0.f;
+    for (int rr = 0; rr < 16; ++rr) x[rr] = (rr == j) ? 1.f : 0.f;
 #pragma unroll
-      for (int i = 0; i < rr; ++i) acc -= a4[rr][i] * x[i];
-      x[rr] = acc;
-    }
+    for (int i = 0; i < 15; ++i)
+#pragma unroll
+      for (int rr = i + 1; rr < 16; ++rr) x[rr] -= a4[rr][i] * x[i];
     const float bj = fabsf(sm.beta[16 * w + j]);
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
@@ -922,49 +962,10 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
   }
   __syncthreads();  // B4: diagonal blocks of T visible
   // off-diagonal blocks: wave b walks column block b downwards,
-  // T_ab = -T_aa sum_{k=b}^{a-1} A_ak T_kb, on 16x16x16 MFMAs with hi + lo operands
-  if (w < 3) {
-    const int b = w;
-    const int c = l & 15, g4 = 4 * (l >> 4);
-#pragma unroll 1
-    for (int a = b + 1; a < 4; ++a) {
-      f32x4 Y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1
-      for (int kb = b; kb < a; ++kb) {
-        const float4 av = *reinterpret_cast<const float4*>(&sm.u.A[16 * a + c][16 * kb + g4]);
-        const float tv[4] = {sm.u2.T[16 * kb + g4][16 * b + c], sm.u2.T[16 * kb + g4 + 1][16 * b + c],
-                             sm.u2.T[16 * kb + g4 + 2][16 * b + c], sm.u2.T[16 * kb + g4 + 3][16 * b + c]};
-        const float aa[4] = {av.x, av.y, av.z, av.w};
-        bf16x4 ah, al, bh, bl;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          SPLIT_BF16(aa[i], ah[i], al[i]);
-          SPLIT_BF16(tv[i], bh[i], bl[i]);
-        }
-        Y = mfma16k16(ah, bh, Y);
-        Y = mfma16k16(al, bh, Y);
-        Y = mfma16k16(ah, bl, Y);
-      }
-      const float4 tv4 = *reinterpret_cast<const float4*>(&sm.u2.T[16 * a + c][16 * a + g4]);
-      const float ta[4] = {tv4.x, tv4.y, tv4.z, tv4.w};
-      bf16x4 th, tl, yh, yl;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        SPLIT_BF16(ta[i], th[i], tl[i]);
-        SPLIT_BF16(Y[i], yh[i], yl[i]);
-      }
-      f32x4 Z = {0.f, 0.f, 0.f, 0.f};
-      Z = mfma16k16(th, yh, Z);
-      Z = mfma16k16(tl, yh, Z);
-      Z = mfma16k16(th, yl, Z);
-      const float bc = fabsf(sm.beta[16 * b + c]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sm.u2.T[16 * a + g4 + i][16 * b + c] = -Z[i];
-        tmax = fmaxf(tmax, fabsf(Z[i]) * bc);
-      }
-    }
-  }
+  // T_ab = -T_aa sum_{k=b}^{a-1} A_ak T_kb, on fp32 MFMA
+  if (w == 0) tmax = levels_column<0>(sm, l, tmax);
+  else if (w == 1) tmax = levels_column<1>(sm, l, tmax);
+  else if (w == 2) tmax = levels_column<2>(sm, l, tmax);
   tmax = wave_max(tmax);
   if (l == 0) sm.tbmax[w] = tmax;
   __syncthreads();  // B5: T complete
