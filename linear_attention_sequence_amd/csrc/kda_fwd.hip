@@ -1206,18 +1206,15 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
   __builtin_amdgcn_sched_barrier(0);
   hook(3);
   __builtin_amdgcn_sched_barrier(0);
-  // S <- e^{G_c} S + (kh e^{G_c - G})^T U  (the four row tiles interleaved)
+  // S <- e^{G_c} S + (kh e^{G_c - G})^T U: the product accumulates from zero
+  // (the four row tiles interleaved) and S takes it with one fma per element,
+  // so S itself is only ever touched by vector ALU code
   {
+    f32x16 dS[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int i0 = 0; i0 < 16; i0 += 8) {
-        const int c = 32 * kt + 16 * (i0 >> 3) + 8 * hg;
-        const float4 d0 = *reinterpret_cast<const float4*>(dvec(sm, c));
-        const float4 d1 = *reinterpret_cast<const float4*>(dvec(sm, c + 4));
-        S[kt][i0 + 0] *= d0.x; S[kt][i0 + 1] *= d0.y; S[kt][i0 + 2] *= d0.z; S[kt][i0 + 3] *= d0.w;
-        S[kt][i0 + 4] *= d1.x; S[kt][i0 + 5] *= d1.y; S[kt][i0 + 6] *= d1.z; S[kt][i0 + 7] *= d1.w;
-      }
+      for (int i = 0; i < 16; ++i) dS[kt][i] = 0.f;
     bf16x8 kb[2][4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
@@ -1228,9 +1225,20 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
       for (int kt = 0; kt < 4; ++kt) {
         if (s + 1 < 4)
           kb[(s + 1) & 1][kt] = *reinterpret_cast<const bf16x8*>(&sm.KbT[32 * kt + rowsel][16 * (s + 1) + 8 * hg]);
-        S[kt] = mfma32(kb[s & 1][kt], Ubh[s], S[kt]);
+        dS[kt] = mfma32(kb[s & 1][kt], Ubh[s], dS[kt]);
       }
     }
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i0 = 0; i0 < 16; i0 += 8) {
+        const int c = 32 * kt + 16 * (i0 >> 3) + 8 * hg;
+        const float4 d0 = *reinterpret_cast<const float4*>(dvec(sm, c));
+        const float4 d1 = *reinterpret_cast<const float4*>(dvec(sm, c + 4));
+        const float d[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) S[kt][i0 + j] = fmaf(d[j], S[kt][i0 + j], dS[kt][i0 + j]);
+      }
   }
 
   // O rows: lane l writes 16 bytes of row 16 it + l / 4 (rows past the end
