@@ -804,18 +804,18 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
     sq += __shfl_xor(sq, 32);
     sk += __shfl_xor(sk, 16);
     sk += __shfl_xor(sk, 32);
-    const float rq = 1.0f / sqrtf(sq + L2_EPS);
-    const float rk = 1.0f / sqrtf(sk + L2_EPS);
-    // inclusive scan over the 16 tokens of the sub-block (one 16-lane row)
+    const float rq = __builtin_amdgcn_rsqf(sq + L2_EPS);  // hardware 1/sqrt (~1 ulp)
+    const float rk = __builtin_amdgcn_rsqf(sk + L2_EPS);
+    // inclusive scan over the 16 tokens of the sub-block (one 16-lane row),
+    // step-major so that no DPP read waits on the write just before it
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      float x = lg[j];
-      x += dpp_row_shr<1>(x);
-      x += dpp_row_shr<2>(x);
-      x += dpp_row_shr<4>(x);
-      x += dpp_row_shr<8>(x);
-      lg[j] = x;
-    }
+    for (int j = 0; j < 32; ++j) lg[j] += dpp_row_shr<1>(lg[j]);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) lg[j] += dpp_row_shr<2>(lg[j]);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) lg[j] += dpp_row_shr<4>(lg[j]);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) lg[j] += dpp_row_shr<8>(lg[j]);
     if (r == 15) {
 #pragma unroll
       for (int j = 0; j < 32; j += 4)
