@@ -685,6 +685,36 @@ __device__ __forceinline__ void fill_tables(Sm& sm, const Sink& sink, int tid) {
   }
 }
 
+// Off-diagonal blocks (W, b), b < W, of M and A on fp16 MFMA.  Left operand
+// x_r e^{G_r - G_end(b)} = l{q,k} e^{G_end(W) - G_end(b)} <= 1; right operand
+// kh_i e^{G_end(b) - G_i} <= 1 (R, written by wave b).
+template <int W, class Sm>
+__device__ __forceinline__ void offdiag_row(Sm& sm, const float (&lq)[32], const float (&lk)[32], int l,
+                                            int cg, float beta_mine) {
+#pragma unroll
+  for (int b = 0; b < W; ++b) {
+    const float* fr = sm.etab[7 + (W * (W - 1)) / 2 + b];
+    f32x4 accM[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    f32x4 accA[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const f16x8 rv = sm.u2.R[b][s][l];
+      const float4 fa = *reinterpret_cast<const float4*>(&fr[32 * s + 8 * cg]);
+      const float4 fb = *reinterpret_cast<const float4*>(&fr[32 * s + 8 * cg + 4]);
+      const float f[8] = {fa.x, fa.y, fa.z, fa.w, fb.x, fb.y, fb.z, fb.w};
+      f16x8 lqv, lkv;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        lqv[j] = (_Float16)(lq[8 * s + j] * f[j]);
+        lkv[j] = (_Float16)(lk[8 * s + j] * f[j]);
+      }
+      accM[s & 1] = mfma16h(lqv, rv, accM[s & 1]);
+      accA[s & 1] = mfma16h(lkv, rv, accA[s & 1]);
+    }
+    store_block(sm, accM[0] + accM[1], accA[0] + accA[1], W, b, l, false, beta_mine);
+  }
+}
+
 // Column block B of T = (I + A)^-1 below the diagonal, on fp32 16x16x4 MFMA
 // (the diagonal blocks T_aa are in LDS).  k-step s of lane group g = l / 16
 // takes k = 4 g + s on both operands, so the C layout of one product (lane l:
@@ -899,30 +929,10 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
   __builtin_amdgcn_sched_barrier(0);
   hook(2);
   __builtin_amdgcn_sched_barrier(0);
-  // ---- off-diagonal blocks (w, b), b < w, on fp16 MFMA:
-  //      left x_r e^{G_r - G_end(b)} = l{q,k} e^{G_end(w) - G_end(b)} <= 1
-#pragma unroll 1
-  for (int b = 0; b < w; ++b) {
-    const float* fr = sm.etab[7 + (w * (w - 1)) / 2 + b];
-    f32x4 accM[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    f32x4 accA[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const f16x8 rv = sm.u2.R[b][s][l];
-      const float4 fa = *reinterpret_cast<const float4*>(&fr[32 * s + 8 * cg]);
-      const float4 fb = *reinterpret_cast<const float4*>(&fr[32 * s + 8 * cg + 4]);
-      const float f[8] = {fa.x, fa.y, fa.z, fa.w, fb.x, fb.y, fb.z, fb.w};
-      f16x8 lqv, lkv;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        lqv[j] = (_Float16)(lq[8 * s + j] * f[j]);
-        lkv[j] = (_Float16)(lk[8 * s + j] * f[j]);
-      }
-      accM[s & 1] = mfma16h(lqv, rv, accM[s & 1]);
-      accA[s & 1] = mfma16h(lkv, rv, accA[s & 1]);
-    }
-    store_block(sm, accM[0] + accM[1], accA[0] + accA[1], w, b, l, false, beta_mine);
-  }
+  // ---- off-diagonal blocks (w, b), b < w, on fp16 MFMA (fully unrolled per wave)
+  if (w == 1) offdiag_row<1>(sm, lq, lk, l, cg, beta_mine);
+  else if (w == 2) offdiag_row<2>(sm, lq, lk, l, cg, beta_mine);
+  else if (w == 3) offdiag_row<3>(sm, lq, lk, l, cg, beta_mine);
 
   __syncthreads();  // B3: A and M complete, R dead
 
