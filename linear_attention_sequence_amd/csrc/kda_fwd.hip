@@ -877,11 +877,12 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
     hook(1);
     __builtin_amdgcn_sched_barrier(0);
     store_block(sm, accM[0] + accM[1], accA[0] + accA[1], w, w, l, true, beta_mine);
-    // blocks above the diagonal are read by the chain's MFMAs: zero them
-#pragma unroll 1
-    for (int bb = w + 1; bb < 4; ++bb)
+    // the chain's MFMAs read the upper blocks (0, 1) and (2, 3) (inside the two
+    // diagonal 32x32 tiles): zero them; the other upper blocks are never read
+    if (w == 0 || w == 2) {
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) sm.M[16 * w + 4 * (l >> 4) + qq][16 * bb + (l & 15)] = (_Float16)0.f;
+      for (int qq = 0; qq < 4; ++qq) sm.M[16 * w + 4 * (l >> 4) + qq][16 * (w + 1) + (l & 15)] = (_Float16)0.f;
+    }
     if (w < 3) {
       // right operand of the pairs (a > w, w): kh_i e^{G_end(w) - G_i} <= 1
 #pragma unroll
@@ -965,10 +966,10 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
       sm.u2.T[16 * w + rr][16 * w + j] = x[rr];
       tmax = fmaxf(tmax, fabsf(x[rr]) * bj);
     }
-#pragma unroll 1
-    for (int bb = w + 1; bb < 4; ++bb)
+    if (w == 0 || w == 2) {  // upper blocks (0, 1) and (2, 3): read by U = Tb X
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) sm.u2.T[16 * w + rr][16 * bb + j] = 0.f;
+      for (int rr = 0; rr < 16; ++rr) sm.u2.T[16 * w + rr][16 * (w + 1) + j] = 0.f;
+    }
   }
   __syncthreads();  // B4: diagonal blocks of T visible
   // off-diagonal blocks: wave b walks column block b downwards,
