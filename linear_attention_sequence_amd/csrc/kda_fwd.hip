@@ -917,14 +917,34 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
       fk[0] = a.x; fk[1] = a.y; fk[2] = a.z; fk[3] = a.w;
       fk[4] = b.x; fk[5] = b.y; fk[6] = b.z; fk[7] = b.w;
     }
-    bf16x8 qt, kt;
+    bf16x8 qt, kt, kb;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       qt[j] = (bf16)(lq[j0 + j] * fq[j]);
       kt[j] = (bf16)(-lk[j0 + j] * fq[j]);
-      sm.KbT[4 * j0 + 8 * cg + j][tok] = (bf16)(kr[j0 + j] * fk[j]);
+      kb[j] = (bf16)(kr[j0 + j] * fk[j]);
     }
     sink.qk(tok, 4 * j0 + 8 * cg, qt, kt);
+    // KbT is the transpose of these rows: multiplying by the identity on
+    // MFMA (exact) leaves lane l with channel 32 s + l % 16 (and + 16) of
+    // tokens 4 (l / 16) .. + 3, one 8-byte LDS store each
+    {
+      const int s8 = j0 / 8;
+      bf16x8 id0, id1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        id0[j] = (bf16)((8 * cg + j == r) ? 1.f : 0.f);
+        id1[j] = (bf16)((8 * cg + j == 16 + r) ? 1.f : 0.f);
+      }
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      const f32x4 c0 = mfma16(kb, id0, z);
+      const f32x4 c1 = mfma16(kb, id1, z);
+      bf16x4 t0, t1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { t0[i] = (bf16)c0[i]; t1[i] = (bf16)c1[i]; }
+      *reinterpret_cast<bf16x4*>(&sm.KbT[32 * s8 + r][16 * w + 4 * cg]) = t0;
+      *reinterpret_cast<bf16x4*>(&sm.KbT[32 * s8 + 16 + r][16 * w + 4 * cg]) = t1;
+    }
   }
 
   __builtin_amdgcn_sched_barrier(0);
