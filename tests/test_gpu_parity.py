@@ -194,6 +194,49 @@ def test_large_beta(monkeypatch):
         check(inp, o, doc_tasks(inp.cu_seqlens, H), f"beta 1.9 ({policy})")
 
 
+@pytest.mark.parametrize("H", [1, 5, 64])
+def test_head_counts(monkeypatch, H):
+    lengths = [37, 600, 64, 129]
+    T = sum(lengths)
+    inp = with_gate_scale(_small(T, H, 35 + H, lengths), 35 + H, -0.5)
+    monkeypatch.setenv("KDA_SPLIT", "never")
+    a = run_gpu(inp)
+    monkeypatch.setenv("KDA_SPLIT", "always")
+    b = run_gpu(inp)
+    assert bool((_bits(a) == _bits(b)).all())
+    heads = sorted({0, H // 2, H - 1})
+    check(inp, b, doc_tasks(inp.cu_seqlens, H, heads=heads), f"H={H}")
+
+
+def test_gate_at_the_lowest_bound():
+    import torch
+    import linear_attention_sequence_amd as kda
+    T, H = 300, 2
+    inp = _small(T, H, 40, [T])
+    inp.g[:] = -5.5
+    inp.g[::5] = -0.01
+    d = to_device(inp)
+    o, _ = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], gate_bound=-5.5)
+    torch.cuda.synchronize()
+    assert kda.device_status() == 0
+    check(inp, o, doc_tasks(inp.cu_seqlens, H), "gate at -5.5")
+
+
+def test_more_splittable_documents_than_candidates(monkeypatch):
+    # 1100 documents of 9 chunks: the scheduler examines the longest 1024 for
+    # splitting, the rest stay fused; the output is the same bit for bit
+    lengths = [515] * 1100
+    T, H = sum(lengths), 1
+    inp = _small(T, H, 41, lengths)
+    monkeypatch.setenv("KDA_SPLIT", "never")
+    a = run_gpu(inp)
+    monkeypatch.setenv("KDA_SPLIT", "always")
+    b = run_gpu(inp)
+    assert bool((_bits(a) == _bits(b)).all())
+    cu = inp.cu_seqlens
+    check(inp, b, [(int(cu[i]), int(cu[i + 1]), 0, 1) for i in (0, 555, 1099)], "1100 split candidates")
+
+
 # ---------------------------------------------------------------- layouts
 
 def test_cu_none_is_one_document():
