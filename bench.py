@@ -42,9 +42,9 @@ COPY_PROBE_BYTES = 1 << 30
 # Valid only for the kernel source with this sha256; otherwise null.
 TRAFFIC = {
     "workload": "packed_lognormal_T32768_H32",
-    "kernel_sha256": "f422c17c0a25f1630df9bacdc326d1ab97808d78aaa83e93e55c557cc3c114a5",
-    "fetch_kib": {"kda_schedule_kernel": 7.2, "kda_pre_kernel": 267304.5, "kda_chunk_fwd_kernel": 686102.2},
-    "write_kib": {"kda_schedule_kernel": 2.2, "kda_pre_kernel": 571134.4, "kda_chunk_fwd_kernel": 262173.8},
+    "kernel_sha256": "0c2a35ce9f2d671b836643ad37f21d63fd9b8c49099ff9b1bb9efdaa47ada5e5",
+    "fetch_kib": {"kda_schedule_kernel": 7.2, "kda_pre_kernel": 268263.6, "kda_chunk_fwd_kernel": 686187.5},
+    "write_kib": {"kda_schedule_kernel": 2.2, "kda_pre_kernel": 573797.3, "kda_chunk_fwd_kernel": 262174.9},
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }
