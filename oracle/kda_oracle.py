@@ -12,7 +12,12 @@ entries): the KDA delta rule, specialised to
 
 * one recurrent state ``S`` of shape K x V per (document, head), starting at
   zero in every document ("no initial or final state"; "the recurrent state
-  resets at every document boundary" in the ``fused_chunk_kda`` docstring);
+  resets at every document boundary" in the ``fused_chunk_kda`` docstring).
+  The state-carrying variant starts each document from a given ``S_0`` and
+  also returns its last state, the convention of FLA's ``chunk_kda``
+  (``initial_state``, ``output_final_state``), of which ``fused_chunk_kda`` is
+  the drop-in with the final state switched off (same page, ``fused_chunk_kda``
+  entry).  ``S_0 = 0`` gives back the plain forward;
 * q and k l2-normalised inside the operator (``use_qk_l2norm_in_kernel``);
 * a log decay ``g`` per token, head and key channel (the "bounded log gate";
   the K3 model page's ``KimiKDAFp32Params`` returns an fp32 ``[b, s, h, d]``
@@ -50,11 +55,13 @@ def l2_normalise(x: np.ndarray, eps: float = DEFAULT_EPS) -> np.ndarray:
 
 
 def kda_document(q, k, v, g, beta, scale: float | None = None,
-                 eps: float = DEFAULT_EPS) -> np.ndarray:
-    """Run one document from a zero state, all given heads at once.
+                 eps: float = DEFAULT_EPS, initial_state=None, final_state: bool = False):
+    """Run one document, all given heads at once.
 
-    q, k: [L, H, K]; v: [L, H, V]; g: [L, H, K]; beta: [L, H].
-    Returns o: [L, H, V] in fp64.  The final state is discarded.
+    q, k: [L, H, K]; v: [L, H, V]; g: [L, H, K]; beta: [L, H];
+    initial_state: [H, K, V] (S_0 of every head, key channel first) or None
+    for zeros.  Returns o: [L, H, V] in fp64, or ``(o, S_L)`` when
+    ``final_state`` is set (S_L = S_0 for an empty document).
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -67,7 +74,10 @@ def kda_document(q, k, v, g, beta, scale: float | None = None,
         scale = K ** -0.5
     qn = l2_normalise(q, eps)
     kn = l2_normalise(k, eps)
-    S = np.zeros((H, K, V))
+    if initial_state is None:
+        S = np.zeros((H, K, V))
+    else:
+        S = np.array(initial_state, np.float64, copy=True).reshape(H, K, V)
     o = np.empty((L, H, V))
     for t in range(L):
         # Diag(exp(g_t)) S_{t-1}: the decay scales the rows of S (key channels)
@@ -76,14 +86,16 @@ def kda_document(q, k, v, g, beta, scale: float | None = None,
         pred = np.matmul(kt[:, None, :], S)[:, 0, :]         # (D S)^T k  -> [H, V]
         S += beta[t][:, None, None] * kt[:, :, None] * (v[t] - pred)[:, None, :]
         o[t] = scale * np.matmul(qn[t][:, None, :], S)[:, 0, :]   # S_t^T q_t
-    return o
+    return (o, S) if final_state else o
 
 
-def document_bounds(cu_seqlens, T: int) -> list[tuple[int, int]]:
+def document_bounds(cu_seqlens, T: int, exact: bool = False) -> list[tuple[int, int]]:
     """Documents ``[cu[i], cu[i+1])`` of a packed stream (``None`` = one document).
 
-    The list is read up to the first entry equal to T; zero-length documents
-    are kept (they produce nothing)."""
+    By default the list is read up to the first entry equal to T.  With
+    ``exact`` every entry counts (N + 1 entries are N documents, the last
+    entry must be T): the reading used when states are passed per document.
+    Zero-length documents are kept (they produce no output)."""
     if cu_seqlens is None:
         return [(0, T)]
     cu = [int(x) for x in np.asarray(cu_seqlens).reshape(-1)]
@@ -94,7 +106,7 @@ def document_bounds(cu_seqlens, T: int) -> list[tuple[int, int]]:
         if b < a or b > T:
             raise ValueError("cu_seqlens must be non-decreasing and end at T")
         out.append((a, b))
-        if b == T:
+        if b == T and not exact:
             break
     if (out[-1][1] if out else 0) != T:
         raise ValueError("cu_seqlens must reach T")
@@ -102,14 +114,28 @@ def document_bounds(cu_seqlens, T: int) -> list[tuple[int, int]]:
 
 
 def kda_forward(q, k, v, g, beta, cu_seqlens=None, scale: float | None = None,
-                eps: float = DEFAULT_EPS) -> np.ndarray:
-    """Packed forward: q, k, g [T, H, K], v [T, H, V], beta [T, H] -> o [T, H, V] (fp64)."""
+                eps: float = DEFAULT_EPS, initial_state=None, output_final_state: bool = False):
+    """Packed forward: q, k, g [T, H, K], v [T, H, V], beta [T, H] -> o [T, H, V] (fp64).
+
+    With ``initial_state`` ([N, H, K, V], document d starts from
+    ``initial_state[d]``) or ``output_final_state``, the N + 1 entries of
+    ``cu_seqlens`` are read exactly and ``(o, final [N, H, K, V])`` is returned."""
     T = q.shape[0]
     o = np.zeros((T,) + tuple(v.shape[1:]))
-    for a, b in document_bounds(cu_seqlens, T):
-        if b > a:
-            o[a:b] = kda_document(q[a:b], k[a:b], v[a:b], g[a:b], beta[a:b], scale, eps)
-    return o
+    stateful = initial_state is not None or output_final_state
+    bounds = document_bounds(cu_seqlens, T, exact=stateful)
+    if not stateful:
+        for a, b in bounds:
+            if b > a:
+                o[a:b] = kda_document(q[a:b], k[a:b], v[a:b], g[a:b], beta[a:b], scale, eps)
+        return o
+    H, K, V = q.shape[1], q.shape[2], v.shape[2]
+    final = np.zeros((len(bounds), H, K, V))
+    for d, (a, b) in enumerate(bounds):
+        s0 = None if initial_state is None else initial_state[d]
+        o[a:b], final[d] = kda_document(q[a:b], k[a:b], v[a:b], g[a:b], beta[a:b], scale, eps,
+                                        initial_state=s0, final_state=True)
+    return o, final
 
 
 # ---------------------------------------------------------------------------
@@ -129,11 +155,14 @@ def _worker_init():
 
 
 def _run_task(task):
-    a, b, h0, h1 = task
+    a, b, h0, h1 = task[:4]
     s = _SHARED
-    return task, kda_document(s["q"][a:b, h0:h1], s["k"][a:b, h0:h1], s["v"][a:b, h0:h1],
-                              s["g"][a:b, h0:h1], s["beta"][a:b, h0:h1],
-                              s["scale"], s["eps"])
+    init = s["initial_state"]
+    s0 = None if init is None else init[task[4], h0:h1]
+    res = kda_document(s["q"][a:b, h0:h1], s["k"][a:b, h0:h1], s["v"][a:b, h0:h1],
+                       s["g"][a:b, h0:h1], s["beta"][a:b, h0:h1], s["scale"], s["eps"],
+                       initial_state=s0, final_state=s["final_state"])
+    return (task,) + (res if s["final_state"] else (res,))
 
 
 def default_workers() -> int:
@@ -145,13 +174,19 @@ def default_workers() -> int:
 
 
 def kda_tasks(q, k, v, g, beta, tasks, workers: int | None = None,
-              scale: float | None = None, eps: float = DEFAULT_EPS):
+              scale: float | None = None, eps: float = DEFAULT_EPS,
+              initial_state=None, final_state: bool = False):
     """Yield ``((a, b, h0, h1), o)`` for each task: tokens [a, b) of one document,
-    heads [h0, h1).  Tasks are run longest first on ``workers`` processes."""
+    heads [h0, h1).  Tasks are run longest first on ``workers`` processes.
+
+    With states, a task is ``(a, b, h0, h1, d)`` (d = document index into
+    ``initial_state`` [N, H, K, V], or None for zeros) and, when
+    ``final_state`` is set, ``(task, o, S_last)`` is yielded."""
     import multiprocessing as mp
     tasks = sorted(tasks, key=lambda t: -(t[1] - t[0]) * (t[3] - t[2]))
     workers = workers or default_workers()
-    _SHARED.update(q=q, k=k, v=v, g=g, beta=beta, scale=scale, eps=eps)
+    _SHARED.update(q=q, k=k, v=v, g=g, beta=beta, scale=scale, eps=eps,
+                   initial_state=initial_state, final_state=final_state)
     try:
         if workers <= 1 or len(tasks) <= 1:
             for t in tasks:

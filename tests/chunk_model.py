@@ -34,8 +34,10 @@ def bf16_round(x):
 
 
 def chunk_document(q, k, v, g, beta, C: int = 64, scale=None, eps: float = 1e-6,
-                   rnd=None, rnd_state=None, rnd_out=None):
-    """One document, one head: q, k, g [L, K]; v [L, V]; beta [L]. Returns o [L, V]."""
+                   rnd=None, rnd_state=None, rnd_out=None, initial_state=None,
+                   final_state: bool = False):
+    """One document, one head: q, k, g [L, K]; v [L, V]; beta [L]; initial_state
+    [K, V] or None (zeros).  Returns o [L, V], or (o, S_last) with final_state."""
     rnd = rnd or _ident
     rnd_state = rnd_state or _ident
     rnd_out = rnd_out or _ident
@@ -50,7 +52,7 @@ def chunk_document(q, k, v, g, beta, C: int = 64, scale=None, eps: float = 1e-6,
         scale = K ** -0.5
     qh = q / np.sqrt((q * q).sum(-1, keepdims=True) + eps)
     kh = k / np.sqrt((k * k).sum(-1, keepdims=True) + eps)
-    S = np.zeros((K, V))
+    S = np.zeros((K, V)) if initial_state is None else np.array(initial_state, np.float64)
     o = np.zeros((L, V))
     for s in range(0, L, C):
         e = min(L, s + C)
@@ -73,4 +75,4 @@ def chunk_document(q, k, v, g, beta, C: int = 64, scale=None, eps: float = 1e-6,
         Ub = rnd(U)
         o[s:e] = rnd_out(scale * (Qt @ Sb + rnd(M) @ Ub))
         S = np.exp(G[-1])[:, None] * S + Kb.T @ Ub
-    return o
+    return (o, S) if final_state else o

@@ -266,3 +266,121 @@ def test_chunk_form_full_head_dim():
     o = oracle.kda_document(inp.q, inp.k, inp.v, inp.g, inp.beta)[:, 0]
     oc = chunk_document(inp.q[:, 0], inp.k[:, 0], inp.v[:, 0], inp.g[:, 0], inp.beta[:, 0])
     np.testing.assert_allclose(oc, o, rtol=1e-9, atol=1e-10)
+
+
+# --------------------------------------------------------------------------
+# initial / final state (the state-carrying variant: document d starts from
+# S_0 = initial_state[d] and returns its last state)
+# --------------------------------------------------------------------------
+
+def _state(H, K, V, seed, std=0.5):
+    return std * np.random.default_rng(seed).standard_normal((H, K, V))
+
+
+def test_state_beta_zero_closed_form():
+    """beta = 0: nothing is written, so S_t = Diag(exp(G_t)) S_0 with G_t the
+    inclusive cumsum of g, and o_t = scale * S_0^T (qh_t * exp(G_t)).  Catches a
+    decay applied to the wrong axis of S_0, one token late or not at all, and
+    S_0 entering transposed."""
+    T, H, K, V = 9, 2, 6, 4
+    q, k, v, g, beta = _rand(T, H, K, V, seed=31, gate_scale=-0.7)
+    beta[:] = 0.0
+    s0 = _state(H, K, V, 32)
+    o, sT = oracle.kda_document(q, k, v, g, beta, initial_state=s0, final_state=True)
+    G = np.cumsum(g, axis=0)                                    # [T, H, K]
+    qn = q / np.sqrt((q * q).sum(-1, keepdims=True) + 1e-6)
+    for t in range(T):
+        for h in range(H):
+            np.testing.assert_allclose(o[t, h], K ** -0.5 * s0[h].T @ (qn[t, h] * np.exp(G[t, h])),
+                                       rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(sT, np.exp(G[-1])[:, :, None] * s0, rtol=1e-12, atol=1e-14)
+
+
+def test_state_unit_beta_writes_value():
+    """beta_t = 1 and ||kh_t|| = 1: the write replaces the state's value along
+    kh_t, so S_t^T kh_t = v_t whatever S_0 and the history were; with q_t = k_t
+    the output is scale * v_t (eps = 0 keeps ||kh|| exactly 1)."""
+    T, H, K, V = 7, 3, 8, 5
+    q, k, v, g, beta = _rand(T, H, K, V, seed=33, gate_scale=-0.3)
+    beta[-1] = 1.0
+    q[-1] = 3.0 * k[-1]
+    s0 = _state(H, K, V, 34, std=2.0)
+    o, sT = oracle.kda_document(q, k, v, g, beta, eps=0.0, initial_state=s0, final_state=True)
+    kn = k[-1] / np.linalg.norm(k[-1], axis=-1, keepdims=True)
+    np.testing.assert_allclose(np.einsum("hkv,hk->hv", sT, kn), v[-1], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(o[-1], K ** -0.5 * v[-1], rtol=1e-11, atol=1e-12)
+
+
+def test_state_segment_composition():
+    """Running [0, L) equals running [0, a) and then [a, L) from the state the
+    first part returned, for every cut a (the recurrence is a semigroup); a
+    zero-length document returns its initial state."""
+    T, H, K, V = 23, 2, 8, 6
+    q, k, v, g, beta = _rand(T, H, K, V, seed=35, gate_scale=-0.4)
+    s0 = _state(H, K, V, 36)
+    o, sT = oracle.kda_document(q, k, v, g, beta, initial_state=s0, final_state=True)
+    for a in (0, 1, 11, 22, 23):
+        o1, s1 = oracle.kda_document(q[:a], k[:a], v[:a], g[:a], beta[:a], initial_state=s0,
+                                     final_state=True)
+        o2, s2 = oracle.kda_document(q[a:], k[a:], v[a:], g[a:], beta[a:], initial_state=s1,
+                                     final_state=True)
+        np.testing.assert_allclose(np.concatenate([o1, o2]), o, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(s2, sT, rtol=1e-12, atol=1e-13)
+    _, s_empty = oracle.kda_document(q[:0], k[:0], v[:0], g[:0], beta[:0], initial_state=s0,
+                                     final_state=True)
+    np.testing.assert_array_equal(s_empty, s0)
+
+
+def test_state_linearity():
+    """o and the last state are jointly linear in (S_0, v): a state that is
+    added after the decay, or scaled by beta, breaks one of the two checks
+    together with the closed form above."""
+    T, H, K, V = 15, 2, 6, 6
+    q, k, v, g, beta = _rand(T, H, K, V, seed=37, gate_scale=-0.2)
+    s0 = _state(H, K, V, 38)
+    o, sT = oracle.kda_document(q, k, v, g, beta, initial_state=s0, final_state=True)
+    o_v, s_v = oracle.kda_document(q, k, v, g, beta, final_state=True)
+    o_s, s_s = oracle.kda_document(q, k, 0 * v, g, beta, initial_state=s0, final_state=True)
+    np.testing.assert_allclose(o, o_v + o_s, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(sT, s_v + s_s, rtol=1e-11, atol=1e-12)
+    assert np.abs(o_s).max() > 1e-3          # the state reaches the output
+
+
+def test_state_packed_exact_reading():
+    """With states, every cu_seqlens entry delimits a document (trailing empty
+    documents included) and document d starts from initial_state[d]."""
+    lengths = [6, 0, 10, 3, 0]
+    T = sum(lengths)
+    H, K, V = 2, 6, 5
+    q, k, v, g, beta = _rand(T, H, K, V, seed=39, gate_scale=-0.5)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    s0 = np.stack([_state(H, K, V, 40 + d) for d in range(len(lengths))])
+    o, fin = oracle.kda_forward(q, k, v, g, beta, cu, initial_state=s0, output_final_state=True)
+    assert fin.shape == (len(lengths), H, K, V)
+    a = 0
+    for d, L in enumerate(lengths):
+        od, sd = oracle.kda_document(q[a:a + L], k[a:a + L], v[a:a + L], g[a:a + L],
+                                     beta[a:a + L], initial_state=s0[d], final_state=True)
+        np.testing.assert_array_equal(o[a:a + L], od)
+        np.testing.assert_array_equal(fin[d], sd)
+        a += L
+    np.testing.assert_array_equal(fin[1], s0[1])
+    np.testing.assert_array_equal(fin[4], s0[4])
+    # zero initial state is the plain forward
+    o0, _ = oracle.kda_forward(q, k, v, g, beta, cu, output_final_state=True)
+    np.testing.assert_array_equal(o0, oracle.kda_forward(q, k, v, g, beta, cu))
+    assert oracle.document_bounds([0, 3, 7, 7], 7, exact=True) == [(0, 3), (3, 7), (7, 7)]
+
+
+@pytest.mark.parametrize("C", [16, 64])
+def test_chunk_form_with_state_matches_oracle(C):
+    """The chunked form with S_0 != 0 (the term e^G S_0 in X, O and the state
+    carry) equals the token recurrence, over full chunks and a ragged tail."""
+    T, K, V = 150, 16, 12
+    q, k, v, g, beta = _rand(T, 1, K, V, seed=41, gate_scale=-0.05)
+    s0 = _state(1, K, V, 42)
+    o, sT = oracle.kda_document(q, k, v, g, beta, initial_state=s0, final_state=True)
+    oc, sc = chunk_document(q[:, 0], k[:, 0], v[:, 0], g[:, 0], beta[:, 0], C=C,
+                            initial_state=s0[0], final_state=True)
+    np.testing.assert_allclose(oc, o[:, 0], rtol=1e-9, atol=1e-10)
+    np.testing.assert_allclose(sc, sT[0], rtol=1e-9, atol=1e-10)
