@@ -32,7 +32,8 @@ BYTES_PER_TOKEN_HEAD = 2 * DK + 2 * DK + 2 * DV + 4 * DK + 4 + 2 * DV  # q k v g
 PEAK_BF16_TFLOPS = 2516.6   # dense bf16 MFMA, 256 CU x 2.4 GHz x 4096 flop/clk/CU
 PEAK_HBM_GBS = 8000.0       # HBM3E
 METRIC_WORKLOAD = 3
-KERNEL_SOURCE = os.path.join(ROOT, "linear_attention_sequence_amd", "csrc", "kda_fwd.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "linear_attention_sequence_amd", "csrc", f)
+                  for f in ("kda_kernels.h", "kda_fwd.hip", "kda_fwd_state.hip")]
 COPY_PROBE_BYTES = 1 << 30
 
 # HBM traffic of one call on the packed 32768-token stream, from two rocprofv3
@@ -66,8 +67,12 @@ def algorithmic_flops(lengths, heads: int) -> int:
 
 
 def kernel_source_sha256() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 over the kernel sources, in a fixed order."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload_name: str):

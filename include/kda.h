@@ -104,9 +104,48 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                   int32_t chunk, float gate_bound, void* out, hipStream_t stream);
 
 /*
- * kda_last_error -- message for the last non-zero return of kda_chunk_fwd on
- * the calling thread ("" if none).  The string is owned by the library and
- * stays valid until the next call on the same thread.
+ * kda_chunk_fwd_state -- kda_chunk_fwd with a state carried into and out of
+ * every document: document d starts from S = initial_state[d] (instead of
+ * zero) and its last state is written to final_state[d].  This is the
+ * initial_state / output_final_state convention of FLA's chunk_kda, for
+ * which fused_chunk_kda (page "nemo_automodel.components.models.kimi_k3.
+ * kda_fused", fused_chunk_kda entry) is the drop-in with the final state
+ * switched off.  With initial_state = NULL and final_state = NULL the output
+ * equals kda_chunk_fwd's bit for bit.
+ *
+ * Arguments as for kda_chunk_fwd, except:
+ *   cu_seqlens     int32 [n_docs+1], or NULL for one document [0, T)
+ *                  (then n_docs must be 1).  Read exactly: cu[0] = 0,
+ *                  non-decreasing, cu[n_docs] = T.  Every entry delimits a
+ *                  document, trailing empty ones included; an empty document
+ *                  passes its initial state through unchanged.
+ *   n_docs         number of documents, >= 1, n_docs * H <= INT32_MAX
+ *   initial_state  fp32 [n_docs][H][128][128] (S[key channel][value channel]
+ *                  of document d, head h), 16-byte aligned, or NULL for zero
+ *   final_state    fp32 [n_docs][H][128][128], 16-byte aligned, or NULL (not
+ *                  written).  May be the same buffer as initial_state (each
+ *                  (document, head) slot is read before it is written, by the
+ *                  same workgroup); any other overlap is undefined.
+ *   T              may be 0: then q, k, v, g, beta and out are not read and
+ *                  may be NULL, cu_seqlens must hold n_docs + 1 zeros, and
+ *                  final_state (if given) receives initial_state (or zeros).
+ *
+ * Errors: as kda_chunk_fwd, in the same order, plus KDA_ERR_BAD_SHAPE for
+ * n_docs (checked with T and H) and KDA_ERR_ALIGN for the two state buffers.
+ * A cu_seqlens that breaks its contract is reported through
+ * kda_device_status; out and final_state are then filled with NaN.
+ */
+int kda_chunk_fwd_state(const void* q, const void* k, const void* v, const float* g,
+                        const float* beta, const int32_t* cu_seqlens, int32_t n_docs,
+                        int64_t T, int32_t H, int32_t chunk, float gate_bound,
+                        const float* initial_state, float* final_state, void* out,
+                        hipStream_t stream);
+
+/*
+ * kda_last_error -- message for the last non-zero return of kda_chunk_fwd or
+ * kda_chunk_fwd_state on the calling thread ("" if none).  The string is
+ * owned by the library and stays valid until the next call on the same
+ * thread.
  */
 const char* kda_last_error(void);
 

@@ -12,12 +12,15 @@ Recipe (one place, used everywhere):
   ``PCG64(SeedSequence(seed, spawn_key=(s, j)))``.  The result therefore does
   not depend on how many threads fill it.
 * Streams: 0 document lengths, 1 q, 2 k, 3 v, 4 the gate pre-activation
-  ``z_g``, 5 the beta pre-activation ``z_b``.
+  ``z_g``, 5 the beta pre-activation ``z_b``, 6 initial states.
 * ``q, k, v ~ N(0, 1)`` drawn in fp32 and rounded to bf16 (round to nearest
   even) before anyone sees them; both sides consume the same bf16 values.
 * ``g = gate_scale * sigmoid(z_g)`` in fp32 with ``gate_scale = -5``: a log
   decay in ``(-5, 0)`` per token, head and key channel.
 * ``beta = sigmoid(z_b)`` in fp32, one value per token and head.
+* Initial states (for the state-carrying variant): ``0.2 * N(0, 1)`` in fp32,
+  one K x V matrix per document and head (0.2 is about the spread of a state
+  a document leaves behind under a slow decay).
 
 The five workloads are the packed streams the Kimi Delta Attention pages
 specialise the fused forward for (head dims K = V = 128, packed batch-1
@@ -41,6 +44,7 @@ STREAM_K = 2
 STREAM_V = 3
 STREAM_ZG = 4
 STREAM_ZB = 5
+STREAM_STATE = 6
 
 
 def _rng(seed: int, stream: int, block: int = 0) -> np.random.Generator:
@@ -235,6 +239,14 @@ def with_gate_scale(inp: Inputs, seed: int, gate_scale: float) -> Inputs:
     g = sigmoid_f32(zg)
     g *= np.float32(gate_scale)
     return dataclasses.replace(inp, g=g)
+
+
+def initial_states(n_docs: int, H: int, seed: int, std: float = 0.2, K: int = HEAD_DIM,
+                   V: int = HEAD_DIM) -> np.ndarray:
+    """fp32 [n_docs, H, K, V] states ``std * N(0, 1)``."""
+    s = standard_normal((n_docs, H, K, V), seed, STREAM_STATE)
+    s *= np.float32(std)
+    return s
 
 
 def one_hot_keys(T: int, H: int, seed: int, K: int = HEAD_DIM) -> np.ndarray:

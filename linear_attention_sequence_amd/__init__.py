@@ -9,7 +9,9 @@ The tensor-level entry point mirrors the fused path of the K3 model
 (page "nemo_automodel.components.models.kimi_k3.kda_fused"):
 ``chunk_fwd(q, k, v, g, beta, cu_seqlens)`` returns ``(o, None)`` like
 ``fused_chunk_kda``; ``unsupported_reason`` names the first violated condition
-like ``fused_kda_unsupported_reason``.
+like ``fused_kda_unsupported_reason``.  ``initial_state`` /
+``output_final_state`` add the state input and output of FLA's ``chunk_kda``
+(through ``kda_chunk_fwd_state``).
 """
 from __future__ import annotations
 
@@ -58,6 +60,12 @@ def load_library():
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
             ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
         lib.kda_chunk_fwd.restype = ctypes.c_int
+        lib.kda_chunk_fwd_state.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+            ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p]
+        lib.kda_chunk_fwd_state.restype = ctypes.c_int
         lib.kda_last_error.argtypes = []
         lib.kda_last_error.restype = ctypes.c_char_p
         lib.kda_device_status.argtypes = [ctypes.c_void_p]
@@ -75,6 +83,15 @@ def kda_chunk_fwd(q, k, v, g, beta, cu_seqlens, T, H, chunk, gate_bound, out, st
     lib = load_library()
     return lib.kda_chunk_fwd(q, k, v, g, beta, cu_seqlens, int(T), int(H), int(chunk),
                              float(gate_bound), out, stream)
+
+
+def kda_chunk_fwd_state(q, k, v, g, beta, cu_seqlens, n_docs, T, H, chunk, gate_bound,
+                        initial_state, final_state, out, stream) -> int:
+    """Call the C entry point with raw addresses (ints or None); returns its status."""
+    lib = load_library()
+    return lib.kda_chunk_fwd_state(q, k, v, g, beta, cu_seqlens, int(n_docs), int(T), int(H),
+                                   int(chunk), float(gate_bound), initial_state, final_state,
+                                   out, stream)
 
 
 def kda_last_error() -> str:
@@ -105,8 +122,9 @@ def unsupported_reason(q, k, v, g, beta, cu_seqlens=None, *, chunk: int = CHUNK,
                        cp_context=None) -> str | None:
     """Why this call cannot run on the library's kernels, or None when it can.
 
-    Checked in order: mode, l2 norm, safe gate, state, context parallelism,
-    chunk, gate bound, dtypes, devices, layout, shapes, contiguity, cu_seqlens."""
+    Checked in order: mode, l2 norm, safe gate, context parallelism, chunk,
+    gate bound, dtypes, devices, layout, shapes, contiguity, cu_seqlens,
+    initial state."""
     import torch
     if mode != "chunk":
         return f"kda_mode must be 'chunk' (got {mode!r})"
@@ -114,8 +132,6 @@ def unsupported_reason(q, k, v, g, beta, cu_seqlens=None, *, chunk: int = CHUNK,
         return "q/k must be l2-normalised inside the kernel"
     if not safe_gate:
         return "the gate must be the bounded (safe) log gate"
-    if initial_state is not None or output_final_state:
-        return "initial / final state is not supported"
     if cp_context is not None:
         return "context parallelism is not supported"
     if chunk != CHUNK:
@@ -161,7 +177,7 @@ def unsupported_reason(q, k, v, g, beta, cu_seqlens=None, *, chunk: int = CHUNK,
             return "cu_seqlens must be on the same GPU as q"
         if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
             return "cu_seqlens must be 1-D with at least 2 entries"
-        if cu_seqlens.numel() > T + 1:
+        if cu_seqlens.numel() > T + 1 and initial_state is None and not output_final_state:
             return "cu_seqlens has more than T + 1 entries"
         if not cu_seqlens.is_contiguous():
             return "cu_seqlens must be contiguous"
@@ -169,20 +185,42 @@ def unsupported_reason(q, k, v, g, beta, cu_seqlens=None, *, chunk: int = CHUNK,
         return "too many tokens (T must be <= INT32_MAX)"
     if H > 4096:
         return "too many heads"
+    if initial_state is not None:
+        N = cu_seqlens.numel() - 1 if cu_seqlens is not None else B
+        if not isinstance(initial_state, torch.Tensor) or initial_state.dtype != torch.float32:
+            return "initial_state must be an fp32 tensor"
+        if initial_state.device != q.device:
+            return "initial_state must be on the same GPU as q"
+        if tuple(initial_state.shape) != (N, H, HEAD_DIM, HEAD_DIM):
+            return (f"initial_state shape {tuple(initial_state.shape)} must be "
+                    f"{(N, H, HEAD_DIM, HEAD_DIM)} (documents, heads, K, V)")
+        if not initial_state.is_contiguous():
+            return "initial_state must be contiguous"
     return None
 
 
 def chunk_fwd(q, k, v, g, beta, cu_seqlens=None, *, chunk: int = CHUNK,
-              gate_bound: float = DEFAULT_GATE_BOUND, out=None):
-    """KDA chunked forward.  Returns ``(o, None)``.
+              gate_bound: float = DEFAULT_GATE_BOUND, out=None, initial_state=None,
+              output_final_state: bool = False):
+    """KDA chunked forward.  Returns ``(o, final_state)``.
 
     Packed input: ``q, k, v, g`` of shape [1, T, H, 128] (or [T, H, 128]),
     ``beta`` [1, T, H], int32 ``cu_seqlens`` [N+1] on the same GPU.  Dense
     input (``cu_seqlens=None``): [B, T, H, 128] is viewed as B packed
-    documents of T tokens (no copy).  Raises ValueError for an unsupported
+    documents of T tokens (no copy).
+
+    Without states (the fused K3 call) ``final_state`` is None and the list
+    ends at its first entry equal to T.  With ``initial_state`` (fp32
+    [N, H, 128, 128], document d starts from ``initial_state[d]``) or
+    ``output_final_state``, all N + 1 entries of ``cu_seqlens`` delimit
+    documents (N = B for dense input) and, when ``output_final_state`` is set,
+    ``final_state`` [N, H, 128, 128] fp32 holds each document's last state
+    (FLA's ``chunk_kda`` convention).  Raises ValueError for an unsupported
     call and KDAError if the library reports an error."""
     import torch
-    reason = unsupported_reason(q, k, v, g, beta, cu_seqlens, chunk=chunk, gate_bound=gate_bound)
+    reason = unsupported_reason(q, k, v, g, beta, cu_seqlens, chunk=chunk, gate_bound=gate_bound,
+                                initial_state=initial_state,
+                                output_final_state=output_final_state)
     if reason is not None:
         raise ValueError(reason)
     B, T = _layout(q)
@@ -193,19 +231,35 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens=None, *, chunk: int = CHUNK,
     elif out.shape != v.shape or out.dtype != torch.bfloat16 or not out.is_contiguous() \
             or out.device != q.device:
         raise ValueError("out must be a contiguous bf16 tensor shaped like v on q's device")
-    if n_tok == 0:
-        return out, None
+    stateful = initial_state is not None or output_final_state
     cu = cu_seqlens
     if cu is None and B > 1:
         cu = torch.arange(0, n_tok + 1, T, dtype=torch.int32, device=q.device)
+    if not stateful:
+        if n_tok == 0:
+            return out, None
+        with torch.cuda.device(q.device):
+            stream = torch.cuda.current_stream(q.device).cuda_stream
+            rc = kda_chunk_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(),
+                               beta.data_ptr(), None if cu is None else cu.data_ptr(), n_tok, H,
+                               chunk, gate_bound, out.data_ptr(), stream)
+        if rc != KDA_OK:
+            raise KDAError(rc, kda_last_error())
+        return out, None
+    n_docs = cu.numel() - 1 if cu is not None else 1
+    final = None
+    if output_final_state:
+        final = torch.empty((n_docs, H, HEAD_DIM, HEAD_DIM), dtype=torch.float32, device=q.device)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        rc = kda_chunk_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(),
-                           None if cu is None else cu.data_ptr(), n_tok, H, chunk, gate_bound,
-                           out.data_ptr(), stream)
+        rc = kda_chunk_fwd_state(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(),
+            None if cu is None else cu.data_ptr(), n_docs, n_tok, H, chunk, gate_bound,
+            None if initial_state is None else initial_state.data_ptr(),
+            None if final is None else final.data_ptr(), out.data_ptr(), stream)
     if rc != KDA_OK:
         raise KDAError(rc, kda_last_error())
-    return out, None
+    return out, final
 
 
 def device_status(device=None) -> int:

@@ -7,7 +7,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = [os.path.join(HERE, "csrc", "kda_fwd.hip")]
+SOURCES = [os.path.join(HERE, "csrc", "kda_fwd.hip"), os.path.join(HERE, "csrc", "kda_fwd_state.hip")]
 OUTPUT = os.path.join(HERE, "libkda.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -17,7 +17,7 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # keep small private arrays in registers (never moved into LDS)
     "-mllvm", "-disable-promote-alloca-to-lds",
-    "-I" + os.path.join(ROOT, "include"),
+    "-I" + os.path.join(ROOT, "include"), "-I" + os.path.join(HERE, "csrc"),
 ]
 
 

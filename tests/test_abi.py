@@ -19,7 +19,8 @@ def _declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert _declared_functions() == ["kda_chunk_fwd", "kda_device_status", "kda_last_error"]
+    assert _declared_functions() == ["kda_chunk_fwd", "kda_chunk_fwd_state", "kda_device_status",
+                                     "kda_last_error"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -90,12 +91,57 @@ def test_empty_stream_is_a_noop():
     assert rc == kda.KDA_OK and err == ""
 
 
+def _call_state(**kw):
+    args = dict(q=P, k=P, v=P, g=P, beta=P, cu=None, n_docs=1, T=128, H=2, chunk=64,
+                gate_bound=-5.0, h0=None, ht=P, out=P, stream=None)
+    args.update(kw)
+    rc = kda.kda_chunk_fwd_state(args["q"], args["k"], args["v"], args["g"], args["beta"],
+                                 args["cu"], args["n_docs"], args["T"], args["H"], args["chunk"],
+                                 args["gate_bound"], args["h0"], args["ht"], args["out"],
+                                 args["stream"])
+    return rc, kda.kda_last_error()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(T=-1), kda.KDA_ERR_BAD_SHAPE, "T must be >= 0"),
+    (dict(H=0), kda.KDA_ERR_BAD_SHAPE, "H must be >= 1"),
+    (dict(n_docs=0), kda.KDA_ERR_BAD_SHAPE, "n_docs must be >= 1"),
+    (dict(n_docs=2), kda.KDA_ERR_BAD_SHAPE, "n_docs must be 1 when cu_seqlens is NULL"),
+    (dict(n_docs=2**30, cu=P), kda.KDA_ERR_BAD_SHAPE, "n_docs * H"),
+    (dict(q=None), kda.KDA_ERR_NULL_PTR, "q is NULL"),
+    (dict(out=None), kda.KDA_ERR_NULL_PTR, "out is NULL"),
+    (dict(chunk=32), kda.KDA_ERR_UNSUPPORTED, "chunk must be 64"),
+    (dict(gate_bound=1.0), kda.KDA_ERR_UNSUPPORTED, "gate_bound"),
+    (dict(T=0, q=None, chunk=32), kda.KDA_ERR_UNSUPPORTED, "chunk must be 64"),
+    (dict(v=P + 4), kda.KDA_ERR_ALIGN, "v is not 16-byte aligned"),
+    (dict(cu=P + 2), kda.KDA_ERR_ALIGN, "cu_seqlens is not 4-byte aligned"),
+    (dict(h0=P + 8), kda.KDA_ERR_ALIGN, "initial_state is not 16-byte aligned"),
+    (dict(ht=P + 4), kda.KDA_ERR_ALIGN, "final_state is not 16-byte aligned"),
+])
+def test_state_argument_validation(kw, code, msg):
+    if not os.path.exists(kda.LIB_PATH):
+        pytest.skip("libkda.so not built")
+    rc, err = _call_state(**kw)
+    assert rc == code
+    assert msg in err
+
+
+def test_state_empty_stream_without_final_state_is_a_noop():
+    if not os.path.exists(kda.LIB_PATH):
+        pytest.skip("libkda.so not built")
+    rc, err = _call_state(T=0, q=None, k=None, v=None, g=None, beta=None, out=None, ht=None,
+                          h0=P)
+    assert rc == kda.KDA_OK and err == ""
+
+
 def test_unsupported_reason_on_cpu_tensors():
     import torch
     q = torch.zeros(1, 8, 2, 128, dtype=torch.bfloat16)
     r = kda.unsupported_reason(q, q, q, q.float(), torch.zeros(1, 8, 2), None)
     assert "must be on a GPU" in r
     assert "kda_mode" in kda.unsupported_reason(q, q, q, q.float(), None, mode="recurrent")
-    assert "initial / final state" in kda.unsupported_reason(q, q, q, q.float(), None,
-                                                             initial_state=q)
+    s0 = torch.zeros(1, 2, 128, 128)
+    assert "must be on a GPU" in kda.unsupported_reason(q, q, q, q.float(),
+                                                        torch.zeros(1, 8, 2), None,
+                                                        initial_state=s0)
     assert "chunk must be 64" in kda.unsupported_reason(q, q, q, q.float(), None, chunk=16)
