@@ -6,8 +6,14 @@ lengths (median 1024, clipped to [17, 8192]).  Inputs are resident in HBM
 before the timed region.  Prints ONE JSON line on stdout.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-probe]
+                    [--with-state] [--decode N]
 
-``--copy-probe`` adds, after the timed region, two plain device-to-device
+``--decode N`` times one decode step instead: N sequences of one token each
+through the token-recurrent entry point, every state updated in place (the
+state read and write, 128 KiB per sequence and head, are the algorithmic
+bytes).  ``--with-state`` times the state-carrying variant instead (every document
+starts from a given fp32 state and returns its final state; the state bytes
+are added to the algorithmic bytes).  ``--copy-probe`` adds, after the timed region, two plain device-to-device
 copies of 1 GiB: under ``rocprofv3 --pmc FETCH_SIZE`` / ``WRITE_SIZE`` their
 counter readings calibrate the chunk kernel's readings to bytes.
 """
@@ -114,6 +120,67 @@ def cpu_baseline(inp, lengths, sample_heads):
     }
 
 
+def time_steps(step, steps, warmup):
+    """Mean ms per step over ``steps`` calls after ``warmup``, HIP events on the
+    current stream (the stream the library launches on)."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps
+
+
+def decode_bench(args):
+    """One decode step of N sequences (one token each, H = 32) through
+    kda_recurrent_fwd, the state of every sequence updated in place."""
+    import torch
+    import linear_attention_sequence_amd as kda
+    from kda_workloads import cu_from_lengths, initial_states, make_inputs
+    N = args.decode
+    seed = 7
+    inp = make_inputs(N, H, seed, cu_from_lengths([1] * N))
+    dev = torch.device("cuda:0")
+    t = {name: torch.from_numpy(getattr(inp, name)).to(dev) for name in ("q", "k", "v", "g", "beta")}
+    for name in ("q", "k", "v"):
+        t[name] = t[name].to(torch.bfloat16)
+    cu = torch.from_numpy(np.asarray(inp.cu_seqlens, np.int32)).to(dev)
+    state = torch.from_numpy(initial_states(N, H, seed)).to(dev)
+    out = torch.empty_like(t["v"])
+
+    def step():
+        kda.recurrent_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], cu, initial_state=state,
+                          final_state=state, out=out)
+
+    ms = time_steps(step, args.steps, args.warmup)
+    status = kda.device_status()
+    sec = ms / 1e3
+    bytes_alg = N * H * (2 * DK * DV * 4 + BYTES_PER_TOKEN_HEAD) + 4 * (N + 1)
+    gbs = bytes_alg / sec / 1e9
+    log(f"[bench] decode N={N} H={H}: {ms * 1e3:.1f} us/step, {N / sec:.4g} tokens/s, "
+        f"{gbs:.0f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% HBM), status {status}")
+    print(json.dumps({
+        "metric": f"KDA decode step tokens/sec (N={N} sequences, H={H}, K=V=128)",
+        "value": N / sec, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"decode_N{N}_H{H}", "N": N, "H": H, "K": DK, "V": DV,
+                   "state": "fp32, updated in place", "seed": seed},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gbs / PEAK_HBM_GBS, "traffic": None,
+                     "algorithmic_bytes": bytes_alg,
+                     "kernel": "kda_recurrent_fwd call (check + recurrent kernels)"},
+        "device_status": status,
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +189,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", type=int, default=METRIC_WORKLOAD)
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--with-state", action="store_true")
+    ap.add_argument("--decode", type=int, default=0, metavar="N")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the KDA forward here is a single-GPU "
@@ -130,9 +199,12 @@ def main():
 
     import torch
     import linear_attention_sequence_amd as kda
-    from kda_workloads import workload_inputs
+    from kda_workloads import initial_states, workload_inputs
 
     kda.load_library()
+    if args.decode:
+        decode_bench(args)
+        return
     w, inp = workload_inputs(args.workload)
     T = w.T
     dev = torch.device("cuda:0")
@@ -143,10 +215,18 @@ def main():
     beta = torch.from_numpy(inp.beta).to(dev)
     cu = torch.from_numpy(np.asarray(inp.cu_seqlens, np.int32)).to(dev)
     out = torch.empty_like(v)
+    n_docs = len(w.lengths)
+    state_kw = {}
+    if args.with_state:
+        state_kw = dict(initial_state=torch.from_numpy(initial_states(n_docs, H, w.seed)).to(dev),
+                        output_final_state=True)
     torch.cuda.synchronize()
 
+    def step():
+        kda.chunk_fwd(q, k, v, g, beta, cu, out=out, **state_kw)
+
     for _ in range(args.warmup):
-        kda.chunk_fwd(q, k, v, g, beta, cu, out=out)
+        step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -155,7 +235,7 @@ def main():
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        kda.chunk_fwd(q, k, v, g, beta, cu, out=out)
+        step()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -174,7 +254,9 @@ def main():
     sec = ms / 1e3
     tokens_per_s = T / sec
     flops = algorithmic_flops(w.lengths, H)
-    bytes_alg = BYTES_PER_TOKEN_HEAD * T * H + 4 * (len(w.lengths) + 1)
+    bytes_alg = BYTES_PER_TOKEN_HEAD * T * H + 4 * (n_docs + 1)
+    if args.with_state:
+        bytes_alg += 2 * n_docs * H * DK * DV * 4   # initial state read, final state written
     tflops = flops / sec / 1e12
     gbs = bytes_alg / sec / 1e9
     log(f"[bench] {w.name}: {ms * 1e3:.1f} us/call, {tokens_per_s:.4g} tokens/s, "
@@ -200,6 +282,7 @@ def main():
             "documents": len(w.lengths),
             "seed": w.seed,
             "description": w.description,
+            **({"state": "initial and final fp32 state per document"} if args.with_state else {}),
         },
         "tflops": tflops,
         "mfma_frac": tflops / PEAK_BF16_TFLOPS,
@@ -210,7 +293,7 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": gbs / PEAK_HBM_GBS,
-            "traffic": measured_traffic(w.name),
+            "traffic": None if args.with_state else measured_traffic(w.name),
             "algorithmic_bytes": bytes_alg,
             "kernel": "kda_chunk_fwd call (kda_schedule_kernel + kda_pre_kernel + kda_chunk_fwd_kernel)",
             "timing": "HIP events on the launch stream around each call",

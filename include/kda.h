@@ -142,8 +142,33 @@ int kda_chunk_fwd_state(const void* q, const void* k, const void* v, const float
                         hipStream_t stream);
 
 /*
- * kda_last_error -- message for the last non-zero return of kda_chunk_fwd or
- * kda_chunk_fwd_state on the calling thread ("" if none).  The string is
+ * kda_recurrent_fwd -- the same operator as kda_chunk_fwd_state, evaluated
+ * token by token instead of in chunks: the recurrent mode that the K3 model
+ * selects for decoding and short sequences (page "nemo_automodel.components.
+ * models.kimi_k3.kda_fused", package docstring: the fused kernels cover the
+ * chunk mode only; the mode is a model option).  Meant for one token (decode)
+ * or a few tokens per document; the chunked entry points are faster beyond
+ * that.  The result equals kda_chunk_fwd_state's within rounding.
+ *
+ * Arguments as for kda_chunk_fwd_state, without chunk and gate_bound (no
+ * decay factorisation is used, so g only needs to be finite; g <= 0 keeps the
+ * state bounded).  cu_seqlens [n_docs+1] is read exactly; n_docs * H <= 2^30.
+ * initial_state / final_state may be NULL or the same buffer (decode updates
+ * the state in place).
+ *
+ * Ownership: as kda_chunk_fwd; the workspace is 256 bytes.
+ * Errors: as kda_chunk_fwd_state (no chunk / gate_bound checks).  A
+ * cu_seqlens that breaks its contract sets KDA_DEV_BAD_CU_SEQLENS and fills
+ * out and final_state with NaN.
+ */
+int kda_recurrent_fwd(const void* q, const void* k, const void* v, const float* g,
+                      const float* beta, const int32_t* cu_seqlens, int32_t n_docs, int64_t T,
+                      int32_t H, const float* initial_state, float* final_state, void* out,
+                      hipStream_t stream);
+
+/*
+ * kda_last_error -- message for the last non-zero return of kda_chunk_fwd,
+ * kda_chunk_fwd_state or kda_recurrent_fwd on the calling thread ("" if none).  The string is
  * owned by the library and stays valid until the next call on the same
  * thread.
  */

@@ -11,7 +11,8 @@ The tensor-level entry point mirrors the fused path of the K3 model
 ``fused_chunk_kda``; ``unsupported_reason`` names the first violated condition
 like ``fused_kda_unsupported_reason``.  ``initial_state`` /
 ``output_final_state`` add the state input and output of FLA's ``chunk_kda``
-(through ``kda_chunk_fwd_state``).
+(through ``kda_chunk_fwd_state``); ``recurrent_fwd`` is the token-recurrent
+form of the same operator (``kda_recurrent_fwd``) for decoding.
 """
 from __future__ import annotations
 
@@ -66,6 +67,11 @@ def load_library():
             ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p]
         lib.kda_chunk_fwd_state.restype = ctypes.c_int
+        lib.kda_recurrent_fwd.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        lib.kda_recurrent_fwd.restype = ctypes.c_int
         lib.kda_last_error.argtypes = []
         lib.kda_last_error.restype = ctypes.c_char_p
         lib.kda_device_status.argtypes = [ctypes.c_void_p]
@@ -92,6 +98,14 @@ def kda_chunk_fwd_state(q, k, v, g, beta, cu_seqlens, n_docs, T, H, chunk, gate_
     return lib.kda_chunk_fwd_state(q, k, v, g, beta, cu_seqlens, int(n_docs), int(T), int(H),
                                    int(chunk), float(gate_bound), initial_state, final_state,
                                    out, stream)
+
+
+def kda_recurrent_fwd(q, k, v, g, beta, cu_seqlens, n_docs, T, H, initial_state, final_state,
+                      out, stream) -> int:
+    """Call the C entry point with raw addresses (ints or None); returns its status."""
+    lib = load_library()
+    return lib.kda_recurrent_fwd(q, k, v, g, beta, cu_seqlens, int(n_docs), int(T), int(H),
+                                 initial_state, final_state, out, stream)
 
 
 def kda_last_error() -> str:
@@ -260,6 +274,54 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens=None, *, chunk: int = CHUNK,
     if rc != KDA_OK:
         raise KDAError(rc, kda_last_error())
     return out, final
+
+
+def recurrent_fwd(q, k, v, g, beta, cu_seqlens=None, *, initial_state=None,
+                  output_final_state: bool = False, final_state=None, out=None):
+    """Token-recurrent KDA forward (decode, short documents).  Returns
+    ``(o, final_state)``.
+
+    Same tensors and document convention as ``chunk_fwd`` with states: all
+    N + 1 ``cu_seqlens`` entries delimit documents (N = B for a dense
+    [B, T, H, 128] batch).  ``final_state`` may be passed in (fp32
+    [N, H, 128, 128], possibly ``initial_state`` itself for an in-place decode
+    step); otherwise one is allocated when ``output_final_state`` is set."""
+    import torch
+    reason = unsupported_reason(q, k, v, g, beta, cu_seqlens, initial_state=initial_state,
+                                output_final_state=True)
+    if reason is not None:
+        raise ValueError(reason)
+    B, T = _layout(q)
+    H = q.shape[-2]
+    n_tok = B * T
+    if out is None:
+        out = torch.empty_like(v)
+    elif out.shape != v.shape or out.dtype != torch.bfloat16 or not out.is_contiguous() \
+            or out.device != q.device:
+        raise ValueError("out must be a contiguous bf16 tensor shaped like v on q's device")
+    cu = cu_seqlens
+    if cu is None and B > 1:
+        cu = torch.arange(0, n_tok + 1, T, dtype=torch.int32, device=q.device)
+    n_docs = cu.numel() - 1 if cu is not None else 1
+    if final_state is not None:
+        if (not isinstance(final_state, torch.Tensor) or final_state.dtype != torch.float32
+                or tuple(final_state.shape) != (n_docs, H, HEAD_DIM, HEAD_DIM)
+                or not final_state.is_contiguous() or final_state.device != q.device):
+            raise ValueError(f"final_state must be a contiguous fp32 tensor of shape "
+                             f"{(n_docs, H, HEAD_DIM, HEAD_DIM)} on q's device")
+    elif output_final_state:
+        final_state = torch.empty((n_docs, H, HEAD_DIM, HEAD_DIM), dtype=torch.float32,
+                                  device=q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = kda_recurrent_fwd(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(),
+            None if cu is None else cu.data_ptr(), n_docs, n_tok, H,
+            None if initial_state is None else initial_state.data_ptr(),
+            None if final_state is None else final_state.data_ptr(), out.data_ptr(), stream)
+    if rc != KDA_OK:
+        raise KDAError(rc, kda_last_error())
+    return out, final_state
 
 
 def device_status(device=None) -> int:

@@ -321,6 +321,7 @@ int fail(int code, const std::string& msg) {
 struct DeviceInfo {
   int num_cu = 0;
   bool pool_ready = false;
+  int* status_word = nullptr;  // device address of this device's g_kda_status
 };
 std::mutex g_mu;
 std::vector<DeviceInfo> g_devices;
@@ -342,6 +343,11 @@ int device_info(int dev, DeviceInfo** out) {
       (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
     }
     d.pool_ready = true;
+  }
+  if (d.status_word == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_kda_status)) != hipSuccess || p == nullptr) return -1;
+    d.status_word = static_cast<int*>(p);
   }
   *out = &d;
   return 0;
@@ -404,7 +410,7 @@ int launch(const Call& c) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(KDA_ERR_HIP, "hipGetDevice failed");
   DeviceInfo* di = nullptr;
-  if (device_info(dev, &di) != 0) return fail(KDA_ERR_HIP, "hipDeviceGetAttribute failed");
+  if (device_info(dev, &di) != 0) return fail(KDA_ERR_HIP, "device query (CU count, status word) failed");
   const int64_t T = c.T;
   const int H = c.H;
 
@@ -465,6 +471,20 @@ int launch(const Call& c) {
 }
 
 }  // namespace
+
+// host helpers shared with the other translation units of the library
+namespace kda_host {
+int fail(int code, const std::string& msg) { return ::fail(code, msg); }
+int device(int* num_cu, int** status_word) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  DeviceInfo* di = nullptr;
+  if (device_info(dev, &di) != 0) return -1;
+  *num_cu = di->num_cu;
+  *status_word = di->status_word;
+  return 0;
+}
+}  // namespace kda_host
 
 extern "C" int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                              const float* beta, const int32_t* cu_seqlens, int64_t T, int32_t H,

@@ -20,7 +20,7 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     assert _declared_functions() == ["kda_chunk_fwd", "kda_chunk_fwd_state", "kda_device_status",
-                                     "kda_last_error"]
+                                     "kda_last_error", "kda_recurrent_fwd"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -132,6 +132,35 @@ def test_state_empty_stream_without_final_state_is_a_noop():
     rc, err = _call_state(T=0, q=None, k=None, v=None, g=None, beta=None, out=None, ht=None,
                           h0=P)
     assert rc == kda.KDA_OK and err == ""
+
+
+def _call_rec(**kw):
+    args = dict(q=P, k=P, v=P, g=P, beta=P, cu=None, n_docs=1, T=4, H=2, h0=P, ht=P, out=P,
+                stream=None)
+    args.update(kw)
+    rc = kda.kda_recurrent_fwd(args["q"], args["k"], args["v"], args["g"], args["beta"],
+                               args["cu"], args["n_docs"], args["T"], args["H"], args["h0"],
+                               args["ht"], args["out"], args["stream"])
+    return rc, kda.kda_last_error()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(T=-1), kda.KDA_ERR_BAD_SHAPE, "T must be >= 0"),
+    (dict(H=0), kda.KDA_ERR_BAD_SHAPE, "H must be >= 1"),
+    (dict(n_docs=0), kda.KDA_ERR_BAD_SHAPE, "n_docs must be >= 1"),
+    (dict(n_docs=2), kda.KDA_ERR_BAD_SHAPE, "n_docs must be 1 when cu_seqlens is NULL"),
+    (dict(n_docs=2**29 + 1, cu=P), kda.KDA_ERR_BAD_SHAPE, "n_docs * H"),
+    (dict(g=None), kda.KDA_ERR_NULL_PTR, "g is NULL"),
+    (dict(k=P + 2), kda.KDA_ERR_ALIGN, "k is not 16-byte aligned"),
+    (dict(h0=P + 4), kda.KDA_ERR_ALIGN, "initial_state is not 16-byte aligned"),
+    (dict(ht=P + 8), kda.KDA_ERR_ALIGN, "final_state is not 16-byte aligned"),
+])
+def test_recurrent_argument_validation(kw, code, msg):
+    if not os.path.exists(kda.LIB_PATH):
+        pytest.skip("libkda.so not built")
+    rc, err = _call_rec(**kw)
+    assert rc == code
+    assert msg in err
 
 
 def test_unsupported_reason_on_cpu_tensors():
