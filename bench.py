@@ -46,12 +46,13 @@ COPY_PROBE_BYTES = 1 << 30
 # --pmc passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch, mean of 3 calls) per
 # kernel of the call, scaled by the same counters' reading for a 1 GiB device
 # copy (FETCH_SIZE reads half the bytes a copy moves, WRITE_SIZE all of them).
-# Valid only for the kernel source with this sha256; otherwise null.
+# Valid only for the kernel sources with this sha256 (kda_kernels.h,
+# kda_fwd.hip, kda_fwd_state.hip in that order); otherwise null.
 TRAFFIC = {
     "workload": "packed_lognormal_T32768_H32",
-    "kernel_sha256": "0c2a35ce9f2d671b836643ad37f21d63fd9b8c49099ff9b1bb9efdaa47ada5e5",
-    "fetch_kib": {"kda_schedule_kernel": 7.2, "kda_pre_kernel": 268263.6, "kda_chunk_fwd_kernel": 686187.5},
-    "write_kib": {"kda_schedule_kernel": 2.2, "kda_pre_kernel": 573797.3, "kda_chunk_fwd_kernel": 262174.9},
+    "kernel_sha256": "f51e3f627315e35ad8497f6a4791221f2518d8d5f2c52fc6dcbefb2d7e206c7d",
+    "fetch_kib": {"kda_schedule_kernel": 8.7, "kda_pre_kernel": 268243.6, "kda_chunk_fwd_kernel": 685585.8},
+    "write_kib": {"kda_schedule_kernel": 2.3, "kda_pre_kernel": 573840.0, "kda_chunk_fwd_kernel": 262175.0},
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }
