@@ -76,3 +76,106 @@ def chunk_document(q, k, v, g, beta, C: int = 64, scale=None, eps: float = 1e-6,
         o[s:e] = rnd_out(scale * (Qt @ Sb + rnd(M) @ Ub))
         S = np.exp(G[-1])[:, None] * S + Kb.T @ Ub
     return (o, S) if final_state else o
+
+
+def chunk_document_backward(q, k, v, g, beta, do, C: int = 64, scale=None, eps: float = 1e-6,
+                            initial_state=None, d_final_state=None):
+    """Gradients of one document, one head, by the chunked backward the GPU
+    implements (fp64).  q, k, g [L, K]; v, do [L, V]; beta [L].  Returns
+    dq, dk, dv, dg, dbeta, dh0.
+
+    Per chunk (rows r, i; state S0 at its start, dSc = dL/dS at its end):
+        dU   = scale M^T dO + Kbar dSc           dX = Tb^T dU  (= dV)
+        dS0  = D dSc + scale Qt^T dO - Kt^T dX   (handed to the previous chunk)
+        dQt  = scale dO S0^T,  dKt = -dX S0^T,   dKbar = U dSc^T,  dD = rowsum(dSc * S0)
+        dM   = scale tril(dO U^T),  dTb = tril(dU X^T)
+        dbeta_i += sum_r dTb_ri T_ri,  dT = dTb diag(beta),  dA = -T^T dT T^T (strict lower)
+        dbeta_r += sum_i dA_ri Kk_ri,  dKk = diag(beta) dA
+    then the bilinear forms M = tril(sum_c qh_rc kh_ic E_ric), Kk (strict) with
+    E_ric = exp(G_rc - G_ic), the decayed tiles Qt, Kt, Kbar, D, the in-chunk
+    cumsum G of g, and the l2 norms."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    g = np.asarray(g, np.float64)
+    beta = np.asarray(beta, np.float64)
+    do = np.asarray(do, np.float64)
+    L, K = q.shape
+    V = v.shape[1]
+    if scale is None:
+        scale = K ** -0.5
+    nq = np.sqrt((q * q).sum(-1, keepdims=True) + eps)
+    nk = np.sqrt((k * k).sum(-1, keepdims=True) + eps)
+    qh, kh = q / nq, k / nk
+    # forward: states at chunk starts
+    starts = list(range(0, L, C))
+    S = np.zeros((K, V)) if initial_state is None else np.array(initial_state, np.float64)
+    S_at = []
+    per = []
+    for s in starts:
+        e = min(L, s + C)
+        c = e - s
+        G = np.cumsum(g[s:e], axis=0)
+        E = np.exp(np.where(np.tril(np.ones((c, c)))[:, :, None] > 0,
+                            G[:, None, :] - G[None, :, :], -np.inf))
+        Kq = np.einsum("rc,ic,ric->ri", qh[s:e], kh[s:e], E)
+        Kk = np.einsum("rc,ic,ric->ri", kh[s:e], kh[s:e], E) * np.tril(np.ones((c, c)), -1)
+        M = Kq * np.tril(np.ones((c, c)))
+        T = np.linalg.inv(np.eye(c) + beta[s:e, None] * Kk)
+        Tb = T * beta[s:e][None, :]
+        eG = np.exp(G)
+        Qt, Kt = qh[s:e] * eG, kh[s:e] * eG
+        Kb = kh[s:e] * np.exp(G[-1][None, :] - G)
+        D = np.exp(G[-1])
+        X = v[s:e] - Kt @ S
+        U = Tb @ X
+        S_at.append(S)
+        per.append(dict(s=s, e=e, c=c, G=G, E=E, Kk=Kk, M=M, T=T, Tb=Tb, eG=eG, Qt=Qt, Kt=Kt,
+                        Kb=Kb, D=D, X=X, U=U))
+        S = D[:, None] * S + Kb.T @ U
+    dq_h = np.zeros_like(q)
+    dk_h = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dg = np.zeros_like(g)
+    dbeta = np.zeros_like(beta)
+    dS = np.zeros((K, V)) if d_final_state is None else np.array(d_final_state, np.float64)
+    for S0, P in reversed(list(zip(S_at, per))):
+        s, e, c = P["s"], P["e"], P["c"]
+        dO = do[s:e]
+        dU = scale * P["M"].T @ dO + P["Kb"] @ dS
+        dX = P["Tb"].T @ dU
+        dv[s:e] = dX
+        dQt = scale * dO @ S0.T
+        dKt = -dX @ S0.T
+        dKb = P["U"] @ dS.T
+        dD = (dS * S0).sum(1)
+        dM = scale * np.tril(dO @ P["U"].T)
+        dTb = np.tril(dU @ P["X"].T)
+        db = (dTb * P["T"]).sum(0)
+        dT = dTb * beta[s:e][None, :]
+        dA = np.tril(-P["T"].T @ dT @ P["T"].T, -1)
+        db += (dA * P["Kk"]).sum(1)
+        dKk = beta[s:e][:, None] * dA
+        dbeta[s:e] = db
+        E = P["E"]
+        qs, ks = qh[s:e], kh[s:e]
+        dqh = np.einsum("ri,ic,ric->rc", dM, ks, E)
+        dkh = (np.einsum("ri,rc,ric->ic", dM, qs, E) + np.einsum("ri,rc,ric->ic", dKk, ks, E)
+               + np.einsum("ri,ic,ric->rc", dKk, ks, E))
+        W = (dM[:, :, None] * qs[:, None, :] + dKk[:, :, None] * ks[:, None, :]) * ks[None, :, :] * E
+        dG = W.sum(1) - W.sum(0)
+        dqh += dQt * P["eG"]
+        dG += dQt * P["Qt"]
+        dkh += dKt * P["eG"]
+        dG += dKt * P["Kt"]
+        eb = np.exp(P["G"][-1][None, :] - P["G"])
+        dkh += dKb * eb
+        dG -= dKb * P["Kb"]
+        dG[-1] += (dKb * P["Kb"]).sum(0) + dD * P["D"]
+        dg[s:e] = np.cumsum(dG[::-1], axis=0)[::-1]
+        dq_h[s:e] = dqh
+        dk_h[s:e] = dkh
+        dS = P["D"][:, None] * dS + scale * P["Qt"].T @ dO - P["Kt"].T @ dX
+    dq = (dq_h - qh * (qh * dq_h).sum(-1, keepdims=True)) / nq
+    dk = (dk_h - kh * (kh * dk_h).sum(-1, keepdims=True)) / nk
+    return dq, dk, dv, dg, dbeta, dS
