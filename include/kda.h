@@ -167,8 +167,43 @@ int kda_recurrent_fwd(const void* q, const void* k, const void* v, const float* 
                       hipStream_t stream);
 
 /*
- * kda_last_error -- message for the last non-zero return of kda_chunk_fwd,
- * kda_chunk_fwd_state or kda_recurrent_fwd on the calling thread ("" if none).  The string is
+ * kda_chunk_bwd -- gradients of the state-carrying forward (kda_chunk_fwd_state)
+ * with respect to q, k, v, g, beta and the initial states, given d_out = dL/do
+ * and d_final_state = dL/dS_end.  It recomputes every intermediate from the
+ * raw inputs, as the backward of the pages' fused forward does (page
+ * "nemo_automodel.components.models.kimi_k3.kda_fused", package docstring:
+ * the autograd function saves only q, k, v, g, beta and cu_seqlens).
+ *
+ * Inputs as for kda_chunk_fwd_state (q, k, v, g, beta, cu_seqlens read exactly
+ * with n_docs + 1 entries, initial_state or NULL), plus
+ *   d_out          bf16 [T][H][128], 16-byte aligned
+ *   d_final_state  fp32 [n_docs][H][128][128] or NULL (zero)
+ * Outputs, all fp32, fully overwritten:
+ *   dq, dk, dv, dg fp32 [T][H][128], 16-byte aligned
+ *   dbeta          fp32 [T][H], 4-byte aligned
+ *   d_initial_state fp32 [n_docs][H][128][128] or NULL (not written)
+ * T = 0 is allowed (then the token tensors are not read and
+ * d_initial_state, if given, receives d_final_state).
+ *
+ * Arithmetic: fp32 throughout (MFMA 16x16x4 fp32 products); the forward
+ * states it differentiates around come from the forward kernels.
+ * Ownership: as kda_chunk_fwd; the stream-ordered workspace holds, per chunk
+ * and head, the state and its gradient at the chunk boundary, the fp32 chunk
+ * image and its transition (about 400 KiB), plus a bf16 copy of the forward
+ * output.
+ * Errors: as kda_chunk_fwd_state, plus KDA_ERR_NULL_PTR for d_out and the
+ * gradient outputs; a cu_seqlens that breaks its contract sets
+ * KDA_DEV_BAD_CU_SEQLENS and fills every gradient output with NaN.
+ */
+int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
+                  const float* beta, const int32_t* cu_seqlens, int32_t n_docs, int64_t T,
+                  int32_t H, int32_t chunk, float gate_bound, const float* initial_state,
+                  const void* d_out, const float* d_final_state, float* dq, float* dk, float* dv,
+                  float* dg, float* dbeta, float* d_initial_state, hipStream_t stream);
+
+/*
+ * kda_last_error -- message for the last non-zero return of any entry point
+ * on the calling thread ("" if none).  The string is
  * owned by the library and stays valid until the next call on the same
  * thread.
  */

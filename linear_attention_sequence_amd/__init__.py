@@ -72,6 +72,13 @@ def load_library():
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         lib.kda_recurrent_fwd.restype = ctypes.c_int
+        lib.kda_chunk_bwd.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+            ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p]
+        lib.kda_chunk_bwd.restype = ctypes.c_int
         lib.kda_last_error.argtypes = []
         lib.kda_last_error.restype = ctypes.c_char_p
         lib.kda_device_status.argtypes = [ctypes.c_void_p]
@@ -106,6 +113,15 @@ def kda_recurrent_fwd(q, k, v, g, beta, cu_seqlens, n_docs, T, H, initial_state,
     lib = load_library()
     return lib.kda_recurrent_fwd(q, k, v, g, beta, cu_seqlens, int(n_docs), int(T), int(H),
                                  initial_state, final_state, out, stream)
+
+
+def kda_chunk_bwd(q, k, v, g, beta, cu_seqlens, n_docs, T, H, chunk, gate_bound, initial_state,
+                  d_out, d_final_state, dq, dk, dv, dg, dbeta, d_initial_state, stream) -> int:
+    """Call the C entry point with raw addresses (ints or None); returns its status."""
+    lib = load_library()
+    return lib.kda_chunk_bwd(q, k, v, g, beta, cu_seqlens, int(n_docs), int(T), int(H),
+                             int(chunk), float(gate_bound), initial_state, d_out, d_final_state,
+                             dq, dk, dv, dg, dbeta, d_initial_state, stream)
 
 
 def kda_last_error() -> str:
@@ -322,6 +338,55 @@ def recurrent_fwd(q, k, v, g, beta, cu_seqlens=None, *, initial_state=None,
     if rc != KDA_OK:
         raise KDAError(rc, kda_last_error())
     return out, final_state
+
+
+def chunk_bwd(q, k, v, g, beta, d_out, cu_seqlens=None, *, initial_state=None,
+              d_final_state=None, chunk: int = CHUNK, gate_bound: float = DEFAULT_GATE_BOUND):
+    """Gradients of ``chunk_fwd(..., initial_state=initial_state,
+    output_final_state=True)`` for ``d_out`` (bf16, shaped like v) and
+    ``d_final_state`` (fp32 [N, H, 128, 128] or None).  Returns fp32
+    ``(dq, dk, dv, dg, dbeta, d_initial_state)`` shaped like the inputs
+    (``d_initial_state`` is None when ``initial_state`` is None)."""
+    import torch
+    reason = unsupported_reason(q, k, v, g, beta, cu_seqlens, chunk=chunk, gate_bound=gate_bound,
+                                initial_state=initial_state, output_final_state=True)
+    if reason is not None:
+        raise ValueError(reason)
+    if (not isinstance(d_out, torch.Tensor) or d_out.dtype != torch.bfloat16
+            or d_out.shape != v.shape or not d_out.is_contiguous() or d_out.device != q.device):
+        raise ValueError("d_out must be a contiguous bf16 tensor shaped like v on q's device")
+    B, T = _layout(q)
+    H = q.shape[-2]
+    n_tok = B * T
+    cu = cu_seqlens
+    if cu is None and B > 1:
+        cu = torch.arange(0, n_tok + 1, T, dtype=torch.int32, device=q.device)
+    n_docs = cu.numel() - 1 if cu is not None else 1
+    if d_final_state is not None:
+        if (not isinstance(d_final_state, torch.Tensor) or d_final_state.dtype != torch.float32
+                or tuple(d_final_state.shape) != (n_docs, H, HEAD_DIM, HEAD_DIM)
+                or not d_final_state.is_contiguous() or d_final_state.device != q.device):
+            raise ValueError(f"d_final_state must be a contiguous fp32 tensor of shape "
+                             f"{(n_docs, H, HEAD_DIM, HEAD_DIM)} on q's device")
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty(q.shape, **f32)
+    dk = torch.empty(q.shape, **f32)
+    dv = torch.empty(v.shape, **f32)
+    dg = torch.empty(g.shape, **f32)
+    dbeta = torch.empty(beta.shape, **f32)
+    dh0 = torch.empty((n_docs, H, HEAD_DIM, HEAD_DIM), **f32) if initial_state is not None else None
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = kda_chunk_bwd(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(),
+            None if cu is None else cu.data_ptr(), n_docs, n_tok, H, chunk, gate_bound,
+            None if initial_state is None else initial_state.data_ptr(), d_out.data_ptr(),
+            None if d_final_state is None else d_final_state.data_ptr(), dq.data_ptr(),
+            dk.data_ptr(), dv.data_ptr(), dg.data_ptr(), dbeta.data_ptr(),
+            None if dh0 is None else dh0.data_ptr(), stream)
+    if rc != KDA_OK:
+        raise KDAError(rc, kda_last_error())
+    return dq, dk, dv, dg, dbeta, dh0
 
 
 def device_status(device=None) -> int:

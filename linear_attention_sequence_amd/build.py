@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = [os.path.join(HERE, "csrc", f)
-           for f in ("kda_fwd.hip", "kda_fwd_state.hip", "kda_recurrent.hip")]
+           for f in ("kda_fwd.hip", "kda_fwd_state.hip", "kda_recurrent.hip", "kda_bwd.hip")]
 OUTPUT = os.path.join(HERE, "libkda.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

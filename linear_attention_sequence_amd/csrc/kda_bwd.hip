@@ -1,0 +1,743 @@
+// kda_bwd.hip -- chunked backward of the KDA forward (fp32).
+//
+// Gradients of L = sum_t <o_t, do_t> + sum_d <S_end(d), dS_end(d)> with
+// respect to q, k, v, g, beta and the initial states, for the operator of
+// include/kda.h.  Like the backward of the pages' fused forward (page
+// "nemo_automodel.components.models.kimi_k3.kda_fused", package docstring),
+// it recomputes every intermediate from q, k, v, g, beta and cu_seqlens.
+//
+// Per chunk (c <= 64 tokens r, i; S0 the state at its start, dSc = dL/dS at
+// its end; Tb = T Diag(beta), T = (I + Diag(beta) Kk)^-1, Kk and M the
+// decayed key-key and query-key products, Qt, Kt, Kbar, D the decayed tiles):
+//
+//   forward:   X = V - Kt S0,   U = Tb X
+//   dS0 = F^T dSc + R  with  F^T = D - Kt^T Tb^T Kbar,
+//                            R   = scale Qt^T dO - Kt^T Tb^T (scale M^T dO)
+//   dU  = scale M^T dO + Kbar dSc,  dX = Tb^T dU (= dV)
+//   dQt = scale dO S0^T, dKt = -dX S0^T, dKbar = U dSc^T, dD = rowsum(dSc * S0)
+//   dM  = scale tril(dO U^T), dTb = tril(dU X^T), dbeta_i += sum_r dTb_ri T_ri
+//   dA  = -T^T (dTb Diag(beta)) T^T (strict lower), dbeta_r += sum_i dA_ri Kk_ri,
+//   dKk = Diag(beta) dA
+// followed by the bilinear forms of M and Kk (exp(G_r - G_i) per channel,
+// never above 1 for i <= r), the decayed tiles, the in-chunk cumsum of g and
+// the l2 norms.  The same derivation, in fp64 numpy, is checked against an
+// autograd oracle.
+//
+// Passes (all on the caller's stream):
+//   1. the stateful forward with S stored at every chunk start (kda_fwd.hip);
+//   2. kda_bwd_setup_kernel: cu_seqlens check and the chunk table;
+//   3. kda_bwd_prep_kernel (parallel over chunks): qh, kh, G, T, Kk, M and
+//      F^T, R of every chunk;
+//   4. kda_bwd_chain_kernel (per document and head, last chunk first):
+//      dS <- F^T dS + R, storing dS at every chunk end;
+//   5. kda_bwd_grads_kernel (parallel over chunks): all input gradients.
+// Products run on fp32 MFMA (16x16x4) with operands staged through LDS.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string>
+
+#include "kda.h"
+
+namespace kda_host {
+int fail(int code, const std::string& msg);
+int device(int* num_cu, int** status_word);
+int forward_with_chunk_states(const void* q, const void* k, const void* v, const float* g,
+                              const float* beta, const int32_t* cu, int32_t n_docs, int64_t T,
+                              int32_t H, float gate_bound, const float* h0, void* out,
+                              float* chunk_states, hipStream_t stream);
+}  // namespace kda_host
+
+namespace {
+
+constexpr int CH = 64;
+constexpr int DK = 128;
+constexpr int DV = 128;
+constexpr int NT = 256;
+constexpr int LD = 129;                      // padded row of a [64][128] LDS tile
+constexpr int LDC = 65;                      // padded row of a [64][64] LDS tile
+constexpr float SCALE = 0.08838834764831845f;  // 128^-1/2
+constexpr float L2_EPS = 1e-6f;
+constexpr int STAGE_FLOATS = 16 * (128 + 1) * 2;
+typedef __bf16 bf16;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// per (chunk, head) image written by the prep pass, fp32
+constexpr int IMG_QH = 0;                    // [64][128] qh
+constexpr int IMG_KH = IMG_QH + CH * DK;     // [64][128] kh
+constexpr int IMG_G = IMG_KH + CH * DK;      // [64][128] in-chunk cumsum of g
+constexpr int IMG_T = IMG_G + CH * DK;       // [64][64] (I + Diag(beta) Kk)^-1
+constexpr int IMG_KK = IMG_T + CH * CH;      // [64][64] Kk (strictly lower)
+constexpr int IMG_M = IMG_KK + CH * CH;      // [64][64] M (lower incl.)
+constexpr int IMG_RQ = IMG_M + CH * CH;      // [64] 1/||q||
+constexpr int IMG_RK = IMG_RQ + CH;          // [64] 1/||k||
+constexpr int IMG_FLOATS = IMG_RK + CH;
+
+// per-workgroup scratch of the gradient pass, fp32
+constexpr int SC_X = 0;
+constexpr int SC_U = SC_X + CH * DV;
+constexpr int SC_DU = SC_U + CH * DV;
+constexpr int SC_DX = SC_DU + CH * DV;
+constexpr int SC_DQK = SC_DX + CH * DV;      // [128][128]: rows 0..63 dQt, 64..127 dKt
+constexpr int SC_DKB = SC_DQK + 2 * CH * DK;
+constexpr int SC_DTB = SC_DKB + CH * DK;     // [64][64]
+constexpr int SC_Z = SC_DTB + CH * CH;
+constexpr int SC_DA = SC_Z + CH * CH;
+constexpr int SC_FLOATS = SC_DA + CH * CH;
+
+// per-workgroup scratch of the prep pass (Y1 = Tb^T Kbar, P1 = scale M^T dO, Y2 = Tb^T P1)
+constexpr int SP_Y1 = 0;
+constexpr int SP_P1 = SP_Y1 + CH * DK;
+constexpr int SP_Y2 = SP_P1 + CH * DV;
+constexpr int SP_FLOATS = SP_Y2 + CH * DV;
+
+struct ChunkDesc {
+  int start;  // first token
+  int len;    // tokens (0: unused slot)
+  int doc;
+  int pad;
+};
+
+__device__ __forceinline__ f32x4 mfma16f(float a, float b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_to_f32(bf16 x) { return (float)x; }
+
+// C (M x N) = sum over K of la(m, k) lb(k, n), then out(m, n, value).
+// fp32 MFMA 16x16x4; operands staged through LDS (stage) in k-tiles of 16.
+// Every thread of the workgroup calls it (tid = its thread index); it
+// synchronises before returning results and before its first staging (so
+// operands may live in LDS buffers that out() overwrites).
+template <int M, int N, int K, class LA, class LB, class OUT>
+__device__ __forceinline__ void wg_gemm(LA la, LB lb, OUT out, float* stage, int tid) {
+  static_assert(M % 16 == 0 && N % 16 == 0 && K % 16 == 0 && M <= 128 && N <= 128, "shape");
+  constexpr int TM = M / 16, TN = N / 16, TILES = TM * TN;
+  static_assert(TILES % 4 == 0, "whole tiles per wave");
+  constexpr int PER = TILES / 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
+  float* sa = stage;                 // [16][M + 1]
+  float* sb = stage + 16 * (M + 1);  // [16][N + 1]
+  f32x4 acc[PER];
+#pragma unroll
+  for (int p = 0; p < PER; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    __syncthreads();
+#pragma unroll 1
+    for (int idx = tid; idx < 16 * M; idx += NT) {
+      const int m = idx >> 4, kk = idx & 15;
+      sa[kk * (M + 1) + m] = la(m, k0 + kk);
+    }
+#pragma unroll 1
+    for (int idx = tid; idx < 16 * N; idx += NT) {
+      const int kk = idx / N, n = idx - kk * N;
+      sb[kk * (N + 1) + n] = lb(k0 + kk, n);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int kk = 4 * s + (l >> 4);
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const int t = w + 4 * p, tm = t / TN, tn = t - tm * TN;
+        acc[p] = mfma16f(sa[kk * (M + 1) + 16 * tm + (l & 15)], sb[kk * (N + 1) + 16 * tn + (l & 15)], acc[p]);
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int t = w + 4 * p, tm = t / TN, tn = t - tm * TN;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out(16 * tm + 4 * (l >> 4) + i, 16 * tn + (l & 15), acc[p][i]);
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// setup: cu_seqlens (exactly n_docs + 1 entries) and the chunk table
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void kda_bwd_setup_kernel(const int32_t* __restrict__ cu,
+                                                             int n_docs, int T, int n_slots,
+                                                             ChunkDesc* __restrict__ table,
+                                                             int* __restrict__ bad,
+                                                             int* __restrict__ status_word) {
+  __shared__ int s_bad;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  if (cu != nullptr) {
+    for (int i = tid; i <= n_docs; i += 1024) {
+      const int val = cu[i];
+      bool b = (i == 0) ? (val != 0) : (val < cu[i - 1] || val > T);
+      if (i == n_docs && val != T) b = true;
+      if (b) atomicOr(&s_bad, 1);
+    }
+  }
+  for (int s = tid; s < n_slots; s += 1024) table[s] = ChunkDesc{0, 0, 0, 0};
+  __syncthreads();
+  if (tid == 0) {
+    *bad = s_bad;
+    if (s_bad) atomicOr(status_word, KDA_DEV_BAD_CU_SEQLENS);
+  }
+  if (s_bad) return;
+  for (int d = tid; d < n_docs; d += 1024) {
+    const int a = cu ? cu[d] : 0, b = cu ? cu[d + 1] : T;
+    const int first = a / CH + d;
+    for (int j = 0; CH * j < b - a; ++j)
+      table[first + j] = ChunkDesc{a + CH * j, min(CH, b - a - CH * j), d, 0};
+  }
+}
+
+// ---------------------------------------------------------------------------
+// prep: per (chunk, head) image and F^T, R
+// ---------------------------------------------------------------------------
+struct PrepSmem {
+  float qh[CH][LD];
+  float kh[CH][LD];
+  float G[CH][LD];
+  float m[CH][LDC];
+  float t[CH][LDC];
+  float beta[CH];
+  union {
+    float kk[CH][LDC];           // until T is built and the image written
+    float stage[STAGE_FLOATS];   // then the products' staging
+  };
+};
+
+// q, k l2-normalised, G = in-chunk cumsum of g (rows past len: qh = kh = 0,
+// g = 0 so G stays at the last row), beta; into LDS and the image
+__device__ __forceinline__ void load_chunk(PrepSmem& sm, float* img, const bf16* __restrict__ q,
+                                           const bf16* __restrict__ k, const float* __restrict__ g,
+                                           const float* __restrict__ beta, int start, int len,
+                                           int H, int h, int tid) {
+  // 4 threads per token, 32 channels each
+  const int t = tid >> 2, c0 = 32 * (tid & 3);
+  float qv[32], kv[32];
+  float sq = 0.f, sk = 0.f;
+  const size_t row = ((size_t)(start + t) * H + h) * DK;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    qv[j] = t < len ? bf16_to_f32(q[row + c0 + j]) : 0.f;
+    kv[j] = t < len ? bf16_to_f32(k[row + c0 + j]) : 0.f;
+    sq += qv[j] * qv[j];
+    sk += kv[j] * kv[j];
+  }
+  sq += __shfl_xor(sq, 1);
+  sq += __shfl_xor(sq, 2);
+  sk += __shfl_xor(sk, 1);
+  sk += __shfl_xor(sk, 2);
+  const float rq = 1.f / sqrtf(sq + L2_EPS), rk = 1.f / sqrtf(sk + L2_EPS);
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    sm.qh[t][c0 + j] = qv[j] * rq;
+    sm.kh[t][c0 + j] = kv[j] * rk;
+    sm.G[t][c0 + j] = t < len ? g[row + c0 + j] : 0.f;
+  }
+  if ((tid & 3) == 0) {
+    img[IMG_RQ + t] = rq;
+    img[IMG_RK + t] = rk;
+    sm.beta[t] = t < len ? beta[(size_t)(start + t) * H + h] : 0.f;
+  }
+  __syncthreads();
+  if (tid < DK) {
+    float acc = 0.f;
+    for (int r = 0; r < CH; ++r) {
+      acc += sm.G[r][tid];
+      sm.G[r][tid] = acc;
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < CH * DK; idx += NT) {
+    const int r = idx >> 7, c = idx & 127;
+    img[IMG_QH + idx] = sm.qh[r][c];
+    img[IMG_KH + idx] = sm.kh[r][c];
+    img[IMG_G + idx] = sm.G[r][c];
+  }
+}
+
+__global__ __launch_bounds__(NT, 1) void kda_bwd_prep_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
+    const float* __restrict__ beta, const bf16* __restrict__ dout, const ChunkDesc* __restrict__ table,
+    const int* __restrict__ bad, int n_items, int H, float* __restrict__ imgs, float* __restrict__ fts,
+    float* __restrict__ rs, float* __restrict__ wscratch) {
+  __shared__ PrepSmem sm;
+  if (*bad) return;
+  float* sp = wscratch + (size_t)blockIdx.x * SP_FLOATS;
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int slot = item / H, h = item - slot * H;
+    const ChunkDesc cd = table[slot];
+    if (cd.len == 0) continue;
+    const int start = cd.start, len = cd.len;
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));  // lane values are recomputed per item, not kept live
+    float* img = imgs + (size_t)item * IMG_FLOATS;
+    __syncthreads();
+    load_chunk(sm, img, q, k, g, beta, start, len, H, h, tid);
+    // Kk (strictly lower) and M (lower incl.), exp(G_r - G_i) <= 1 per channel
+    for (int idx = tid; idx < CH * CH; idx += NT) {
+      const int r = idx >> 6, i = idx & 63;
+      float a = 0.f, mm = 0.f;
+      if (i <= r) {
+        for (int c = 0; c < DK; ++c) {
+          const float e = __expf(sm.G[r][c] - sm.G[i][c]);
+          const float ki = sm.kh[i][c] * e;
+          a = fmaf(sm.kh[r][c], ki, a);
+          mm = fmaf(sm.qh[r][c], ki, mm);
+        }
+      }
+      sm.kk[r][i] = i < r ? a : 0.f;
+      sm.m[r][i] = mm;
+    }
+    __syncthreads();
+    // T = (I + Diag(beta) Kk)^-1 by forward substitution, one row at a time
+    if (tid < CH) sm.t[0][tid] = tid == 0 ? 1.f : 0.f;
+    for (int r = 1; r < CH; ++r) {
+      __syncthreads();
+      if (tid < CH) {
+        const int i = tid;
+        float acc = 0.f;
+        if (i < r) {
+          for (int m = i; m < r; ++m) acc = fmaf(sm.kk[r][m], sm.t[m][i], acc);
+          acc *= -sm.beta[r];
+        }
+        sm.t[r][i] = i < r ? acc : (i == r ? 1.f : 0.f);
+      }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < CH * CH; idx += NT) {
+      const int r = idx >> 6, i = idx & 63;
+      img[IMG_T + idx] = sm.t[r][i];
+      img[IMG_KK + idx] = sm.kk[r][i];
+      img[IMG_M + idx] = sm.m[r][i];
+    }
+    const float* Gl = sm.G[CH - 1];
+    const size_t drow0 = (size_t)start * H + h;
+    auto dO = [&](int r, int v) -> float {
+      return r < len ? bf16_to_f32(dout[(drow0 + (size_t)r * H) * DV + v]) : 0.f;
+    };
+    // Y1 = Tb^T Kbar  [t][c]
+    wg_gemm<CH, DK, CH>(
+        [&](int t, int r) { return sm.t[r][t] * sm.beta[t]; },
+        [&](int r, int c) { return sm.kh[r][c] * __expf(Gl[c] - sm.G[r][c]); },
+        [&](int t, int c, float x) { sp[SP_Y1 + t * DK + c] = x; }, sm.stage, tid);
+    // P1 = scale M^T dO  [t][v]
+    wg_gemm<CH, DV, CH>(
+        [&](int t, int r) { return SCALE * sm.m[r][t]; }, [&](int r, int v) { return dO(r, v); },
+        [&](int t, int v, float x) { sp[SP_P1 + t * DV + v] = x; }, sm.stage, tid);
+    // Y2 = Tb^T P1
+    wg_gemm<CH, DV, CH>(
+        [&](int t, int r) { return sm.t[r][t] * sm.beta[t]; },
+        [&](int r, int v) { return sp[SP_P1 + r * DV + v]; },
+        [&](int t, int v, float x) { sp[SP_Y2 + t * DV + v] = x; }, sm.stage, tid);
+    // F^T = D - Kt^T Y1  [c][c']
+    float* ft = fts + (size_t)item * DK * DK;
+    wg_gemm<DK, DK, CH>(
+        [&](int c, int t) { return sm.kh[t][c] * __expf(sm.G[t][c]); },
+        [&](int t, int c2) { return sp[SP_Y1 + t * DK + c2]; },
+        [&](int c, int c2, float x) { ft[c * DK + c2] = (c == c2 ? __expf(Gl[c]) : 0.f) - x; },
+        sm.stage, tid);
+    // R = scale Qt^T dO - Kt^T Y2  [c][v]  (one product over the stacked rows)
+    float* rr = rs + (size_t)item * DK * DV;
+    wg_gemm<DK, DV, 2 * CH>(
+        [&](int c, int t) {
+          return t < CH ? SCALE * sm.qh[t][c] * __expf(sm.G[t][c])
+                        : -sm.kh[t - CH][c] * __expf(sm.G[t - CH][c]);
+        },
+        [&](int t, int v) { return t < CH ? dO(t, v) : sp[SP_Y2 + (t - CH) * DV + v]; },
+        [&](int c, int v, float x) { rr[c * DV + v] = x; }, sm.stage, tid);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// chain: per (document, head), last chunk first: dS <- F^T dS + R
+// ---------------------------------------------------------------------------
+struct ChainSmem {
+  float ds[DK][LD];
+  float stage[STAGE_FLOATS];
+};
+
+__global__ __launch_bounds__(NT, 1) void kda_bwd_chain_kernel(
+    const int32_t* __restrict__ cu, int T, int H, const int* __restrict__ bad,
+    const float* __restrict__ fts, const float* __restrict__ rs, const float* __restrict__ dht,
+    float* __restrict__ dstates, float* __restrict__ dh0) {
+  __shared__ ChainSmem sm;
+  if (*bad) return;
+  const int tid = threadIdx.x;
+  const int d = blockIdx.x / H, h = blockIdx.x - d * H;
+  const int a = cu ? cu[d] : 0, b = cu ? cu[d + 1] : T;
+  const int first = a / CH + d;
+  const int n = (b - a + CH - 1) / CH;
+  for (int idx = tid; idx < DK * DV; idx += NT) {
+    const int c = idx >> 7, v = idx & 127;
+    sm.ds[c][v] = dht ? dht[((size_t)d * H + h) * DK * DV + idx] : 0.f;
+  }
+  for (int j = n - 1; j >= 0; --j) {
+    const size_t item = (size_t)(first + j) * H + h;
+    __syncthreads();
+    float* dst = dstates + item * DK * DV;
+    for (int idx = tid; idx < DK * DV; idx += NT) dst[idx] = sm.ds[idx >> 7][idx & 127];
+    const float* ft = fts + item * DK * DK;
+    const float* rr = rs + item * DK * DV;
+    wg_gemm<DK, DV, DK>([&](int c, int c2) { return ft[c * DK + c2]; },
+                        [&](int c2, int v) { return sm.ds[c2][v]; },
+                        [&](int c, int v, float x) { sm.ds[c][v] = x + rr[c * DV + v]; }, sm.stage, tid);
+  }
+  __syncthreads();
+  if (dh0 != nullptr)
+    for (int idx = tid; idx < DK * DV; idx += NT)
+      dh0[((size_t)d * H + h) * DK * DV + idx] = sm.ds[idx >> 7][idx & 127];
+}
+
+// ---------------------------------------------------------------------------
+// gradients: per (chunk, head), in parallel
+// ---------------------------------------------------------------------------
+struct GradSmem {
+  float qh[CH][LD];
+  float kh[CH][LD];
+  float G[CH][LD];
+  float dm[CH][LDC];     // dM (lower incl.); later dG
+  float dkk[CH][LDC];    // dKk (strictly lower)
+  float beta[CH];
+  float dbeta[CH];
+  float dD[DK];
+  float gl[DK];          // G of the last row
+  float kbsum[2][DK];
+  float stage[STAGE_FLOATS];
+};
+
+__global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
+    const bf16* __restrict__ v, const float* __restrict__ beta, const bf16* __restrict__ dout,
+    const ChunkDesc* __restrict__ table, const int* __restrict__ bad, int n_items, int H,
+    const float* __restrict__ imgs, const float* __restrict__ states,
+    const float* __restrict__ dstates, float* __restrict__ wscratch, float* __restrict__ dq,
+    float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dg,
+    float* __restrict__ dbeta) {
+  __shared__ GradSmem sm;
+  if (*bad) return;
+  float* sc = wscratch + (size_t)blockIdx.x * SC_FLOATS;
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int slot = item / H, h = item - slot * H;
+    const ChunkDesc cd = table[slot];
+    if (cd.len == 0) continue;
+    const int start = cd.start, len = cd.len;
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));  // lane values are recomputed per item, not kept live
+    const float* img = imgs + (size_t)item * IMG_FLOATS;
+    const float* S0 = states + (size_t)item * DK * DV;
+    const float* dSc = dstates + (size_t)item * DK * DV;
+    const float* T = img + IMG_T;
+    const float* Kk = img + IMG_KK;
+    const float* Mm = img + IMG_M;
+    __syncthreads();
+    for (int idx = tid; idx < CH * DK; idx += NT) {
+      const int r = idx >> 7, c = idx & 127;
+      sm.qh[r][c] = img[IMG_QH + idx];
+      sm.kh[r][c] = img[IMG_KH + idx];
+      sm.G[r][c] = img[IMG_G + idx];
+    }
+    if (tid < CH) {
+      sm.beta[tid] = tid < len ? beta[(size_t)(start + tid) * H + h] : 0.f;
+    }
+    if (tid < DK) sm.gl[tid] = img[IMG_G + (CH - 1) * DK + tid];
+    __syncthreads();
+    const size_t row0 = (size_t)start * H + h;
+    auto dO = [&](int r, int c) -> float {
+      return r < len ? bf16_to_f32(dout[(row0 + (size_t)r * H) * DV + c]) : 0.f;
+    };
+    auto Vv = [&](int r, int c) -> float {
+      return r < len ? bf16_to_f32(v[(row0 + (size_t)r * H) * DV + c]) : 0.f;
+    };
+    // X = V - Kt S0
+    wg_gemm<CH, DV, DK>(
+        [&](int t, int c) { return sm.kh[t][c] * __expf(sm.G[t][c]); },
+        [&](int c, int vv) { return S0[c * DV + vv]; },
+        [&](int t, int vv, float x) { sc[SC_X + t * DV + vv] = Vv(t, vv) - x; }, sm.stage, tid);
+    // U = Tb X
+    wg_gemm<CH, DV, CH>(
+        [&](int t, int i) { return T[t * CH + i] * sm.beta[i]; },
+        [&](int i, int vv) { return sc[SC_X + i * DV + vv]; },
+        [&](int t, int vv, float x) { sc[SC_U + t * DV + vv] = x; }, sm.stage, tid);
+    // dU = scale M^T dO + Kbar dSc  (stacked k: 64 rows of M^T, then 128 channels)
+    wg_gemm<CH, DV, CH + DK>(
+        [&](int t, int kk) {
+          return kk < CH ? SCALE * Mm[kk * CH + t]
+                         : sm.kh[t][kk - CH] * __expf(sm.gl[kk - CH] - sm.G[t][kk - CH]);
+        },
+        [&](int kk, int vv) { return kk < CH ? dO(kk, vv) : dSc[(kk - CH) * DV + vv]; },
+        [&](int t, int vv, float x) { sc[SC_DU + t * DV + vv] = x; }, sm.stage, tid);
+    // dX = Tb^T dU  (= dV)
+    wg_gemm<CH, DV, CH>(
+        [&](int t, int r) { return T[r * CH + t] * sm.beta[t]; },
+        [&](int r, int vv) { return sc[SC_DU + r * DV + vv]; },
+        [&](int t, int vv, float x) {
+          sc[SC_DX + t * DV + vv] = x;
+          if (t < len) dv[(row0 + (size_t)t * H) * DV + vv] = x;
+        },
+        sm.stage, tid);
+    // rows 0..63: dQt = scale dO S0^T; rows 64..127: dKt = -dX S0^T
+    wg_gemm<2 * CH, DK, DV>(
+        [&](int t, int vv) { return t < CH ? SCALE * dO(t, vv) : -sc[SC_DX + (t - CH) * DV + vv]; },
+        [&](int vv, int c) { return S0[c * DV + vv]; },
+        [&](int t, int c, float x) { sc[SC_DQK + t * DK + c] = x; }, sm.stage, tid);
+    // dKbar = U dSc^T
+    wg_gemm<CH, DK, DV>(
+        [&](int t, int vv) { return sc[SC_U + t * DV + vv]; },
+        [&](int vv, int c) { return dSc[c * DV + vv]; },
+        [&](int t, int c, float x) { sc[SC_DKB + t * DK + c] = x; }, sm.stage, tid);
+    // dM = scale tril(dO U^T)
+    wg_gemm<CH, CH, DV>(
+        [&](int r, int vv) { return SCALE * dO(r, vv); },
+        [&](int vv, int i) { return sc[SC_U + i * DV + vv]; },
+        [&](int r, int i, float x) { sm.dm[r][i] = i <= r ? x : 0.f; }, sm.stage, tid);
+    // dTb = tril(dU X^T)
+    wg_gemm<CH, CH, DV>(
+        [&](int r, int vv) { return sc[SC_DU + r * DV + vv]; },
+        [&](int vv, int i) { return sc[SC_X + i * DV + vv]; },
+        [&](int r, int i, float x) { sc[SC_DTB + r * CH + i] = i <= r ? x : 0.f; }, sm.stage, tid);
+    // dD[c] = sum_v dSc[c][v] S0[c][v]; dbeta_i = sum_r dTb_ri T_ri
+    {
+      const int c = tid >> 1, half = tid & 1;
+      float acc = 0.f;
+      for (int vv = 64 * half; vv < 64 * half + 64; ++vv) acc = fmaf(dSc[c * DV + vv], S0[c * DV + vv], acc);
+      acc += __shfl_xor(acc, 1);
+      if (half == 0) sm.dD[c] = acc;
+      if (tid < CH) {
+        float db = 0.f;
+        for (int r = tid; r < CH; ++r) db = fmaf(sc[SC_DTB + r * CH + tid], T[r * CH + tid], db);
+        sm.dbeta[tid] = db;
+      }
+    }
+    // Z = (dTb Diag(beta)) T^T;  dA = -T^T Z (strictly lower)
+    wg_gemm<CH, CH, CH>(
+        [&](int r, int m) { return sc[SC_DTB + r * CH + m] * sm.beta[m]; },
+        [&](int m, int i) { return T[i * CH + m]; },
+        [&](int r, int i, float x) { sc[SC_Z + r * CH + i] = x; }, sm.stage, tid);
+    wg_gemm<CH, CH, CH>(
+        [&](int r, int m) { return -T[m * CH + r]; },
+        [&](int m, int i) { return sc[SC_Z + m * CH + i]; },
+        [&](int r, int i, float x) { sm.dkk[r][i] = i < r ? x : 0.f; }, sm.stage, tid);
+    // dbeta_r += sum_i dA_ri Kk_ri; dKk = Diag(beta) dA
+    if (tid < CH) {
+      const int r = tid;
+      float db = 0.f;
+      for (int i = 0; i < r; ++i) db = fmaf(sm.dkk[r][i], Kk[r * CH + i], db);
+      sm.dbeta[r] += db;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < CH * CH; idx += NT) {
+      const int r = idx >> 6, i = idx & 63;
+      sm.dkk[r][i] *= sm.beta[r];
+    }
+    if (tid < CH && tid < len) dbeta[row0 + (size_t)tid * H] = sm.dbeta[tid];
+    __syncthreads();
+    // bilinear forms and the decayed tiles: thread = channel c, rows r = half + 2 j.
+    // dqh, dkh and dG of (r, c) replace dQt, dKt and dKbar of (r, c) in the
+    // scratch (the same thread reads them first)
+    {
+      const int c = tid & 127, half = tid >> 7;
+      const float gl = sm.gl[c];
+      float kbsum = 0.f;  // sum over this thread's rows of dKbar Kbar
+#pragma unroll 1
+      for (int j = 0; j < 32; ++j) {
+        const int r = half + 2 * j;
+        const float Gr = sm.G[r][c];
+        float sa1 = 0.f, sa2 = 0.f, sb = 0.f;
+        const float qr = sm.qh[r][c], kr = sm.kh[r][c];
+        // row role: i <= r
+        for (int i = 0; i <= r; ++i) {
+          const float ki = sm.kh[i][c] * __expf(Gr - sm.G[i][c]);
+          sa1 = fmaf(sm.dm[r][i], ki, sa1);
+          sa2 = fmaf(sm.dkk[r][i], ki, sa2);
+        }
+        // column role: rows rr >= r
+        for (int rr = r; rr < CH; ++rr) {
+          const float e = __expf(sm.G[rr][c] - Gr);
+          sb = fmaf(fmaf(sm.dm[rr][r], sm.qh[rr][c], sm.dkk[rr][r] * sm.kh[rr][c]), e, sb);
+        }
+        const float eg = __expf(Gr), eb = __expf(gl - Gr);
+        float* pq = sc + SC_DQK + r * DK + c;
+        float* pk = sc + SC_DQK + (CH + r) * DK + c;
+        float* pb = sc + SC_DKB + r * DK + c;
+        const float dqt = *pq, dkt = *pk, dkb = *pb;
+        kbsum = fmaf(dkb, kr * eb, kbsum);
+        *pq = sa1 + dqt * eg;
+        *pk = sa2 + sb + dkt * eg + dkb * eb;
+        *pb = qr * sa1 + kr * sa2 - kr * sb + dqt * qr * eg + dkt * kr * eg - dkb * kr * eb;
+      }
+      sm.kbsum[half][c] = kbsum;
+    }
+    __syncthreads();
+    // dg = reverse cumsum of dG within the chunk; the last row gains
+    // sum_r dKbar_r Kbar_r + dD D (G_last is the cumsum up to the last token)
+    if (tid < DK) {
+      const int c = tid;
+      float acc = sm.kbsum[0][c] + sm.kbsum[1][c] + sm.dD[c] * __expf(sm.gl[c]);
+      for (int r = CH - 1; r >= 0; --r) {
+        acc += sc[SC_DKB + r * DK + c];
+        if (r < len) dg[(row0 + (size_t)r * H) * DK + c] = acc;
+      }
+    }
+    // l2 norms: dq = rq (dqh - qh (qh . dqh)), dk likewise; 4 threads per token
+    {
+      const int t = tid >> 2, c0 = 32 * (tid & 3);
+#pragma unroll 1
+      for (int which = 0; which < 2; ++which) {
+        const float* dxh = sc + SC_DQK + (which * CH + t) * DK;
+        float sdot = 0.f;
+        for (int j = 0; j < 32; ++j) {
+          const float xh = which == 0 ? sm.qh[t][c0 + j] : sm.kh[t][c0 + j];
+          sdot = fmaf(xh, dxh[c0 + j], sdot);
+        }
+        sdot += __shfl_xor(sdot, 1);
+        sdot += __shfl_xor(sdot, 2);
+        if (t < len) {
+          const float rn = img[(which == 0 ? IMG_RQ : IMG_RK) + t];
+          float* dst = (which == 0 ? dq : dk) + (row0 + (size_t)t * H) * DK;
+          for (int j = 0; j < 32; ++j) {
+            const float xh = which == 0 ? sm.qh[t][c0 + j] : sm.kh[t][c0 + j];
+            dst[c0 + j] = rn * (dxh[c0 + j] - xh * sdot);
+          }
+        }
+      }
+    }
+  }
+}
+
+__global__ void kda_bwd_nan_kernel(const int* __restrict__ bad, float* dq, float* dk, float* dv,
+                                   float* dg, float* dbeta, float* dh0, size_t n_tok_ch,
+                                   size_t n_tok, size_t n_state) {
+  if (!*bad) return;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  const float nan = __builtin_nanf("");
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_tok_ch; i += stride) {
+    dq[i] = nan;
+    dk[i] = nan;
+    dv[i] = nan;
+    dg[i] = nan;
+  }
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_tok; i += stride) dbeta[i] = nan;
+  if (dh0 != nullptr)
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_state; i += stride) dh0[i] = nan;
+}
+
+bool aligned(const void* p, uintptr_t al) { return (reinterpret_cast<uintptr_t>(p) & (al - 1)) == 0; }
+
+}  // namespace
+
+extern "C" int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
+                             const float* beta, const int32_t* cu_seqlens, int32_t n_docs,
+                             int64_t T, int32_t H, int32_t chunk, float gate_bound,
+                             const float* initial_state, const void* d_out,
+                             const float* d_final_state, float* dq, float* dk, float* dv,
+                             float* dg, float* dbeta, float* d_initial_state, hipStream_t stream) {
+  using kda_host::fail;
+  fail(KDA_OK, "");
+  if (T < 0) return fail(KDA_ERR_BAD_SHAPE, "T must be >= 0");
+  if (T > INT32_MAX) return fail(KDA_ERR_BAD_SHAPE, "T must be <= INT32_MAX");
+  if (H < 1) return fail(KDA_ERR_BAD_SHAPE, "H must be >= 1");
+  if (H > KDA_MAX_HEADS) return fail(KDA_ERR_BAD_SHAPE, "H must be <= KDA_MAX_HEADS");
+  if (n_docs < 1) return fail(KDA_ERR_BAD_SHAPE, "n_docs must be >= 1");
+  if ((int64_t)n_docs * H > INT32_MAX) return fail(KDA_ERR_BAD_SHAPE, "n_docs * H must be <= INT32_MAX");
+  if (!cu_seqlens && n_docs != 1) return fail(KDA_ERR_BAD_SHAPE, "n_docs must be 1 when cu_seqlens is NULL");
+  if (T == 0 && !d_initial_state) return KDA_OK;
+  if (T > 0) {
+    if (!q) return fail(KDA_ERR_NULL_PTR, "q is NULL");
+    if (!k) return fail(KDA_ERR_NULL_PTR, "k is NULL");
+    if (!v) return fail(KDA_ERR_NULL_PTR, "v is NULL");
+    if (!g) return fail(KDA_ERR_NULL_PTR, "g is NULL");
+    if (!beta) return fail(KDA_ERR_NULL_PTR, "beta is NULL");
+    if (!d_out) return fail(KDA_ERR_NULL_PTR, "d_out is NULL");
+    if (!dq || !dk || !dv || !dg || !dbeta) return fail(KDA_ERR_NULL_PTR, "a gradient output is NULL");
+  }
+  if (chunk != 64) return fail(KDA_ERR_UNSUPPORTED, "chunk must be 64");
+  if (!(gate_bound >= -5.5f && gate_bound < 0.f))
+    return fail(KDA_ERR_UNSUPPORTED, "gate_bound must be finite and in [-5.5, 0)");
+  if (T > 0) {
+    if (!aligned(q, 16)) return fail(KDA_ERR_ALIGN, "q is not 16-byte aligned");
+    if (!aligned(k, 16)) return fail(KDA_ERR_ALIGN, "k is not 16-byte aligned");
+    if (!aligned(v, 16)) return fail(KDA_ERR_ALIGN, "v is not 16-byte aligned");
+    if (!aligned(g, 16)) return fail(KDA_ERR_ALIGN, "g is not 16-byte aligned");
+    if (!aligned(beta, 4)) return fail(KDA_ERR_ALIGN, "beta is not 4-byte aligned");
+    if (!aligned(d_out, 16)) return fail(KDA_ERR_ALIGN, "d_out is not 16-byte aligned");
+    if (!aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(dg, 16) || !aligned(dbeta, 4))
+      return fail(KDA_ERR_ALIGN, "a gradient output is not aligned");
+  }
+  if (cu_seqlens && !aligned(cu_seqlens, 4)) return fail(KDA_ERR_ALIGN, "cu_seqlens is not 4-byte aligned");
+  if (initial_state && !aligned(initial_state, 16)) return fail(KDA_ERR_ALIGN, "initial_state is not 16-byte aligned");
+  if (d_final_state && !aligned(d_final_state, 16)) return fail(KDA_ERR_ALIGN, "d_final_state is not 16-byte aligned");
+  if (d_initial_state && !aligned(d_initial_state, 16)) return fail(KDA_ERR_ALIGN, "d_initial_state is not 16-byte aligned");
+
+  int num_cu = 0;
+  int* status_word = nullptr;
+  if (kda_host::device(&num_cu, &status_word) != 0)
+    return fail(KDA_ERR_HIP, "device query (CU count, status word) failed");
+
+  // workspace: bad | table | states | dstates | images | F^T | R | prep scratch | grads scratch | o
+  const size_t n_slots = (size_t)T / CH + (size_t)n_docs + 1;
+  const size_t items = n_slots * (size_t)H;
+  const int grid = num_cu;
+  auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+  size_t off = 256;
+  const size_t off_table = off; off = al(off + sizeof(ChunkDesc) * n_slots);
+  const size_t off_states = off; off = al(off + sizeof(float) * items * DK * DV);
+  const size_t off_dstates = off; off = al(off + sizeof(float) * items * DK * DV);
+  const size_t off_img = off; off = al(off + sizeof(float) * items * IMG_FLOATS);
+  const size_t off_ft = off; off = al(off + sizeof(float) * items * DK * DK);
+  const size_t off_r = off; off = al(off + sizeof(float) * items * DK * DV);
+  const size_t off_sp = off; off = al(off + sizeof(float) * (size_t)grid * SP_FLOATS);
+  const size_t off_sc = off; off = al(off + sizeof(float) * (size_t)grid * SC_FLOATS);
+  const size_t off_o = off; off = al(off + 2 * (size_t)T * H * DV);
+  uint8_t* ws = nullptr;
+  if (hipMallocAsync(reinterpret_cast<void**>(&ws), off, stream) != hipSuccess || !ws)
+    return fail(KDA_ERR_ALLOC, "hipMallocAsync of the backward workspace failed");
+  int* bad = reinterpret_cast<int*>(ws);
+  ChunkDesc* table = reinterpret_cast<ChunkDesc*>(ws + off_table);
+  float* states = reinterpret_cast<float*>(ws + off_states);
+  float* dstates = reinterpret_cast<float*>(ws + off_dstates);
+  float* imgs = reinterpret_cast<float*>(ws + off_img);
+  float* fts = reinterpret_cast<float*>(ws + off_ft);
+  float* rs = reinterpret_cast<float*>(ws + off_r);
+  float* sp = reinterpret_cast<float*>(ws + off_sp);
+  float* sc = reinterpret_cast<float*>(ws + off_sc);
+  void* o_scratch = ws + off_o;
+
+  int rc = KDA_OK;
+  hipError_t e = hipSuccess;
+  hipLaunchKernelGGL(kda_bwd_setup_kernel, dim3(1), dim3(1024), 0, stream, cu_seqlens, (int)n_docs,
+                     (int)T, (int)n_slots, table, bad, status_word);
+  e = hipGetLastError();
+  if (e == hipSuccess && T > 0) {
+    rc = kda_host::forward_with_chunk_states(q, k, v, g, beta, cu_seqlens, n_docs, T, H,
+                                             gate_bound, initial_state, o_scratch, states, stream);
+    if (rc == KDA_OK && T > 0) {
+      hipLaunchKernelGGL(kda_bwd_prep_kernel, dim3(grid), dim3(NT), 0, stream,
+                         static_cast<const bf16*>(q), static_cast<const bf16*>(k), g, beta,
+                         static_cast<const bf16*>(d_out), table, bad, (int)items, (int)H, imgs, fts,
+                         rs, sp);
+      e = hipGetLastError();
+    }
+  }
+  if (e == hipSuccess && rc == KDA_OK) {
+    hipLaunchKernelGGL(kda_bwd_chain_kernel, dim3(n_docs * H), dim3(NT), 0, stream, cu_seqlens,
+                       (int)T, (int)H, bad, fts, rs, d_final_state, dstates, d_initial_state);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess && rc == KDA_OK && T > 0) {
+    hipLaunchKernelGGL(kda_bwd_grads_kernel, dim3(grid), dim3(NT), 0, stream,
+                       static_cast<const bf16*>(v), beta, static_cast<const bf16*>(d_out), table,
+                       bad, (int)items, (int)H, imgs, states, dstates, sc, dq, dk, dv, dg, dbeta);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess && rc == KDA_OK) {
+    hipLaunchKernelGGL(kda_bwd_nan_kernel, dim3(grid), dim3(NT), 0, stream, bad, dq, dk, dv, dg,
+                       dbeta, d_initial_state, (size_t)T * H * DK, (size_t)T * H,
+                       (size_t)n_docs * H * DK * DV);
+    e = hipGetLastError();
+  }
+  const hipError_t ef = hipFreeAsync(ws, stream);
+  if (rc != KDA_OK) return rc;
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  if (ef != hipSuccess) return fail(KDA_ERR_HIP, "hipFreeAsync of the backward workspace failed");
+  return KDA_OK;
+}

@@ -75,10 +75,11 @@ namespace {
 // state through) and doc_ids[i] receives the index of docs[i] in cu.
 __global__ __launch_bounds__(SCHED_THREADS) void kda_schedule_kernel(
     const int32_t* __restrict__ cu, int T, int H, int n_cu, int cap_chunks, int policy,
-    int n_exact, const float* h0, float* ht, WorkHeader* __restrict__ hdr,
+    int n_exact, const float* h0, float* ht, float* chunk_states, WorkHeader* __restrict__ hdr,
     int2* __restrict__ docs, int* __restrict__ doc_ids, int2* __restrict__ split,
     int2* __restrict__ pre_chunks) {
   if (threadIdx.x == 0) {
+    hdr->chunk_states = chunk_states;
     hdr->n_state_docs = n_exact >= 0 ? n_exact : 0;
     hdr->h0 = h0;
     hdr->ht = ht;
@@ -384,6 +385,7 @@ struct Call {
   const float* h0;
   float* ht;
   hipStream_t stream;
+  float* chunk_states = nullptr;  // S at every chunk start (the backward's forward pass)
 };
 
 // checks shared by both entry points for the token tensors (T > 0)
@@ -443,8 +445,8 @@ int launch(const Call& c) {
   uint8_t* images = ws + off_img;
 
   hipLaunchKernelGGL(kda_schedule_kernel, dim3(1), dim3(SCHED_THREADS), 0, c.stream, c.cu,
-                     (int)T, H, di->num_cu, (int)cap_chunks, policy, c.n_exact, c.h0, c.ht, hdr,
-                     docs, doc_ids, split, pre_chunks);
+                     (int)T, H, di->num_cu, (int)cap_chunks, policy, c.n_exact, c.h0, c.ht,
+                     c.chunk_states, hdr, docs, doc_ids, split, pre_chunks);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && cap_chunks > 0) {
     hipLaunchKernelGGL(kda_pre_kernel, dim3(2 * di->num_cu), dim3(NTHR), 0, c.stream,
@@ -453,7 +455,7 @@ int launch(const Call& c) {
     e = hipGetLastError();
   }
   if (e == hipSuccess) {
-    if (c.h0 || c.ht) {
+    if (c.h0 || c.ht || c.chunk_states) {
       e = kda_state_tu::launch_main_state(dim3(di->num_cu), c.stream, c.q, c.k, c.v, c.g, c.beta,
                                           c.out, hdr, docs, split, images, T, H, c.gate_bound);
     } else {
@@ -475,6 +477,17 @@ int launch(const Call& c) {
 // host helpers shared with the other translation units of the library
 namespace kda_host {
 int fail(int code, const std::string& msg) { return ::fail(code, msg); }
+// The stateful forward with S stored at every chunk start (see
+// WorkHeader::chunk_states): the first pass of the backward.  Arguments were
+// checked by the caller.
+int forward_with_chunk_states(const void* q, const void* k, const void* v, const float* g,
+                              const float* beta, const int32_t* cu, int32_t n_docs, int64_t T,
+                              int32_t H, float gate_bound, const float* h0, void* out,
+                              float* chunk_states, hipStream_t stream) {
+  Call c{q, k, v, g, beta, cu, T, H, gate_bound, out, n_docs, h0, nullptr, stream};
+  c.chunk_states = chunk_states;
+  return launch(c);
+}
 int device(int* num_cu, int** status_word) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;

@@ -209,6 +209,10 @@ struct WorkHeader {
   float* ht;
   const int* doc_ids;
   int* status_word;  // the sticky device status word the main kernel reports to
+  // with states: when not null, S at the start of every chunk is stored here,
+  // fp32 [slot][H][K][V], slot = first token / 64 + document index + chunk
+  // index in the document (distinct for all chunks of all documents)
+  float* chunk_states;
 };
 
 // Sticky kda_device_flags of this device.  Every translation unit that
@@ -1156,6 +1160,20 @@ __global__ __launch_bounds__(NTHR, 1) void kda_chunk_fwd_kernel(
           for (int i = 0; i < 16; ++i) S[kt][i] = 0.f;
       }
     };
+    // S at the start of the chunk that begins at token c0 (states only)
+    auto save_chunk = [&](const f32x16 (&S)[4], int64_t c0) {
+      if constexpr (kState) {
+        float* cs = hdr->chunk_states;
+        if (cs != nullptr) {
+          const int u = __builtin_amdgcn_readfirstlane(sm.unit);
+          const int d = u / H;
+          const int2 dd = docs[d];
+          const int64_t first = dd.x < 0 ? (int64_t)split[-dd.x - 1].x : (int64_t)dd.x;
+          const int64_t slot = first / CH + hdr->doc_ids[d] + (c0 - first) / CH;
+          store_state(S, cs + ((size_t)slot * H + (u - d * H)) * (DK * DV), ln);
+        }
+      }
+    };
     auto state_out = [&](const f32x16 (&S)[4]) {
       if constexpr (kState) {
         // the unit's indices again, from LDS (nothing kept live across the chain)
@@ -1179,6 +1197,7 @@ __global__ __launch_bounds__(NTHR, 1) void kda_chunk_fwd_kernel(
       state_in(S);
       for (int64_t c0 = bos; c0 < eos; c0 += CH) {
         const int n = (int)min<int64_t>(CH, eos - c0);
+        save_chunk(S, c0);
         image_to_lds(sm, im, tid);
         __syncthreads();  // the image is in LDS
         img += img_stride;
@@ -1217,6 +1236,7 @@ __global__ __launch_bounds__(NTHR, 1) void kda_chunk_fwd_kernel(
         const int64_t c1 = c0 + CH;
         const int n1 = (int)min<int64_t>(CH, eos - c1);
         const RawSrc src = raw_src(q, k, g, beta, c1, n1, H, h);
+        save_chunk(S, c0);
         prepare_chunk(sm, LdsSink{&sm}, cur, n, gate_bound, ln,
                       [&](int part) { load_raw_part(cur, src, of, part); });
         chain_chunk(sm, S, vcur, n, c0, H, h, out, ln, of, [&](int stage) {

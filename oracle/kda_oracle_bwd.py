@@ -122,3 +122,63 @@ def kda_backward(q, k, v, g, beta, do, cu_seqlens, initial_state=None, d_final_s
             out[name][a:b] = r[name]
         out["dh0"][d] = r["dh0"]
     return out
+
+
+# ---------------------------------------------------------------------------
+# task-parallel driver: independent (document, head-range) tasks on a fork
+# pool, like kda_oracle.kda_tasks
+# ---------------------------------------------------------------------------
+
+_SHARED: dict = {}
+
+
+def _worker_init():
+    import torch
+    torch.set_num_threads(1)
+
+
+def _run_task(task):
+    a, b, h0, h1, d = task
+    s = _SHARED
+    init = s["initial_state"]
+    dfin = s["d_final_state"]
+    r = kda_document_backward(s["q"][a:b, h0:h1], s["k"][a:b, h0:h1], s["v"][a:b, h0:h1],
+                              s["g"][a:b, h0:h1], s["beta"][a:b, h0:h1], s["do"][a:b, h0:h1],
+                              None if init is None else init[d, h0:h1],
+                              None if dfin is None else dfin[d, h0:h1])
+    return task, r
+
+
+def kda_backward_tasks(q, k, v, g, beta, do, tasks, initial_state=None, d_final_state=None,
+                       workers: int | None = None):
+    """Yield ``(task, grads)`` for tasks ``(a, b, h0, h1, d)``: tokens [a, b) of
+    document d, heads [h0, h1).  Longest first, on ``workers`` processes."""
+    import multiprocessing as mp
+    import os
+    from concurrent.futures import ProcessPoolExecutor
+    from .kda_oracle import default_workers
+    tasks = sorted(tasks, key=lambda t: -(t[1] - t[0]) * (t[3] - t[2]))
+    workers = workers or default_workers()
+    _SHARED.update(q=q, k=k, v=v, g=g, beta=beta, do=do, initial_state=initial_state,
+                   d_final_state=d_final_state)
+    try:
+        if workers <= 1 or len(tasks) <= 1:
+            for t in tasks:
+                yield _run_task(t)
+            return
+        keep = {x: os.environ.get(x) for x in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS")}
+        os.environ["OMP_NUM_THREADS"] = "1"
+        os.environ["OPENBLAS_NUM_THREADS"] = "1"
+        try:
+            with ProcessPoolExecutor(workers, mp_context=mp.get_context("fork"),
+                                     initializer=_worker_init) as ex:
+                for r in ex.map(_run_task, tasks, chunksize=1):
+                    yield r
+        finally:
+            for key, val in keep.items():
+                if val is None:
+                    os.environ.pop(key, None)
+                else:
+                    os.environ[key] = val
+    finally:
+        _SHARED.clear()

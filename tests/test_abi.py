@@ -19,8 +19,8 @@ def _declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert _declared_functions() == ["kda_chunk_fwd", "kda_chunk_fwd_state", "kda_device_status",
-                                     "kda_last_error", "kda_recurrent_fwd"]
+    assert _declared_functions() == ["kda_chunk_bwd", "kda_chunk_fwd", "kda_chunk_fwd_state",
+                                     "kda_device_status", "kda_last_error", "kda_recurrent_fwd"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -161,6 +161,46 @@ def test_recurrent_argument_validation(kw, code, msg):
     rc, err = _call_rec(**kw)
     assert rc == code
     assert msg in err
+
+
+def _call_bwd(**kw):
+    args = dict(q=P, k=P, v=P, g=P, beta=P, cu=None, n_docs=1, T=64, H=2, chunk=64,
+                gate_bound=-5.0, h0=None, do=P, dht=None, dq=P, dk=P, dv=P, dg=P, db=P,
+                dh0=None, stream=None)
+    args.update(kw)
+    rc = kda.kda_chunk_bwd(*(args[x] for x in ("q", "k", "v", "g", "beta", "cu", "n_docs", "T",
+                                               "H", "chunk", "gate_bound", "h0", "do", "dht",
+                                               "dq", "dk", "dv", "dg", "db", "dh0", "stream")))
+    return rc, kda.kda_last_error()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(T=-1), kda.KDA_ERR_BAD_SHAPE, "T must be >= 0"),
+    (dict(n_docs=0), kda.KDA_ERR_BAD_SHAPE, "n_docs must be >= 1"),
+    (dict(n_docs=3), kda.KDA_ERR_BAD_SHAPE, "n_docs must be 1 when cu_seqlens is NULL"),
+    (dict(do=None), kda.KDA_ERR_NULL_PTR, "d_out is NULL"),
+    (dict(dg=None), kda.KDA_ERR_NULL_PTR, "a gradient output is NULL"),
+    (dict(chunk=16), kda.KDA_ERR_UNSUPPORTED, "chunk must be 64"),
+    (dict(gate_bound=-9.0), kda.KDA_ERR_UNSUPPORTED, "gate_bound"),
+    (dict(do=P + 2), kda.KDA_ERR_ALIGN, "d_out is not 16-byte aligned"),
+    (dict(dk=P + 4), kda.KDA_ERR_ALIGN, "a gradient output is not aligned"),
+    (dict(dht=P + 8), kda.KDA_ERR_ALIGN, "d_final_state is not 16-byte aligned"),
+    (dict(dh0=P + 8), kda.KDA_ERR_ALIGN, "d_initial_state is not 16-byte aligned"),
+])
+def test_backward_argument_validation(kw, code, msg):
+    if not os.path.exists(kda.LIB_PATH):
+        pytest.skip("libkda.so not built")
+    rc, err = _call_bwd(**kw)
+    assert rc == code
+    assert msg in err
+
+
+def test_backward_empty_stream_without_state_gradient_is_a_noop():
+    if not os.path.exists(kda.LIB_PATH):
+        pytest.skip("libkda.so not built")
+    rc, err = _call_bwd(T=0, q=None, k=None, v=None, g=None, beta=None, do=None, dq=None,
+                        dk=None, dv=None, dg=None, db=None)
+    assert rc == kda.KDA_OK and err == ""
 
 
 def test_unsupported_reason_on_cpu_tensors():

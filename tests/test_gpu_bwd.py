@@ -1,0 +1,141 @@
+"""GPU parity of the chunked backward (kda_chunk_bwd) against the fp64
+autograd oracle (oracle/kda_oracle_bwd.py).
+
+Bar, per gradient tensor: relative L2 error <= 5e-3 and max absolute error
+<= 3e-2 times max(1, max |reference|).  The backward runs in fp32; its error
+comes mostly from the forward states it differentiates around, which the
+bf16/fp16 forward pipeline produces (relative error ~2e-3, the forward's own
+bar)."""
+import numpy as np
+import pytest
+
+from kda_gpu_util import REL_L2_TOL, log, to_device
+from kda_workloads import (cu_from_lengths, initial_states, make_inputs, standard_normal,
+                           round_to_bf16, with_gate_scale)
+from oracle.kda_oracle_bwd import kda_backward_tasks
+
+pytestmark = pytest.mark.gpu
+ABS_TOL = 3e-2
+NAMES = ("dq", "dk", "dv", "dg", "dbeta")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import linear_attention_sequence_amd as kda
+    kda.load_library()
+
+
+def _dout(T, H, seed):
+    return round_to_bf16(standard_normal((T, H, 128), seed, 11))
+
+
+def _run(inp, do, h0=None, dht=None, cu=True):
+    import torch
+    import linear_attention_sequence_amd as kda
+    d = to_device(inp)
+    t = lambda x: None if x is None else torch.from_numpy(np.ascontiguousarray(x)).cuda()  # noqa
+    r = kda.chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                      torch.from_numpy(do).to(torch.bfloat16).cuda(), d["cu"] if cu else None,
+                      initial_state=t(h0), d_final_state=t(dht))
+    torch.cuda.synchronize()
+    return [None if x is None else x.cpu().numpy().astype(np.float64) for x in r]
+
+
+def _check(inp, do, got, h0, dht, label, heads=None):
+    cu = [int(x) for x in inp.cu_seqlens]
+    heads = range(inp.H) if heads is None else heads
+    tasks = [(a, b, h, h + 1, d) for d, (a, b) in enumerate(zip(cu[:-1], cu[1:])) for h in heads]
+    acc = {n: [0.0, 0.0, 0.0, 0.0] for n in NAMES + ("dh0",)}   # num, den, maxdiff, maxref
+    for (a, b, h0_, h1_, d), ref in kda_backward_tasks(inp.q, inp.k, inp.v, inp.g, inp.beta, do,
+                                                       tasks, h0, dht):
+        for i, n in enumerate(NAMES):
+            if b > a:
+                x = got[i][a:b, h0_:h1_] - ref[n]
+                acc[n][0] += float((x * x).sum())
+                acc[n][1] += float((ref[n] * ref[n]).sum())
+                acc[n][2] = max(acc[n][2], float(np.abs(x).max()))
+                acc[n][3] = max(acc[n][3], float(np.abs(ref[n]).max()))
+        if got[5] is not None:
+            x = got[5][d, h0_:h1_] - ref["dh0"]
+            acc["dh0"][0] += float((x * x).sum())
+            acc["dh0"][1] += float((ref["dh0"] * ref["dh0"]).sum())
+            acc["dh0"][2] = max(acc["dh0"][2], float(np.abs(x).max()))
+            acc["dh0"][3] = max(acc["dh0"][3], float(np.abs(ref["dh0"]).max()))
+    for n, (num, den, mx, mref) in acc.items():
+        if den == 0:
+            continue
+        rel = np.sqrt(num / den)
+        log(f"[parity] {label} {n}: relL2={rel:.3e} maxabs={mx:.3e} (max|ref| {mref:.3e})")
+        assert rel <= REL_L2_TOL, (label, n, rel)
+        assert mx <= ABS_TOL * max(1.0, mref), (label, n, mx)
+
+
+LENGTHS = [130, 0, 37, 200, 64, 1]
+
+
+@pytest.mark.parametrize("states", [False, True])
+def test_backward_small_packed(states):
+    T, H = sum(LENGTHS), 2
+    inp = with_gate_scale(make_inputs(T, H, 71, cu_from_lengths(LENGTHS)), 71, -0.05)
+    do = _dout(T, H, 71)
+    h0 = initial_states(len(LENGTHS), H, 71) if states else None
+    dht = initial_states(len(LENGTHS), H, 72, std=1.0) if states else None
+    log(f"[case] bwd small packed states={states}")
+    got = _run(inp, do, h0, dht)
+    _check(inp, do, got, h0, dht, f"bwd small (states={states})")
+
+
+@pytest.mark.parametrize("policy", ["never", "always"])
+def test_backward_split_and_fused_forward(monkeypatch, policy):
+    monkeypatch.setenv("KDA_SPLIT", policy)
+    lengths = [700, 300]
+    T, H = sum(lengths), 2
+    inp = make_inputs(T, H, 73, cu_from_lengths(lengths))
+    do = _dout(T, H, 73)
+    log(f"[case] bwd forward policy={policy}")
+    got = _run(inp, do)
+    _check(inp, do, got, None, None, f"bwd workload gate ({policy})")
+
+
+def test_backward_single_document_without_cu_seqlens():
+    T, H = 515, 3
+    inp = with_gate_scale(make_inputs(T, H, 74, cu_from_lengths([T])), 74, -0.3)
+    do = _dout(T, H, 74)
+    h0 = initial_states(1, H, 74)
+    got = _run(inp, do, h0, None, cu=False)
+    _check(inp, do, got, h0, None, "bwd one document, cu None")
+
+
+def test_backward_empty_stream_and_bad_cu_seqlens():
+    import torch
+    import linear_attention_sequence_amd as kda
+    H = 2
+    e = torch.empty(0, H, 128, device="cuda")
+    q = e.to(torch.bfloat16)
+    cu = torch.zeros(3, dtype=torch.int32, device="cuda")
+    h0 = torch.from_numpy(initial_states(2, H, 75)).cuda()
+    dht = torch.from_numpy(initial_states(2, H, 76)).cuda()
+    r = kda.chunk_bwd(q, q, q, e, torch.empty(0, H, device="cuda"), q, cu, initial_state=h0,
+                      d_final_state=dht)
+    torch.cuda.synchronize()
+    assert bool((r[5] == dht).all())
+    inp = make_inputs(100, H, 77, cu_from_lengths([50, 50]))
+    d = to_device(inp)
+    kda.device_status()
+    bad = torch.tensor([0, 60, 40], dtype=torch.int32, device="cuda")
+    r = kda.chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["v"].clone(), bad)
+    assert kda.device_status() & kda.KDA_DEV_BAD_CU_SEQLENS
+    for x in r[:5]:
+        assert bool(torch.isnan(x).all())
+
+
+def test_backward_4096_token_document_sampled_heads():
+    T, H = 4096, 8
+    inp = make_inputs(T, H, 78, cu_from_lengths([T]))
+    do = _dout(T, H, 78)
+    log("[case] bwd T=4096 H=8")
+    got = _run(inp, do)
+    _check(inp, do, got, None, None, "bwd T=4096", heads=[0, 5])
