@@ -52,7 +52,11 @@ namespace {
 constexpr int CH = 64;
 constexpr int DK = 128;
 constexpr int DV = 128;
-constexpr int NT = 256;
+constexpr int NT = 512;                      // threads per workgroup: 8 waves, 2 per SIMD
+constexpr int NW = NT / 64;                  // waves per workgroup
+constexpr int TPT = NT / CH;                 // threads per token row (8)
+constexpr int CPT = DK / TPT;                // channels per thread in a token row (16)
+constexpr int RG = NT / DK;                  // row groups when a thread owns one channel (4)
 constexpr int LD = 129;                      // padded row of a [64][128] LDS tile
 constexpr int LDC = 65;                      // padded row of a [64][64] LDS tile
 constexpr float SCALE = 0.08838834764831845f;  // 128^-1/2
@@ -104,52 +108,109 @@ __device__ __forceinline__ f32x4 mfma16f(float a, float b, const f32x4& c) {
 __device__ __forceinline__ float bf16_to_f32(bf16 x) { return (float)x; }
 
 // C (M x N) = sum over K of la(m, k) lb(k, n), then out(m, n, value).
-// fp32 MFMA 16x16x4; operands staged through LDS (stage) in k-tiles of 16.
+// fp32 MFMA 16x16x4; operands staged through LDS (stage) in k-tiles of 16,
+// the next k-tiles loaded into registers while the current one multiplies.
+// AK / BK: whether consecutive threads fetch consecutive k (operand stored
+// along k) or consecutive m / n, so that global fetches are contiguous.
+// out(m, n, value, old) receives old(m, n) as well (zero by default).
 // Every thread of the workgroup calls it (tid = its thread index); it
 // synchronises before returning results and before its first staging (so
 // operands may live in LDS buffers that out() overwrites).
-template <int M, int N, int K, class LA, class LB, class OUT>
-__device__ __forceinline__ void wg_gemm(LA la, LB lb, OUT out, float* stage, int tid) {
+struct NoOld {
+  __device__ float operator()(int, int) const { return 0.f; }
+};
+
+template <int M, int N, int K, bool AK, bool BK, class LA, class LB, class OUT, class OLD = NoOld>
+__device__ __forceinline__ void wg_gemm(LA la, LB lb, OUT out, float* stage, int tid,
+                                        OLD old = OLD()) {
   static_assert(M % 16 == 0 && N % 16 == 0 && K % 16 == 0 && M <= 128 && N <= 128, "shape");
   constexpr int TM = M / 16, TN = N / 16, TILES = TM * TN;
-  static_assert(TILES % 4 == 0, "whole tiles per wave");
-  constexpr int PER = TILES / 4;
+  static_assert(TILES % NW == 0, "whole tiles per wave");
+  constexpr int PER = TILES / NW;
+  constexpr int NA = (16 * M + NT - 1) / NT, NB = (16 * N + NT - 1) / NT;  // staged per thread
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
   float* sa = stage;                 // [16][M + 1]
   float* sb = stage + 16 * (M + 1);  // [16][N + 1]
+  // (m or n, kk) of this thread's staged element j
+  auto a_mk = [&](int j, int& m, int& kk) {
+    const int idx = tid + NT * j;
+    if (AK) { m = idx >> 4; kk = idx & 15; } else { kk = idx / M; m = idx - kk * M; }
+  };
+  auto b_nk = [&](int j, int& n, int& kk) {
+    const int idx = tid + NT * j;
+    if (BK) { n = idx >> 4; kk = idx & 15; } else { kk = idx / N; n = idx - kk * N; }
+  };
+  // up to PF k-tiles in flight: tile k is multiplied while tiles k+1 .. k+PF-1
+  // are on their way (a load round trip is several tiles' worth of MFMA time)
+  constexpr int KT = K / 16;
+  constexpr int PF = KT < 3 ? KT : 3;
+  float ra[PF][NA], rb[PF][NB];
+  auto fetch = [&](int set, int k0) {
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      int m, kk;
+      a_mk(j, m, kk);
+      if (NA * NT == 16 * M || tid + NT * j < 16 * M) ra[set][j] = la(m, k0 + kk);
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      int n, kk;
+      b_nk(j, n, kk);
+      if (NB * NT == 16 * N || tid + NT * j < 16 * N) rb[set][j] = lb(k0 + kk, n);
+    }
+  };
   f32x4 acc[PER];
 #pragma unroll
   for (int p = 0; p < PER; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1
-  for (int k0 = 0; k0 < K; k0 += 16) {
+  auto tile = [&](int set, int kt) {
     __syncthreads();
-#pragma unroll 1
-    for (int idx = tid; idx < 16 * M; idx += NT) {
-      const int m = idx >> 4, kk = idx & 15;
-      sa[kk * (M + 1) + m] = la(m, k0 + kk);
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      int m, kk;
+      a_mk(j, m, kk);
+      if (NA * NT == 16 * M || tid + NT * j < 16 * M) sa[kk * (M + 1) + m] = ra[set][j];
     }
-#pragma unroll 1
-    for (int idx = tid; idx < 16 * N; idx += NT) {
-      const int kk = idx / N, n = idx - kk * N;
-      sb[kk * (N + 1) + n] = lb(k0 + kk, n);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      int n, kk;
+      b_nk(j, n, kk);
+      if (NB * NT == 16 * N || tid + NT * j < 16 * N) sb[kk * (N + 1) + n] = rb[set][j];
     }
     __syncthreads();
+    if (kt + PF < KT) fetch(set, 16 * (kt + PF));
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int kk = 4 * s + (l >> 4);
 #pragma unroll
       for (int p = 0; p < PER; ++p) {
-        const int t = w + 4 * p, tm = t / TN, tn = t - tm * TN;
+        const int t = w + NW * p, tm = t / TN, tn = t - tm * TN;
         acc[p] = mfma16f(sa[kk * (M + 1) + 16 * tm + (l & 15)], sb[kk * (N + 1) + 16 * tn + (l & 15)], acc[p]);
       }
     }
+  };
+#pragma unroll
+  for (int set = 0; set < PF; ++set) fetch(set, 16 * set);
+#pragma unroll 1
+  for (int kt = 0; kt < KT; kt += PF) {
+#pragma unroll
+    for (int set = 0; set < PF; ++set)
+      if (kt + set < KT) tile(set, kt + set);
   }
   __syncthreads();
+  // old(m, n): values out() adds to, all fetched before the first out() so
+  // that the loads are not ordered behind its stores
+  f32x4 prev[PER];
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
-    const int t = w + 4 * p, tm = t / TN, tn = t - tm * TN;
+    const int t = w + NW * p, tm = t / TN, tn = t - tm * TN;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) out(16 * tm + 4 * (l >> 4) + i, 16 * tn + (l & 15), acc[p][i]);
+    for (int i = 0; i < 4; ++i) prev[p][i] = old(16 * tm + 4 * (l >> 4) + i, 16 * tn + (l & 15));
+  }
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int t = w + NW * p, tm = t / TN, tn = t - tm * TN;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out(16 * tm + 4 * (l >> 4) + i, 16 * tn + (l & 15), acc[p][i], prev[p][i]);
   }
   __syncthreads();
 }
@@ -211,30 +272,31 @@ __device__ __forceinline__ void load_chunk(PrepSmem& sm, float* img, const bf16*
                                            const bf16* __restrict__ k, const float* __restrict__ g,
                                            const float* __restrict__ beta, int start, int len,
                                            int H, int h, int tid) {
-  // 4 threads per token, 32 channels each
-  const int t = tid >> 2, c0 = 32 * (tid & 3);
-  float qv[32], kv[32];
+  // TPT threads per token, CPT channels each
+  const int t = tid / TPT, c0 = CPT * (tid % TPT);
+  float qv[CPT], kv[CPT];
   float sq = 0.f, sk = 0.f;
   const size_t row = ((size_t)(start + t) * H + h) * DK;
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
+  for (int j = 0; j < CPT; ++j) {
     qv[j] = t < len ? bf16_to_f32(q[row + c0 + j]) : 0.f;
     kv[j] = t < len ? bf16_to_f32(k[row + c0 + j]) : 0.f;
     sq += qv[j] * qv[j];
     sk += kv[j] * kv[j];
   }
-  sq += __shfl_xor(sq, 1);
-  sq += __shfl_xor(sq, 2);
-  sk += __shfl_xor(sk, 1);
-  sk += __shfl_xor(sk, 2);
+#pragma unroll
+  for (int o = 1; o < TPT; o <<= 1) {
+    sq += __shfl_xor(sq, o);
+    sk += __shfl_xor(sk, o);
+  }
   const float rq = 1.f / sqrtf(sq + L2_EPS), rk = 1.f / sqrtf(sk + L2_EPS);
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
+  for (int j = 0; j < CPT; ++j) {
     sm.qh[t][c0 + j] = qv[j] * rq;
     sm.kh[t][c0 + j] = kv[j] * rk;
     sm.G[t][c0 + j] = t < len ? g[row + c0 + j] : 0.f;
   }
-  if ((tid & 3) == 0) {
+  if (tid % TPT == 0) {
     img[IMG_RQ + t] = rq;
     img[IMG_RK + t] = rk;
     sm.beta[t] = t < len ? beta[(size_t)(start + t) * H + h] : 0.f;
@@ -274,41 +336,71 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_prep_kernel(
     float* img = imgs + (size_t)item * IMG_FLOATS;
     __syncthreads();
     load_chunk(sm, img, q, k, g, beta, start, len, H, h, tid);
-    // Kk (strictly lower) and M (lower incl.), exp(G_r - G_i) <= 1 per channel
+    // Kk (strictly lower, to the image) and M (lower incl., LDS) in 16-token
+    // blocks.  Blocks above the diagonal are zero.
     for (int idx = tid; idx < CH * CH; idx += NT) {
       const int r = idx >> 6, i = idx & 63;
+      if ((i >> 4) > (r >> 4)) {
+        img[IMG_KK + idx] = 0.f;
+        sm.m[r][i] = 0.f;
+      }
+    }
+    // diagonal blocks directly: exp(G_r - G_i) <= 1 per channel for i <= r
+    for (int idx = tid; idx < 4 * 16 * 16; idx += NT) {
+      const int blk = idx >> 8, r = 16 * blk + ((idx >> 4) & 15), i = 16 * blk + (idx & 15);
       float a = 0.f, mm = 0.f;
       if (i <= r) {
         for (int c = 0; c < DK; ++c) {
-          const float e = __expf(sm.G[r][c] - sm.G[i][c]);
-          const float ki = sm.kh[i][c] * e;
+          const float ki = sm.kh[i][c] * __expf(sm.G[r][c] - sm.G[i][c]);
           a = fmaf(sm.kh[r][c], ki, a);
           mm = fmaf(sm.qh[r][c], ki, mm);
         }
       }
-      sm.kk[r][i] = i < r ? a : 0.f;
-      sm.m[r][i] = mm;
+      img[IMG_KK + r * CH + i] = i < r ? a : 0.f;
+      sm.m[r][i] = i <= r ? mm : 0.f;
     }
+    // blocks below the diagonal: for column block b the decay splits at
+    // rho = G of its last row, exp(G_r - rho) <= 1 for rows below the block and
+    // exp(rho - G_i) <= 1 inside it.  Rows 0..63 of the product are Kk, 64..127 M.
+    for (int b = 0; b < 3; ++b) {
+      const int rmin = 16 * (b + 1);
+      const float* rho = sm.G[16 * b + 15];
+      wg_gemm<2 * CH, 16, DK, true, true>(
+          [&](int row, int c) {
+            const int r = row & 63;
+            if (r < rmin) return 0.f;
+            return (row < CH ? sm.kh[r][c] : sm.qh[r][c]) * __expf(sm.G[r][c] - rho[c]);
+          },
+          [&](int c, int i) { return sm.kh[16 * b + i][c] * __expf(rho[c] - sm.G[16 * b + i][c]); },
+          [&](int row, int i, float x, float) {
+            const int r = row & 63;
+            if (r < rmin) return;
+            if (row < CH) img[IMG_KK + r * CH + 16 * b + i] = x;
+            else sm.m[r][16 * b + i] = x;
+          },
+          sm.stage, tid);
+    }
+    // T = (I + Diag(beta) Kk)^-1: column i solves (I + Diag(beta) Kk) x = e_i by
+    // forward substitution; one thread per column, no barriers
+    for (int idx = tid; idx < CH * CH; idx += NT) sm.kk[idx >> 6][idx & 63] = img[IMG_KK + idx];
     __syncthreads();
-    // T = (I + Diag(beta) Kk)^-1 by forward substitution, one row at a time
-    if (tid < CH) sm.t[0][tid] = tid == 0 ? 1.f : 0.f;
-    for (int r = 1; r < CH; ++r) {
-      __syncthreads();
-      if (tid < CH) {
-        const int i = tid;
+    if (tid < CH) {
+      const int i = tid;
+      float col[CH];
+#pragma unroll
+      for (int r = 0; r < CH; ++r) {
         float acc = 0.f;
-        if (i < r) {
-          for (int m = i; m < r; ++m) acc = fmaf(sm.kk[r][m], sm.t[m][i], acc);
-          acc *= -sm.beta[r];
-        }
-        sm.t[r][i] = i < r ? acc : (i == r ? 1.f : 0.f);
+#pragma unroll
+        for (int m = 0; m < r; ++m) acc = fmaf(sm.kk[r][m], col[m], acc);
+        col[r] = r < i ? 0.f : (r == i ? 1.f : -sm.beta[r] * acc);
       }
+#pragma unroll
+      for (int r = 0; r < CH; ++r) sm.t[r][i] = col[r];
     }
     __syncthreads();
     for (int idx = tid; idx < CH * CH; idx += NT) {
       const int r = idx >> 6, i = idx & 63;
       img[IMG_T + idx] = sm.t[r][i];
-      img[IMG_KK + idx] = sm.kk[r][i];
       img[IMG_M + idx] = sm.m[r][i];
     }
     const float* Gl = sm.G[CH - 1];
@@ -317,35 +409,35 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_prep_kernel(
       return r < len ? bf16_to_f32(dout[(drow0 + (size_t)r * H) * DV + v]) : 0.f;
     };
     // Y1 = Tb^T Kbar  [t][c]
-    wg_gemm<CH, DK, CH>(
+    wg_gemm<CH, DK, CH, false, false>(
         [&](int t, int r) { return sm.t[r][t] * sm.beta[t]; },
         [&](int r, int c) { return sm.kh[r][c] * __expf(Gl[c] - sm.G[r][c]); },
-        [&](int t, int c, float x) { sp[SP_Y1 + t * DK + c] = x; }, sm.stage, tid);
+        [&](int t, int c, float x, float) { sp[SP_Y1 + t * DK + c] = x; }, sm.stage, tid);
     // P1 = scale M^T dO  [t][v]
-    wg_gemm<CH, DV, CH>(
+    wg_gemm<CH, DV, CH, false, false>(
         [&](int t, int r) { return SCALE * sm.m[r][t]; }, [&](int r, int v) { return dO(r, v); },
-        [&](int t, int v, float x) { sp[SP_P1 + t * DV + v] = x; }, sm.stage, tid);
+        [&](int t, int v, float x, float) { sp[SP_P1 + t * DV + v] = x; }, sm.stage, tid);
     // Y2 = Tb^T P1
-    wg_gemm<CH, DV, CH>(
+    wg_gemm<CH, DV, CH, false, false>(
         [&](int t, int r) { return sm.t[r][t] * sm.beta[t]; },
         [&](int r, int v) { return sp[SP_P1 + r * DV + v]; },
-        [&](int t, int v, float x) { sp[SP_Y2 + t * DV + v] = x; }, sm.stage, tid);
+        [&](int t, int v, float x, float) { sp[SP_Y2 + t * DV + v] = x; }, sm.stage, tid);
     // F^T = D - Kt^T Y1  [c][c']
     float* ft = fts + (size_t)item * DK * DK;
-    wg_gemm<DK, DK, CH>(
+    wg_gemm<DK, DK, CH, false, false>(
         [&](int c, int t) { return sm.kh[t][c] * __expf(sm.G[t][c]); },
         [&](int t, int c2) { return sp[SP_Y1 + t * DK + c2]; },
-        [&](int c, int c2, float x) { ft[c * DK + c2] = (c == c2 ? __expf(Gl[c]) : 0.f) - x; },
+        [&](int c, int c2, float x, float) { ft[c * DK + c2] = (c == c2 ? __expf(Gl[c]) : 0.f) - x; },
         sm.stage, tid);
     // R = scale Qt^T dO - Kt^T Y2  [c][v]  (one product over the stacked rows)
     float* rr = rs + (size_t)item * DK * DV;
-    wg_gemm<DK, DV, 2 * CH>(
+    wg_gemm<DK, DV, 2 * CH, false, false>(
         [&](int c, int t) {
           return t < CH ? SCALE * sm.qh[t][c] * __expf(sm.G[t][c])
                         : -sm.kh[t - CH][c] * __expf(sm.G[t - CH][c]);
         },
         [&](int t, int v) { return t < CH ? dO(t, v) : sp[SP_Y2 + (t - CH) * DV + v]; },
-        [&](int c, int v, float x) { rr[c * DV + v] = x; }, sm.stage, tid);
+        [&](int c, int v, float x, float) { rr[c * DV + v] = x; }, sm.stage, tid);
   }
 }
 
@@ -379,9 +471,9 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_chain_kernel(
     for (int idx = tid; idx < DK * DV; idx += NT) dst[idx] = sm.ds[idx >> 7][idx & 127];
     const float* ft = fts + item * DK * DK;
     const float* rr = rs + item * DK * DV;
-    wg_gemm<DK, DV, DK>([&](int c, int c2) { return ft[c * DK + c2]; },
+    wg_gemm<DK, DV, DK, true, false>([&](int c, int c2) { return ft[c * DK + c2]; },
                         [&](int c2, int v) { return sm.ds[c2][v]; },
-                        [&](int c, int v, float x) { sm.ds[c][v] = x + rr[c * DV + v]; }, sm.stage, tid);
+                        [&](int c, int v, float x, float) { sm.ds[c][v] = x + rr[c * DV + v]; }, sm.stage, tid);
   }
   __syncthreads();
   if (dh0 != nullptr)
@@ -402,7 +494,7 @@ struct GradSmem {
   float dbeta[CH];
   float dD[DK];
   float gl[DK];          // G of the last row
-  float kbsum[2][DK];
+  float kbsum[RG][DK];
   float stage[STAGE_FLOATS];
 };
 
@@ -449,59 +541,61 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
       return r < len ? bf16_to_f32(v[(row0 + (size_t)r * H) * DV + c]) : 0.f;
     };
     // X = V - Kt S0
-    wg_gemm<CH, DV, DK>(
+    wg_gemm<CH, DV, DK, true, false>(
         [&](int t, int c) { return sm.kh[t][c] * __expf(sm.G[t][c]); },
         [&](int c, int vv) { return S0[c * DV + vv]; },
-        [&](int t, int vv, float x) { sc[SC_X + t * DV + vv] = Vv(t, vv) - x; }, sm.stage, tid);
+        [&](int t, int vv, float x, float) { sc[SC_X + t * DV + vv] = Vv(t, vv) - x; }, sm.stage, tid);
     // U = Tb X
-    wg_gemm<CH, DV, CH>(
+    wg_gemm<CH, DV, CH, true, false>(
         [&](int t, int i) { return T[t * CH + i] * sm.beta[i]; },
         [&](int i, int vv) { return sc[SC_X + i * DV + vv]; },
-        [&](int t, int vv, float x) { sc[SC_U + t * DV + vv] = x; }, sm.stage, tid);
+        [&](int t, int vv, float x, float) { sc[SC_U + t * DV + vv] = x; }, sm.stage, tid);
     // dU = scale M^T dO + Kbar dSc  (stacked k: 64 rows of M^T, then 128 channels)
-    wg_gemm<CH, DV, CH + DK>(
+    wg_gemm<CH, DV, CH + DK, false, false>(
         [&](int t, int kk) {
           return kk < CH ? SCALE * Mm[kk * CH + t]
                          : sm.kh[t][kk - CH] * __expf(sm.gl[kk - CH] - sm.G[t][kk - CH]);
         },
         [&](int kk, int vv) { return kk < CH ? dO(kk, vv) : dSc[(kk - CH) * DV + vv]; },
-        [&](int t, int vv, float x) { sc[SC_DU + t * DV + vv] = x; }, sm.stage, tid);
+        [&](int t, int vv, float x, float) { sc[SC_DU + t * DV + vv] = x; }, sm.stage, tid);
     // dX = Tb^T dU  (= dV)
-    wg_gemm<CH, DV, CH>(
+    wg_gemm<CH, DV, CH, false, false>(
         [&](int t, int r) { return T[r * CH + t] * sm.beta[t]; },
         [&](int r, int vv) { return sc[SC_DU + r * DV + vv]; },
-        [&](int t, int vv, float x) {
+        [&](int t, int vv, float x, float) {
           sc[SC_DX + t * DV + vv] = x;
           if (t < len) dv[(row0 + (size_t)t * H) * DV + vv] = x;
         },
         sm.stage, tid);
     // rows 0..63: dQt = scale dO S0^T; rows 64..127: dKt = -dX S0^T
-    wg_gemm<2 * CH, DK, DV>(
+    wg_gemm<2 * CH, DK, DV, true, true>(
         [&](int t, int vv) { return t < CH ? SCALE * dO(t, vv) : -sc[SC_DX + (t - CH) * DV + vv]; },
         [&](int vv, int c) { return S0[c * DV + vv]; },
-        [&](int t, int c, float x) { sc[SC_DQK + t * DK + c] = x; }, sm.stage, tid);
+        [&](int t, int c, float x, float) { sc[SC_DQK + t * DK + c] = x; }, sm.stage, tid);
     // dKbar = U dSc^T
-    wg_gemm<CH, DK, DV>(
+    wg_gemm<CH, DK, DV, true, true>(
         [&](int t, int vv) { return sc[SC_U + t * DV + vv]; },
         [&](int vv, int c) { return dSc[c * DV + vv]; },
-        [&](int t, int c, float x) { sc[SC_DKB + t * DK + c] = x; }, sm.stage, tid);
+        [&](int t, int c, float x, float) { sc[SC_DKB + t * DK + c] = x; }, sm.stage, tid);
     // dM = scale tril(dO U^T)
-    wg_gemm<CH, CH, DV>(
+    wg_gemm<CH, CH, DV, true, true>(
         [&](int r, int vv) { return SCALE * dO(r, vv); },
         [&](int vv, int i) { return sc[SC_U + i * DV + vv]; },
-        [&](int r, int i, float x) { sm.dm[r][i] = i <= r ? x : 0.f; }, sm.stage, tid);
+        [&](int r, int i, float x, float) { sm.dm[r][i] = i <= r ? x : 0.f; }, sm.stage, tid);
     // dTb = tril(dU X^T)
-    wg_gemm<CH, CH, DV>(
+    wg_gemm<CH, CH, DV, true, true>(
         [&](int r, int vv) { return sc[SC_DU + r * DV + vv]; },
         [&](int vv, int i) { return sc[SC_X + i * DV + vv]; },
-        [&](int r, int i, float x) { sc[SC_DTB + r * CH + i] = i <= r ? x : 0.f; }, sm.stage, tid);
+        [&](int r, int i, float x, float) { sc[SC_DTB + r * CH + i] = i <= r ? x : 0.f; }, sm.stage, tid);
     // dD[c] = sum_v dSc[c][v] S0[c][v]; dbeta_i = sum_r dTb_ri T_ri
     {
-      const int c = tid >> 1, half = tid & 1;
+      const int c = tid / RG, part = tid % RG;
       float acc = 0.f;
-      for (int vv = 64 * half; vv < 64 * half + 64; ++vv) acc = fmaf(dSc[c * DV + vv], S0[c * DV + vv], acc);
-      acc += __shfl_xor(acc, 1);
-      if (half == 0) sm.dD[c] = acc;
+      for (int vv = (DV / RG) * part; vv < (DV / RG) * (part + 1); ++vv)
+        acc = fmaf(dSc[c * DV + vv], S0[c * DV + vv], acc);
+#pragma unroll
+      for (int o = 1; o < RG; o <<= 1) acc += __shfl_xor(acc, o);
+      if (part == 0) sm.dD[c] = acc;
       if (tid < CH) {
         float db = 0.f;
         for (int r = tid; r < CH; ++r) db = fmaf(sc[SC_DTB + r * CH + tid], T[r * CH + tid], db);
@@ -509,14 +603,14 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
       }
     }
     // Z = (dTb Diag(beta)) T^T;  dA = -T^T Z (strictly lower)
-    wg_gemm<CH, CH, CH>(
+    wg_gemm<CH, CH, CH, true, true>(
         [&](int r, int m) { return sc[SC_DTB + r * CH + m] * sm.beta[m]; },
         [&](int m, int i) { return T[i * CH + m]; },
-        [&](int r, int i, float x) { sc[SC_Z + r * CH + i] = x; }, sm.stage, tid);
-    wg_gemm<CH, CH, CH>(
+        [&](int r, int i, float x, float) { sc[SC_Z + r * CH + i] = x; }, sm.stage, tid);
+    wg_gemm<CH, CH, CH, false, false>(
         [&](int r, int m) { return -T[m * CH + r]; },
         [&](int m, int i) { return sc[SC_Z + m * CH + i]; },
-        [&](int r, int i, float x) { sm.dkk[r][i] = i < r ? x : 0.f; }, sm.stage, tid);
+        [&](int r, int i, float x, float) { sm.dkk[r][i] = i < r ? x : 0.f; }, sm.stage, tid);
     // dbeta_r += sum_i dA_ri Kk_ri; dKk = Diag(beta) dA
     if (tid < CH) {
       const int r = tid;
@@ -531,70 +625,140 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
     }
     if (tid < CH && tid < len) dbeta[row0 + (size_t)tid * H] = sm.dbeta[tid];
     __syncthreads();
-    // bilinear forms and the decayed tiles: thread = channel c, rows r = half + 2 j.
-    // dqh, dkh and dG of (r, c) replace dQt, dKt and dKbar of (r, c) in the
-    // scratch (the same thread reads them first)
+    // bilinear forms of M and Kk: for (r, c)
+    //   Sa1 = sum_{i <= r} dM_ri kh_ic E_ric,  Sa2 = sum_{i < r} dKk_ri kh_ic E_ric,
+    //   Sb  = sum_{rr >= r} (dM_rr,r qh_rr,c + dKk_rr,r kh_rr,c) E_rr,r,c
+    // with E_ric = exp(G_rc - G_ic).  Pairs inside one 16-token block directly;
+    // pairs across blocks by products with the decay split at the end of the
+    // column block (both factors <= 1).  Sa1, Sa2, Sb go to the X, U, dU
+    // scratch, which is no longer needed.
+    float* Sa1 = sc + SC_X;
+    float* Sa2 = sc + SC_U;
+    float* Sb = sc + SC_DU;
+    for (int idx = tid; idx < CH * DK; idx += NT) {
+      const int r = idx >> 7, c = idx & 127;
+      const int r0 = r & ~15, r1 = r0 + 16;
+      const float Gr = sm.G[r][c];
+      float sa1 = 0.f, sa2 = 0.f, sb = 0.f;
+      for (int i = r0; i <= r; ++i) {
+        const float ki = sm.kh[i][c] * __expf(Gr - sm.G[i][c]);
+        sa1 = fmaf(sm.dm[r][i], ki, sa1);
+        sa2 = fmaf(sm.dkk[r][i], ki, sa2);
+      }
+      for (int rr = r; rr < r1; ++rr)
+        sb = fmaf(fmaf(sm.dm[rr][r], sm.qh[rr][c], sm.dkk[rr][r] * sm.kh[rr][c]),
+                  __expf(sm.G[rr][c] - Gr), sb);
+      Sa1[idx] = sa1;
+      Sa2[idx] = sa2;
+      Sb[idx] = sb;
+    }
+    for (int b = 0; b < 3; ++b) {
+      const int rmin = 16 * (b + 1);
+      const float* rho = sm.G[16 * b + 15];
+      // rows r below block b: Sa1 (with dM) and Sa2 (with dKk) gain
+      // exp(G_r - rho) sum_{i in b} dM|dKk_ri (kh_i exp(rho - G_i))
+      for (int which = 0; which < 2; ++which) {
+        const float(*dmat)[LDC] = which == 0 ? sm.dm : sm.dkk;
+        float* Sa = which == 0 ? Sa1 : Sa2;
+        wg_gemm<CH, DK, 16, true, false>(
+            [&](int r, int i) { return r < rmin ? 0.f : dmat[r][16 * b + i]; },
+            [&](int i, int c) { return sm.kh[16 * b + i][c] * __expf(rho[c] - sm.G[16 * b + i][c]); },
+            [&](int r, int c, float x, float prev) {
+              if (r >= rmin) Sa[r * DK + c] = prev + x * __expf(sm.G[r][c] - rho[c]);
+            },
+            sm.stage, tid, [&](int r, int c) { return r < rmin ? 0.f : Sa[r * DK + c]; });
+      }
+      // rows i of block b: Sb gains exp(rho - G_i) sum_{r below b}
+      // (dM_ri qh_r + dKk_ri kh_r) exp(G_r - rho)
+      wg_gemm<16, DK, 2 * CH, false, false>(
+          [&](int i, int kk) {
+            const int r = kk & 63;
+            if (r < rmin) return 0.f;
+            return kk < CH ? sm.dm[r][16 * b + i] : sm.dkk[r][16 * b + i];
+          },
+          [&](int kk, int c) {
+            const int r = kk & 63;
+            if (r < rmin) return 0.f;
+            return (kk < CH ? sm.qh[r][c] : sm.kh[r][c]) * __expf(sm.G[r][c] - rho[c]);
+          },
+          [&](int i, int c, float x, float prev) {
+            Sb[(16 * b + i) * DK + c] = prev + x * __expf(rho[c] - sm.G[16 * b + i][c]);
+          },
+          sm.stage, tid, [&](int i, int c) { return Sb[(16 * b + i) * DK + c]; });
+    }
+    // combine with the decayed tiles: dqh, dkh and dG of (r, c) replace dQt,
+    // dKt and dKbar of (r, c) in the scratch
     {
-      const int c = tid & 127, half = tid >> 7;
+      const int c = tid % DK, grp = tid / DK;
       const float gl = sm.gl[c];
       float kbsum = 0.f;  // sum over this thread's rows of dKbar Kbar
 #pragma unroll 1
-      for (int j = 0; j < 32; ++j) {
-        const int r = half + 2 * j;
-        const float Gr = sm.G[r][c];
-        float sa1 = 0.f, sa2 = 0.f, sb = 0.f;
-        const float qr = sm.qh[r][c], kr = sm.kh[r][c];
-        // row role: i <= r
-        for (int i = 0; i <= r; ++i) {
-          const float ki = sm.kh[i][c] * __expf(Gr - sm.G[i][c]);
-          sa1 = fmaf(sm.dm[r][i], ki, sa1);
-          sa2 = fmaf(sm.dkk[r][i], ki, sa2);
+      for (int j0 = 0; j0 < CH / RG; j0 += 8) {
+        // the batch's loads before its stores (same buffer: not reordered otherwise)
+        float in[8][6];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int r = grp + RG * (j0 + j);
+          in[j][0] = Sa1[r * DK + c];
+          in[j][1] = Sa2[r * DK + c];
+          in[j][2] = Sb[r * DK + c];
+          in[j][3] = sc[SC_DQK + r * DK + c];
+          in[j][4] = sc[SC_DQK + (CH + r) * DK + c];
+          in[j][5] = sc[SC_DKB + r * DK + c];
         }
-        // column role: rows rr >= r
-        for (int rr = r; rr < CH; ++rr) {
-          const float e = __expf(sm.G[rr][c] - Gr);
-          sb = fmaf(fmaf(sm.dm[rr][r], sm.qh[rr][c], sm.dkk[rr][r] * sm.kh[rr][c]), e, sb);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int r = grp + RG * (j0 + j);
+          const float Gr = sm.G[r][c];
+          const float qr = sm.qh[r][c], kr = sm.kh[r][c];
+          const float sa1 = in[j][0], sa2 = in[j][1], sb = in[j][2];
+          const float dqt = in[j][3], dkt = in[j][4], dkb = in[j][5];
+          const float eg = __expf(Gr), eb = __expf(gl - Gr);
+          kbsum = fmaf(dkb, kr * eb, kbsum);
+          sc[SC_DQK + r * DK + c] = sa1 + dqt * eg;
+          sc[SC_DQK + (CH + r) * DK + c] = sa2 + sb + dkt * eg + dkb * eb;
+          sc[SC_DKB + r * DK + c] = qr * sa1 + kr * sa2 - kr * sb + dqt * qr * eg + dkt * kr * eg - dkb * kr * eb;
         }
-        const float eg = __expf(Gr), eb = __expf(gl - Gr);
-        float* pq = sc + SC_DQK + r * DK + c;
-        float* pk = sc + SC_DQK + (CH + r) * DK + c;
-        float* pb = sc + SC_DKB + r * DK + c;
-        const float dqt = *pq, dkt = *pk, dkb = *pb;
-        kbsum = fmaf(dkb, kr * eb, kbsum);
-        *pq = sa1 + dqt * eg;
-        *pk = sa2 + sb + dkt * eg + dkb * eb;
-        *pb = qr * sa1 + kr * sa2 - kr * sb + dqt * qr * eg + dkt * kr * eg - dkb * kr * eb;
       }
-      sm.kbsum[half][c] = kbsum;
+      sm.kbsum[grp][c] = kbsum;
     }
     __syncthreads();
     // dg = reverse cumsum of dG within the chunk; the last row gains
     // sum_r dKbar_r Kbar_r + dD D (G_last is the cumsum up to the last token)
     if (tid < DK) {
       const int c = tid;
-      float acc = sm.kbsum[0][c] + sm.kbsum[1][c] + sm.dD[c] * __expf(sm.gl[c]);
-      for (int r = CH - 1; r >= 0; --r) {
-        acc += sc[SC_DKB + r * DK + c];
-        if (r < len) dg[(row0 + (size_t)r * H) * DK + c] = acc;
+      float acc = sm.dD[c] * __expf(sm.gl[c]);
+#pragma unroll
+      for (int gi = 0; gi < RG; ++gi) acc += sm.kbsum[gi][c];
+#pragma unroll 1
+      for (int r0 = CH - 16; r0 >= 0; r0 -= 16) {
+        float x[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) x[j] = sc[SC_DKB + (r0 + j) * DK + c];
+#pragma unroll
+        for (int j = 15; j >= 0; --j) {
+          acc += x[j];
+          if (r0 + j < len) dg[(row0 + (size_t)(r0 + j) * H) * DK + c] = acc;
+        }
       }
     }
-    // l2 norms: dq = rq (dqh - qh (qh . dqh)), dk likewise; 4 threads per token
+    // l2 norms: dq = rq (dqh - qh (qh . dqh)), dk likewise; TPT threads per token
     {
-      const int t = tid >> 2, c0 = 32 * (tid & 3);
+      const int t = tid / TPT, c0 = CPT * (tid % TPT);
 #pragma unroll 1
       for (int which = 0; which < 2; ++which) {
         const float* dxh = sc + SC_DQK + (which * CH + t) * DK;
         float sdot = 0.f;
-        for (int j = 0; j < 32; ++j) {
+        for (int j = 0; j < CPT; ++j) {
           const float xh = which == 0 ? sm.qh[t][c0 + j] : sm.kh[t][c0 + j];
           sdot = fmaf(xh, dxh[c0 + j], sdot);
         }
-        sdot += __shfl_xor(sdot, 1);
-        sdot += __shfl_xor(sdot, 2);
+#pragma unroll
+        for (int o = 1; o < TPT; o <<= 1) sdot += __shfl_xor(sdot, o);
         if (t < len) {
           const float rn = img[(which == 0 ? IMG_RQ : IMG_RK) + t];
           float* dst = (which == 0 ? dq : dk) + (row0 + (size_t)t * H) * DK;
-          for (int j = 0; j < 32; ++j) {
+          for (int j = 0; j < CPT; ++j) {
             const float xh = which == 0 ? sm.qh[t][c0 + j] : sm.kh[t][c0 + j];
             dst[c0 + j] = rn * (dxh[c0 + j] - xh * sdot);
           }
