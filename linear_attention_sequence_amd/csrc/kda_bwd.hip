@@ -61,7 +61,8 @@ constexpr int LD = 129;                      // padded row of a [64][128] LDS ti
 constexpr int LDC = 65;                      // padded row of a [64][64] LDS tile
 constexpr float SCALE = 0.08838834764831845f;  // 128^-1/2
 constexpr float L2_EPS = 1e-6f;
-constexpr int STAGE_FLOATS = 16 * (128 + 1) * 2;
+constexpr int SROW = 20;                     // staged row: 16 k values + 4 padding (conflict-free b128)
+constexpr int STAGE_FLOATS = SROW * (128 + 128);
 typedef __bf16 bf16;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -129,15 +130,15 @@ __device__ __forceinline__ void wg_gemm(LA la, LB lb, OUT out, float* stage, int
   constexpr int PER = TILES / NW;
   constexpr int NA = (16 * M + NT - 1) / NT, NB = (16 * N + NT - 1) / NT;  // staged per thread
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
-  float* sa = stage;                 // [16][M + 1]
-  float* sb = stage + 16 * (M + 1);  // [16][N + 1]
+  float* sa = stage;              // [M][SROW]: row m holds k = k0 .. k0 + 15
+  float* sb = stage + M * SROW;   // [N][SROW]
   // (m or n, kk) of this thread's staged element j
   auto a_mk = [&](int j, int& m, int& kk) {
-    const int idx = tid + NT * j;
+    const int idx = min(tid + NT * j, 16 * M - 1);
     if (AK) { m = idx >> 4; kk = idx & 15; } else { kk = idx / M; m = idx - kk * M; }
   };
   auto b_nk = [&](int j, int& n, int& kk) {
-    const int idx = tid + NT * j;
+    const int idx = min(tid + NT * j, 16 * N - 1);
     if (BK) { n = idx >> 4; kk = idx & 15; } else { kk = idx / N; n = idx - kk * N; }
   };
   // up to PF k-tiles in flight: tile k is multiplied while tiles k+1 .. k+PF-1
@@ -150,13 +151,13 @@ __device__ __forceinline__ void wg_gemm(LA la, LB lb, OUT out, float* stage, int
     for (int j = 0; j < NA; ++j) {
       int m, kk;
       a_mk(j, m, kk);
-      if (NA * NT == 16 * M || tid + NT * j < 16 * M) ra[set][j] = la(m, k0 + kk);
+      ra[set][j] = la(m, k0 + kk);  // clamped index: always a valid element
     }
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       int n, kk;
       b_nk(j, n, kk);
-      if (NB * NT == 16 * N || tid + NT * j < 16 * N) rb[set][j] = lb(k0 + kk, n);
+      rb[set][j] = lb(k0 + kk, n);
     }
   };
   f32x4 acc[PER];
@@ -168,24 +169,28 @@ __device__ __forceinline__ void wg_gemm(LA la, LB lb, OUT out, float* stage, int
     for (int j = 0; j < NA; ++j) {
       int m, kk;
       a_mk(j, m, kk);
-      if (NA * NT == 16 * M || tid + NT * j < 16 * M) sa[kk * (M + 1) + m] = ra[set][j];
+      if (NA * NT == 16 * M || tid + NT * j < 16 * M) sa[m * SROW + kk] = ra[set][j];
     }
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       int n, kk;
       b_nk(j, n, kk);
-      if (NB * NT == 16 * N || tid + NT * j < 16 * N) sb[kk * (N + 1) + n] = rb[set][j];
+      if (NB * NT == 16 * N || tid + NT * j < 16 * N) sb[n * SROW + kk] = rb[set][j];
     }
     __syncthreads();
     if (kt + PF < KT) fetch(set, 16 * (kt + PF));
+    // k-step s pairs lane group g = l / 16 with k = 4 g + s on both operands,
+    // so each lane reads its four k values of a tile as one 16-byte vector
+    const int kq = 4 * (l >> 4);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int kk = 4 * s + (l >> 4);
-#pragma unroll
-      for (int p = 0; p < PER; ++p) {
-        const int t = w + NW * p, tm = t / TN, tn = t - tm * TN;
-        acc[p] = mfma16f(sa[kk * (M + 1) + 16 * tm + (l & 15)], sb[kk * (N + 1) + 16 * tn + (l & 15)], acc[p]);
-      }
+    for (int p = 0; p < PER; ++p) {
+      const int t = w + NW * p, tm = t / TN, tn = t - tm * TN;
+      const float4 av = *reinterpret_cast<const float4*>(&sa[(16 * tm + (l & 15)) * SROW + kq]);
+      const float4 bv = *reinterpret_cast<const float4*>(&sb[(16 * tn + (l & 15)) * SROW + kq]);
+      acc[p] = mfma16f(av.x, bv.x, acc[p]);
+      acc[p] = mfma16f(av.y, bv.y, acc[p]);
+      acc[p] = mfma16f(av.z, bv.z, acc[p]);
+      acc[p] = mfma16f(av.w, bv.w, acc[p]);
     }
   };
 #pragma unroll
@@ -262,7 +267,7 @@ struct PrepSmem {
   float beta[CH];
   union {
     float kk[CH][LDC];           // until T is built and the image written
-    float stage[STAGE_FLOATS];   // then the products' staging
+    alignas(16) float stage[STAGE_FLOATS];  // then the products' staging
   };
 };
 
@@ -274,13 +279,35 @@ __device__ __forceinline__ void load_chunk(PrepSmem& sm, float* img, const bf16*
                                            int H, int h, int tid) {
   // TPT threads per token, CPT channels each
   const int t = tid / TPT, c0 = CPT * (tid % TPT);
-  float qv[CPT], kv[CPT];
+  float qv[CPT], kv[CPT], gv[CPT];
   float sq = 0.f, sk = 0.f;
   const size_t row = ((size_t)(start + t) * H + h) * DK;
+  static_assert(CPT % 8 == 0, "whole 16-byte vectors");
+  if (t < len) {
+#pragma unroll
+    for (int j = 0; j < CPT; j += 8) {
+      const uint4 uq = *reinterpret_cast<const uint4*>(q + row + c0 + j);
+      const uint4 uk = *reinterpret_cast<const uint4*>(k + row + c0 + j);
+      const float4 g0 = *reinterpret_cast<const float4*>(g + row + c0 + j);
+      const float4 g1 = *reinterpret_cast<const float4*>(g + row + c0 + j + 4);
+      const uint32_t wq[4] = {uq.x, uq.y, uq.z, uq.w}, wk[4] = {uk.x, uk.y, uk.z, uk.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        qv[j + 2 * u] = __uint_as_float(wq[u] << 16);
+        qv[j + 2 * u + 1] = __uint_as_float(wq[u] & 0xFFFF0000u);
+        kv[j + 2 * u] = __uint_as_float(wk[u] << 16);
+        kv[j + 2 * u + 1] = __uint_as_float(wk[u] & 0xFFFF0000u);
+      }
+      const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+      for (int u = 0; u < 8; ++u) gv[j + u] = gg[u];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) qv[j] = kv[j] = gv[j] = 0.f;
+  }
 #pragma unroll
   for (int j = 0; j < CPT; ++j) {
-    qv[j] = t < len ? bf16_to_f32(q[row + c0 + j]) : 0.f;
-    kv[j] = t < len ? bf16_to_f32(k[row + c0 + j]) : 0.f;
     sq += qv[j] * qv[j];
     sk += kv[j] * kv[j];
   }
@@ -294,7 +321,7 @@ __device__ __forceinline__ void load_chunk(PrepSmem& sm, float* img, const bf16*
   for (int j = 0; j < CPT; ++j) {
     sm.qh[t][c0 + j] = qv[j] * rq;
     sm.kh[t][c0 + j] = kv[j] * rk;
-    sm.G[t][c0 + j] = t < len ? g[row + c0 + j] : 0.f;
+    sm.G[t][c0 + j] = gv[j];
   }
   if (tid % TPT == 0) {
     img[IMG_RQ + t] = rq;
@@ -367,9 +394,9 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_prep_kernel(
       const float* rho = sm.G[16 * b + 15];
       wg_gemm<2 * CH, 16, DK, true, true>(
           [&](int row, int c) {
-            const int r = row & 63;
-            if (r < rmin) return 0.f;
-            return (row < CH ? sm.kh[r][c] : sm.qh[r][c]) * __expf(sm.G[r][c] - rho[c]);
+            const int r = max(row & 63, rmin);  // rows above the block: a valid row, then zero
+            const float x = (row < CH ? sm.kh[r][c] : sm.qh[r][c]) * __expf(sm.G[r][c] - rho[c]);
+            return (row & 63) < rmin ? 0.f : x;
           },
           [&](int c, int i) { return sm.kh[16 * b + i][c] * __expf(rho[c] - sm.G[16 * b + i][c]); },
           [&](int row, int i, float x, float) {
@@ -405,8 +432,11 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_prep_kernel(
     }
     const float* Gl = sm.G[CH - 1];
     const size_t drow0 = (size_t)start * H + h;
+    // rows past the chunk read the last row, then select zero: no branch
+    // around the load (so the loads can be waited for by count)
     auto dO = [&](int r, int v) -> float {
-      return r < len ? bf16_to_f32(dout[(drow0 + (size_t)r * H) * DV + v]) : 0.f;
+      const float x = bf16_to_f32(dout[(drow0 + (size_t)min(r, len - 1) * H) * DV + v]);
+      return r < len ? x : 0.f;
     };
     // Y1 = Tb^T Kbar  [t][c]
     wg_gemm<CH, DK, CH, false, false>(
@@ -429,15 +459,17 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_prep_kernel(
         [&](int t, int c2) { return sp[SP_Y1 + t * DK + c2]; },
         [&](int c, int c2, float x, float) { ft[c * DK + c2] = (c == c2 ? __expf(Gl[c]) : 0.f) - x; },
         sm.stage, tid);
-    // R = scale Qt^T dO - Kt^T Y2  [c][v]  (one product over the stacked rows)
+    // R = scale Qt^T dO - Kt^T Y2  [c][v]
     float* rr = rs + (size_t)item * DK * DV;
-    wg_gemm<DK, DV, 2 * CH, false, false>(
-        [&](int c, int t) {
-          return t < CH ? SCALE * sm.qh[t][c] * __expf(sm.G[t][c])
-                        : -sm.kh[t - CH][c] * __expf(sm.G[t - CH][c]);
-        },
-        [&](int t, int v) { return t < CH ? dO(t, v) : sp[SP_Y2 + (t - CH) * DV + v]; },
+    wg_gemm<DK, DV, CH, false, false>(
+        [&](int c, int t) { return SCALE * sm.qh[t][c] * __expf(sm.G[t][c]); },
+        [&](int t, int v) { return dO(t, v); },
         [&](int c, int v, float x, float) { rr[c * DV + v] = x; }, sm.stage, tid);
+    wg_gemm<DK, DV, CH, false, false>(
+        [&](int c, int t) { return -sm.kh[t][c] * __expf(sm.G[t][c]); },
+        [&](int t, int v) { return sp[SP_Y2 + t * DV + v]; },
+        [&](int c, int v, float x, float prev) { rr[c * DV + v] = prev + x; }, sm.stage, tid,
+        [&](int c, int v) { return rr[c * DV + v]; });
   }
 }
 
@@ -446,7 +478,7 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_prep_kernel(
 // ---------------------------------------------------------------------------
 struct ChainSmem {
   float ds[DK][LD];
-  float stage[STAGE_FLOATS];
+  alignas(16) float stage[STAGE_FLOATS];
 };
 
 __global__ __launch_bounds__(NT, 1) void kda_bwd_chain_kernel(
@@ -495,7 +527,7 @@ struct GradSmem {
   float dD[DK];
   float gl[DK];          // G of the last row
   float kbsum[RG][DK];
-  float stage[STAGE_FLOATS];
+  alignas(16) float stage[STAGE_FLOATS];
 };
 
 __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
@@ -522,11 +554,30 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
     const float* Kk = img + IMG_KK;
     const float* Mm = img + IMG_M;
     __syncthreads();
-    for (int idx = tid; idx < CH * DK; idx += NT) {
-      const int r = idx >> 7, c = idx & 127;
-      sm.qh[r][c] = img[IMG_QH + idx];
-      sm.kh[r][c] = img[IMG_KH + idx];
-      sm.G[r][c] = img[IMG_G + idx];
+    {
+      // qh, kh, G of the image into LDS: all loads first (16-byte vectors)
+      constexpr int PV = CH * DK / 4 / NT;  // float4 per thread per tile
+      float4 vq[PV], vk[PV], vg[PV];
+#pragma unroll
+      for (int j = 0; j < PV; ++j) {
+        const int e = 4 * (tid + NT * j);
+        vq[j] = *reinterpret_cast<const float4*>(img + IMG_QH + e);
+        vk[j] = *reinterpret_cast<const float4*>(img + IMG_KH + e);
+        vg[j] = *reinterpret_cast<const float4*>(img + IMG_G + e);
+      }
+#pragma unroll
+      for (int j = 0; j < PV; ++j) {
+        const int e = 4 * (tid + NT * j), r = e >> 7, c = e & 127;
+        const float q4[4] = {vq[j].x, vq[j].y, vq[j].z, vq[j].w};
+        const float k4[4] = {vk[j].x, vk[j].y, vk[j].z, vk[j].w};
+        const float g4[4] = {vg[j].x, vg[j].y, vg[j].z, vg[j].w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          sm.qh[r][c + u] = q4[u];
+          sm.kh[r][c + u] = k4[u];
+          sm.G[r][c + u] = g4[u];
+        }
+      }
     }
     if (tid < CH) {
       sm.beta[tid] = tid < len ? beta[(size_t)(start + tid) * H + h] : 0.f;
@@ -534,30 +585,37 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
     if (tid < DK) sm.gl[tid] = img[IMG_G + (CH - 1) * DK + tid];
     __syncthreads();
     const size_t row0 = (size_t)start * H + h;
+    // rows past the chunk read the last row, then select zero (no branch
+    // around the loads)
     auto dO = [&](int r, int c) -> float {
-      return r < len ? bf16_to_f32(dout[(row0 + (size_t)r * H) * DV + c]) : 0.f;
+      const float x = bf16_to_f32(dout[(row0 + (size_t)min(r, len - 1) * H) * DV + c]);
+      return r < len ? x : 0.f;
     };
     auto Vv = [&](int r, int c) -> float {
-      return r < len ? bf16_to_f32(v[(row0 + (size_t)r * H) * DV + c]) : 0.f;
+      const float x = bf16_to_f32(v[(row0 + (size_t)min(r, len - 1) * H) * DV + c]);
+      return r < len ? x : 0.f;
     };
     // X = V - Kt S0
     wg_gemm<CH, DV, DK, true, false>(
         [&](int t, int c) { return sm.kh[t][c] * __expf(sm.G[t][c]); },
         [&](int c, int vv) { return S0[c * DV + vv]; },
-        [&](int t, int vv, float x, float) { sc[SC_X + t * DV + vv] = Vv(t, vv) - x; }, sm.stage, tid);
+        [&](int t, int vv, float x, float vt) { sc[SC_X + t * DV + vv] = vt - x; }, sm.stage, tid,
+        [&](int t, int vv) { return Vv(t, vv); });
     // U = Tb X
     wg_gemm<CH, DV, CH, true, false>(
         [&](int t, int i) { return T[t * CH + i] * sm.beta[i]; },
         [&](int i, int vv) { return sc[SC_X + i * DV + vv]; },
         [&](int t, int vv, float x, float) { sc[SC_U + t * DV + vv] = x; }, sm.stage, tid);
-    // dU = scale M^T dO + Kbar dSc  (stacked k: 64 rows of M^T, then 128 channels)
-    wg_gemm<CH, DV, CH + DK, false, false>(
-        [&](int t, int kk) {
-          return kk < CH ? SCALE * Mm[kk * CH + t]
-                         : sm.kh[t][kk - CH] * __expf(sm.gl[kk - CH] - sm.G[t][kk - CH]);
-        },
-        [&](int kk, int vv) { return kk < CH ? dO(kk, vv) : dSc[(kk - CH) * DV + vv]; },
+    // dU = scale M^T dO + Kbar dSc
+    wg_gemm<CH, DV, CH, false, false>(
+        [&](int t, int r) { return SCALE * Mm[r * CH + t]; },
+        [&](int r, int vv) { return dO(r, vv); },
         [&](int t, int vv, float x, float) { sc[SC_DU + t * DV + vv] = x; }, sm.stage, tid);
+    wg_gemm<CH, DV, DK, true, false>(
+        [&](int t, int c) { return sm.kh[t][c] * __expf(sm.gl[c] - sm.G[t][c]); },
+        [&](int c, int vv) { return dSc[c * DV + vv]; },
+        [&](int t, int vv, float x, float prev) { sc[SC_DU + t * DV + vv] = prev + x; }, sm.stage,
+        tid, [&](int t, int vv) { return sc[SC_DU + t * DV + vv]; });
     // dX = Tb^T dU  (= dV)
     wg_gemm<CH, DV, CH, false, false>(
         [&](int t, int r) { return T[r * CH + t] * sm.beta[t]; },
@@ -567,11 +625,15 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
           if (t < len) dv[(row0 + (size_t)t * H) * DV + vv] = x;
         },
         sm.stage, tid);
-    // rows 0..63: dQt = scale dO S0^T; rows 64..127: dKt = -dX S0^T
-    wg_gemm<2 * CH, DK, DV, true, true>(
-        [&](int t, int vv) { return t < CH ? SCALE * dO(t, vv) : -sc[SC_DX + (t - CH) * DV + vv]; },
+    // dQt = scale dO S0^T (rows 0..63 of SC_DQK); dKt = -dX S0^T (rows 64..127)
+    wg_gemm<CH, DK, DV, true, true>(
+        [&](int t, int vv) { return SCALE * dO(t, vv); },
         [&](int vv, int c) { return S0[c * DV + vv]; },
         [&](int t, int c, float x, float) { sc[SC_DQK + t * DK + c] = x; }, sm.stage, tid);
+    wg_gemm<CH, DK, DV, true, true>(
+        [&](int t, int vv) { return -sc[SC_DX + t * DV + vv]; },
+        [&](int vv, int c) { return S0[c * DV + vv]; },
+        [&](int t, int c, float x, float) { sc[SC_DQK + (CH + t) * DK + c] = x; }, sm.stage, tid);
     // dKbar = U dSc^T
     wg_gemm<CH, DK, DV, true, true>(
         [&](int t, int vv) { return sc[SC_U + t * DV + vv]; },
@@ -661,25 +723,28 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
         const float(*dmat)[LDC] = which == 0 ? sm.dm : sm.dkk;
         float* Sa = which == 0 ? Sa1 : Sa2;
         wg_gemm<CH, DK, 16, true, false>(
-            [&](int r, int i) { return r < rmin ? 0.f : dmat[r][16 * b + i]; },
+            [&](int r, int i) {
+              const float x = dmat[r][16 * b + i];
+              return r < rmin ? 0.f : x;
+            },
             [&](int i, int c) { return sm.kh[16 * b + i][c] * __expf(rho[c] - sm.G[16 * b + i][c]); },
             [&](int r, int c, float x, float prev) {
               if (r >= rmin) Sa[r * DK + c] = prev + x * __expf(sm.G[r][c] - rho[c]);
             },
-            sm.stage, tid, [&](int r, int c) { return r < rmin ? 0.f : Sa[r * DK + c]; });
+            sm.stage, tid, [&](int r, int c) { return Sa[r * DK + c]; });
       }
       // rows i of block b: Sb gains exp(rho - G_i) sum_{r below b}
       // (dM_ri qh_r + dKk_ri kh_r) exp(G_r - rho)
       wg_gemm<16, DK, 2 * CH, false, false>(
           [&](int i, int kk) {
             const int r = kk & 63;
-            if (r < rmin) return 0.f;
-            return kk < CH ? sm.dm[r][16 * b + i] : sm.dkk[r][16 * b + i];
+            const float x = kk < CH ? sm.dm[r][16 * b + i] : sm.dkk[r][16 * b + i];
+            return r < rmin ? 0.f : x;
           },
           [&](int kk, int c) {
-            const int r = kk & 63;
-            if (r < rmin) return 0.f;
-            return (kk < CH ? sm.qh[r][c] : sm.kh[r][c]) * __expf(sm.G[r][c] - rho[c]);
+            const int r = max(kk & 63, rmin);  // rows above the block: a valid row, then zero
+            const float x = (kk < CH ? sm.qh[r][c] : sm.kh[r][c]) * __expf(sm.G[r][c] - rho[c]);
+            return (kk & 63) < rmin ? 0.f : x;
           },
           [&](int i, int c, float x, float prev) {
             Sb[(16 * b + i) * DK + c] = prev + x * __expf(rho[c] - sm.G[16 * b + i][c]);
