@@ -6,8 +6,10 @@ lengths (median 1024, clipped to [17, 8192]).  Inputs are resident in HBM
 before the timed region.  Prints ONE JSON line on stdout.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-probe]
-                    [--with-state] [--decode N]
+                    [--with-state] [--decode N] [--backward]
 
+``--backward`` times the chunked backward (kda_chunk_bwd) on the same packed
+stream instead: gradients of q, k, v, g, beta for a seeded d_out.
 ``--decode N`` times one decode step instead: N sequences of one token each
 through the token-recurrent entry point, every state updated in place (the
 state read and write, 128 KiB per sequence and head, are the algorithmic
@@ -139,6 +141,72 @@ def time_steps(step, steps, warmup):
     return ev0.elapsed_time(ev1) / steps
 
 
+PEAK_FP32_MFMA_TFLOPS = 157.3  # dense fp32 MFMA
+BWD_BYTES_PER_TOKEN_HEAD = 2 * DK + 2 * DK + 2 * DV + 4 * DK + 4 + 2 * DV + 4 * (2 * DK + DV + DK) + 4
+
+
+def bwd_chunk_flops(c: int, K: int = DK, V: int = DV) -> int:
+    """Flops of the products of the chunked backward for one chunk of c tokens
+    of one head (fp32 MACs x 2): per-chunk factors (Kk, M, Tb^T Kbar, M^T dO,
+    Tb^T P1, F^T, R), the reverse state chain (F^T dS), and the gradient
+    products (X, U, dU, dX, dQt, dKt, dKbar, dM, dTb, the inverse's backward,
+    the bilinear terms, dD)."""
+    tri = c * c // 2
+    prep = c * c * K + tri * K + tri * V + tri * V + K * K * c + 2 * K * V * c + c ** 3 // 6
+    chain = K * K * V
+    grads = (c * K * V + tri * V + (tri * V + c * K * V) + tri * V + 3 * c * V * K + tri * V
+             + tri * V + c ** 3 + 3 * tri * K + K * V)
+    return 2 * (prep + chain + grads)
+
+
+def backward_bench(args):
+    """kda_chunk_bwd on the packed stream (default workload), d_out seeded."""
+    import torch
+    import linear_attention_sequence_amd as kda
+    from kda_workloads import round_to_bf16, standard_normal, workload_inputs
+    w, inp = workload_inputs(args.workload)
+    dev = torch.device("cuda:0")
+    t = {n: torch.from_numpy(getattr(inp, n)).to(dev) for n in ("q", "k", "v", "g", "beta")}
+    for n in ("q", "k", "v"):
+        t[n] = t[n].to(torch.bfloat16)
+    cu = torch.from_numpy(np.asarray(inp.cu_seqlens, np.int32)).to(dev)
+    do = torch.from_numpy(round_to_bf16(standard_normal(inp.v.shape, w.seed, 11))).to(
+        torch.bfloat16).to(dev)
+
+    def step():
+        kda.chunk_bwd(t["q"], t["k"], t["v"], t["g"], t["beta"], do, cu)
+
+    steps = min(args.steps, 10)
+    ms = time_steps(step, steps, min(args.warmup, 2))
+    status = kda.device_status()
+    sec = ms / 1e3
+    flops = 0
+    for L in w.lengths:
+        full, tail = divmod(int(L), CHUNK)
+        flops += full * bwd_chunk_flops(CHUNK) + (bwd_chunk_flops(tail) if tail else 0)
+    flops *= H
+    tflops = flops / sec / 1e12
+    bytes_alg = BWD_BYTES_PER_TOKEN_HEAD * w.T * H
+    log(f"[bench] backward {w.name}: {ms:.3f} ms/call, {w.T / sec:.4g} tokens/s, "
+        f"{tflops:.1f} TFLOP/s fp32 ({100 * tflops / PEAK_FP32_MFMA_TFLOPS:.1f}% fp32 MFMA), "
+        f"{bytes_alg / sec / 1e9:.0f} GB/s, status {status}")
+    print(json.dumps({
+        "metric": "KDA chunk bwd tokens/sec (H=32, K=V=128)",
+        "value": w.T / sec, "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": min(args.warmup, 2), "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "H": H, "K": DK, "V": DV, "chunk": CHUNK,
+                   "documents": len(w.lengths), "seed": w.seed,
+                   "d_out": "bf16 N(0,1), stream 11 of the same seed"},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_FP32_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / PEAK_FP32_MFMA_TFLOPS, "traffic": None,
+                     "algorithmic_flops": flops, "algorithmic_bytes": bytes_alg,
+                     "kernel": "kda_chunk_bwd call (forward with chunk states + setup, prep, "
+                               "chain, grads kernels)"},
+        "device_status": status,
+    }), flush=True)
+
+
 def decode_bench(args):
     """One decode step of N sequences (one token each, H = 32) through
     kda_recurrent_fwd, the state of every sequence updated in place."""
@@ -192,6 +260,7 @@ def main():
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--with-state", action="store_true")
     ap.add_argument("--decode", type=int, default=0, metavar="N")
+    ap.add_argument("--backward", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the KDA forward here is a single-GPU "
@@ -205,6 +274,9 @@ def main():
     kda.load_library()
     if args.decode:
         decode_bench(args)
+        return
+    if args.backward:
+        backward_bench(args)
         return
     w, inp = workload_inputs(args.workload)
     T = w.T
