@@ -389,6 +389,54 @@ def chunk_bwd(q, k, v, g, beta, d_out, cu_seqlens=None, *, initial_state=None,
     return dq, dk, dv, dg, dbeta, dh0
 
 
+def _autograd_function():
+    import torch
+
+    class _ChunkKDAFunction(torch.autograd.Function):
+        """Autograd over the library's forward and backward: saves only q, k, v,
+        g, beta, cu_seqlens and the initial state; the backward recomputes every
+        intermediate (page "nemo_automodel.components.models.kimi_k3.kda_fused",
+        package docstring)."""
+
+        @staticmethod
+        def forward(ctx, q, k, v, g, beta, cu_seqlens, initial_state, gate_bound,
+                    output_final_state):
+            o, final = chunk_fwd(q, k, v, g, beta, cu_seqlens, gate_bound=gate_bound,
+                                 initial_state=initial_state,
+                                 output_final_state=output_final_state)
+            ctx.save_for_backward(q, k, v, g, beta, cu_seqlens, initial_state)
+            ctx.gate_bound = gate_bound
+            if final is None:
+                return o
+            return o, final
+
+        @staticmethod
+        def backward(ctx, d_o, *rest):
+            q, k, v, g, beta, cu, h0 = ctx.saved_tensors
+            d_final = rest[0] if rest else None
+            if d_final is not None:
+                d_final = d_final.float().contiguous()
+            dq, dk, dv, dg, dbeta, dh0 = chunk_bwd(
+                q, k, v, g, beta, d_o.to(torch.bfloat16).contiguous(), cu, initial_state=h0,
+                d_final_state=d_final, gate_bound=ctx.gate_bound)
+            return (dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), dg.to(g.dtype),
+                    dbeta.to(beta.dtype), None, dh0, None, None)
+
+    return _ChunkKDAFunction
+
+
+def chunk_kda(q, k, v, g, beta, cu_seqlens=None, *, initial_state=None,
+              output_final_state: bool = False, gate_bound: float = DEFAULT_GATE_BOUND):
+    """Differentiable KDA chunked forward: ``(o, final_state or None)``, with
+    the gradients of q, k, v, g, beta (and of ``initial_state``) from
+    ``kda_chunk_bwd``.  Same tensors and document convention as ``chunk_fwd``."""
+    fn = _autograd_function()
+    r = fn.apply(q, k, v, g, beta, cu_seqlens, initial_state, gate_bound, output_final_state)
+    if output_final_state:
+        return r
+    return r, None
+
+
 def device_status(device=None) -> int:
     """Synchronise the current stream and return / clear the sticky device flags."""
     import torch

@@ -139,3 +139,30 @@ def test_backward_4096_token_document_sampled_heads():
     log("[case] bwd T=4096 H=8")
     got = _run(inp, do)
     _check(inp, do, got, None, None, "bwd T=4096", heads=[0, 5])
+
+
+def test_autograd_wrapper_matches_the_oracle():
+    """chunk_kda through torch.autograd: q, k, v keep their bf16 dtype (their
+    gradients are rounded to bf16), g and beta fp32, the initial state fp32."""
+    import torch
+    import linear_attention_sequence_amd as kda
+    from oracle.kda_oracle_bwd import kda_backward
+    lengths = [90, 200]
+    T, H = sum(lengths), 2
+    inp = with_gate_scale(make_inputs(T, H, 79, cu_from_lengths(lengths)), 79, -0.1)
+    do = _dout(T, H, 79)
+    h0 = initial_states(len(lengths), H, 79)
+    d = to_device(inp)
+    leaves = [d[x].detach().clone().requires_grad_(True) for x in ("q", "k", "v", "g", "beta")]
+    s0 = torch.from_numpy(h0).cuda().requires_grad_(True)
+    o, fin = kda.chunk_kda(*leaves, d["cu"], initial_state=s0, output_final_state=True)
+    dfin = torch.from_numpy(initial_states(len(lengths), H, 80)).cuda()
+    torch.autograd.backward([o, fin], [torch.from_numpy(do).to(torch.bfloat16).cuda(), dfin])
+    ref = kda_backward(inp.q, inp.k, inp.v, inp.g, inp.beta, do, inp.cu_seqlens, h0,
+                       dfin.cpu().numpy().astype(np.float64))
+    for name, leaf in zip(NAMES + ("dh0",), leaves + [s0]):
+        got = leaf.grad.float().cpu().numpy().astype(np.float64)
+        rel = np.linalg.norm(got - ref[name]) / np.linalg.norm(ref[name])
+        log(f"[parity] autograd {name}: relL2={rel:.3e} dtype={leaf.grad.dtype}")
+        assert leaf.grad.dtype == leaf.dtype
+        assert rel <= REL_L2_TOL, (name, rel)
