@@ -78,16 +78,15 @@ constexpr int IMG_RK = IMG_RQ + CH;          // [64] 1/||k||
 constexpr int IMG_FLOATS = IMG_RK + CH;
 
 // per-workgroup scratch of the gradient pass, fp32
-constexpr int SC_X = 0;
-constexpr int SC_U = SC_X + CH * DV;
-constexpr int SC_DU = SC_U + CH * DV;
-constexpr int SC_DX = SC_DU + CH * DV;
-constexpr int SC_DQK = SC_DX + CH * DV;      // [128][128]: rows 0..63 dQt, 64..127 dKt
-constexpr int SC_DKB = SC_DQK + 2 * CH * DK;
-constexpr int SC_DTB = SC_DKB + CH * DK;     // [64][64]
+constexpr int SC_DQK = 0;                    // [128][128]: rows 0..63 dQt, 64..127 dKt
+constexpr int SC_DKB = SC_DQK + 2 * CH * DK;  // [64][128] dKbar
+constexpr int SC_SA1 = SC_DKB + CH * DK;      // [64][128] bilinear sums
+constexpr int SC_SA2 = SC_SA1 + CH * DK;
+constexpr int SC_SB = SC_SA2 + CH * DK;
+constexpr int SC_DM = SC_SB + CH * DK;        // [64][64]
+constexpr int SC_DTB = SC_DM + CH * CH;
 constexpr int SC_Z = SC_DTB + CH * CH;
-constexpr int SC_DA = SC_Z + CH * CH;
-constexpr int SC_FLOATS = SC_DA + CH * CH;
+constexpr int SC_FLOATS = SC_Z + CH * CH;
 
 // per-workgroup scratch of the prep pass (Y1 = Tb^T Kbar, P1 = scale M^T dO, Y2 = Tb^T P1)
 constexpr int SP_Y1 = 0;
@@ -516,12 +515,24 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_chain_kernel(
 // ---------------------------------------------------------------------------
 // gradients: per (chunk, head), in parallel
 // ---------------------------------------------------------------------------
+// Two phases share the big LDS area: the products (X, U, dU, dX) and then
+// the bilinear terms (qh, kh, G, dM, dKk).
 struct GradSmem {
-  float qh[CH][LD];
-  float kh[CH][LD];
-  float G[CH][LD];
-  float dm[CH][LDC];     // dM (lower incl.); later dG
-  float dkk[CH][LDC];    // dKk (strictly lower)
+  union {
+    struct {
+      float x[CH][LD];
+      float u[CH][LD];
+      float du[CH][LD];
+      float dx[CH][LD];
+    } a;
+    struct {
+      float qh[CH][LD];
+      float kh[CH][LD];
+      float G[CH][LD];
+      float dm[CH][LDC];   // dM (lower incl.)
+      float dkk[CH][LDC];  // dKk (strictly lower)
+    } b;
+  };
   float beta[CH];
   float dbeta[CH];
   float dD[DK];
@@ -554,37 +565,14 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
     const float* Kk = img + IMG_KK;
     const float* Mm = img + IMG_M;
     __syncthreads();
-    {
-      // qh, kh, G of the image into LDS: all loads first (16-byte vectors)
-      constexpr int PV = CH * DK / 4 / NT;  // float4 per thread per tile
-      float4 vq[PV], vk[PV], vg[PV];
-#pragma unroll
-      for (int j = 0; j < PV; ++j) {
-        const int e = 4 * (tid + NT * j);
-        vq[j] = *reinterpret_cast<const float4*>(img + IMG_QH + e);
-        vk[j] = *reinterpret_cast<const float4*>(img + IMG_KH + e);
-        vg[j] = *reinterpret_cast<const float4*>(img + IMG_G + e);
-      }
-#pragma unroll
-      for (int j = 0; j < PV; ++j) {
-        const int e = 4 * (tid + NT * j), r = e >> 7, c = e & 127;
-        const float q4[4] = {vq[j].x, vq[j].y, vq[j].z, vq[j].w};
-        const float k4[4] = {vk[j].x, vk[j].y, vk[j].z, vk[j].w};
-        const float g4[4] = {vg[j].x, vg[j].y, vg[j].z, vg[j].w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          sm.qh[r][c + u] = q4[u];
-          sm.kh[r][c + u] = k4[u];
-          sm.G[r][c + u] = g4[u];
-        }
-      }
-    }
     if (tid < CH) {
       sm.beta[tid] = tid < len ? beta[(size_t)(start + tid) * H + h] : 0.f;
     }
     if (tid < DK) sm.gl[tid] = img[IMG_G + (CH - 1) * DK + tid];
     __syncthreads();
     const size_t row0 = (size_t)start * H + h;
+    const float* ikh = img + IMG_KH;
+    const float* iG = img + IMG_G;
     // rows past the chunk read the last row, then select zero (no branch
     // around the loads)
     auto dO = [&](int r, int c) -> float {
@@ -595,33 +583,34 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
       const float x = bf16_to_f32(v[(row0 + (size_t)min(r, len - 1) * H) * DV + c]);
       return r < len ? x : 0.f;
     };
+    // ---- phase A: the products, X, U, dU, dX in LDS
     // X = V - Kt S0
     wg_gemm<CH, DV, DK, true, false>(
-        [&](int t, int c) { return sm.kh[t][c] * __expf(sm.G[t][c]); },
+        [&](int t, int c) { return ikh[t * DK + c] * __expf(iG[t * DK + c]); },
         [&](int c, int vv) { return S0[c * DV + vv]; },
-        [&](int t, int vv, float x, float vt) { sc[SC_X + t * DV + vv] = vt - x; }, sm.stage, tid,
+        [&](int t, int vv, float x, float vt) { sm.a.x[t][vv] = vt - x; }, sm.stage, tid,
         [&](int t, int vv) { return Vv(t, vv); });
     // U = Tb X
     wg_gemm<CH, DV, CH, true, false>(
         [&](int t, int i) { return T[t * CH + i] * sm.beta[i]; },
-        [&](int i, int vv) { return sc[SC_X + i * DV + vv]; },
-        [&](int t, int vv, float x, float) { sc[SC_U + t * DV + vv] = x; }, sm.stage, tid);
+        [&](int i, int vv) { return sm.a.x[i][vv]; },
+        [&](int t, int vv, float x, float) { sm.a.u[t][vv] = x; }, sm.stage, tid);
     // dU = scale M^T dO + Kbar dSc
     wg_gemm<CH, DV, CH, false, false>(
         [&](int t, int r) { return SCALE * Mm[r * CH + t]; },
         [&](int r, int vv) { return dO(r, vv); },
-        [&](int t, int vv, float x, float) { sc[SC_DU + t * DV + vv] = x; }, sm.stage, tid);
+        [&](int t, int vv, float x, float) { sm.a.du[t][vv] = x; }, sm.stage, tid);
     wg_gemm<CH, DV, DK, true, false>(
-        [&](int t, int c) { return sm.kh[t][c] * __expf(sm.gl[c] - sm.G[t][c]); },
+        [&](int t, int c) { return ikh[t * DK + c] * __expf(sm.gl[c] - iG[t * DK + c]); },
         [&](int c, int vv) { return dSc[c * DV + vv]; },
-        [&](int t, int vv, float x, float prev) { sc[SC_DU + t * DV + vv] = prev + x; }, sm.stage,
-        tid, [&](int t, int vv) { return sc[SC_DU + t * DV + vv]; });
+        [&](int t, int vv, float x, float prev) { sm.a.du[t][vv] = prev + x; }, sm.stage, tid,
+        [&](int t, int vv) { return sm.a.du[t][vv]; });
     // dX = Tb^T dU  (= dV)
     wg_gemm<CH, DV, CH, false, false>(
         [&](int t, int r) { return T[r * CH + t] * sm.beta[t]; },
-        [&](int r, int vv) { return sc[SC_DU + r * DV + vv]; },
+        [&](int r, int vv) { return sm.a.du[r][vv]; },
         [&](int t, int vv, float x, float) {
-          sc[SC_DX + t * DV + vv] = x;
+          sm.a.dx[t][vv] = x;
           if (t < len) dv[(row0 + (size_t)t * H) * DV + vv] = x;
         },
         sm.stage, tid);
@@ -631,24 +620,25 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
         [&](int vv, int c) { return S0[c * DV + vv]; },
         [&](int t, int c, float x, float) { sc[SC_DQK + t * DK + c] = x; }, sm.stage, tid);
     wg_gemm<CH, DK, DV, true, true>(
-        [&](int t, int vv) { return -sc[SC_DX + t * DV + vv]; },
+        [&](int t, int vv) { return -sm.a.dx[t][vv]; },
         [&](int vv, int c) { return S0[c * DV + vv]; },
         [&](int t, int c, float x, float) { sc[SC_DQK + (CH + t) * DK + c] = x; }, sm.stage, tid);
     // dKbar = U dSc^T
     wg_gemm<CH, DK, DV, true, true>(
-        [&](int t, int vv) { return sc[SC_U + t * DV + vv]; },
+        [&](int t, int vv) { return sm.a.u[t][vv]; },
         [&](int vv, int c) { return dSc[c * DV + vv]; },
         [&](int t, int c, float x, float) { sc[SC_DKB + t * DK + c] = x; }, sm.stage, tid);
     // dM = scale tril(dO U^T)
     wg_gemm<CH, CH, DV, true, true>(
         [&](int r, int vv) { return SCALE * dO(r, vv); },
-        [&](int vv, int i) { return sc[SC_U + i * DV + vv]; },
-        [&](int r, int i, float x, float) { sm.dm[r][i] = i <= r ? x : 0.f; }, sm.stage, tid);
+        [&](int vv, int i) { return sm.a.u[i][vv]; },
+        [&](int r, int i, float x, float) { sc[SC_DM + r * CH + i] = i <= r ? x : 0.f; }, sm.stage, tid);
     // dTb = tril(dU X^T)
     wg_gemm<CH, CH, DV, true, true>(
-        [&](int r, int vv) { return sc[SC_DU + r * DV + vv]; },
-        [&](int vv, int i) { return sc[SC_X + i * DV + vv]; },
+        [&](int r, int vv) { return sm.a.du[r][vv]; },
+        [&](int vv, int i) { return sm.a.x[i][vv]; },
         [&](int r, int i, float x, float) { sc[SC_DTB + r * CH + i] = i <= r ? x : 0.f; }, sm.stage, tid);
+    // ---- phase A's LDS is free from here
     // dD[c] = sum_v dSc[c][v] S0[c][v]; dbeta_i = sum_r dTb_ri T_ri
     {
       const int c = tid / RG, part = tid % RG;
@@ -672,18 +662,53 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
     wg_gemm<CH, CH, CH, false, false>(
         [&](int r, int m) { return -T[m * CH + r]; },
         [&](int m, int i) { return sc[SC_Z + m * CH + i]; },
-        [&](int r, int i, float x, float) { sm.dkk[r][i] = i < r ? x : 0.f; }, sm.stage, tid);
+        [&](int r, int i, float x, float) { sm.b.dkk[r][i] = i < r ? x : 0.f; }, sm.stage, tid);
+    // ---- phase B: qh, kh, G of the image and dM into LDS (16-byte vectors,
+    // all loads first)
+    {
+      constexpr int PV = CH * DK / 4 / NT;  // float4 per thread per tile
+      float4 vq[PV], vk[PV], vg[PV];
+#pragma unroll
+      for (int j = 0; j < PV; ++j) {
+        const int e = 4 * (tid + NT * j);
+        vq[j] = *reinterpret_cast<const float4*>(img + IMG_QH + e);
+        vk[j] = *reinterpret_cast<const float4*>(img + IMG_KH + e);
+        vg[j] = *reinterpret_cast<const float4*>(img + IMG_G + e);
+      }
+      constexpr int PM = CH * CH / NT;
+      float vm[PM];
+#pragma unroll
+      for (int j = 0; j < PM; ++j) vm[j] = sc[SC_DM + tid + NT * j];
+#pragma unroll
+      for (int j = 0; j < PV; ++j) {
+        const int e = 4 * (tid + NT * j), r = e >> 7, c = e & 127;
+        const float q4[4] = {vq[j].x, vq[j].y, vq[j].z, vq[j].w};
+        const float k4[4] = {vk[j].x, vk[j].y, vk[j].z, vk[j].w};
+        const float g4[4] = {vg[j].x, vg[j].y, vg[j].z, vg[j].w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          sm.b.qh[r][c + u] = q4[u];
+          sm.b.kh[r][c + u] = k4[u];
+          sm.b.G[r][c + u] = g4[u];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < PM; ++j) {
+        const int e = tid + NT * j;
+        sm.b.dm[e >> 6][e & 63] = vm[j];
+      }
+    }
     // dbeta_r += sum_i dA_ri Kk_ri; dKk = Diag(beta) dA
     if (tid < CH) {
       const int r = tid;
       float db = 0.f;
-      for (int i = 0; i < r; ++i) db = fmaf(sm.dkk[r][i], Kk[r * CH + i], db);
+      for (int i = 0; i < r; ++i) db = fmaf(sm.b.dkk[r][i], Kk[r * CH + i], db);
       sm.dbeta[r] += db;
     }
     __syncthreads();
     for (int idx = tid; idx < CH * CH; idx += NT) {
       const int r = idx >> 6, i = idx & 63;
-      sm.dkk[r][i] *= sm.beta[r];
+      sm.b.dkk[r][i] *= sm.beta[r];
     }
     if (tid < CH && tid < len) dbeta[row0 + (size_t)tid * H] = sm.dbeta[tid];
     __syncthreads();
@@ -692,44 +717,43 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
     //   Sb  = sum_{rr >= r} (dM_rr,r qh_rr,c + dKk_rr,r kh_rr,c) E_rr,r,c
     // with E_ric = exp(G_rc - G_ic).  Pairs inside one 16-token block directly;
     // pairs across blocks by products with the decay split at the end of the
-    // column block (both factors <= 1).  Sa1, Sa2, Sb go to the X, U, dU
-    // scratch, which is no longer needed.
-    float* Sa1 = sc + SC_X;
-    float* Sa2 = sc + SC_U;
-    float* Sb = sc + SC_DU;
+    // column block (both factors <= 1).  Sa1, Sa2, Sb live in the scratch.
+    float* Sa1 = sc + SC_SA1;
+    float* Sa2 = sc + SC_SA2;
+    float* Sb = sc + SC_SB;
     for (int idx = tid; idx < CH * DK; idx += NT) {
       const int r = idx >> 7, c = idx & 127;
       const int r0 = r & ~15, r1 = r0 + 16;
-      const float Gr = sm.G[r][c];
+      const float Gr = sm.b.G[r][c];
       float sa1 = 0.f, sa2 = 0.f, sb = 0.f;
       for (int i = r0; i <= r; ++i) {
-        const float ki = sm.kh[i][c] * __expf(Gr - sm.G[i][c]);
-        sa1 = fmaf(sm.dm[r][i], ki, sa1);
-        sa2 = fmaf(sm.dkk[r][i], ki, sa2);
+        const float ki = sm.b.kh[i][c] * __expf(Gr - sm.b.G[i][c]);
+        sa1 = fmaf(sm.b.dm[r][i], ki, sa1);
+        sa2 = fmaf(sm.b.dkk[r][i], ki, sa2);
       }
       for (int rr = r; rr < r1; ++rr)
-        sb = fmaf(fmaf(sm.dm[rr][r], sm.qh[rr][c], sm.dkk[rr][r] * sm.kh[rr][c]),
-                  __expf(sm.G[rr][c] - Gr), sb);
+        sb = fmaf(fmaf(sm.b.dm[rr][r], sm.b.qh[rr][c], sm.b.dkk[rr][r] * sm.b.kh[rr][c]),
+                  __expf(sm.b.G[rr][c] - Gr), sb);
       Sa1[idx] = sa1;
       Sa2[idx] = sa2;
       Sb[idx] = sb;
     }
     for (int b = 0; b < 3; ++b) {
       const int rmin = 16 * (b + 1);
-      const float* rho = sm.G[16 * b + 15];
+      const float* rho = sm.b.G[16 * b + 15];
       // rows r below block b: Sa1 (with dM) and Sa2 (with dKk) gain
       // exp(G_r - rho) sum_{i in b} dM|dKk_ri (kh_i exp(rho - G_i))
       for (int which = 0; which < 2; ++which) {
-        const float(*dmat)[LDC] = which == 0 ? sm.dm : sm.dkk;
+        const float(*dmat)[LDC] = which == 0 ? sm.b.dm : sm.b.dkk;
         float* Sa = which == 0 ? Sa1 : Sa2;
         wg_gemm<CH, DK, 16, true, false>(
             [&](int r, int i) {
               const float x = dmat[r][16 * b + i];
               return r < rmin ? 0.f : x;
             },
-            [&](int i, int c) { return sm.kh[16 * b + i][c] * __expf(rho[c] - sm.G[16 * b + i][c]); },
+            [&](int i, int c) { return sm.b.kh[16 * b + i][c] * __expf(rho[c] - sm.b.G[16 * b + i][c]); },
             [&](int r, int c, float x, float prev) {
-              if (r >= rmin) Sa[r * DK + c] = prev + x * __expf(sm.G[r][c] - rho[c]);
+              if (r >= rmin) Sa[r * DK + c] = prev + x * __expf(sm.b.G[r][c] - rho[c]);
             },
             sm.stage, tid, [&](int r, int c) { return Sa[r * DK + c]; });
       }
@@ -738,16 +762,16 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
       wg_gemm<16, DK, 2 * CH, false, false>(
           [&](int i, int kk) {
             const int r = kk & 63;
-            const float x = kk < CH ? sm.dm[r][16 * b + i] : sm.dkk[r][16 * b + i];
+            const float x = kk < CH ? sm.b.dm[r][16 * b + i] : sm.b.dkk[r][16 * b + i];
             return r < rmin ? 0.f : x;
           },
           [&](int kk, int c) {
             const int r = max(kk & 63, rmin);  // rows above the block: a valid row, then zero
-            const float x = (kk < CH ? sm.qh[r][c] : sm.kh[r][c]) * __expf(sm.G[r][c] - rho[c]);
+            const float x = (kk < CH ? sm.b.qh[r][c] : sm.b.kh[r][c]) * __expf(sm.b.G[r][c] - rho[c]);
             return (kk & 63) < rmin ? 0.f : x;
           },
           [&](int i, int c, float x, float prev) {
-            Sb[(16 * b + i) * DK + c] = prev + x * __expf(rho[c] - sm.G[16 * b + i][c]);
+            Sb[(16 * b + i) * DK + c] = prev + x * __expf(rho[c] - sm.b.G[16 * b + i][c]);
           },
           sm.stage, tid, [&](int i, int c) { return Sb[(16 * b + i) * DK + c]; });
     }
@@ -774,8 +798,8 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int r = grp + RG * (j0 + j);
-          const float Gr = sm.G[r][c];
-          const float qr = sm.qh[r][c], kr = sm.kh[r][c];
+          const float Gr = sm.b.G[r][c];
+          const float qr = sm.b.qh[r][c], kr = sm.b.kh[r][c];
           const float sa1 = in[j][0], sa2 = in[j][1], sb = in[j][2];
           const float dqt = in[j][3], dkt = in[j][4], dkb = in[j][5];
           const float eg = __expf(Gr), eb = __expf(gl - Gr);
@@ -815,7 +839,7 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
         const float* dxh = sc + SC_DQK + (which * CH + t) * DK;
         float sdot = 0.f;
         for (int j = 0; j < CPT; ++j) {
-          const float xh = which == 0 ? sm.qh[t][c0 + j] : sm.kh[t][c0 + j];
+          const float xh = which == 0 ? sm.b.qh[t][c0 + j] : sm.b.kh[t][c0 + j];
           sdot = fmaf(xh, dxh[c0 + j], sdot);
         }
 #pragma unroll
@@ -824,7 +848,7 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
           const float rn = img[(which == 0 ? IMG_RQ : IMG_RK) + t];
           float* dst = (which == 0 ? dq : dk) + (row0 + (size_t)t * H) * DK;
           for (int j = 0; j < CPT; ++j) {
-            const float xh = which == 0 ? sm.qh[t][c0 + j] : sm.kh[t][c0 + j];
+            const float xh = which == 0 ? sm.b.qh[t][c0 + j] : sm.b.kh[t][c0 + j];
             dst[c0 + j] = rn * (dxh[c0 + j] - xh * sdot);
           }
         }

@@ -132,9 +132,11 @@ def kda_backward(q, k, v, g, beta, do, cu_seqlens, initial_state=None, d_final_s
 _SHARED: dict = {}
 
 
-def _worker_init():
+def _worker_init(shared=None):
     import torch
     torch.set_num_threads(1)
+    if shared is not None:
+        _SHARED.update(shared)
 
 
 def _run_task(task):
@@ -152,33 +154,26 @@ def _run_task(task):
 def kda_backward_tasks(q, k, v, g, beta, do, tasks, initial_state=None, d_final_state=None,
                        workers: int | None = None):
     """Yield ``(task, grads)`` for tasks ``(a, b, h0, h1, d)``: tokens [a, b) of
-    document d, heads [h0, h1).  Longest first, on ``workers`` processes."""
+    document d, heads [h0, h1).  Longest first, on ``workers`` processes.
+
+    The workers are spawned (not forked): autograd cannot run in a process
+    forked from one that has used it, and the caller may have."""
     import multiprocessing as mp
-    import os
     from concurrent.futures import ProcessPoolExecutor
     from .kda_oracle import default_workers
     tasks = sorted(tasks, key=lambda t: -(t[1] - t[0]) * (t[3] - t[2]))
-    workers = workers or default_workers()
-    _SHARED.update(q=q, k=k, v=v, g=g, beta=beta, do=do, initial_state=initial_state,
-                   d_final_state=d_final_state)
-    try:
-        if workers <= 1 or len(tasks) <= 1:
+    workers = min(workers or default_workers(), len(tasks))
+    shared = dict(q=q, k=k, v=v, g=g, beta=beta, do=do, initial_state=initial_state,
+                  d_final_state=d_final_state)
+    if workers <= 1:
+        _SHARED.update(shared)
+        try:
             for t in tasks:
                 yield _run_task(t)
-            return
-        keep = {x: os.environ.get(x) for x in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS")}
-        os.environ["OMP_NUM_THREADS"] = "1"
-        os.environ["OPENBLAS_NUM_THREADS"] = "1"
-        try:
-            with ProcessPoolExecutor(workers, mp_context=mp.get_context("fork"),
-                                     initializer=_worker_init) as ex:
-                for r in ex.map(_run_task, tasks, chunksize=1):
-                    yield r
         finally:
-            for key, val in keep.items():
-                if val is None:
-                    os.environ.pop(key, None)
-                else:
-                    os.environ[key] = val
-    finally:
-        _SHARED.clear()
+            _SHARED.clear()
+        return
+    with ProcessPoolExecutor(workers, mp_context=mp.get_context("spawn"),
+                             initializer=_worker_init, initargs=(shared,)) as ex:
+        for r in ex.map(_run_task, tasks, chunksize=1):
+            yield r

@@ -166,3 +166,30 @@ def test_autograd_wrapper_matches_the_oracle():
         log(f"[parity] autograd {name}: relL2={rel:.3e} dtype={leaf.grad.dtype}")
         assert leaf.grad.dtype == leaf.dtype
         assert rel <= REL_L2_TOL, (name, rel)
+
+
+@pytest.mark.parametrize("H", [1, 5])
+def test_backward_head_counts(H):
+    lengths = [65, 130]
+    T = sum(lengths)
+    inp = with_gate_scale(make_inputs(T, H, 81, cu_from_lengths(lengths)), 81, -0.2)
+    do = _dout(T, H, 81)
+    got = _run(inp, do)
+    _check(inp, do, got, None, None, f"bwd H={H}")
+
+
+def test_backward_special_inputs():
+    """beta = 0 (nothing is written: dq = dk = dg = 0 without a state) and
+    g = 0 (no decay), one-token and exactly-one-chunk documents."""
+    lengths = [1, 64, 100]
+    T, H = sum(lengths), 2
+    inp = make_inputs(T, H, 82, cu_from_lengths(lengths))
+    inp.beta[:] = 0.0
+    do = _dout(T, H, 82)
+    got = _run(inp, do)
+    for i in (0, 1, 3):
+        assert np.abs(got[i]).max() == 0.0, i
+    _check(inp, do, got, None, None, "bwd beta = 0")
+    inp2 = with_gate_scale(make_inputs(T, H, 83, cu_from_lengths(lengths)), 83, 0.0)
+    got2 = _run(inp2, do)
+    _check(inp2, do, got2, None, None, "bwd g = 0")
