@@ -6,8 +6,10 @@ lengths (median 1024, clipped to [17, 8192]).  Inputs are resident in HBM
 before the timed region.  Prints ONE JSON line on stdout.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-probe]
-                    [--with-state] [--decode N] [--backward]
+                    [--with-state] [--decode N] [--backward] [--peaks]
 
+``--peaks`` measures the practical ceilings instead: a 1 GiB device-to-device
+copy (GB/s) and a large bf16 GEMM through the vendor library (TFLOP/s).
 ``--backward`` times the chunked backward (kda_chunk_bwd) on the same packed
 stream instead: gradients of q, k, v, g, beta for a seeded d_out.
 ``--decode N`` times one decode step instead: N sequences of one token each
@@ -207,6 +209,31 @@ def backward_bench(args):
     }), flush=True)
 
 
+def peaks_bench():
+    """Practical ceilings on this GPU: device copy bandwidth and bf16 GEMM rate."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = COPY_PROBE_BYTES // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    ms_copy = time_steps(lambda: dst.copy_(src), 20, 3)
+    copy_gbs = 2 * COPY_PROBE_BYTES / (ms_copy / 1e3) / 1e9
+    del src, dst
+    m = 8192
+    a = torch.randn(m, m, device=dev).to(torch.bfloat16)
+    b = torch.randn(m, m, device=dev).to(torch.bfloat16)
+    c = torch.empty(m, m, device=dev, dtype=torch.bfloat16)
+    ms_mm = time_steps(lambda: torch.matmul(a, b, out=c), 20, 3)
+    tflops = 2 * m ** 3 / (ms_mm / 1e3) / 1e12
+    log(f"[bench] peaks: 1 GiB copy {copy_gbs:.0f} GB/s ({100 * copy_gbs / PEAK_HBM_GBS:.1f}% of "
+        f"{PEAK_HBM_GBS:.0f}); bf16 GEMM {m}^3 {tflops:.0f} TFLOP/s "
+        f"({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of {PEAK_BF16_TFLOPS:.0f})")
+    print(json.dumps({"copy_gbs": copy_gbs, "copy_bytes": 2 * COPY_PROBE_BYTES,
+                      "bf16_gemm_tflops": tflops, "gemm_shape": [m, m, m],
+                      "peak_hbm_gbs": PEAK_HBM_GBS, "peak_bf16_tflops": PEAK_BF16_TFLOPS}),
+          flush=True)
+
+
 def decode_bench(args):
     """One decode step of N sequences (one token each, H = 32) through
     kda_recurrent_fwd, the state of every sequence updated in place."""
@@ -261,6 +288,7 @@ def main():
     ap.add_argument("--with-state", action="store_true")
     ap.add_argument("--decode", type=int, default=0, metavar="N")
     ap.add_argument("--backward", action="store_true")
+    ap.add_argument("--peaks", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the KDA forward here is a single-GPU "
@@ -277,6 +305,9 @@ def main():
         return
     if args.backward:
         backward_bench(args)
+        return
+    if args.peaks:
+        peaks_bench()
         return
     w, inp = workload_inputs(args.workload)
     T = w.T
