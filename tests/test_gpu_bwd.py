@@ -193,3 +193,34 @@ def test_backward_special_inputs():
     inp2 = with_gate_scale(make_inputs(T, H, 83, cu_from_lengths(lengths)), 83, 0.0)
     got2 = _run(inp2, do)
     _check(inp2, do, got2, None, None, "bwd g = 0")
+
+
+def test_backward_packed_stream_sampled_heads():
+    """The 32768-token packed lognormal stream (H = 32), every document, two
+    sampled heads; the same launch configuration as the backward benchmark."""
+    from kda_workloads import workload_inputs
+    w, inp = workload_inputs(3)
+    do = _dout(w.T, w.H, w.seed)
+    log(f"[case] bwd {w.name}")
+    got = _run(inp, do)
+    _check(inp, do, got, None, None, f"bwd {w.name}", heads=[0, 31])
+
+
+def test_backward_long_document_one_head():
+    """The 65536-token document of the long-plus-short stream (1024 chunks
+    through the state-gradient chain), one sampled head."""
+    from kda_workloads import workload_inputs
+    w, inp = workload_inputs(5)
+    do = _dout(w.T, w.H, w.seed)
+    log(f"[case] bwd {w.name} long document")
+    got = _run(inp, do)
+    cu = [int(x) for x in inp.cu_seqlens]
+    tasks = [(cu[0], cu[1], 7, 8, 0)]
+    for (a, b, h0_, h1_, d), ref in kda_backward_tasks(inp.q, inp.k, inp.v, inp.g, inp.beta, do,
+                                                       tasks):
+        for i, n in enumerate(NAMES):
+            x = got[i][a:b, h0_:h1_] - ref[n]
+            rel = float(np.sqrt((x * x).sum() / (ref[n] * ref[n]).sum()))
+            mx = float(np.abs(x).max())
+            log(f"[parity] bwd long document {n}: relL2={rel:.3e} maxabs={mx:.3e}")
+            assert rel <= REL_L2_TOL and mx <= ABS_TOL * max(1.0, float(np.abs(ref[n]).max())), n
