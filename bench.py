@@ -54,9 +54,9 @@ COPY_PROBE_BYTES = 1 << 30
 # kda_fwd.hip, kda_fwd_state.hip in that order); otherwise null.
 TRAFFIC = {
     "workload": "packed_lognormal_T32768_H32",
-    "kernel_sha256": "f51e3f627315e35ad8497f6a4791221f2518d8d5f2c52fc6dcbefb2d7e206c7d",
-    "fetch_kib": {"kda_schedule_kernel": 8.7, "kda_pre_kernel": 268243.6, "kda_chunk_fwd_kernel": 685585.8},
-    "write_kib": {"kda_schedule_kernel": 2.3, "kda_pre_kernel": 573840.0, "kda_chunk_fwd_kernel": 262175.0},
+    "kernel_sha256": "87a209a7507b3e3a4fa90b4304feed6205f4333f983fe49480f268e723dcba5b",
+    "fetch_kib": {"kda_schedule_kernel": 8.7, "kda_pre_kernel": 268177.2, "kda_chunk_fwd_kernel": 686344.9},
+    "write_kib": {"kda_schedule_kernel": 2.3, "kda_pre_kernel": 573665.0, "kda_chunk_fwd_kernel": 262175.3},
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }
