@@ -35,6 +35,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string>
+#include <type_traits>
 
 #include "kda.h"
 
@@ -721,60 +722,76 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
     float* Sa1 = sc + SC_SA1;
     float* Sa2 = sc + SC_SA2;
     float* Sb = sc + SC_SB;
-    for (int idx = tid; idx < CH * DK; idx += NT) {
-      const int r = idx >> 7, c = idx & 127;
-      const int r0 = r & ~15, r1 = r0 + 16;
-      const float Gr = sm.b.G[r][c];
-      float sa1 = 0.f, sa2 = 0.f, sb = 0.f;
-      for (int i = r0; i <= r; ++i) {
-        const float ki = sm.b.kh[i][c] * __expf(Gr - sm.b.G[i][c]);
-        sa1 = fmaf(sm.b.dm[r][i], ki, sa1);
-        sa2 = fmaf(sm.b.dkk[r][i], ki, sa2);
+    // Pairs inside a block: thread (block bb, channel c) keeps the block's 16
+    // rows of G, kh and qh in registers; each pair i <= r takes one exp, which
+    // serves Sa1 and Sa2 of row r and Sb of row i.
+    {
+      static_assert(NT == 4 * DK, "one thread per (16-row block, channel)");
+      const int bb = tid / DK, c = tid % DK, r0 = 16 * bb;
+      float Gv[16], kv[16], qv[16], sa1[16], sa2[16], sb[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        Gv[j] = sm.b.G[r0 + j][c];
+        kv[j] = sm.b.kh[r0 + j][c];
+        qv[j] = sm.b.qh[r0 + j][c];
+        sa1[j] = sa2[j] = sb[j] = 0.f;
       }
-      for (int rr = r; rr < r1; ++rr)
-        sb = fmaf(fmaf(sm.b.dm[rr][r], sm.b.qh[rr][c], sm.b.dkk[rr][r] * sm.b.kh[rr][c]),
-                  __expf(sm.b.G[rr][c] - Gr), sb);
-      Sa1[idx] = sa1;
-      Sa2[idx] = sa2;
-      Sb[idx] = sb;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+#pragma unroll
+        for (int i = 0; i <= r; ++i) {
+          const float e = __expf(Gv[r] - Gv[i]);  // <= 1
+          const float dmri = sm.b.dm[r0 + r][r0 + i], dkri = sm.b.dkk[r0 + r][r0 + i];
+          const float ki = kv[i] * e;
+          sa1[r] = fmaf(dmri, ki, sa1[r]);
+          sa2[r] = fmaf(dkri, ki, sa2[r]);
+          sb[i] = fmaf(fmaf(dmri, qv[r], dkri * kv[r]), e, sb[i]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        Sa1[(r0 + j) * DK + c] = sa1[j];
+        Sa2[(r0 + j) * DK + c] = sa2[j];
+        Sb[(r0 + j) * DK + c] = sb[j];
+      }
     }
-    for (int b = 0; b < 3; ++b) {
-      const int rmin = 16 * (b + 1);
+    // Pairs across blocks, per column block b: only the NR = 64 - 16 (b + 1)
+    // rows below the block contribute, so the products run over those rows.
+    auto cross = [&](auto bconst) {
+      constexpr int b = decltype(bconst)::value, rmin = 16 * (b + 1), NR = CH - rmin;
       const float* rho = sm.b.G[16 * b + 15];
-      // rows r below block b: Sa1 (with dM) and Sa2 (with dKk) gain
-      // exp(G_r - rho) sum_{i in b} dM|dKk_ri (kh_i exp(rho - G_i))
-      for (int which = 0; which < 2; ++which) {
-        const float(*dmat)[LDC] = which == 0 ? sm.b.dm : sm.b.dkk;
-        float* Sa = which == 0 ? Sa1 : Sa2;
-        wg_gemm<CH, DK, 16, true, false>(
-            [&](int r, int i) {
-              const float x = dmat[r][16 * b + i];
-              return r < rmin ? 0.f : x;
-            },
-            [&](int i, int c) { return sm.b.kh[16 * b + i][c] * __expf(rho[c] - sm.b.G[16 * b + i][c]); },
-            [&](int r, int c, float x, float prev) {
-              if (r >= rmin) Sa[r * DK + c] = prev + x * __expf(sm.b.G[r][c] - rho[c]);
-            },
-            sm.stage, tid, [&](int r, int c) { return Sa[r * DK + c]; });
-      }
+      // rows r below block b: Sa1 (with dM, product rows 0..NR-1) and Sa2 (with
+      // dKk, rows NR..2NR-1) gain exp(G_r - rho) sum_{i in b} dM|dKk_ri (kh_i exp(rho - G_i))
+      wg_gemm<2 * NR, DK, 16, true, false>(
+          [&](int rr, int i) {
+            const int r = rmin + rr % NR;
+            return rr < NR ? sm.b.dm[r][16 * b + i] : sm.b.dkk[r][16 * b + i];
+          },
+          [&](int i, int c) { return sm.b.kh[16 * b + i][c] * __expf(rho[c] - sm.b.G[16 * b + i][c]); },
+          [&](int rr, int c, float x, float prev) {
+            const int r = rmin + rr % NR;
+            (rr < NR ? Sa1 : Sa2)[r * DK + c] = prev + x * __expf(sm.b.G[r][c] - rho[c]);
+          },
+          sm.stage, tid, [&](int rr, int c) { return (rr < NR ? Sa1 : Sa2)[(rmin + rr % NR) * DK + c]; });
       // rows i of block b: Sb gains exp(rho - G_i) sum_{r below b}
       // (dM_ri qh_r + dKk_ri kh_r) exp(G_r - rho)
-      wg_gemm<16, DK, 2 * CH, false, false>(
+      wg_gemm<16, DK, 2 * NR, false, false>(
           [&](int i, int kk) {
-            const int r = kk & 63;
-            const float x = kk < CH ? sm.b.dm[r][16 * b + i] : sm.b.dkk[r][16 * b + i];
-            return r < rmin ? 0.f : x;
+            const int r = rmin + kk % NR;
+            return kk < NR ? sm.b.dm[r][16 * b + i] : sm.b.dkk[r][16 * b + i];
           },
           [&](int kk, int c) {
-            const int r = max(kk & 63, rmin);  // rows above the block: a valid row, then zero
-            const float x = (kk < CH ? sm.b.qh[r][c] : sm.b.kh[r][c]) * __expf(sm.b.G[r][c] - rho[c]);
-            return (kk & 63) < rmin ? 0.f : x;
+            const int r = rmin + kk % NR;
+            return (kk < NR ? sm.b.qh[r][c] : sm.b.kh[r][c]) * __expf(sm.b.G[r][c] - rho[c]);
           },
           [&](int i, int c, float x, float prev) {
             Sb[(16 * b + i) * DK + c] = prev + x * __expf(rho[c] - sm.b.G[16 * b + i][c]);
           },
           sm.stage, tid, [&](int i, int c) { return Sb[(16 * b + i) * DK + c]; });
-    }
+    };
+    cross(std::integral_constant<int, 0>());
+    cross(std::integral_constant<int, 1>());
+    cross(std::integral_constant<int, 2>());
     // combine with the decayed tiles: dqh, dkh and dG of (r, c) replace dQt,
     // dKt and dKbar of (r, c) in the scratch
     {
