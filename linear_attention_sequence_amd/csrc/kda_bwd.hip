@@ -538,7 +538,10 @@ struct GradSmem {
   float dbeta[CH];
   float dD[DK];
   float gl[DK];          // G of the last row
-  float kbsum[RG][DK];
+  union {
+    float kbsum[RG][DK];
+    float part[NT / CH][CH];  // per-row-group partial sums of dbeta
+  };
   alignas(16) float stage[STAGE_FLOATS];
 };
 
@@ -640,19 +643,41 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
         [&](int vv, int i) { return sm.a.x[i][vv]; },
         [&](int r, int i, float x, float) { sc[SC_DTB + r * CH + i] = i <= r ? x : 0.f; }, sm.stage, tid);
     // ---- phase A's LDS is free from here
-    // dD[c] = sum_v dSc[c][v] S0[c][v]; dbeta_i = sum_r dTb_ri T_ri
+    // dD[c] = sum_v dSc[c][v] S0[c][v] (32 threads per row, 16-byte loads);
+    // dbeta_i = sum_r dTb_ri T_ri (both lower: the sum runs over all rows, in 8
+    // row groups of 8 combined through LDS)
     {
-      const int c = tid / RG, part = tid % RG;
-      float acc = 0.f;
-      for (int vv = (DV / RG) * part; vv < (DV / RG) * (part + 1); ++vv)
-        acc = fmaf(dSc[c * DV + vv], S0[c * DV + vv], acc);
+      constexpr int P = DK * DV / 4 / NT;
+      float4 a4[P], b4[P];
 #pragma unroll
-      for (int o = 1; o < RG; o <<= 1) acc += __shfl_xor(acc, o);
-      if (part == 0) sm.dD[c] = acc;
+      for (int j = 0; j < P; ++j) {
+        a4[j] = *reinterpret_cast<const float4*>(dSc + 4 * (tid + NT * j));
+        b4[j] = *reinterpret_cast<const float4*>(S0 + 4 * (tid + NT * j));
+      }
+      const int i = tid & (CH - 1), part = tid / CH;
+      float tv[8], dv8[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        tv[j] = T[(8 * part + j) * CH + i];
+        dv8[j] = sc[SC_DTB + (8 * part + j) * CH + i];
+      }
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        float acc = fmaf(a4[j].x, b4[j].x, fmaf(a4[j].y, b4[j].y, fmaf(a4[j].z, b4[j].z, a4[j].w * b4[j].w)));
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) acc += __shfl_xor(acc, o);
+        if ((tid & 31) == 0) sm.dD[(tid >> 5) + (NT / 32) * j] = acc;
+      }
+      float db = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) db = fmaf(dv8[j], tv[j], db);
+      sm.part[part][i] = db;
+      __syncthreads();
       if (tid < CH) {
-        float db = 0.f;
-        for (int r = tid; r < CH; ++r) db = fmaf(sc[SC_DTB + r * CH + tid], T[r * CH + tid], db);
-        sm.dbeta[tid] = db;
+        float s = 0.f;
+#pragma unroll
+        for (int p = 0; p < NT / CH; ++p) s += sm.part[p][tid];
+        sm.dbeta[tid] = s;
       }
     }
     // Z = (dTb Diag(beta)) T^T;  dA = -T^T Z (strictly lower)
@@ -699,14 +724,22 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
         sm.b.dm[e >> 6][e & 63] = vm[j];
       }
     }
-    // dbeta_r += sum_i dA_ri Kk_ri; dKk = Diag(beta) dA
-    if (tid < CH) {
-      const int r = tid;
+    // dbeta_r += sum_i dA_ri Kk_ri (both strictly lower: all i, 8 threads per row)
+    {
+      const int r = tid / 8, i0 = 8 * (tid % 8);
+      const float4 ka = *reinterpret_cast<const float4*>(Kk + r * CH + i0);
+      const float4 kb = *reinterpret_cast<const float4*>(Kk + r * CH + i0 + 4);
+      const float kv8[8] = {ka.x, ka.y, ka.z, ka.w, kb.x, kb.y, kb.z, kb.w};
       float db = 0.f;
-      for (int i = 0; i < r; ++i) db = fmaf(sm.b.dkk[r][i], Kk[r * CH + i], db);
-      sm.dbeta[r] += db;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) db = fmaf(sm.b.dkk[r][i0 + j], kv8[j], db);
+      db += __shfl_xor(db, 1);
+      db += __shfl_xor(db, 2);
+      db += __shfl_xor(db, 4);
+      if (tid % 8 == 0) sm.dbeta[r] += db;
     }
     __syncthreads();
+    // dKk = Diag(beta) dA
     for (int idx = tid; idx < CH * CH; idx += NT) {
       const int r = idx >> 6, i = idx & 63;
       sm.b.dkk[r][i] *= sm.beta[r];
