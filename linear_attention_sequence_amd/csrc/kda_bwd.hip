@@ -108,6 +108,12 @@ __device__ __forceinline__ f32x4 mfma16f(float a, float b, const f32x4& c) {
 
 __device__ __forceinline__ float bf16_to_f32(bf16 x) { return (float)x; }
 
+// x of another lane in the same row of 16, chosen by the DPP control CTRL
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
 // C (M x N) = sum over K of la(m, k) lb(k, n), then out(m, n, value).
 // fp32 MFMA 16x16x4; operands staged through LDS (stage) in k-tiles of 16,
 // the next k-tiles loaded into registers while the current one multiplies.
@@ -126,8 +132,7 @@ __device__ __forceinline__ void wg_gemm(LA la, LB lb, OUT out, float* stage, int
                                         OLD old = OLD()) {
   static_assert(M % 16 == 0 && N % 16 == 0 && K % 16 == 0 && M <= 128 && N <= 128, "shape");
   constexpr int TM = M / 16, TN = N / 16, TILES = TM * TN;
-  static_assert(TILES % NW == 0, "whole tiles per wave");
-  constexpr int PER = TILES / NW;
+  constexpr int PER = (TILES + NW - 1) / NW;  // output tiles per wave (the last round may be partial)
   constexpr int NA = (16 * M + NT - 1) / NT, NB = (16 * N + NT - 1) / NT;  // staged per thread
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
   float* sa = stage;              // [M][SROW]: row m holds k = k0 .. k0 + 15
@@ -185,6 +190,7 @@ __device__ __forceinline__ void wg_gemm(LA la, LB lb, OUT out, float* stage, int
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int t = w + NW * p, tm = t / TN, tn = t - tm * TN;
+      if (TILES % NW != 0 && t >= TILES) break;  // wave-uniform
       const float4 av = *reinterpret_cast<const float4*>(&sa[(16 * tm + (l & 15)) * SROW + kq]);
       const float4 bv = *reinterpret_cast<const float4*>(&sb[(16 * tn + (l & 15)) * SROW + kq]);
       acc[p] = mfma16f(av.x, bv.x, acc[p]);
@@ -208,12 +214,14 @@ __device__ __forceinline__ void wg_gemm(LA la, LB lb, OUT out, float* stage, int
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
     const int t = w + NW * p, tm = t / TN, tn = t - tm * TN;
+    if (TILES % NW != 0 && t >= TILES) break;
 #pragma unroll
     for (int i = 0; i < 4; ++i) prev[p][i] = old(16 * tm + 4 * (l >> 4) + i, 16 * tn + (l & 15));
   }
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
     const int t = w + NW * p, tm = t / TN, tn = t - tm * TN;
+    if (TILES % NW != 0 && t >= TILES) break;
 #pragma unroll
     for (int i = 0; i < 4; ++i) out(16 * tm + 4 * (l >> 4) + i, 16 * tn + (l & 15), acc[p][i], prev[p][i]);
   }
@@ -329,12 +337,25 @@ __device__ __forceinline__ void load_chunk(PrepSmem& sm, float* img, const bf16*
     sm.beta[t] = t < len ? beta[(size_t)(start + t) * H + h] : 0.f;
   }
   __syncthreads();
-  if (tid < DK) {
-    float acc = 0.f;
-    for (int r = 0; r < CH; ++r) {
-      acc += sm.G[r][tid];
-      sm.G[r][tid] = acc;
-    }
+  // cumsum over the rows of each channel: RG groups of CH / RG rows, the
+  // group totals combined through LDS (sm.t is free until T is built)
+  {
+    constexpr int RR = CH / RG;
+    const int c = tid % DK, part = tid / DK;
+    float x[RR];
+#pragma unroll
+    for (int j = 0; j < RR; ++j) x[j] = sm.G[RR * part + j][c];
+#pragma unroll
+    for (int j = 1; j < RR; ++j) x[j] += x[j - 1];
+    float* tot = &sm.t[0][0];
+    tot[part * DK + c] = x[RR - 1];
+    __syncthreads();
+    float off = 0.f;
+#pragma unroll
+    for (int p2 = 0; p2 < RG - 1; ++p2)
+      if (p2 < part) off += tot[p2 * DK + c];
+#pragma unroll
+    for (int j = 0; j < RR; ++j) sm.G[RR * part + j][c] = x[j] + off;
   }
   __syncthreads();
   for (int idx = tid; idx < CH * DK; idx += NT) {
@@ -372,57 +393,60 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_prep_kernel(
         sm.m[r][i] = 0.f;
       }
     }
-    // diagonal blocks directly: exp(G_r - G_i) <= 1 per channel for i <= r
-    for (int idx = tid; idx < 4 * 16 * 16; idx += NT) {
-      const int blk = idx >> 8, r = 16 * blk + ((idx >> 4) & 15), i = 16 * blk + (idx & 15);
-      float a = 0.f, mm = 0.f;
-      if (i <= r) {
-        for (int c = 0; c < DK; ++c) {
-          const float ki = sm.kh[i][c] * __expf(sm.G[r][c] - sm.G[i][c]);
-          a = fmaf(sm.kh[r][c], ki, a);
-          mm = fmaf(sm.qh[r][c], ki, mm);
-        }
-      }
-      img[IMG_KK + r * CH + i] = i < r ? a : 0.f;
-      sm.m[r][i] = i <= r ? mm : 0.f;
-    }
-    // blocks below the diagonal: for column block b the decay splits at
-    // rho = G of its last row, exp(G_r - rho) <= 1 for rows below the block and
-    // exp(rho - G_i) <= 1 inside it.  Rows 0..63 of the product are Kk, 64..127 M.
-    for (int b = 0; b < 3; ++b) {
-      const int rmin = 16 * (b + 1);
-      const float* rho = sm.G[16 * b + 15];
-      wg_gemm<2 * CH, 16, DK, true, true>(
+    // Row block a (rows 16a .. 16a + 15) against column blocks 0 .. a, one
+    // product per row block: the decay exp(G_r - G_i) splits at rho = G of row
+    // 16a + 7.  Both factors stay within e^{+-44} for the pairs of the diagonal
+    // block (bounded gate, |g| <= 5.5 per token) and are <= 1 or underflow
+    // harmlessly for the blocks to the left (the product is what underflows);
+    // entries above the diagonal are discarded, never used.  Product rows
+    // 0..15 are Kk, 16..31 M.
+    auto rowblock = [&](auto aconst) {
+      constexpr int a = decltype(aconst)::value;
+      const float* rho = sm.G[16 * a + 7];
+      wg_gemm<32, 16 * (a + 1), DK, true, true>(
           [&](int row, int c) {
-            const int r = max(row & 63, rmin);  // rows above the block: a valid row, then zero
-            const float x = (row < CH ? sm.kh[r][c] : sm.qh[r][c]) * __expf(sm.G[r][c] - rho[c]);
-            return (row & 63) < rmin ? 0.f : x;
+            const int r = 16 * a + (row & 15);
+            return (row < 16 ? sm.kh[r][c] : sm.qh[r][c]) * __expf(sm.G[r][c] - rho[c]);
           },
-          [&](int c, int i) { return sm.kh[16 * b + i][c] * __expf(rho[c] - sm.G[16 * b + i][c]); },
+          [&](int c, int i) { return sm.kh[i][c] * __expf(rho[c] - sm.G[i][c]); },
           [&](int row, int i, float x, float) {
-            const int r = row & 63;
-            if (r < rmin) return;
-            if (row < CH) img[IMG_KK + r * CH + 16 * b + i] = x;
-            else sm.m[r][16 * b + i] = x;
+            const int r = 16 * a + (row & 15);
+            if (row < 16) img[IMG_KK + r * CH + i] = i < r ? x : 0.f;
+            else sm.m[r][i] = i <= r ? x : 0.f;
           },
           sm.stage, tid);
-    }
+    };
+    rowblock(std::integral_constant<int, 0>());
+    rowblock(std::integral_constant<int, 1>());
+    rowblock(std::integral_constant<int, 2>());
+    rowblock(std::integral_constant<int, 3>());
     // T = (I + Diag(beta) Kk)^-1: column i solves (I + Diag(beta) Kk) x = e_i by
-    // forward substitution; one thread per column, no barriers
+    // forward substitution.  Eight consecutive lanes share a column: lane j
+    // sums the terms m = j (mod 8) of each row, the eight partial sums are
+    // combined by DPP (every lane ends with the same total), and lane r % 8
+    // keeps x_r.  No barriers.
     for (int idx = tid; idx < CH * CH; idx += NT) sm.kk[idx >> 6][idx & 63] = img[IMG_KK + idx];
     __syncthreads();
-    if (tid < CH) {
-      const int i = tid;
-      float col[CH];
+    {
+      static_assert(NT == 8 * CH, "eight lanes per column");
+      const int i = tid >> 3, j = tid & 7;
+      float colj[CH / 8];  // x_{8 u + j}; zero until solved
+#pragma unroll
+      for (int u = 0; u < CH / 8; ++u) colj[u] = 0.f;
 #pragma unroll
       for (int r = 0; r < CH; ++r) {
+        // terms m >= r vanish: Kk is strictly lower and x_m is still zero
         float acc = 0.f;
 #pragma unroll
-        for (int m = 0; m < r; ++m) acc = fmaf(sm.kk[r][m], col[m], acc);
-        col[r] = r < i ? 0.f : (r == i ? 1.f : -sm.beta[r] * acc);
+        for (int u = 0; 8 * u < r; ++u) acc = fmaf(sm.kk[r][8 * u + j], colj[u], acc);
+        acc += dpp_mov<0xB1>(acc);   // lanes k ^ 1
+        acc += dpp_mov<0x4E>(acc);   // lanes k ^ 2
+        acc += dpp_mov<0x141>(acc);  // lane 7 - k of the same eight
+        const float xr = r < i ? 0.f : (r == i ? 1.f : -sm.beta[r] * acc);
+        if (j == (r & 7)) colj[r >> 3] = xr;
       }
 #pragma unroll
-      for (int r = 0; r < CH; ++r) sm.t[r][i] = col[r];
+      for (int u = 0; u < CH / 8; ++u) sm.t[8 * u + j][i] = colj[u];
     }
     __syncthreads();
     for (int idx = tid; idx < CH * CH; idx += NT) {
@@ -618,15 +642,15 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
           if (t < len) dv[(row0 + (size_t)t * H) * DV + vv] = x;
         },
         sm.stage, tid);
-    // dQt = scale dO S0^T (rows 0..63 of SC_DQK); dKt = -dX S0^T (rows 64..127)
-    wg_gemm<CH, DK, DV, true, true>(
-        [&](int t, int vv) { return SCALE * dO(t, vv); },
+    // dQt = scale dO S0^T (rows 0..63 of SC_DQK) and dKt = -dX S0^T (rows
+    // 64..127) as one product: S0 is streamed once for both
+    wg_gemm<2 * CH, DK, DV, true, true>(
+        [&](int t, int vv) {
+          const float a = SCALE * dO(min(t, CH - 1), vv), b = -sm.a.dx[t & (CH - 1)][vv];
+          return t < CH ? a : b;
+        },
         [&](int vv, int c) { return S0[c * DV + vv]; },
         [&](int t, int c, float x, float) { sc[SC_DQK + t * DK + c] = x; }, sm.stage, tid);
-    wg_gemm<CH, DK, DV, true, true>(
-        [&](int t, int vv) { return -sm.a.dx[t][vv]; },
-        [&](int vv, int c) { return S0[c * DV + vv]; },
-        [&](int t, int c, float x, float) { sc[SC_DQK + (CH + t) * DK + c] = x; }, sm.stage, tid);
     // dKbar = U dSc^T
     wg_gemm<CH, DK, DV, true, true>(
         [&](int t, int vv) { return sm.a.u[t][vv]; },
