@@ -60,6 +60,7 @@ constexpr int CPT = DK / TPT;                // channels per thread in a token r
 constexpr int RG = NT / DK;                  // row groups when a thread owns one channel (4)
 constexpr int LD = 129;                      // padded row of a [64][128] LDS tile
 constexpr int LDC = 65;                      // padded row of a [64][64] LDS tile
+constexpr int LDM = 68;                      // [64][64] LDS tile read in 16-byte row pieces
 constexpr float SCALE = 0.08838834764831845f;  // 128^-1/2
 constexpr float L2_EPS = 1e-6f;
 constexpr int SROW = 20;                     // staged row: 16 k values + 4 padding (conflict-free b128)
@@ -81,10 +82,7 @@ constexpr int IMG_FLOATS = IMG_RK + CH;
 // per-workgroup scratch of the gradient pass, fp32
 constexpr int SC_DQK = 0;                    // [128][128]: rows 0..63 dQt, 64..127 dKt
 constexpr int SC_DKB = SC_DQK + 2 * CH * DK;  // [64][128] dKbar
-constexpr int SC_SA1 = SC_DKB + CH * DK;      // [64][128] bilinear sums
-constexpr int SC_SA2 = SC_SA1 + CH * DK;
-constexpr int SC_SB = SC_SA2 + CH * DK;
-constexpr int SC_DM = SC_SB + CH * DK;        // [64][64]
+constexpr int SC_DM = SC_DKB + CH * DK;       // [64][64]
 constexpr int SC_DTB = SC_DM + CH * CH;
 constexpr int SC_Z = SC_DTB + CH * CH;
 constexpr int SC_FLOATS = SC_Z + CH * CH;
@@ -554,9 +552,15 @@ struct GradSmem {
       float qh[CH][LD];
       float kh[CH][LD];
       float G[CH][LD];
-      float dm[CH][LDC];   // dM (lower incl.)
-      float dkk[CH][LDC];  // dKk (strictly lower)
+      float dm[CH][LDM];   // dM (lower incl.)
+      float dkk[CH][LDM];  // dKk (strictly lower)
     } b;
+    struct {               // after the bilinear sums: dqh over G, dkh over dM, dKk
+      float qh[CH][LD];
+      float kh[CH][LD];
+      float dqh[CH][LD];
+      float dkh[CH][LD];
+    } c;
   };
   float beta[CH];
   float dbeta[CH];
@@ -566,6 +570,7 @@ struct GradSmem {
     float kbsum[RG][DK];
     float part[NT / CH][CH];  // per-row-group partial sums of dbeta
   };
+  float dgtot[RG][DK];        // per-row-block totals of dG
   alignas(16) float stage[STAGE_FLOATS];
 };
 
@@ -770,161 +775,163 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
     }
     if (tid < CH && tid < len) dbeta[row0 + (size_t)tid * H] = sm.dbeta[tid];
     __syncthreads();
-    // bilinear forms of M and Kk: for (r, c)
+    // Bilinear forms of M and Kk, for (r, c):
     //   Sa1 = sum_{i <= r} dM_ri kh_ic E_ric,  Sa2 = sum_{i < r} dKk_ri kh_ic E_ric,
     //   Sb  = sum_{rr >= r} (dM_rr,r qh_rr,c + dKk_rr,r kh_rr,c) E_rr,r,c
-    // with E_ric = exp(G_rc - G_ic).  Pairs inside one 16-token block directly;
-    // pairs across blocks by products with the decay split at the end of the
-    // column block (both factors <= 1).  Sa1, Sa2, Sb live in the scratch.
-    float* Sa1 = sc + SC_SA1;
-    float* Sa2 = sc + SC_SA2;
-    float* Sb = sc + SC_SB;
-    // Pairs inside a block: thread (block bb, channel c) keeps the block's 16
-    // rows of G, kh and qh in registers; each pair i <= r takes one exp, which
-    // serves Sa1 and Sa2 of row r and Sb of row i.
-    {
-      static_assert(NT == 4 * DK, "one thread per (16-row block, channel)");
-      const int bb = tid / DK, c = tid % DK, r0 = 16 * bb;
-      float Gv[16], kv[16], qv[16], sa1[16], sa2[16], sb[16];
+    // with E_ric = exp(G_rc - G_ic), then combined with the decayed tiles into
+    // dqh, dkh and dG.  Thread (block bb, channel c) owns rows 16 bb .. 16 bb + 15
+    // of channel c and keeps everything of them in registers; bb is uniform
+    // over a wave, so the rows of dM and dKk it reads are broadcasts.
+    static_assert(NT == 4 * DK, "one thread per (16-row block, channel)");
+    asm volatile("" : "+v"(tid));  // lane values from here on are recomputed, not kept live
+    const int bb = __builtin_amdgcn_readfirstlane(tid / DK), c = tid % DK, r0 = 16 * bb;
+    float Gv[16], kv[16], qv[16], sa1[16], sa2[16], sb[16];
+    // 16 entries of row R of dM or dKk from column C0 (a multiple of 16)
+    auto row16 = [&](const float (*mat)[LDM], int R, int C0, float (&out)[16]) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        Gv[j] = sm.b.G[r0 + j][c];
-        kv[j] = sm.b.kh[r0 + j][c];
-        qv[j] = sm.b.qh[r0 + j][c];
-        sa1[j] = sa2[j] = sb[j] = 0.f;
+      for (int u = 0; u < 4; ++u) {
+        const float4 x = *reinterpret_cast<const float4*>(&mat[R][C0 + 4 * u]);
+        out[4 * u] = x.x;
+        out[4 * u + 1] = x.y;
+        out[4 * u + 2] = x.z;
+        out[4 * u + 3] = x.w;
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-#pragma unroll
-        for (int i = 0; i <= r; ++i) {
-          const float e = __expf(Gv[r] - Gv[i]);  // <= 1
-          const float dmri = sm.b.dm[r0 + r][r0 + i], dkri = sm.b.dkk[r0 + r][r0 + i];
-          const float ki = kv[i] * e;
-          sa1[r] = fmaf(dmri, ki, sa1[r]);
-          sa2[r] = fmaf(dkri, ki, sa2[r]);
-          sb[i] = fmaf(fmaf(dmri, qv[r], dkri * kv[r]), e, sb[i]);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        Sa1[(r0 + j) * DK + c] = sa1[j];
-        Sa2[(r0 + j) * DK + c] = sa2[j];
-        Sb[(r0 + j) * DK + c] = sb[j];
-      }
-    }
-    // Pairs across blocks, per column block b: only the NR = 64 - 16 (b + 1)
-    // rows below the block contribute, so the products run over those rows.
-    auto cross = [&](auto bconst) {
-      constexpr int b = decltype(bconst)::value, rmin = 16 * (b + 1), NR = CH - rmin;
-      const float* rho = sm.b.G[16 * b + 15];
-      // rows r below block b: Sa1 (with dM, product rows 0..NR-1) and Sa2 (with
-      // dKk, rows NR..2NR-1) gain exp(G_r - rho) sum_{i in b} dM|dKk_ri (kh_i exp(rho - G_i))
-      wg_gemm<2 * NR, DK, 16, true, false>(
-          [&](int rr, int i) {
-            const int r = rmin + rr % NR;
-            return rr < NR ? sm.b.dm[r][16 * b + i] : sm.b.dkk[r][16 * b + i];
-          },
-          [&](int i, int c) { return sm.b.kh[16 * b + i][c] * __expf(rho[c] - sm.b.G[16 * b + i][c]); },
-          [&](int rr, int c, float x, float prev) {
-            const int r = rmin + rr % NR;
-            (rr < NR ? Sa1 : Sa2)[r * DK + c] = prev + x * __expf(sm.b.G[r][c] - rho[c]);
-          },
-          sm.stage, tid, [&](int rr, int c) { return (rr < NR ? Sa1 : Sa2)[(rmin + rr % NR) * DK + c]; });
-      // rows i of block b: Sb gains exp(rho - G_i) sum_{r below b}
-      // (dM_ri qh_r + dKk_ri kh_r) exp(G_r - rho)
-      wg_gemm<16, DK, 2 * NR, false, false>(
-          [&](int i, int kk) {
-            const int r = rmin + kk % NR;
-            return kk < NR ? sm.b.dm[r][16 * b + i] : sm.b.dkk[r][16 * b + i];
-          },
-          [&](int kk, int c) {
-            const int r = rmin + kk % NR;
-            return (kk < NR ? sm.b.qh[r][c] : sm.b.kh[r][c]) * __expf(sm.b.G[r][c] - rho[c]);
-          },
-          [&](int i, int c, float x, float prev) {
-            Sb[(16 * b + i) * DK + c] = prev + x * __expf(rho[c] - sm.b.G[16 * b + i][c]);
-          },
-          sm.stage, tid, [&](int i, int c) { return Sb[(16 * b + i) * DK + c]; });
     };
-    cross(std::integral_constant<int, 0>());
-    cross(std::integral_constant<int, 1>());
-    cross(std::integral_constant<int, 2>());
-    // combine with the decayed tiles: dqh, dkh and dG of (r, c) replace dQt,
-    // dKt and dKbar of (r, c) in the scratch
-    {
-      const int c = tid % DK, grp = tid / DK;
-      const float gl = sm.gl[c];
-      float kbsum = 0.f;  // sum over this thread's rows of dKbar Kbar
-#pragma unroll 1
-      for (int j0 = 0; j0 < CH / RG; j0 += 8) {
-        // the batch's loads before its stores (same buffer: not reordered otherwise)
-        float in[8][6];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int r = grp + RG * (j0 + j);
-          in[j][0] = Sa1[r * DK + c];
-          in[j][1] = Sa2[r * DK + c];
-          in[j][2] = Sb[r * DK + c];
-          in[j][3] = sc[SC_DQK + r * DK + c];
-          in[j][4] = sc[SC_DQK + (CH + r) * DK + c];
-          in[j][5] = sc[SC_DKB + r * DK + c];
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int r = grp + RG * (j0 + j);
-          const float Gr = sm.b.G[r][c];
-          const float qr = sm.b.qh[r][c], kr = sm.b.kh[r][c];
-          const float sa1 = in[j][0], sa2 = in[j][1], sb = in[j][2];
-          const float dqt = in[j][3], dkt = in[j][4], dkb = in[j][5];
-          const float eg = __expf(Gr), eb = __expf(gl - Gr);
-          kbsum = fmaf(dkb, kr * eb, kbsum);
-          sc[SC_DQK + r * DK + c] = sa1 + dqt * eg;
-          sc[SC_DQK + (CH + r) * DK + c] = sa2 + sb + dkt * eg + dkb * eb;
-          sc[SC_DKB + r * DK + c] = qr * sa1 + kr * sa2 - kr * sb + dqt * qr * eg + dkt * kr * eg - dkb * kr * eb;
-        }
-      }
-      sm.kbsum[grp][c] = kbsum;
+    for (int j = 0; j < 16; ++j) {
+      Gv[j] = sm.b.G[r0 + j][c];
+      kv[j] = sm.b.kh[r0 + j][c];
+      qv[j] = sm.b.qh[r0 + j][c];
+      sa1[j] = sa2[j] = sb[j] = 0.f;
     }
-    __syncthreads();
-    // dg = reverse cumsum of dG within the chunk; the last row gains
-    // sum_r dKbar_r Kbar_r + dD D (G_last is the cumsum up to the last token)
-    if (tid < DK) {
-      const int c = tid;
-      float acc = sm.dD[c] * __expf(sm.gl[c]);
+    // pairs inside the block: one exp per pair i <= r serves Sa1, Sa2 of row r
+    // and Sb of row i
 #pragma unroll
-      for (int gi = 0; gi < RG; ++gi) acc += sm.kbsum[gi][c];
-#pragma unroll 1
-      for (int r0 = CH - 16; r0 >= 0; r0 -= 16) {
-        float x[16];
+    for (int r = 0; r < 16; ++r) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) x[j] = sc[SC_DKB + (r0 + j) * DK + c];
+      for (int i = 0; i <= r; ++i) {
+        const float e = __expf(Gv[r] - Gv[i]);  // <= 1
+        const float dmri = sm.b.dm[r0 + r][r0 + i], dkri = sm.b.dkk[r0 + r][r0 + i];
+        const float ki = kv[i] * e;
+        sa1[r] = fmaf(dmri, ki, sa1[r]);
+        sa2[r] = fmaf(dkri, ki, sa2[r]);
+        sb[i] = fmaf(fmaf(dmri, qv[r], dkri * kv[r]), e, sb[i]);
+      }
+    }
+    // Pairs across blocks, written for each row block BB at compile time (the
+    // branch on bb is uniform over a wave).  Sa1, Sa2 from the column blocks b
+    // before BB: the decay splits at rho = G of the last row of block b,
+    // exp(G_r - rho) <= 1 and exp(rho - G_i) <= 1.  Sb from the row blocks
+    // after BB: the decay splits at rho = G of the last row of block BB.
+    auto cross = [&](auto bconst) {
+      constexpr int BB = decltype(bconst)::value, R0 = 16 * BB;
 #pragma unroll
-        for (int j = 15; j >= 0; --j) {
-          acc += x[j];
-          if (r0 + j < len) dg[(row0 + (size_t)(r0 + j) * H) * DK + c] = acc;
+      for (int b = 0; b < BB; ++b) {
+        const float rho = sm.b.G[16 * b + 15][c];
+        float kb[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) kb[i] = sm.b.kh[16 * b + i][c] * __expf(rho - sm.b.G[16 * b + i][c]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float dmr[16], dkr[16];
+          row16(sm.b.dm, R0 + r, 16 * b, dmr);
+          row16(sm.b.dkk, R0 + r, 16 * b, dkr);
+          float t1 = 0.f, t2 = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            t1 = fmaf(dmr[i], kb[i], t1);
+            t2 = fmaf(dkr[i], kb[i], t2);
+          }
+          const float e = __expf(Gv[r] - rho);
+          sa1[r] = fmaf(e, t1, sa1[r]);
+          sa2[r] = fmaf(e, t2, sa2[r]);
         }
       }
+      if (BB < 3) {
+        const float rho = Gv[15];
+        float sbx[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sbx[i] = 0.f;
+#pragma unroll
+        for (int R = R0 + 16; R < CH; ++R) {
+          const float e = __expf(sm.b.G[R][c] - rho);
+          const float qa = sm.b.qh[R][c] * e, ka = sm.b.kh[R][c] * e;
+          float dmr[16], dkr[16];
+          row16(sm.b.dm, R, R0, dmr);
+          row16(sm.b.dkk, R, R0, dkr);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sbx[i] = fmaf(dmr[i], qa, fmaf(dkr[i], ka, sbx[i]));
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sb[i] = fmaf(__expf(rho - Gv[i]), sbx[i], sb[i]);
+      }
+    };
+    if (bb == 0) cross(std::integral_constant<int, 0>());
+    else if (bb == 1) cross(std::integral_constant<int, 1>());
+    else if (bb == 2) cross(std::integral_constant<int, 2>());
+    else cross(std::integral_constant<int, 3>());
+    // combine with the decayed tiles (Qt = qh e^G, Kt = -kh e^G, Kbar = kh e^{G_last - G}):
+    // dqh, dkh and dG of the thread's rows; dG is summed from the last row up
+    const float gl = sm.gl[c];
+    float dqt[16], dkt[16], dkb[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      dqt[j] = sc[SC_DQK + (r0 + j) * DK + c];
+      dkt[j] = sc[SC_DQK + (CH + r0 + j) * DK + c];
+      dkb[j] = sc[SC_DKB + (r0 + j) * DK + c];
+    }
+    float dqh[16], dkh[16], kbs = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float eg = __expf(Gv[j]), eb = __expf(gl - Gv[j]);
+      const float qr = qv[j], kr = kv[j];
+      kbs = fmaf(dkb[j], kr * eb, kbs);
+      dqh[j] = sa1[j] + dqt[j] * eg;
+      dkh[j] = sa2[j] + sb[j] + dkt[j] * eg + dkb[j] * eb;
+      // dG, kept in sa1
+      sa1[j] = qr * sa1[j] + kr * sa2[j] - kr * sb[j] + dqt[j] * qr * eg + dkt[j] * kr * eg - dkb[j] * kr * eb;
+    }
+#pragma unroll
+    for (int j = 14; j >= 0; --j) sa1[j] += sa1[j + 1];
+    __syncthreads();  // G, dM and dKk are read by every thread until here
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      sm.c.dqh[r0 + j][c] = dqh[j];
+      sm.c.dkh[r0 + j][c] = dkh[j];
+    }
+    sm.kbsum[bb][c] = kbs;
+    sm.dgtot[bb][c] = sa1[0];
+    __syncthreads();
+    // dg = reverse cumsum of dG within the chunk; the last row also gains
+    // sum_r dKbar_r Kbar_r + dD D (G_last is the cumsum up to the last token)
+    {
+      float base = sm.dD[c] * __expf(gl);
+#pragma unroll
+      for (int g2 = 0; g2 < RG; ++g2) base += sm.kbsum[g2][c];
+#pragma unroll
+      for (int g2 = 1; g2 < RG; ++g2)
+        if (g2 > bb) base += sm.dgtot[g2][c];
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (r0 + j < len) dg[(row0 + (size_t)(r0 + j) * H) * DK + c] = base + sa1[j];
     }
     // l2 norms: dq = rq (dqh - qh (qh . dqh)), dk likewise; TPT threads per token
     {
       const int t = tid / TPT, c0 = CPT * (tid % TPT);
 #pragma unroll 1
       for (int which = 0; which < 2; ++which) {
-        const float* dxh = sc + SC_DQK + (which * CH + t) * DK;
+        const float (*dxh)[LD] = which == 0 ? sm.c.dqh : sm.c.dkh;
+        const float (*xh)[LD] = which == 0 ? sm.c.qh : sm.c.kh;
         float sdot = 0.f;
-        for (int j = 0; j < CPT; ++j) {
-          const float xh = which == 0 ? sm.b.qh[t][c0 + j] : sm.b.kh[t][c0 + j];
-          sdot = fmaf(xh, dxh[c0 + j], sdot);
-        }
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) sdot = fmaf(xh[t][c0 + j], dxh[t][c0 + j], sdot);
 #pragma unroll
         for (int o = 1; o < TPT; o <<= 1) sdot += __shfl_xor(sdot, o);
         if (t < len) {
           const float rn = img[(which == 0 ? IMG_RQ : IMG_RK) + t];
           float* dst = (which == 0 ? dq : dk) + (row0 + (size_t)t * H) * DK;
-          for (int j = 0; j < CPT; ++j) {
-            const float xh = which == 0 ? sm.b.qh[t][c0 + j] : sm.b.kh[t][c0 + j];
-            dst[c0 + j] = rn * (dxh[c0 + j] - xh * sdot);
-          }
+#pragma unroll
+          for (int j = 0; j < CPT; ++j) dst[c0 + j] = rn * (dxh[t][c0 + j] - xh[t][c0 + j] * sdot);
         }
       }
     }
