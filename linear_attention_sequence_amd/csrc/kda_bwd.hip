@@ -112,6 +112,13 @@ __device__ __forceinline__ float dpp_mov(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
+// LDS written by the lanes of a wave visible to the same wave
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // C (M x N) = sum over K of la(m, k) lb(k, n), then out(m, n, value).
 // fp32 MFMA 16x16x4; operands staged through LDS (stage) in k-tiles of 16,
 // the next k-tiles loaded into registers while the current one multiplies.
@@ -785,91 +792,152 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
     static_assert(NT == 4 * DK, "one thread per (16-row block, channel)");
     asm volatile("" : "+v"(tid));  // lane values from here on are recomputed, not kept live
     const int bb = __builtin_amdgcn_readfirstlane(tid / DK), c = tid % DK, r0 = 16 * bb;
-    float Gv[16], kv[16], qv[16], sa1[16], sa2[16], sb[16];
-    // 16 entries of row R of dM or dKk from column C0 (a multiple of 16)
-    auto row16 = [&](const float (*mat)[LDM], int R, int C0, float (&out)[16]) {
+    float sa1[16], sa2[16], sb[16];
+    // pairs inside the block: one exp per pair i <= r serves Sa1, Sa2 of row r
+    // and Sb of row i
+    {
+      float Gv[16], kv[16], qv[16];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float4 x = *reinterpret_cast<const float4*>(&mat[R][C0 + 4 * u]);
-        out[4 * u] = x.x;
-        out[4 * u + 1] = x.y;
-        out[4 * u + 2] = x.z;
-        out[4 * u + 3] = x.w;
+      for (int j = 0; j < 16; ++j) {
+        Gv[j] = sm.b.G[r0 + j][c];
+        kv[j] = sm.b.kh[r0 + j][c];
+        qv[j] = sm.b.qh[r0 + j][c];
+        sa1[j] = sa2[j] = sb[j] = 0.f;
       }
-    };
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+#pragma unroll
+        for (int i = 0; i <= r; ++i) {
+          const float e = __expf(Gv[r] - Gv[i]);  // <= 1
+          const float dmri = sm.b.dm[r0 + r][r0 + i], dkri = sm.b.dkk[r0 + r][r0 + i];
+          const float ki = kv[i] * e;
+          sa1[r] = fmaf(dmri, ki, sa1[r]);
+          sa2[r] = fmaf(dkri, ki, sa2[r]);
+          sb[i] = fmaf(fmaf(dmri, qv[r], dkri * kv[r]), e, sb[i]);
+        }
+      }
+    }
+    // Pairs across blocks, on fp32 MFMA (16x16x4).  The wave's rows are block
+    // BB (uniform over the wave; the code is written per BB at compile time) and
+    // its channels CW .. CW + 63, four 16-channel tiles.  In the MFMA C layout
+    // lane l = 16 g + j holds rows 4 g + i (i = 0..3) of the block for channel
+    // CW + 16 t + j of tile t; k-step s pairs lane group g with k = 4 g + s on
+    // both operands.
+    //   Sa1, Sa2 from column block b < BB: the decay splits at rho = G of the
+    //   last row of block b; A = the (BB, b) block of dM / dKk, B = kh_i
+    //   exp(rho - G_i) <= 1, the product scaled by exp(G_r - rho) <= 1.
+    //   Sb from row blocks a > BB: the decay splits at rho = G of the last row of
+    //   block BB; A = the (a, BB) block of dM / dKk transposed, B = qh_r | kh_r
+    //   exp(G_r - rho) <= 1, the sum scaled by exp(rho - G_i) <= 1.
+    // The sums then move to the thread layout through a per-wave slice of the
+    // staging area (unused in this phase).
+    {
+      const int l = tid & 63, g = l >> 4, j = l & 15;
+      const int CW = c - l;  // first channel of the wave
+      static_assert(NW * 2 * 16 * 17 <= STAGE_FLOATS, "per-wave slices fit the staging area");
+      float* xp = sm.stage + (tid >> 6) * (2 * 16 * 17);  // this wave's slice
+      // C layout -> thread layout: dst[r] += x of (row r, channel c)
+      auto to_rows = [&](const f32x4 (&x)[4], float (&dst)[16]) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          wave_sync_lds();
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xp[(tt * 16 + 4 * g + i) * 17 + j] = x[2 * h + tt][i];
+          wave_sync_lds();
+          if ((l >> 5) == h) {
+            const int tt = (l >> 4) & 1;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dst[r] += xp[(tt * 16 + r) * 17 + j];
+          }
+        }
+      };
+      auto cross = [&](auto bconst) {
+        constexpr int BB = decltype(bconst)::value, R0 = 16 * BB;
+        float Gc[4][4];  // G of the C layout's rows and channels
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Gc[t][i] = sm.b.G[R0 + 4 * g + i][CW + 16 * t + j];
+        if (BB > 0) {
+          f32x4 acc1[4], acc2[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc1[t] = acc2[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int b = 0; b < BB; ++b) {
+            const float4 am = *reinterpret_cast<const float4*>(&sm.b.dm[R0 + j][16 * b + 4 * g]);
+            const float4 ak = *reinterpret_cast<const float4*>(&sm.b.dkk[R0 + j][16 * b + 4 * g]);
+            const float amv[4] = {am.x, am.y, am.z, am.w}, akv[4] = {ak.x, ak.y, ak.z, ak.w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const int cc = CW + 16 * t + j;
+              const float rho = sm.b.G[16 * b + 15][cc];
+              f32x4 p1 = {0.f, 0.f, 0.f, 0.f}, p2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int s2 = 0; s2 < 4; ++s2) {
+                const int ri = 16 * b + 4 * g + s2;
+                const float kb = sm.b.kh[ri][cc] * __expf(rho - sm.b.G[ri][cc]);
+                p1 = mfma16f(amv[s2], kb, p1);
+                p2 = mfma16f(akv[s2], kb, p2);
+              }
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float e = __expf(Gc[t][i] - rho);
+                acc1[t][i] = fmaf(e, p1[i], acc1[t][i]);
+                acc2[t][i] = fmaf(e, p2[i], acc2[t][i]);
+              }
+            }
+          }
+          to_rows(acc1, sa1);
+          to_rows(acc2, sa2);
+        }
+        if (BB < 3) {
+          f32x4 acc3[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc3[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+          float rho[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) rho[t] = sm.b.G[R0 + 15][CW + 16 * t + j];
+#pragma unroll
+          for (int a2 = BB + 1; a2 < 4; ++a2) {
+            float amv[4], akv[4];
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+              amv[s2] = sm.b.dm[16 * a2 + 4 * g + s2][R0 + j];
+              akv[s2] = sm.b.dkk[16 * a2 + 4 * g + s2][R0 + j];
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const int cc = CW + 16 * t + j;
+#pragma unroll
+              for (int s2 = 0; s2 < 4; ++s2) {
+                const int rr = 16 * a2 + 4 * g + s2;
+                const float e = __expf(sm.b.G[rr][cc] - rho[t]);
+                acc3[t] = mfma16f(amv[s2], sm.b.qh[rr][cc] * e, acc3[t]);
+                acc3[t] = mfma16f(akv[s2], sm.b.kh[rr][cc] * e, acc3[t]);
+              }
+            }
+          }
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc3[t][i] *= __expf(rho[t] - Gc[t][i]);
+          to_rows(acc3, sb);
+        }
+      };
+      if (bb == 0) cross(std::integral_constant<int, 0>());
+      else if (bb == 1) cross(std::integral_constant<int, 1>());
+      else if (bb == 2) cross(std::integral_constant<int, 2>());
+      else cross(std::integral_constant<int, 3>());
+    }
+    float Gv[16], kv[16], qv[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       Gv[j] = sm.b.G[r0 + j][c];
       kv[j] = sm.b.kh[r0 + j][c];
       qv[j] = sm.b.qh[r0 + j][c];
-      sa1[j] = sa2[j] = sb[j] = 0.f;
     }
-    // pairs inside the block: one exp per pair i <= r serves Sa1, Sa2 of row r
-    // and Sb of row i
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-#pragma unroll
-      for (int i = 0; i <= r; ++i) {
-        const float e = __expf(Gv[r] - Gv[i]);  // <= 1
-        const float dmri = sm.b.dm[r0 + r][r0 + i], dkri = sm.b.dkk[r0 + r][r0 + i];
-        const float ki = kv[i] * e;
-        sa1[r] = fmaf(dmri, ki, sa1[r]);
-        sa2[r] = fmaf(dkri, ki, sa2[r]);
-        sb[i] = fmaf(fmaf(dmri, qv[r], dkri * kv[r]), e, sb[i]);
-      }
-    }
-    // Pairs across blocks, written for each row block BB at compile time (the
-    // branch on bb is uniform over a wave).  Sa1, Sa2 from the column blocks b
-    // before BB: the decay splits at rho = G of the last row of block b,
-    // exp(G_r - rho) <= 1 and exp(rho - G_i) <= 1.  Sb from the row blocks
-    // after BB: the decay splits at rho = G of the last row of block BB.
-    auto cross = [&](auto bconst) {
-      constexpr int BB = decltype(bconst)::value, R0 = 16 * BB;
-#pragma unroll
-      for (int b = 0; b < BB; ++b) {
-        const float rho = sm.b.G[16 * b + 15][c];
-        float kb[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) kb[i] = sm.b.kh[16 * b + i][c] * __expf(rho - sm.b.G[16 * b + i][c]);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float dmr[16], dkr[16];
-          row16(sm.b.dm, R0 + r, 16 * b, dmr);
-          row16(sm.b.dkk, R0 + r, 16 * b, dkr);
-          float t1 = 0.f, t2 = 0.f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            t1 = fmaf(dmr[i], kb[i], t1);
-            t2 = fmaf(dkr[i], kb[i], t2);
-          }
-          const float e = __expf(Gv[r] - rho);
-          sa1[r] = fmaf(e, t1, sa1[r]);
-          sa2[r] = fmaf(e, t2, sa2[r]);
-        }
-      }
-      if (BB < 3) {
-        const float rho = Gv[15];
-        float sbx[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sbx[i] = 0.f;
-#pragma unroll
-        for (int R = R0 + 16; R < CH; ++R) {
-          const float e = __expf(sm.b.G[R][c] - rho);
-          const float qa = sm.b.qh[R][c] * e, ka = sm.b.kh[R][c] * e;
-          float dmr[16], dkr[16];
-          row16(sm.b.dm, R, R0, dmr);
-          row16(sm.b.dkk, R, R0, dkr);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sbx[i] = fmaf(dmr[i], qa, fmaf(dkr[i], ka, sbx[i]));
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sb[i] = fmaf(__expf(rho - Gv[i]), sbx[i], sb[i]);
-      }
-    };
-    if (bb == 0) cross(std::integral_constant<int, 0>());
-    else if (bb == 1) cross(std::integral_constant<int, 1>());
-    else if (bb == 2) cross(std::integral_constant<int, 2>());
-    else cross(std::integral_constant<int, 3>());
     // combine with the decayed tiles (Qt = qh e^G, Kt = -kh e^G, Kbar = kh e^{G_last - G}):
     // dqh, dkh and dG of the thread's rows; dG is summed from the last row up
     const float gl = sm.gl[c];
