@@ -51,6 +51,9 @@ def load_library():
     """Load ``libkda.so`` (raises if it was not built)."""
     global _lib
     if _lib is None:
+        # torch first: its HIP runtime and the one libkda.so links carry the same
+        # soname, and the library must use the runtime torch's tensors live in
+        import torch  # noqa: F401
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(
                 f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
