@@ -28,8 +28,9 @@
 //   2. kda_bwd_setup_kernel: cu_seqlens check and the chunk table;
 //   3. kda_bwd_prep_kernel (parallel over chunks): qh, kh, G, T, Kk, M and
 //      F^T, R of every chunk;
-//   4. kda_bwd_chain_kernel (per document and head, last chunk first):
-//      dS <- F^T dS + R, storing dS at every chunk end;
+//   4. kda_bwd_chain_kernel (per document, head and half of the value
+//      columns, last chunk first): dS <- F^T dS + R, storing dS at every
+//      chunk end;
 //   5. kda_bwd_grads_kernel (parallel over chunks): all input gradients.
 // Products run on fp32 MFMA (16x16x4) with operands staged through LDS.
 #include <hip/hip_runtime.h>
@@ -503,10 +504,16 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_prep_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// chain: per (document, head), last chunk first: dS <- F^T dS + R
+// chain: per (document, head, half of the value columns), last chunk first:
+// dS <- F^T dS + R.  F^T acts on the key index, so the value columns of dS
+// evolve independently: each (document, head) chain is split over two
+// workgroups of CV columns (blockIdx.y), which halves the product on the
+// sequential path of a chunk.
 // ---------------------------------------------------------------------------
+constexpr int CV = DV / 2;  // value columns per chain workgroup
+
 struct ChainSmem {
-  float ds[DK][LD];
+  float ds[DK][CV + 1];
   alignas(16) float stage[STAGE_FLOATS];
 };
 
@@ -517,29 +524,36 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_chain_kernel(
   __shared__ ChainSmem sm;
   if (*bad) return;
   const int tid = threadIdx.x;
-  const int d = blockIdx.x / H, h = blockIdx.x - d * H;
+  const int d = blockIdx.x / H, h = blockIdx.x - d * H, v0 = CV * (int)blockIdx.y;
   const int a = cu ? cu[d] : 0, b = cu ? cu[d + 1] : T;
   const int first = a / CH + d;
   const int n = (b - a + CH - 1) / CH;
-  for (int idx = tid; idx < DK * DV; idx += NT) {
-    const int c = idx >> 7, v = idx & 127;
-    sm.ds[c][v] = dht ? dht[((size_t)d * H + h) * DK * DV + idx] : 0.f;
+  const size_t dh = ((size_t)d * H + h) * DK * DV;
+  for (int idx = tid; idx < DK * CV; idx += NT) {
+    const int c = idx / CV, v = idx % CV;
+    sm.ds[c][v] = dht ? dht[dh + c * DV + v0 + v] : 0.f;
   }
   for (int j = n - 1; j >= 0; --j) {
     const size_t item = (size_t)(first + j) * H + h;
     __syncthreads();
     float* dst = dstates + item * DK * DV;
-    for (int idx = tid; idx < DK * DV; idx += NT) dst[idx] = sm.ds[idx >> 7][idx & 127];
+    for (int idx = tid; idx < DK * CV; idx += NT) {
+      const int c = idx / CV, v = idx % CV;
+      dst[c * DV + v0 + v] = sm.ds[c][v];
+    }
     const float* ft = fts + item * DK * DK;
-    const float* rr = rs + item * DK * DV;
-    wg_gemm<DK, DV, DK, true, false>([&](int c, int c2) { return ft[c * DK + c2]; },
-                        [&](int c2, int v) { return sm.ds[c2][v]; },
-                        [&](int c, int v, float x, float) { sm.ds[c][v] = x + rr[c * DV + v]; }, sm.stage, tid);
+    const float* rr = rs + item * DK * DV + v0;
+    wg_gemm<DK, CV, DK, true, false>([&](int c, int c2) { return ft[c * DK + c2]; },
+                                     [&](int c2, int v) { return sm.ds[c2][v]; },
+                                     [&](int c, int v, float x, float) { sm.ds[c][v] = x + rr[c * DV + v]; },
+                                     sm.stage, tid);
   }
   __syncthreads();
   if (dh0 != nullptr)
-    for (int idx = tid; idx < DK * DV; idx += NT)
-      dh0[((size_t)d * H + h) * DK * DV + idx] = sm.ds[idx >> 7][idx & 127];
+    for (int idx = tid; idx < DK * CV; idx += NT) {
+      const int c = idx / CV, v = idx % CV;
+      dh0[dh + c * DV + v0 + v] = sm.ds[c][v];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1121,7 +1135,7 @@ extern "C" int kda_chunk_bwd(const void* q, const void* k, const void* v, const 
     }
   }
   if (e == hipSuccess && rc == KDA_OK) {
-    hipLaunchKernelGGL(kda_bwd_chain_kernel, dim3(n_docs * H), dim3(NT), 0, stream, cu_seqlens,
+    hipLaunchKernelGGL(kda_bwd_chain_kernel, dim3(n_docs * H, DV / CV), dim3(NT), 0, stream, cu_seqlens,
                        (int)T, (int)H, bad, fts, rs, d_final_state, dstates, d_initial_state);
     e = hipGetLastError();
   }
