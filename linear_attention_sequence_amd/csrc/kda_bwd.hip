@@ -426,33 +426,74 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_prep_kernel(
     rowblock(std::integral_constant<int, 1>());
     rowblock(std::integral_constant<int, 2>());
     rowblock(std::integral_constant<int, 3>());
-    // T = (I + Diag(beta) Kk)^-1: column i solves (I + Diag(beta) Kk) x = e_i by
-    // forward substitution.  Eight consecutive lanes share a column: lane j
-    // sums the terms m = j (mod 8) of each row, the eight partial sums are
-    // combined by DPP (every lane ends with the same total), and lane r % 8
-    // keeps x_r.  No barriers.
+    // T = (I + B)^-1 with B = Diag(beta) Kk (strictly lower), in 16-row blocks.
+    // Diagonal blocks T_aa = (I + B_aa)^-1 by forward substitution: eight
+    // consecutive lanes share a column, lane j sums the terms m = j (mod 8) of a
+    // row, DPP combines the eight partial sums (every lane ends with the same
+    // total) and lane r % 8 keeps x_r.  Then the blocks below the diagonal,
+    // T_ab = -T_aa sum_{b <= k < a} B_ak T_kb, by column block (one wave each)
+    // on fp32 MFMA.  Blocks above the diagonal are zero.
     for (int idx = tid; idx < CH * CH; idx += NT) sm.kk[idx >> 6][idx & 63] = img[IMG_KK + idx];
+    for (int idx = tid; idx < CH * CH; idx += NT) {
+      const int r = idx >> 6, i = idx & 63;
+      if ((i >> 4) > (r >> 4)) sm.t[r][i] = 0.f;
+    }
     __syncthreads();
     {
       static_assert(NT == 8 * CH, "eight lanes per column");
-      const int i = tid >> 3, j = tid & 7;
-      float colj[CH / 8];  // x_{8 u + j}; zero until solved
+      const int R0 = 16 * (tid >> 7), i = (tid >> 3) & 15, j = tid & 7;
+      float x0 = 0.f, x1 = 0.f;  // x of rows R0 + j and R0 + 8 + j; zero until solved
 #pragma unroll
-      for (int u = 0; u < CH / 8; ++u) colj[u] = 0.f;
-#pragma unroll
-      for (int r = 0; r < CH; ++r) {
+      for (int r = 0; r < 16; ++r) {
         // terms m >= r vanish: Kk is strictly lower and x_m is still zero
-        float acc = 0.f;
-#pragma unroll
-        for (int u = 0; 8 * u < r; ++u) acc = fmaf(sm.kk[r][8 * u + j], colj[u], acc);
+        float acc = sm.kk[R0 + r][R0 + j] * x0;
+        if (r > 8) acc = fmaf(sm.kk[R0 + r][R0 + 8 + j], x1, acc);
         acc += dpp_mov<0xB1>(acc);   // lanes k ^ 1
         acc += dpp_mov<0x4E>(acc);   // lanes k ^ 2
         acc += dpp_mov<0x141>(acc);  // lane 7 - k of the same eight
-        const float xr = r < i ? 0.f : (r == i ? 1.f : -sm.beta[r] * acc);
-        if (j == (r & 7)) colj[r >> 3] = xr;
+        const float xr = r < i ? 0.f : (r == i ? 1.f : -sm.beta[R0 + r] * acc);
+        if (j == (r & 7)) {
+          if (r < 8) x0 = xr;
+          else x1 = xr;
+        }
       }
+      sm.t[R0 + j][R0 + i] = x0;
+      sm.t[R0 + 8 + j][R0 + i] = x1;
+    }
+    __syncthreads();
+    // Column block BC of T below the diagonal, wave BC.  MFMA 16x16x4: k-step s
+    // of lane group g takes k = 4 g + s on both operands, so the C layout of a
+    // product (lane l: rows 4 g .. 4 g + 3 of column l % 16) is the B operand
+    // of the next and the blocks T_k,BC stay in registers.
+    {
+      const int w = tid >> 6, l = tid & 63, g = l >> 4, cl = l & 15;
+      auto column = [&](auto bconst) {
+        constexpr int BC = decltype(bconst)::value;
+        f32x4 tcol[4];
 #pragma unroll
-      for (int u = 0; u < CH / 8; ++u) sm.t[8 * u + j][i] = colj[u];
+        for (int i = 0; i < 4; ++i) tcol[BC][i] = sm.t[16 * BC + 4 * g + i][16 * BC + cl];
+#pragma unroll
+        for (int a = BC + 1; a < 4; ++a) {
+          const float ba = sm.beta[16 * a + cl];
+          f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = BC; kb < a; ++kb)
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2)
+              y = mfma16f(ba * sm.kk[16 * a + cl][16 * kb + 4 * g + s2], tcol[kb][s2], y);
+          f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2) z = mfma16f(sm.t[16 * a + cl][16 * a + 4 * g + s2], y[s2], z);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            tcol[a][i] = -z[i];
+            sm.t[16 * a + 4 * g + i][16 * BC + cl] = -z[i];
+          }
+        }
+      };
+      if (w == 0) column(std::integral_constant<int, 0>());
+      else if (w == 1) column(std::integral_constant<int, 1>());
+      else if (w == 2) column(std::integral_constant<int, 2>());
     }
     __syncthreads();
     for (int idx = tid; idx < CH * CH; idx += NT) {
