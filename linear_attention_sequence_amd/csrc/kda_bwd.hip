@@ -399,33 +399,40 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_prep_kernel(
         sm.m[r][i] = 0.f;
       }
     }
-    // Row block a (rows 16a .. 16a + 15) against column blocks 0 .. a, one
-    // product per row block: the decay exp(G_r - G_i) splits at rho = G of row
-    // 16a + 7.  Both factors stay within e^{+-44} for the pairs of the diagonal
-    // block (bounded gate, |g| <= 5.5 per token) and are <= 1 or underflow
-    // harmlessly for the blocks to the left (the product is what underflows);
-    // entries above the diagonal are discarded, never used.  Product rows
-    // 0..15 are Kk, 16..31 M.
-    auto rowblock = [&](auto aconst) {
-      constexpr int a = decltype(aconst)::value;
-      const float* rho = sm.G[16 * a + 7];
-      wg_gemm<32, 16 * (a + 1), DK, true, true>(
-          [&](int row, int c) {
-            const int r = 16 * a + (row & 15);
-            return (row < 16 ? sm.kh[r][c] : sm.qh[r][c]) * __expf(sm.G[r][c] - rho[c]);
-          },
-          [&](int c, int i) { return sm.kh[i][c] * __expf(rho[c] - sm.G[i][c]); },
-          [&](int row, int i, float x, float) {
-            const int r = 16 * a + (row & 15);
-            if (row < 16) img[IMG_KK + r * CH + i] = i < r ? x : 0.f;
-            else sm.m[r][i] = i <= r ? x : 0.f;
-          },
-          sm.stage, tid);
-    };
-    rowblock(std::integral_constant<int, 0>());
-    rowblock(std::integral_constant<int, 1>());
-    rowblock(std::integral_constant<int, 2>());
-    rowblock(std::integral_constant<int, 3>());
+    // Kk and M by 16x16 tiles (a, b), b <= a, one wave per tile pair on fp32
+    // MFMA (the Kk and M tiles share the right operand).  The decay
+    // exp(G_r - G_i) splits at rho = G of row 16a + 7: both factors stay within
+    // e^{+-44} for the pairs of a diagonal tile (bounded gate, |g| <= 5.5 per
+    // token), and for the tiles to the left they are <= 1 or underflow
+    // harmlessly (the product is what underflows); entries above the diagonal
+    // are discarded, never used.  k-step ks of lane group g takes channel
+    // c = 4 ks + g on both operands.
+    {
+      const int w = tid >> 6, l = tid & 63, g = l >> 4, cl = l & 15;
+      for (int p = w; p < 10; p += NW) {  // wave-uniform
+        const int a = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3, b = p - a * (a + 1) / 2;
+        const int ra = 16 * a + cl, ib = 16 * b + cl;
+        const float* rho = sm.G[16 * a + 7];
+        f32x4 kk = {0.f, 0.f, 0.f, 0.f}, mm = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+        for (int ks = 0; ks < DK / 4; ++ks) {
+          const int c = 4 * ks + g;
+          const float rc = rho[c];
+          const float ea = __expf(sm.G[ra][c] - rc), eb = __expf(rc - sm.G[ib][c]);
+          const float bop = sm.kh[ib][c] * eb;
+          kk = mfma16f(sm.kh[ra][c] * ea, bop, kk);
+          mm = mfma16f(sm.qh[ra][c] * ea, bop, mm);
+        }
+        // C layout: lane (g, cl) holds rows 16a + 4g + i of column 16b + cl
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * a + 4 * g + i, col = 16 * b + cl;
+          img[IMG_KK + r * CH + col] = col < r ? kk[i] : 0.f;
+          sm.m[r][col] = col <= r ? mm[i] : 0.f;
+        }
+      }
+    }
+    __syncthreads();
     // T = (I + B)^-1 with B = Diag(beta) Kk (strictly lower), in 16-row blocks.
     // Diagonal blocks T_aa = (I + B_aa)^-1 by forward substitution: eight
     // consecutive lanes share a column, lane j sums the terms m = j (mod 8) of a
