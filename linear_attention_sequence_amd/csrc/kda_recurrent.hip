@@ -41,7 +41,7 @@ constexpr float L2_EPS = 1e-6f;
 typedef __bf16 bf16;
 
 // cu_seqlens holds exactly n_docs + 1 entries: 0, non-decreasing, ending at T.
-// One workgroup; writes the verdict to *bad (0 or 1) and the sticky flag.
+// One workgroup; writes the outcome of the check to *bad (0 or 1) and the sticky flag.
 __global__ __launch_bounds__(CHECK_THREADS) void kda_recurrent_check_kernel(
     const int32_t* __restrict__ cu, int n_docs, int T, int* __restrict__ bad,
     int* __restrict__ status_word) {
