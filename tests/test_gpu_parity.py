@@ -93,8 +93,11 @@ def test_all_length_one_documents():
     assert rel <= 5e-3
 
 
-@pytest.mark.parametrize("gate_scale,T", [(-0.05, 2048), (0.0, 512)])
+@pytest.mark.parametrize("gate_scale,T", [(-0.05, 2048), (0.0, 512), (0.0, 8192)])
 def test_slow_decay_exercises_the_state(gate_scale, T):
+    """The state carries across every chunk; g = 0 (no decay at all) is the
+    hardest case for the bf16 copy of S in the products (relL2 grows slowly
+    with the document length: ~3.8e-3 at 512 tokens, ~4.2e-3 at 8192)."""
     H = 4
     inp = with_gate_scale(_small(T, H, 23, [T]), 23, gate_scale)
     o = run_gpu(inp)
