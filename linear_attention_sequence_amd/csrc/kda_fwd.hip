@@ -32,11 +32,13 @@
 //                        itself, a split unit only chains precomputed images,
 //                        so a long document's sequential chain is short.
 //
-// Precision: Qt, Kt, KbT and the state's MFMA copy are bf16; S stays fp32 in
-// registers.  M (|M| <= 1) and Tb are fp16, and so are X and U where they meet
-// them (Tb X, M U): fp16 carries three more mantissa bits than bf16 and those
-// two products dominate the error.  Values that would not fit fp16 are scaled
-// by exact powers of two (Tb per chunk, X and U per wave; almost never taken).
+// Precision: Qt, Kt and the state's MFMA copy are bf16; S stays fp32 in
+// registers.  M (|M| <= 1), KbT (<= 1) and Tb are fp16, and so are X and U
+// where they meet them (Tb X, M U, KbT U): fp16 carries three more mantissa
+// bits than bf16, and these products dominate the error (the state update's
+// rounding accumulates from chunk to chunk).  Values that would not fit fp16
+// are scaled by exact powers of two (Tb per chunk, X and U per wave; almost
+// never taken).
 // The diagonal 16x16 blocks of A and M, and the block levels of the
 // triangular solve, run on fp32 MFMA.
 //

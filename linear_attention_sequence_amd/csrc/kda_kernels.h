@@ -35,6 +35,7 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -84,7 +85,7 @@ __device__ __forceinline__ f32x16 mfma32h(const f16x8& a, const f16x8& b, const 
 struct alignas(16) Smem {
   bf16 Qt[CH][DK + 8];       // qh * e^G                      (A operand of Qt S)
   bf16 Kt[CH][DK + 8];       // -kh * e^G                     (A operand of X = V - Kt S)
-  bf16 KbT[DK][CH + 8];      // (kh * e^{G_c - G})^T          (A operand of the state update)
+  _Float16 KbT[DK][CH + 8];  // (kh * e^{G_c - G})^T <= 1     (A operand of the state update)
   _Float16 M[CH][CH + 8];    // M (|M| <= 1), lower incl.
   union {
     _Float16 tb[CH][CH + 8];  // Tb 2^-e (written after the solve; 2^e in tbscale)
@@ -137,7 +138,7 @@ static_assert(OFF_TB == (int)offsetof(Smem, M) + CH * ROW_CC, "Tb follows M");
 // staged here in the image's own layout; Qt, Kt, Tb and D go straight from
 // registers to the image in global memory.
 struct alignas(16) PreSmem {
-  bf16 KbT[DK][CH + 8];
+  _Float16 KbT[DK][CH + 8];
   _Float16 M[CH][CH + 8];
   struct {
     float A[CH][CH + 4];
@@ -706,12 +707,13 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
       fk[0] = a.x; fk[1] = a.y; fk[2] = a.z; fk[3] = a.w;
       fk[4] = b.x; fk[5] = b.y; fk[6] = b.z; fk[7] = b.w;
     }
-    bf16x8 qt, kt, kb;
+    bf16x8 qt, kt;
+    f16x8 kb;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       qt[j] = (bf16)(lq[j0 + j] * fq[j]);
       kt[j] = (bf16)(-lk[j0 + j] * fq[j]);
-      kb[j] = (bf16)(kr[j0 + j] * fk[j]);
+      kb[j] = (_Float16)(kr[j0 + j] * fk[j]);
     }
     sink.qk(tok, 4 * j0 + 8 * cg, qt, kt);
     // KbT is the transpose of these rows: multiplying by the identity on
@@ -719,20 +721,20 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
     // tokens 4 (l / 16) .. + 3, one 8-byte LDS store each
     {
       const int s8 = j0 / 8;
-      bf16x8 id0, id1;
+      f16x8 id0, id1;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        id0[j] = (bf16)((8 * cg + j == r) ? 1.f : 0.f);
-        id1[j] = (bf16)((8 * cg + j == 16 + r) ? 1.f : 0.f);
+        id0[j] = (_Float16)((8 * cg + j == r) ? 1.f : 0.f);
+        id1[j] = (_Float16)((8 * cg + j == 16 + r) ? 1.f : 0.f);
       }
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      const f32x4 c0 = mfma16(kb, id0, z);
-      const f32x4 c1 = mfma16(kb, id1, z);
-      bf16x4 t0, t1;
+      const f32x4 c0 = mfma16h(kb, id0, z);
+      const f32x4 c1 = mfma16h(kb, id1, z);
+      f16x4 t0, t1;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { t0[i] = (bf16)c0[i]; t1[i] = (bf16)c1[i]; }
-      *reinterpret_cast<bf16x4*>(&sm.KbT[32 * s8 + r][16 * w + 4 * cg]) = t0;
-      *reinterpret_cast<bf16x4*>(&sm.KbT[32 * s8 + 16 + r][16 * w + 4 * cg]) = t1;
+      for (int i = 0; i < 4; ++i) { t0[i] = (_Float16)c0[i]; t1[i] = (_Float16)c1[i]; }
+      *reinterpret_cast<f16x4*>(&sm.KbT[32 * s8 + r][16 * w + 4 * cg]) = t0;
+      *reinterpret_cast<f16x4*>(&sm.KbT[32 * s8 + 16 + r][16 * w + 4 * cg]) = t1;
     }
   }
 
@@ -949,8 +951,7 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
         for (int i = 0; i < 16; ++i) U[mt][i] *= up;
     }
   }
-  // U in bf16 for the state update; in fp16 (divided by 2^eu when needed) for M U
-  bf16x8 Ubh[4];
+  // U in fp16 (divided by 2^eu when needed) for M U and the state update
   f16x8 Uh[4];
   float umax = 0.f;
 #pragma unroll
@@ -963,7 +964,6 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
   for (int s = 0; s < 4; ++s)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      Ubh[s][j] = (bf16)U[s >> 1][8 * (s & 1) + j];
       Uh[s][j] = (_Float16)(U[s >> 1][8 * (s & 1) + j] * udown);
     }
   if (eu != 0) {
@@ -1035,18 +1035,25 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) dS[kt][i] = 0.f;
-    bf16x8 kb[2][4];
+    f16x8 kb[2][4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
-      kb[0][kt] = *reinterpret_cast<const bf16x8*>(&sm.KbT[32 * kt + rowsel][8 * hg]);
+      kb[0][kt] = *reinterpret_cast<const f16x8*>(&sm.KbT[32 * kt + rowsel][8 * hg]);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         if (s + 1 < 4)
-          kb[(s + 1) & 1][kt] = *reinterpret_cast<const bf16x8*>(&sm.KbT[32 * kt + rowsel][16 * (s + 1) + 8 * hg]);
-        dS[kt] = mfma32(kb[s & 1][kt], Ubh[s], dS[kt]);
+          kb[(s + 1) & 1][kt] = *reinterpret_cast<const f16x8*>(&sm.KbT[32 * kt + rowsel][16 * (s + 1) + 8 * hg]);
+        dS[kt] = mfma32h(kb[s & 1][kt], Uh[s], dS[kt]);
       }
+    }
+    if (eu != 0) {  // the product took U 2^-eu (exact power of two)
+      const float up = pow2i(eu);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dS[kt][i] *= up;
     }
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
