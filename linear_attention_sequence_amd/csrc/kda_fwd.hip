@@ -297,13 +297,13 @@ __global__ __launch_bounds__(NTHR, 2) void kda_pre_kernel(
     uint8_t* img = images + ((size_t)(unit / H) * H + h) * IMG_BYTES;
     const GlobalSink sink{make_rsrc(img, IMG_BYTES)};
     prepare_chunk(sm, sink, cur, ch.y, gate_bound, ln, [&](int) {});
-    // KbT and M: LDS staging -> image
+    // KbT and M: padded LDS staging rows -> unpadded image rows
     const uint8_t* st = reinterpret_cast<const uint8_t*>(&sm.KbT[0][0]);
 #pragma unroll
-    for (int i = 0; i < (PRE_STAGED_VEC + NTHR - 1) / NTHR; ++i) {
+    for (int i = 0; i < PRE_STAGED_VEC / NTHR; ++i) {
       const int pc = ln.tid + NTHR * i;
-      if (pc < PRE_STAGED_VEC)
-        bstore(*reinterpret_cast<const u32x4*>(st + 16 * pc), sink.r, OFF_KBT + 16 * pc);
+      bstore(*reinterpret_cast<const u32x4*>(st + (pc >> 3) * ROW_CC + (pc & 7) * 16), sink.r,
+             GOFF_CC + 16 * pc);
     }
     __syncthreads();  // the staging is read out before the next unit rewrites it
   }

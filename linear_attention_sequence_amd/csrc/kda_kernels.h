@@ -110,10 +110,6 @@ struct alignas(16) Smem {
   int gate_bad;
 };
 
-constexpr int IMG_BYTES = (int)(offsetof(Smem, u) + sizeof(((Smem*)nullptr)->u.tb));
-constexpr int IMG_VEC = IMG_BYTES / 16;                         // 16-byte pieces of an image
-constexpr int IMG_PER_THREAD = (IMG_VEC + NTHR - 1) / NTHR;     // pieces per thread (the last partial)
-static_assert(IMG_BYTES % 16 == 0 && (IMG_VEC % NTHR) % 64 == 0, "the last piece round is whole waves");
 
 // e^{G_c} of channels c .. c + 3 (c a multiple of 4): the padding of Kt row c / 4
 __device__ __forceinline__ float* dvec(Smem& sm, int c) {
@@ -133,6 +129,25 @@ constexpr int ROW_QK = (DK + 8) * 2;   // bytes per Qt / Kt row
 constexpr int ROW_CC = (CH + 8) * 2;   // bytes per M / Tb row
 static_assert(offsetof(Smem, M) == OFF_KBT + DK * ROW_CC, "KbT and M are contiguous");
 static_assert(OFF_TB == (int)offsetof(Smem, M) + CH * ROW_CC, "Tb follows M");
+static_assert(OFF_KT == OFF_QT + CH * ROW_QK, "Kt follows Qt");
+
+// The image in global memory holds the same tiles without the LDS row
+// padding, in 16-byte pieces: the Qt and Kt rows (16 pieces each), then the
+// KbT, M and Tb rows (8 each), then one piece per Kt row padding for D (rows
+// 0..31) and Tb's scale (row 32); image_to_lds puts each piece back in place.
+constexpr int IMG_QK = 2 * CH * (DK / 8);                      // Qt, Kt pieces
+constexpr int IMG_CC = (DK + 2 * CH) * (CH / 8);                // KbT, M, Tb pieces
+constexpr int IMG_PAD = DK / 4 + 1;                            // Kt row paddings in use
+constexpr int IMG_VEC = IMG_QK + IMG_CC + IMG_PAD;
+constexpr int IMG_BYTES = 16 * IMG_VEC;                        // one image in global memory
+constexpr int IMG_PER_THREAD = (IMG_VEC + NTHR - 1) / NTHR;     // pieces per thread (the last partial)
+static_assert(ROW_QK == 17 * 16 && ROW_CC == 9 * 16, "rows are whole pieces plus one of padding");
+
+// global byte offsets of the parts the pre kernel writes
+constexpr int GOFF_KT = 16 * CH * (DK / 8);                    // Kt rows
+constexpr int GOFF_CC = 16 * IMG_QK;                            // KbT rows, then M, then Tb
+constexpr int GOFF_TB = GOFF_CC + 16 * (DK + CH) * (CH / 8);    // Tb rows
+constexpr int GOFF_PAD = GOFF_CC + 16 * IMG_CC;                 // Kt row paddings
 
 // LDS of the pre kernel (~70 KB: two workgroups per CU).  KbT and M are
 // staged here in the image's own layout; Qt, Kt, Tb and D go straight from
@@ -153,9 +168,11 @@ struct alignas(16) PreSmem {
   float tbmax[8];
   int gate_bad;
 };
-constexpr int PRE_STAGED = (int)(sizeof(((PreSmem*)nullptr)->KbT) + sizeof(((PreSmem*)nullptr)->M));
-constexpr int PRE_STAGED_VEC = PRE_STAGED / 16;
-static_assert(PRE_STAGED % 16 == 0 && (PRE_STAGED_VEC % NTHR) % 64 == 0, "staged parts: whole waves");
+// KbT and M rows staged in PreSmem (padded like Smem), as image pieces
+constexpr int PRE_STAGED_VEC = (DK + CH) * (CH / 8);
+static_assert(offsetof(PreSmem, M) == sizeof(((PreSmem*)nullptr)->KbT) && ROW_CC * DK == sizeof(((PreSmem*)nullptr)->KbT),
+              "KbT and M rows are contiguous in the staging, ROW_CC apart");
+static_assert(PRE_STAGED_VEC % NTHR == 0, "staged parts: whole rounds");
 
 // Store the 16x16 block (a, b) of M (lower incl., fp16) and of A
 // (beta-scaled, strictly lower, fp32).  C layout of a 16x16 MFMA tile: lane l
@@ -356,11 +373,25 @@ __device__ __forceinline__ void load_image(Image& im, const uint8_t* __restrict_
   load_image_part(im, make_rsrc(src, IMG_BYTES), tid, 0, IMG_PER_THREAD);
 }
 
+// every round of NTHR pieces lies in one part of the image, so the part of
+// round i is known at compile time
+static_assert(IMG_QK % NTHR == 0 && IMG_CC % NTHR == 0, "parts start at whole rounds");
 __device__ __forceinline__ void image_to_lds(Smem& sm, const Image& im, int tid) {
   uint8_t* dst = reinterpret_cast<uint8_t*>(&sm);
 #pragma unroll
-  for (int i = 0; i < IMG_PER_THREAD; ++i)
-    if (tid + NTHR * i < IMG_VEC) *reinterpret_cast<u32x4*>(dst + 16 * (tid + NTHR * i)) = im.p[i];
+  for (int i = 0; i < IMG_PER_THREAD; ++i) {
+    const int p = tid + NTHR * i;
+    int off;
+    if (NTHR * (i + 1) <= IMG_QK) {
+      off = OFF_QT + (p >> 4) * ROW_QK + (p & 15) * 16;
+    } else if (NTHR * (i + 1) <= IMG_QK + IMG_CC) {
+      const int q = p - IMG_QK;
+      off = OFF_KBT + (q >> 3) * ROW_CC + (q & 7) * 16;
+    } else {
+      off = OFF_KT + (p - IMG_QK - IMG_CC) * ROW_QK + 2 * DK;
+    }
+    if (p < IMG_VEC) *reinterpret_cast<u32x4*>(dst + off) = im.p[i];
+  }
 }
 
 
@@ -380,20 +411,20 @@ struct LdsSink {
 };
 
 struct GlobalSink {
-  Rsrc r;  // one image, IMG_BYTES
+  Rsrc r;  // one image, IMG_BYTES (the unpadded layout above)
   __device__ __forceinline__ void qk(int tok, int col, const bf16x8& qt, const bf16x8& kt) const {
-    const uint32_t o = (uint32_t)(tok * ROW_QK + 2 * col);
-    bstore(__builtin_bit_cast(u32x4, qt), r, OFF_QT + o);
-    bstore(__builtin_bit_cast(u32x4, kt), r, OFF_KT + o);
+    const uint32_t o = (uint32_t)(tok * 2 * DK + 2 * col);
+    bstore(__builtin_bit_cast(u32x4, qt), r, o);
+    bstore(__builtin_bit_cast(u32x4, kt), r, GOFF_KT + o);
   }
   __device__ __forceinline__ void dv(int c, float f) const {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f), r, OFF_KT + (c >> 2) * ROW_QK + 2 * DK + 4 * (c & 3), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f), r, GOFF_PAD + 16 * (c >> 2) + 4 * (c & 3), 0, 0);
   }
   __device__ __forceinline__ void tb(int row, int col, const f16x8& x) const {
-    bstore(__builtin_bit_cast(u32x4, x), r, OFF_TB + (uint32_t)(row * ROW_CC + 2 * col));
+    bstore(__builtin_bit_cast(u32x4, x), r, GOFF_TB + (uint32_t)(row * 2 * CH + 2 * col));
   }
   __device__ __forceinline__ void tbs(float f) const {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f), r, OFF_KT + 32 * ROW_QK + 2 * DK, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f), r, GOFF_PAD + 16 * (DK / 4), 0, 0);
   }
 };
 
@@ -1212,15 +1243,16 @@ __global__ __launch_bounds__(NTHR, 1) void kda_chunk_fwd_kernel(
         const int n1 = (int)min<int64_t>(CH, eos - c1);
         const Rsrc rimg = make_rsrc(img, c1 < eos ? IMG_BYTES : 0);
         chain_chunk(sm, S, vcur, n, c0, H, h, out, ln, of, [&](int stage) {
+          static_assert(IMG_PER_THREAD == 17, "the four load parts cover the image");
           if (stage == 0) {
             vcur = load_v(v, c1, n1, H, h, of);
-            load_image_part(im, rimg, tid, 0, 6);
+            load_image_part(im, rimg, tid, 0, 5);
           } else if (stage == 1) {
-            load_image_part(im, rimg, tid, 6, 12);
+            load_image_part(im, rimg, tid, 5, 9);
           } else if (stage == 2) {
-            load_image_part(im, rimg, tid, 12, 17);
+            load_image_part(im, rimg, tid, 9, 13);
           } else {
-            load_image_part(im, rimg, tid, 17, IMG_PER_THREAD);
+            load_image_part(im, rimg, tid, 13, IMG_PER_THREAD);
           }
         });
         __syncthreads();  // the next chunk overwrites the image
