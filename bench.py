@@ -54,9 +54,9 @@ COPY_PROBE_BYTES = 1 << 30
 # kda_fwd.hip, kda_fwd_state.hip in that order); otherwise null.
 TRAFFIC = {
     "workload": "packed_lognormal_T32768_H32",
-    "kernel_sha256": "c7a47fe52a328e7245950d968874fecd9f2ecb76b8806eac629f96590f3ccf7d",
-    "fetch_kib": {"kda_schedule_kernel": 8.7, "kda_pre_kernel": 268072.5, "kda_chunk_fwd_kernel": 686375.2},
-    "write_kib": {"kda_schedule_kernel": 2.3, "kda_pre_kernel": 573855.3, "kda_chunk_fwd_kernel": 262174.1},
+    "kernel_sha256": "38a81dded80f9b1eced301d2a4b8ab565508b9d645bf614120dba3f76bde46e8",
+    "fetch_kib": {"kda_schedule_kernel": 8.7, "kda_pre_kernel": 267249.1, "kda_chunk_fwd_kernel": 663926.2},
+    "write_kib": {"kda_schedule_kernel": 2.3, "kda_pre_kernel": 534220.2, "kda_chunk_fwd_kernel": 262173.5},
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }
