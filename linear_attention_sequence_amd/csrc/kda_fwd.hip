@@ -297,13 +297,20 @@ __global__ __launch_bounds__(NTHR, 2) void kda_pre_kernel(
     uint8_t* img = images + ((size_t)(unit / H) * H + h) * IMG_BYTES;
     const GlobalSink sink{make_rsrc(img, IMG_BYTES)};
     prepare_chunk(sm, sink, cur, ch.y, gate_bound, ln, [&](int) {});
-    // KbT and M: padded LDS staging rows -> unpadded image rows
+    // KbT and M: padded LDS staging rows -> image pieces
     const uint8_t* st = reinterpret_cast<const uint8_t*>(&sm.KbT[0][0]);
 #pragma unroll
-    for (int i = 0; i < PRE_STAGED_VEC / NTHR; ++i) {
+    for (int i = 0; i < IMG_KB / NTHR; ++i) {
       const int pc = ln.tid + NTHR * i;
       bstore(*reinterpret_cast<const u32x4*>(st + (pc >> 3) * ROW_CC + (pc & 7) * 16), sink.r,
-             GOFF_CC + 16 * pc);
+             16 * (GP_KB + pc));
+    }
+    const uint8_t* sm_m = st + DK * ROW_CC;
+#pragma unroll
+    for (int i = 0; i < (CH * (CH / 8) + NTHR - 1) / NTHR; ++i) {
+      const int pc = ln.tid + NTHR * i, row = pc >> 3, cp = pc & 7;
+      const int gp = img_mt_piece(0, row, cp);
+      if (gp >= 0) bstore(*reinterpret_cast<const u32x4*>(sm_m + row * ROW_CC + cp * 16), sink.r, 16 * gp);
     }
     __syncthreads();  // the staging is read out before the next unit rewrites it
   }

@@ -131,23 +131,40 @@ static_assert(offsetof(Smem, M) == OFF_KBT + DK * ROW_CC, "KbT and M are contigu
 static_assert(OFF_TB == (int)offsetof(Smem, M) + CH * ROW_CC, "Tb follows M");
 static_assert(OFF_KT == OFF_QT + CH * ROW_QK, "Kt follows Qt");
 
-// The image in global memory holds the same tiles without the LDS row
-// padding, in 16-byte pieces: the Qt and Kt rows (16 pieces each), then the
-// KbT, M and Tb rows (8 each), then one piece per Kt row padding for D (rows
-// 0..31) and Tb's scale (row 32); image_to_lds puts each piece back in place.
-constexpr int IMG_QK = 2 * CH * (DK / 8);                      // Qt, Kt pieces
-constexpr int IMG_CC = (DK + 2 * CH) * (CH / 8);                // KbT, M, Tb pieces
-constexpr int IMG_PAD = DK / 4 + 1;                            // Kt row paddings in use
-constexpr int IMG_VEC = IMG_QK + IMG_CC + IMG_PAD;
-constexpr int IMG_BYTES = 16 * IMG_VEC;                        // one image in global memory
-constexpr int IMG_PER_THREAD = (IMG_VEC + NTHR - 1) / NTHR;     // pieces per thread (the last partial)
+// The image in global memory holds the tiles the chain reads, without the LDS
+// row padding, in 16-byte pieces:
+//   the Qt and Kt rows (16 pieces each);
+//   the KbT rows (8 each);
+//   the first 32 columns of rows 0..31 of M, then of Tb (4 each: the chain's
+//   first row tile reads only those);
+//   rows 32..63 of M, then of Tb (8 each);
+//   one piece per Kt row padding for D (rows 0..31) and Tb's scale (row 32).
+// Every part but the last fills whole rounds of NTHR pieces, so image_to_lds
+// knows the part of each round at compile time.
+constexpr int IMG_QK = 2 * CH * (DK / 8);          // Qt, Kt pieces
+constexpr int IMG_KB = DK * (CH / 8);              // KbT pieces
+constexpr int IMG_SHORT = 2 * 32 * 4;              // rows 0..31 of M and Tb, columns 0..31
+constexpr int IMG_LONG = 32 * (CH / 8);            // rows 32..63 of M (or of Tb)
+constexpr int IMG_PAD = DK / 4 + 1;                // Kt row paddings in use
+constexpr int IMG_VEC = IMG_QK + IMG_KB + IMG_SHORT + 2 * IMG_LONG + IMG_PAD;
+constexpr int IMG_BYTES = 16 * IMG_VEC;            // one image in global memory
+constexpr int IMG_PER_THREAD = (IMG_VEC + NTHR - 1) / NTHR;  // pieces per thread (the last partial)
 static_assert(ROW_QK == 17 * 16 && ROW_CC == 9 * 16, "rows are whole pieces plus one of padding");
-
-// global byte offsets of the parts the pre kernel writes
-constexpr int GOFF_KT = 16 * CH * (DK / 8);                    // Kt rows
-constexpr int GOFF_CC = 16 * IMG_QK;                            // KbT rows, then M, then Tb
-constexpr int GOFF_TB = GOFF_CC + 16 * (DK + CH) * (CH / 8);    // Tb rows
-constexpr int GOFF_PAD = GOFF_CC + 16 * IMG_CC;                 // Kt row paddings
+static_assert(IMG_QK % NTHR == 0 && IMG_KB % NTHR == 0 && IMG_SHORT == NTHR && IMG_LONG == NTHR,
+              "every part but the last fills whole rounds");
+constexpr int OFF_M = OFF_KBT + DK * ROW_CC;       // LDS rows of M, then Tb
+// global piece indices of the parts the pre kernel writes
+constexpr int GP_KB = IMG_QK;
+constexpr int GP_SHORT = GP_KB + IMG_KB;
+constexpr int GP_MLONG = GP_SHORT + IMG_SHORT;
+constexpr int GP_TLONG = GP_MLONG + IMG_LONG;
+constexpr int GP_PAD = GP_TLONG + IMG_LONG;
+// global piece of (row, 8-column piece cp) of M (t = 0) or Tb (t = 1); -1 for
+// the pieces the chain never reads (rows 0..31, columns 32..63)
+__device__ __forceinline__ int img_mt_piece(int t, int row, int cp) {
+  if (row < 32) return cp < 4 ? GP_SHORT + 128 * t + 4 * row + cp : -1;
+  return (t ? GP_TLONG : GP_MLONG) + 8 * (row - 32) + cp;
+}
 
 // LDS of the pre kernel (~70 KB: two workgroups per CU).  KbT and M are
 // staged here in the image's own layout; Qt, Kt, Tb and D go straight from
@@ -168,11 +185,10 @@ struct alignas(16) PreSmem {
   float tbmax[8];
   int gate_bad;
 };
-// KbT and M rows staged in PreSmem (padded like Smem), as image pieces
-constexpr int PRE_STAGED_VEC = (DK + CH) * (CH / 8);
+// KbT and M rows staged in PreSmem (padded like Smem) go to the image piece by
+// piece: KbT (whole rounds), then the M pieces the chain reads
 static_assert(offsetof(PreSmem, M) == sizeof(((PreSmem*)nullptr)->KbT) && ROW_CC * DK == sizeof(((PreSmem*)nullptr)->KbT),
               "KbT and M rows are contiguous in the staging, ROW_CC apart");
-static_assert(PRE_STAGED_VEC % NTHR == 0, "staged parts: whole rounds");
 
 // Store the 16x16 block (a, b) of M (lower incl., fp16) and of A
 // (beta-scaled, strictly lower, fp32).  C layout of a 16x16 MFMA tile: lane l
@@ -373,27 +389,32 @@ __device__ __forceinline__ void load_image(Image& im, const uint8_t* __restrict_
   load_image_part(im, make_rsrc(src, IMG_BYTES), tid, 0, IMG_PER_THREAD);
 }
 
-// every round of NTHR pieces lies in one part of the image, so the part of
-// round i is known at compile time
-static_assert(IMG_QK % NTHR == 0 && IMG_CC % NTHR == 0, "parts start at whole rounds");
+// each round of NTHR pieces lies in one part of the image: the part of round
+// i is known at compile time
 __device__ __forceinline__ void image_to_lds(Smem& sm, const Image& im, int tid) {
   uint8_t* dst = reinterpret_cast<uint8_t*>(&sm);
 #pragma unroll
   for (int i = 0; i < IMG_PER_THREAD; ++i) {
     const int p = tid + NTHR * i;
+    const int r0 = NTHR * i;  // first piece of the round
     int off;
-    if (NTHR * (i + 1) <= IMG_QK) {
+    if (r0 < GP_KB) {
       off = OFF_QT + (p >> 4) * ROW_QK + (p & 15) * 16;
-    } else if (NTHR * (i + 1) <= IMG_QK + IMG_CC) {
-      const int q = p - IMG_QK;
+    } else if (r0 < GP_SHORT) {
+      const int q = p - GP_KB;
       off = OFF_KBT + (q >> 3) * ROW_CC + (q & 7) * 16;
+    } else if (r0 < GP_MLONG) {
+      const int q = p - GP_SHORT;  // Tb rows follow M rows in LDS: row (q >> 2) + 64 (q >> 7)
+      off = OFF_M + ((q & 127) >> 2) * ROW_CC + CH * ROW_CC * (q >> 7) + (q & 3) * 16;
+    } else if (r0 < GP_PAD) {
+      const int q = p - GP_MLONG;  // M rows 32..63, then Tb rows 32..63
+      off = OFF_M + (32 + ((q & 255) >> 3)) * ROW_CC + CH * ROW_CC * (q >> 8) + (q & 7) * 16;
     } else {
-      off = OFF_KT + (p - IMG_QK - IMG_CC) * ROW_QK + 2 * DK;
+      off = OFF_KT + (p - GP_PAD) * ROW_QK + 2 * DK;
     }
     if (p < IMG_VEC) *reinterpret_cast<u32x4*>(dst + off) = im.p[i];
   }
 }
-
 
 // Where prepare_chunk puts the image parts it holds in registers (Qt, Kt, Tb
 // and D): the LDS image of the main kernel, or the global image.
@@ -411,20 +432,21 @@ struct LdsSink {
 };
 
 struct GlobalSink {
-  Rsrc r;  // one image, IMG_BYTES (the unpadded layout above)
+  Rsrc r;  // one image, IMG_BYTES (the layout above)
   __device__ __forceinline__ void qk(int tok, int col, const bf16x8& qt, const bf16x8& kt) const {
     const uint32_t o = (uint32_t)(tok * 2 * DK + 2 * col);
     bstore(__builtin_bit_cast(u32x4, qt), r, o);
-    bstore(__builtin_bit_cast(u32x4, kt), r, GOFF_KT + o);
+    bstore(__builtin_bit_cast(u32x4, kt), r, 16 * CH * (DK / 8) + o);
   }
   __device__ __forceinline__ void dv(int c, float f) const {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f), r, GOFF_PAD + 16 * (c >> 2) + 4 * (c & 3), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f), r, 16 * (GP_PAD + (c >> 2)) + 4 * (c & 3), 0, 0);
   }
   __device__ __forceinline__ void tb(int row, int col, const f16x8& x) const {
-    bstore(__builtin_bit_cast(u32x4, x), r, GOFF_TB + (uint32_t)(row * 2 * CH + 2 * col));
+    const int pc = img_mt_piece(1, row, col >> 3);
+    if (pc >= 0) bstore(__builtin_bit_cast(u32x4, x), r, 16 * pc);
   }
   __device__ __forceinline__ void tbs(float f) const {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f), r, GOFF_PAD + 16 * (DK / 4), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f), r, 16 * (GP_PAD + DK / 4), 0, 0);
   }
 };
 
@@ -1243,16 +1265,16 @@ __global__ __launch_bounds__(NTHR, 1) void kda_chunk_fwd_kernel(
         const int n1 = (int)min<int64_t>(CH, eos - c1);
         const Rsrc rimg = make_rsrc(img, c1 < eos ? IMG_BYTES : 0);
         chain_chunk(sm, S, vcur, n, c0, H, h, out, ln, of, [&](int stage) {
-          static_assert(IMG_PER_THREAD == 17, "the four load parts cover the image");
+          static_assert(IMG_PER_THREAD == 16, "the four load parts cover the image");
           if (stage == 0) {
             vcur = load_v(v, c1, n1, H, h, of);
-            load_image_part(im, rimg, tid, 0, 5);
+            load_image_part(im, rimg, tid, 0, 4);
           } else if (stage == 1) {
-            load_image_part(im, rimg, tid, 5, 9);
+            load_image_part(im, rimg, tid, 4, 8);
           } else if (stage == 2) {
-            load_image_part(im, rimg, tid, 9, 13);
+            load_image_part(im, rimg, tid, 8, 12);
           } else {
-            load_image_part(im, rimg, tid, 13, IMG_PER_THREAD);
+            load_image_part(im, rimg, tid, 12, IMG_PER_THREAD);
           }
         });
         __syncthreads();  // the next chunk overwrites the image
