@@ -224,3 +224,18 @@ def test_backward_long_document_one_head():
             mx = float(np.abs(x).max())
             log(f"[parity] bwd long document {n}: relL2={rel:.3e} maxabs={mx:.3e}")
             assert rel <= REL_L2_TOL and mx <= ABS_TOL * max(1.0, float(np.abs(ref[n]).max())), n
+
+
+def test_backward_many_tiny_documents():
+    """300 documents of 1 to 5 tokens with states: chunks of a few rows, most
+    of every 16-row block empty, a long chunk table and many chains."""
+    rng = np.random.default_rng(71)
+    lengths = [int(x) for x in rng.integers(1, 6, size=300)]
+    T, H = sum(lengths), 2
+    inp = make_inputs(T, H, 71, cu_from_lengths(lengths))
+    do = _dout(T, H, 71)
+    h0 = initial_states(len(lengths), H, 71)
+    dht = np.ascontiguousarray(initial_states(len(lengths), H, 72))
+    log(f"[case] bwd {len(lengths)} tiny documents, T={T}")
+    got = _run(inp, do, h0, dht)
+    _check(inp, do, got, h0, dht, "bwd tiny documents")
