@@ -849,8 +849,8 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
     //   Sb  = sum_{rr >= r} (dM_rr,r qh_rr,c + dKk_rr,r kh_rr,c) E_rr,r,c
     // with E_ric = exp(G_rc - G_ic), then combined with the decayed tiles into
     // dqh, dkh and dG.  Thread (block bb, channel c) owns rows 16 bb .. 16 bb + 15
-    // of channel c and keeps everything of them in registers; bb is uniform
-    // over a wave, so the rows of dM and dKk it reads are broadcasts.
+    // of channel c and keeps their sums in registers; bb is uniform over a
+    // wave, so the in-block rows of dM and dKk it reads are broadcasts.
     static_assert(NT == 4 * DK, "one thread per (16-row block, channel)");
     asm volatile("" : "+v"(tid));  // lane values from here on are recomputed, not kept live
     const int bb = __builtin_amdgcn_readfirstlane(tid / DK), c = tid % DK, r0 = 16 * bb;
