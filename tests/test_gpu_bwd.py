@@ -239,3 +239,28 @@ def test_backward_many_tiny_documents():
     log(f"[case] bwd {len(lengths)} tiny documents, T={T}")
     got = _run(inp, do, h0, dht)
     _check(inp, do, got, h0, dht, "bwd tiny documents")
+
+
+def test_backward_gate_at_the_lowest_bound():
+    """g = -5.5 on every token and channel (the lowest bound the interface
+    accepts): every decay split of the backward takes its widest factors,
+    exp(+-5.5 x 8) inside a 16-row block, with an initial state and a
+    final-state gradient."""
+    import dataclasses
+    lengths = [150, 64, 17]
+    T, H = sum(lengths), 2
+    base = make_inputs(T, H, 84, cu_from_lengths(lengths))
+    inp = dataclasses.replace(base, g=np.full_like(base.g, -5.5))
+    do = _dout(T, H, 84)
+    h0 = initial_states(len(lengths), H, 84)
+    dht = np.ascontiguousarray(initial_states(len(lengths), H, 85))
+    import torch
+    import linear_attention_sequence_amd as kda
+    d = to_device(inp)
+    r = kda.chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                      torch.from_numpy(do).to(torch.bfloat16).cuda(), d["cu"],
+                      initial_state=torch.from_numpy(h0).cuda(),
+                      d_final_state=torch.from_numpy(dht).cuda(), gate_bound=-5.5)
+    torch.cuda.synchronize()
+    got = [x.cpu().numpy().astype(np.float64) for x in r]
+    _check(inp, do, got, h0, dht, "bwd gate at -5.5")
