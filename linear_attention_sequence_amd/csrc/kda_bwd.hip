@@ -59,7 +59,8 @@ constexpr int NW = NT / 64;                  // waves per workgroup
 constexpr int TPT = NT / CH;                 // threads per token row (8)
 constexpr int CPT = DK / TPT;                // channels per thread in a token row (16)
 constexpr int RG = NT / DK;                  // row groups when a thread owns one channel (4)
-constexpr int LD = 129;                      // padded row of a [64][128] LDS tile
+constexpr int LD = 132;                      // padded row of a [64][128] LDS tile (= 4 mod 8: the two rows
+                                             // of a half-wave's C-layout store hit different banks)
 constexpr int LDC = 65;                      // padded row of a [64][64] LDS tile
 constexpr int LDM = 68;                      // [64][64] LDS tile read in 16-byte row pieces
 constexpr float SCALE = 0.08838834764831845f;  // 128^-1/2
