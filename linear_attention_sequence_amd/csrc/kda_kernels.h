@@ -892,8 +892,10 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
     const uint32_t uu[4] = {u[0], u[1], u[2], u[3]};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      vt[8 * (l & 3) + 2 * j][t] = (unsigned short)(uu[j] & 0xFFFFu);
-      vt[8 * (l & 3) + 2 * j + 1][t] = (unsigned short)(uu[j] >> 16);
+      // column c keeps token t at t ^ 8 (c / 8): columns 8 apart (whose rows
+      // share banks) write different banks; 8-token groups stay contiguous
+      vt[8 * (l & 3) + 2 * j][t ^ (8 * (l & 3))] = (unsigned short)(uu[j] & 0xFFFFu);
+      vt[8 * (l & 3) + 2 * j + 1][t ^ (8 * (l & 3))] = (unsigned short)(uu[j] >> 16);
     }
   }
   wave_sync_lds();
@@ -904,7 +906,7 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
-      vx[mt][hh] = *reinterpret_cast<const u32x4*>(&vt[m][32 * mt + 16 * hh + 8 * hg]);
+      vx[mt][hh] = *reinterpret_cast<const u32x4*>(&vt[m][(32 * mt + 16 * hh + 8 * hg) ^ (8 * (m >> 3))]);
   wave_sync_lds();  // V read out before the slice stages O
   __builtin_amdgcn_sched_barrier(0);
   hook(0);
