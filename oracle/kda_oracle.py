@@ -166,11 +166,15 @@ def _run_task(task):
 
 
 def default_workers() -> int:
+    """Worker processes for the task pools: the CPUs this process may use, at
+    most 12.  Forked workers inherit the parent's open device handles, so a
+    caller that has used a GPU counts them as processes holding it; 12 keeps
+    parent and workers well inside a per-device limit of 16 processes."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
         n = os.cpu_count() or 1
-    return max(1, min(16, n))
+    return max(1, min(12, n))
 
 
 def kda_tasks(q, k, v, g, beta, tasks, workers: int | None = None,
