@@ -142,8 +142,13 @@ __device__ __forceinline__ void wg_gemm(LA la, LB lb, OUT out, float* stage, int
   constexpr int PER = (TILES + NW - 1) / NW;  // output tiles per wave (the last round may be partial)
   constexpr int NA = (16 * M + NT - 1) / NT, NB = (16 * N + NT - 1) / NT;  // staged per thread
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
-  float* sa = stage;              // [M][SROW]: row m holds k = k0 .. k0 + 15
-  float* sb = stage + M * SROW;   // [N][SROW]
+  // An operand fetched along k is staged m-major, [M][SROW] (row m holds
+  // k = k0 .. k0 + 15); one fetched along m (n) is staged k-major,
+  // [16][M + 4], so that a wave's staging stores fill consecutive banks.
+  constexpr int MP = M + 4, NP = N + 4;
+  static_assert(16 * MP <= M * SROW && 16 * NP <= N * SROW, "k-major tile fits the stage");
+  float* sa = stage;
+  float* sb = stage + M * SROW;
   // (m or n, kk) of this thread's staged element j
   auto a_mk = [&](int j, int& m, int& kk) {
     const int idx = min(tid + NT * j, 16 * M - 1);
@@ -181,25 +186,34 @@ __device__ __forceinline__ void wg_gemm(LA la, LB lb, OUT out, float* stage, int
     for (int j = 0; j < NA; ++j) {
       int m, kk;
       a_mk(j, m, kk);
-      if (NA * NT == 16 * M || tid + NT * j < 16 * M) sa[m * SROW + kk] = ra[set][j];
+      if (NA * NT == 16 * M || tid + NT * j < 16 * M)
+        sa[AK ? m * SROW + kk : kk * MP + m] = ra[set][j];
     }
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       int n, kk;
       b_nk(j, n, kk);
-      if (NB * NT == 16 * N || tid + NT * j < 16 * N) sb[n * SROW + kk] = rb[set][j];
+      if (NB * NT == 16 * N || tid + NT * j < 16 * N)
+        sb[BK ? n * SROW + kk : kk * NP + n] = rb[set][j];
     }
     __syncthreads();
     if (kt + PF < KT) fetch(set, 16 * (kt + PF));
     // k-step s pairs lane group g = l / 16 with k = 4 g + s on both operands,
-    // so each lane reads its four k values of a tile as one 16-byte vector
+    // so each lane reads its four k values of an m-major tile as one 16-byte
+    // vector; of a k-major one, as four 4-byte reads whose lane groups start
+    // 4 (M + 4) = 16 (mod 64) floats apart, so they read different banks
     const int kq = 4 * (l >> 4);
+    auto rd = [&](const float* s_, int rowp, bool along_k, int i0) {
+      if (along_k) return *reinterpret_cast<const float4*>(&s_[(i0 + (l & 15)) * SROW + kq]);
+      const float* c = &s_[kq * rowp + i0 + (l & 15)];
+      return float4{c[0], c[rowp], c[2 * rowp], c[3 * rowp]};
+    };
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int t = w + NW * p, tm = t / TN, tn = t - tm * TN;
       if (TILES % NW != 0 && t >= TILES) break;  // wave-uniform
-      const float4 av = *reinterpret_cast<const float4*>(&sa[(16 * tm + (l & 15)) * SROW + kq]);
-      const float4 bv = *reinterpret_cast<const float4*>(&sb[(16 * tn + (l & 15)) * SROW + kq]);
+      const float4 av = rd(sa, MP, AK, 16 * tm);
+      const float4 bv = rd(sb, NP, BK, 16 * tn);
       acc[p] = mfma16f(av.x, bv.x, acc[p]);
       acc[p] = mfma16f(av.y, bv.y, acc[p]);
       acc[p] = mfma16f(av.z, bv.z, acc[p]);
