@@ -794,45 +794,57 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
   __builtin_amdgcn_sched_barrier(0);
   hook(2);
   __builtin_amdgcn_sched_barrier(0);
-  // ---- off-diagonal blocks (w, b), b < w, on fp16 MFMA (fully unrolled per wave)
+  // ---- off-diagonal blocks (w, b), b < w, on fp16 MFMA (fully unrolled per
+  // wave).  Wave 0, which has none, meanwhile inverts the four diagonal
+  // blocks of I + A (complete since B1): T = (I + A)^-1 by 16x16 blocks, by
+  // forward substitution, lane l owning column l % 16 of diagonal block
+  // l / 16.  tmax tracks the largest |Tb| = |T_ij beta_j| a wave produces.
+  // T shares its space with R, which waves 1-3 still read: until B3 the
+  // columns wait in an upper block of A (A is strictly lower; its upper
+  // blocks are never written or read): block da in block (pr, pc).
+  const int da = l >> 4, dj = l & 15;
+  const int pr = da == 3 ? 1 : da, pc = da == 3 ? 3 : da + 1;
+  float tmax = 0.f;
   if (w == 1) offdiag_row<1>(sm, lq, lk, l, cg, beta_mine);
   else if (w == 2) offdiag_row<2>(sm, lq, lk, l, cg, beta_mine);
   else if (w == 3) offdiag_row<3>(sm, lq, lk, l, cg, beta_mine);
-
-  __syncthreads();  // B3: A and M complete, R dead
-
-  // ================= T = (I + A)^-1 by 16x16 blocks =================
-  // diagonal blocks: forward substitution, lane j < 16 of wave w owns column j;
-  // tmax tracks the largest |Tb| = |T_ij beta_j| this wave produces
-  float tmax = 0.f;
-  if (l < 16) {
-    const int j = l;
-    float a4[16][16];
-#pragma unroll
-    for (int rr = 1; rr < 16; ++rr)
-#pragma unroll
-      for (int i0 = 0; i0 < rr; i0 += 4) {
-        const float4 av = *reinterpret_cast<const float4*>(&sm.u.A[16 * w + rr][16 * w + i0]);
-        a4[rr][i0] = av.x; a4[rr][i0 + 1] = av.y; a4[rr][i0 + 2] = av.z; a4[rr][i0 + 3] = av.w;
-      }
+  else {
     // column-oriented: once x_i is final, subtract its share from every later
-    // row (dependency depth 16 instead of the 120 terms of row dot products)
+    // row (dependency depth 16 instead of the 120 terms of row dot products);
+    // A is read four columns at a time (off the critical path, few registers)
     float x[16];
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) x[rr] = (rr == j) ? 1.f : 0.f;
+    for (int rr = 0; rr < 16; ++rr) x[rr] = (rr == dj) ? 1.f : 0.f;
 #pragma unroll
-    for (int i = 0; i < 15; ++i)
+    for (int i0 = 0; i0 < 16; i0 += 4) {
+      float4 ac[16];
 #pragma unroll
-      for (int rr = i + 1; rr < 16; ++rr) x[rr] -= a4[rr][i] * x[i];
-    const float bj = fabsf(sm.beta[16 * w + j]);
+      for (int rr = i0 + 1; rr < 16; ++rr)
+        ac[rr] = *reinterpret_cast<const float4*>(&sm.u.A[16 * da + rr][16 * da + i0]);
+#pragma unroll
+      for (int i = i0; i < i0 + 4 && i < 15; ++i)
+#pragma unroll
+        for (int rr = i + 1; rr < 16; ++rr) {
+          const float4 a = ac[rr];
+          const float air = i == i0 ? a.x : i == i0 + 1 ? a.y : i == i0 + 2 ? a.z : a.w;
+          x[rr] -= air * x[i];
+        }
+    }
+    const float bj = fabsf(sm.beta[16 * da + dj]);
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-      sm.u2.T[16 * w + rr][16 * w + j] = x[rr];
+      sm.u.A[16 * pr + rr][16 * pc + dj] = x[rr];
       tmax = fmaxf(tmax, fabsf(x[rr]) * bj);
     }
-    if (w == 0 || w == 2) {  // upper blocks (0, 1) and (2, 3): read by U = Tb X
+  }
+
+  __syncthreads();  // B3: A and M complete, R dead (T, which shares its space, may be written)
+  if (w == 0) {
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) sm.u2.T[16 * w + rr][16 * (w + 1) + j] = 0.f;
+    for (int rr = 0; rr < 16; ++rr) sm.u2.T[16 * da + rr][16 * da + dj] = sm.u.A[16 * pr + rr][16 * pc + dj];
+    if (da == 0 || da == 2) {  // upper blocks (0, 1) and (2, 3): read by U = Tb X
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) sm.u2.T[16 * da + rr][16 * (da + 1) + dj] = 0.f;
     }
   }
   __syncthreads();  // B4: diagonal blocks of T visible
