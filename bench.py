@@ -54,9 +54,9 @@ COPY_PROBE_BYTES = 1 << 30
 # kda_fwd.hip, kda_fwd_state.hip in that order); otherwise null.
 TRAFFIC = {
     "workload": "packed_lognormal_T32768_H32",
-    "kernel_sha256": "f075eddb6a0494e74edcfac59a7031ba5148c1a7e117ca5b3535a5125dd94f0b",
-    "fetch_kib": {"kda_schedule_kernel": 8.7, "kda_pre_kernel": 267104.1, "kda_chunk_fwd_kernel": 646596.9},
-    "write_kib": {"kda_schedule_kernel": 2.3, "kda_pre_kernel": 496596.7, "kda_chunk_fwd_kernel": 262173.2},
+    "kernel_sha256": "8a214a2c1582f9897dfc78233533c33522eb9b1f5d4b0db21d724516b4d900f3",
+    "fetch_kib": {"kda_schedule_kernel": 8.7, "kda_pre_kernel": 270042.0, "kda_chunk_fwd_kernel": 648274.7},
+    "write_kib": {"kda_schedule_kernel": 2.3, "kda_pre_kernel": 497450.5, "kda_chunk_fwd_kernel": 262173.7},
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }
