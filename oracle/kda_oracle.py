@@ -167,9 +167,9 @@ def _run_task(task):
 
 def default_workers() -> int:
     """Worker processes for the task pools: the CPUs this process may use, at
-    most 12.  Forked workers inherit the parent's open device handles, so a
-    caller that has used a GPU counts them as processes holding it; 12 keeps
-    parent and workers well inside a per-device limit of 16 processes."""
+    most 12.  Forked workers inherit the parent's open device handles, so when
+    the caller has used a GPU every worker also counts as a process holding
+    that device; the cap keeps that count small."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
