@@ -129,7 +129,9 @@ __device__ __forceinline__ void wave_sync_lds() {
 // out(m, n, value, old) receives old(m, n) as well (zero by default).
 // Every thread of the workgroup calls it (tid = its thread index); it
 // synchronises before returning results and before its first staging (so
-// operands may live in LDS buffers that out() overwrites).
+// operands may live in LDS buffers that out() overwrites), and again after
+// the last out().  Its first operand fetches come before any barrier: LDS
+// operands written just before the call need a barrier from the caller.
 struct NoOld {
   __device__ float operator()(int, int) const { return 0.f; }
 };
