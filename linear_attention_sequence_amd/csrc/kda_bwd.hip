@@ -252,11 +252,15 @@ __device__ __forceinline__ void wg_gemm(LA la, LB lb, OUT out, float* stage, int
 }
 
 // ---------------------------------------------------------------------------
-// setup: cu_seqlens (exactly n_docs + 1 entries) and the chunk table
+// setup: cu_seqlens (exactly n_docs + 1 entries), the chunk table and the
+// order in which the chain kernel takes the documents
 // ---------------------------------------------------------------------------
+constexpr int SETUP_RANK_DOCS = 1024;  // documents ranked by length (beyond: cu_seqlens order)
+
 __global__ __launch_bounds__(1024) void kda_bwd_setup_kernel(const int32_t* __restrict__ cu,
                                                              int n_docs, int T, int n_slots,
                                                              ChunkDesc* __restrict__ table,
+                                                             int* __restrict__ order,
                                                              int* __restrict__ bad,
                                                              int* __restrict__ status_word) {
   __shared__ int s_bad;
@@ -283,6 +287,24 @@ __global__ __launch_bounds__(1024) void kda_bwd_setup_kernel(const int32_t* __re
     const int first = a / CH + d;
     for (int j = 0; CH * j < b - a; ++j)
       table[first + j] = ChunkDesc{a + CH * j, min(CH, b - a - CH * j), d, 0};
+  }
+  // longest document first (ties by index), so that the longest sequential
+  // chains start first: order[rank] = document
+  __shared__ int s_len[SETUP_RANK_DOCS];
+  if (n_docs <= SETUP_RANK_DOCS) {
+    for (int d = tid; d < n_docs; d += 1024) s_len[d] = cu ? cu[d + 1] - cu[d] : T;
+    __syncthreads();
+    for (int d = tid; d < n_docs; d += 1024) {
+      const int len = s_len[d];
+      int rank = 0;
+      for (int e = 0; e < n_docs; ++e) {
+        const int le = s_len[e];
+        rank += (le > len || (le == len && e < d)) ? 1 : 0;
+      }
+      order[rank] = d;
+    }
+  } else {
+    for (int d = tid; d < n_docs; d += 1024) order[d] = d;
   }
 }
 
@@ -572,8 +594,9 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_prep_kernel(
 // chain: per (document, head, half of the value columns), last chunk first:
 // dS <- F^T dS + R.  F^T acts on the key index, so the value columns of dS
 // evolve independently: each (document, head) chain is split over two
-// workgroups of CV columns (blockIdx.y), which halves the product on the
-// sequential path of a chunk.
+// workgroups of CV columns, which halves the product on the sequential path
+// of a chunk.  Workgroups take documents longest first (order, from the setup
+// kernel), both halves of a chain next to each other.
 // ---------------------------------------------------------------------------
 constexpr int CV = DV / 2;  // value columns per chain workgroup
 
@@ -584,12 +607,15 @@ struct ChainSmem {
 
 __global__ __launch_bounds__(NT, 1) void kda_bwd_chain_kernel(
     const int32_t* __restrict__ cu, int T, int H, const int* __restrict__ bad,
-    const float* __restrict__ fts, const float* __restrict__ rs, const float* __restrict__ dht,
-    float* __restrict__ dstates, float* __restrict__ dh0) {
+    const int* __restrict__ order, const float* __restrict__ fts, const float* __restrict__ rs,
+    const float* __restrict__ dht, float* __restrict__ dstates, float* __restrict__ dh0) {
   __shared__ ChainSmem sm;
   if (*bad) return;
   const int tid = threadIdx.x;
-  const int d = blockIdx.x / H, h = blockIdx.x - d * H, v0 = CV * (int)blockIdx.y;
+  constexpr int NH = DV / CV;  // workgroups per chain
+  const int rk = blockIdx.x / (H * NH), rem = blockIdx.x - rk * (H * NH);
+  const int h = rem / NH, v0 = CV * (rem - h * NH);
+  const int d = order[rk];
   const int a = cu ? cu[d] : 0, b = cu ? cu[d + 1] : T;
   const int first = a / CH + d;
   const int n = (b - a + CH - 1) / CH;
@@ -1119,7 +1145,8 @@ extern "C" int kda_chunk_bwd(const void* q, const void* k, const void* v, const 
   if (H < 1) return fail(KDA_ERR_BAD_SHAPE, "H must be >= 1");
   if (H > KDA_MAX_HEADS) return fail(KDA_ERR_BAD_SHAPE, "H must be <= KDA_MAX_HEADS");
   if (n_docs < 1) return fail(KDA_ERR_BAD_SHAPE, "n_docs must be >= 1");
-  if ((int64_t)n_docs * H > INT32_MAX) return fail(KDA_ERR_BAD_SHAPE, "n_docs * H must be <= INT32_MAX");
+  if ((int64_t)n_docs * H * (DV / CV) > INT32_MAX)
+    return fail(KDA_ERR_BAD_SHAPE, "2 * n_docs * H must be <= INT32_MAX");
   if (!cu_seqlens && n_docs != 1) return fail(KDA_ERR_BAD_SHAPE, "n_docs must be 1 when cu_seqlens is NULL");
   if (T == 0 && !d_initial_state) return KDA_OK;
   if (T > 0) {
@@ -1154,13 +1181,14 @@ extern "C" int kda_chunk_bwd(const void* q, const void* k, const void* v, const 
   if (kda_host::device(&num_cu, &status_word) != 0)
     return fail(KDA_ERR_HIP, "device query (CU count, status word) failed");
 
-  // workspace: bad | table | states | dstates | images | F^T | R | prep scratch | grads scratch | o
+  // workspace: bad | table | order | states | dstates | images | F^T | R | prep scratch | grads scratch | o
   const size_t n_slots = (size_t)T / CH + (size_t)n_docs + 1;
   const size_t items = n_slots * (size_t)H;
   const int grid = num_cu;
   auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
   size_t off = 256;
   const size_t off_table = off; off = al(off + sizeof(ChunkDesc) * n_slots);
+  const size_t off_order = off; off = al(off + sizeof(int) * (size_t)n_docs);
   const size_t off_states = off; off = al(off + sizeof(float) * items * DK * DV);
   const size_t off_dstates = off; off = al(off + sizeof(float) * items * DK * DV);
   const size_t off_img = off; off = al(off + sizeof(float) * items * IMG_FLOATS);
@@ -1174,6 +1202,7 @@ extern "C" int kda_chunk_bwd(const void* q, const void* k, const void* v, const 
     return fail(KDA_ERR_ALLOC, "hipMallocAsync of the backward workspace failed");
   int* bad = reinterpret_cast<int*>(ws);
   ChunkDesc* table = reinterpret_cast<ChunkDesc*>(ws + off_table);
+  int* order = reinterpret_cast<int*>(ws + off_order);
   float* states = reinterpret_cast<float*>(ws + off_states);
   float* dstates = reinterpret_cast<float*>(ws + off_dstates);
   float* imgs = reinterpret_cast<float*>(ws + off_img);
@@ -1186,7 +1215,7 @@ extern "C" int kda_chunk_bwd(const void* q, const void* k, const void* v, const 
   int rc = KDA_OK;
   hipError_t e = hipSuccess;
   hipLaunchKernelGGL(kda_bwd_setup_kernel, dim3(1), dim3(1024), 0, stream, cu_seqlens, (int)n_docs,
-                     (int)T, (int)n_slots, table, bad, status_word);
+                     (int)T, (int)n_slots, table, order, bad, status_word);
   e = hipGetLastError();
   if (e == hipSuccess && T > 0) {
     rc = kda_host::forward_with_chunk_states(q, k, v, g, beta, cu_seqlens, n_docs, T, H,
@@ -1200,8 +1229,9 @@ extern "C" int kda_chunk_bwd(const void* q, const void* k, const void* v, const 
     }
   }
   if (e == hipSuccess && rc == KDA_OK) {
-    hipLaunchKernelGGL(kda_bwd_chain_kernel, dim3(n_docs * H, DV / CV), dim3(NT), 0, stream, cu_seqlens,
-                       (int)T, (int)H, bad, fts, rs, d_final_state, dstates, d_initial_state);
+    hipLaunchKernelGGL(kda_bwd_chain_kernel, dim3(n_docs * H * (DV / CV)), dim3(NT), 0, stream,
+                       cu_seqlens, (int)T, (int)H, bad, order, fts, rs, d_final_state, dstates,
+                       d_initial_state);
     e = hipGetLastError();
   }
   if (e == hipSuccess && rc == KDA_OK && T > 0) {
