@@ -241,6 +241,23 @@ def test_backward_many_tiny_documents():
     _check(inp, do, got, h0, dht, "bwd tiny documents")
 
 
+def test_backward_more_documents_than_ranked():
+    """1100 documents, more than the setup kernel ranks by length (their
+    state-gradient chains then run in cu_seqlens order): 1 to 5 tokens each,
+    two of them longer, with states."""
+    rng = np.random.default_rng(73)
+    lengths = [int(x) for x in rng.integers(1, 6, size=1100)]
+    lengths[17], lengths[900] = 130, 70
+    T, H = sum(lengths), 1
+    inp = make_inputs(T, H, 73, cu_from_lengths(lengths))
+    do = _dout(T, H, 73)
+    h0 = initial_states(len(lengths), H, 73)
+    dht = np.ascontiguousarray(initial_states(len(lengths), H, 74))
+    log(f"[case] bwd {len(lengths)} documents (unranked chain order), T={T}")
+    got = _run(inp, do, h0, dht)
+    _check(inp, do, got, h0, dht, "bwd 1100 documents")
+
+
 def test_backward_gate_at_the_lowest_bound():
     """g = -5.5 on every token and channel (the lowest bound the interface
     accepts): every decay split of the backward takes its widest factors,
