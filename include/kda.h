@@ -192,8 +192,8 @@ int kda_recurrent_fwd(const void* q, const void* k, const void* v, const float* 
  * image and its transition (about 400 KiB), plus a bf16 copy of the forward
  * output.
  * Errors: as kda_chunk_fwd_state, plus KDA_ERR_NULL_PTR for d_out and the
- * gradient outputs and KDA_ERR_BAD_SHAPE when 2 * n_docs * H exceeds
- * INT32_MAX (one state-gradient chain per document, head and half of the
+ * gradient outputs and KDA_ERR_BAD_SHAPE when 4 * n_docs * H exceeds
+ * INT32_MAX (one state-gradient chain per document, head and quarter of the
  * value columns); a cu_seqlens that breaks its contract sets
  * KDA_DEV_BAD_CU_SEQLENS and fills every gradient output with NaN.
  */

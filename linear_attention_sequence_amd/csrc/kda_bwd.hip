@@ -28,7 +28,7 @@
 //   2. kda_bwd_setup_kernel: cu_seqlens check and the chunk table;
 //   3. kda_bwd_prep_kernel (parallel over chunks): qh, kh, G, T, Kk, M and
 //      F^T, R of every chunk;
-//   4. kda_bwd_chain_kernel (per document, head and half of the value
+//   4. kda_bwd_chain_kernel (per document, head and quarter of the value
 //      columns, last chunk first): dS <- F^T dS + R, storing dS at every
 //      chunk end;
 //   5. kda_bwd_grads_kernel (parallel over chunks): all input gradients.
@@ -591,14 +591,14 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_prep_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// chain: per (document, head, half of the value columns), last chunk first:
-// dS <- F^T dS + R.  F^T acts on the key index, so the value columns of dS
-// evolve independently: each (document, head) chain is split over two
-// workgroups of CV columns, which halves the product on the sequential path
+// chain: per (document, head, quarter of the value columns), last chunk
+// first: dS <- F^T dS + R.  F^T acts on the key index, so the value columns
+// of dS evolve independently: each (document, head) chain is split over four
+// workgroups of CV columns, which quarters the product on the sequential path
 // of a chunk.  Workgroups take documents longest first (order, from the setup
-// kernel), both halves of a chain next to each other.
+// kernel), the four parts of a chain next to each other.
 // ---------------------------------------------------------------------------
-constexpr int CV = DV / 2;  // value columns per chain workgroup
+constexpr int CV = DV / 4;  // value columns per chain workgroup
 
 struct ChainSmem {
   float ds[DK][CV + 1];
@@ -1146,7 +1146,7 @@ extern "C" int kda_chunk_bwd(const void* q, const void* k, const void* v, const 
   if (H > KDA_MAX_HEADS) return fail(KDA_ERR_BAD_SHAPE, "H must be <= KDA_MAX_HEADS");
   if (n_docs < 1) return fail(KDA_ERR_BAD_SHAPE, "n_docs must be >= 1");
   if ((int64_t)n_docs * H * (DV / CV) > INT32_MAX)
-    return fail(KDA_ERR_BAD_SHAPE, "2 * n_docs * H must be <= INT32_MAX");
+    return fail(KDA_ERR_BAD_SHAPE, "4 * n_docs * H must be <= INT32_MAX");
   if (!cu_seqlens && n_docs != 1) return fail(KDA_ERR_BAD_SHAPE, "n_docs must be 1 when cu_seqlens is NULL");
   if (T == 0 && !d_initial_state) return KDA_OK;
   if (T > 0) {
