@@ -178,6 +178,7 @@ def _call_bwd(**kw):
     (dict(T=-1), kda.KDA_ERR_BAD_SHAPE, "T must be >= 0"),
     (dict(n_docs=0), kda.KDA_ERR_BAD_SHAPE, "n_docs must be >= 1"),
     (dict(n_docs=3), kda.KDA_ERR_BAD_SHAPE, "n_docs must be 1 when cu_seqlens is NULL"),
+    (dict(n_docs=2**28, cu=P), kda.KDA_ERR_BAD_SHAPE, "4 * n_docs * H"),
     (dict(do=None), kda.KDA_ERR_NULL_PTR, "d_out is NULL"),
     (dict(dg=None), kda.KDA_ERR_NULL_PTR, "a gradient output is NULL"),
     (dict(chunk=16), kda.KDA_ERR_UNSUPPORTED, "chunk must be 64"),
