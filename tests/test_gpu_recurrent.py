@@ -89,6 +89,22 @@ def test_short_documents_with_states(gate_scale):
     np.testing.assert_array_equal(ht_np[6], h0[6])
 
 
+@pytest.mark.parametrize("gate", ["zero", "lowest"])
+def test_extreme_gates_with_states(gate):
+    """g = 0 everywhere (no decay: the state keeps every token) over a
+    200-token document, and g = -5.5 everywhere (the lowest accepted gate),
+    with initial and final states."""
+    import dataclasses
+    lengths = [200, 17, 1]
+    T, H = sum(lengths), 2
+    base = make_inputs(T, H, 68, cu_from_lengths(lengths))
+    inp = dataclasses.replace(base, g=np.full_like(base.g, 0.0 if gate == "zero" else -5.5))
+    h0 = initial_states(len(lengths), H, 68)
+    log(f"[case] recurrent extreme gate {gate}")
+    o, ht = _rec(to_device(inp), h0)
+    _check(inp, o, ht, h0, f"recurrent gate {gate}", state_tol=1e-4)
+
+
 def test_no_states_and_dense_batch():
     import torch
     import linear_attention_sequence_amd as kda
