@@ -116,6 +116,22 @@ def test_split_and_fused_states_are_bit_identical(monkeypatch):
     assert bool((s1 == s2).all())
 
 
+def test_no_decay_with_states(monkeypatch):
+    """g = 0 (the initial state never decays and every token stays in the
+    state) over a 2048-token and a 300-token document: the slowest-decaying
+    case of the chunked state path, fused and split, which agree bit for bit."""
+    lengths = [2048, 300]
+    T, H = sum(lengths), 2
+    inp = with_gate_scale(make_inputs(T, H, 91, cu_from_lengths(lengths)), 91, 0.0)
+    h0 = initial_states(len(lengths), H, 91)
+    monkeypatch.setenv("KDA_SPLIT", "never")
+    o1, s1 = _run(inp, h0)
+    monkeypatch.setenv("KDA_SPLIT", "always")
+    o2, s2 = _run(inp, h0)
+    assert bool((o1 == o2).all()) and bool((s1 == s2).all())
+    _check(inp, o2, s2, h0, "state, no decay")
+
+
 def test_initial_state_only_and_final_state_only():
     lengths = [333, 1000]
     T, H = sum(lengths), 3
