@@ -195,6 +195,21 @@ def test_backward_special_inputs():
     _check(inp2, do, got2, None, None, "bwd g = 0")
 
 
+def test_backward_no_decay_long_document():
+    """g = 0 over a 1024-token document (16 chunks) and a short one, with an
+    initial state and a final-state gradient: nothing decays, so the state
+    gradient of the last chunk reaches the first undiminished."""
+    lengths = [1024, 40]
+    T, H = sum(lengths), 1
+    inp = with_gate_scale(make_inputs(T, H, 86, cu_from_lengths(lengths)), 86, 0.0)
+    do = _dout(T, H, 86)
+    h0 = initial_states(len(lengths), H, 86)
+    dht = np.ascontiguousarray(initial_states(len(lengths), H, 87))
+    log(f"[case] bwd no decay, T={T}")
+    got = _run(inp, do, h0, dht)
+    _check(inp, do, got, h0, dht, "bwd no decay, 1024 tokens")
+
+
 def test_backward_packed_stream_sampled_heads():
     """The 32768-token packed lognormal stream (H = 32), every document, two
     sampled heads; the same launch configuration as the backward benchmark."""
