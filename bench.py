@@ -107,6 +107,10 @@ def cpu_baseline(inp, lengths, sample_heads):
     tasks = [(int(a), int(b), h, h + 1) for a, b in zip(cu[:-1], cu[1:]) if b > a
              for h in sample_heads]
     workers = oracle.default_workers()
+    try:
+        host_cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        host_cores = os.cpu_count()
     t0 = time.perf_counter()
     n = 0
     for (a, b, h0, h1), _ in oracle.kda_tasks(inp.q, inp.k, inp.v, inp.g, inp.beta, tasks,
@@ -118,10 +122,12 @@ def cpu_baseline(inp, lengths, sample_heads):
         "value": token_heads_per_s / H,
         "unit": "tokens/s",
         "cores": workers,
+        "host_cores": host_cores,
         "kind": "oracle",
         "sample": (f"fp64 token-by-token oracle on all {len(lengths)} documents x "
-                   f"{len(sample_heads)} of {H} heads ({n} token-heads, {wall:.1f} s wall); "
-                   f"tokens/s = token-heads/s / {H}"),
+                   f"{len(sample_heads)} of {H} heads ({n} token-heads, {wall:.1f} s wall) on "
+                   f"{workers} worker processes, one per core up to 12 of the {host_cores} "
+                   f"cores this process may use; tokens/s = token-heads/s / {H}"),
     }
 
 
@@ -141,6 +147,43 @@ def time_steps(step, steps, warmup):
     ev1.record(stream)
     torch.cuda.synchronize()
     return ev0.elapsed_time(ev1) / steps
+
+
+def time_calls(step, steps, warmup, flush=None):
+    """Per-call ms of ``steps`` calls after ``warmup``: a pair of HIP events on
+    the launch stream around each call.  ``flush`` (untimed, before each call)
+    evicts the caches.  Returns (per-call ms list, wall seconds of the timed
+    loop)."""
+    import torch
+    for _ in range(warmup):
+        if flush is not None:
+            flush()
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in evs:
+        if flush is not None:
+            flush()
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return [a.elapsed_time(b) for a, b in evs], wall
+
+
+def cache_flusher(dev):
+    """A 1 GiB device write: larger than the 256 MB Infinity Cache and the L2s."""
+    import torch
+    buf = torch.empty(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
+
+    def flush():
+        buf.fill_(1.0)
+    return flush
 
 
 PEAK_FP32_MFMA_TFLOPS = 157.3  # dense fp32 MFMA
@@ -277,38 +320,11 @@ def decode_bench(args):
     }), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", type=int, default=METRIC_WORKLOAD)
-    ap.add_argument("--copy-probe", action="store_true")
-    ap.add_argument("--with-state", action="store_true")
-    ap.add_argument("--decode", type=int, default=0, metavar="N")
-    ap.add_argument("--backward", action="store_true")
-    ap.add_argument("--peaks", action="store_true")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: the KDA forward here is a single-GPU "
-              "operator (multi-GPU sharding is a design note, not built)", file=sys.stderr)
-        sys.exit(2)
-
+def forward_bench(args):
+    """kda_chunk_fwd on workload ``args.workload``: one JSON line."""
     import torch
     import linear_attention_sequence_amd as kda
     from kda_workloads import initial_states, workload_inputs
-
-    kda.load_library()
-    if args.decode:
-        decode_bench(args)
-        return
-    if args.backward:
-        backward_bench(args)
-        return
-    if args.peaks:
-        peaks_bench()
-        return
     w, inp = workload_inputs(args.workload)
     T = w.T
     dev = torch.device("cuda:0")
@@ -329,21 +345,15 @@ def main():
     def step():
         kda.chunk_fwd(q, k, v, g, beta, cu, out=out, **state_kw)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / args.steps
+    per_call, wall = time_calls(step, args.steps, args.warmup)
+    ms = float(np.median(per_call))
+    flushed = None
+    if args.workload in (1, 2):
+        # these fit in the Infinity Cache: also time them with it flushed
+        fl, _ = time_calls(step, args.steps, args.warmup, flush=cache_flusher(dev))
+        flushed = {"median_ms": float(np.median(fl)), "mean_ms": float(np.mean(fl)),
+                   "tokens_per_s": T / (float(np.median(fl)) / 1e3),
+                   "flush": "1 GiB device write before each call (untimed)"}
     status = kda.device_status()
 
     if args.copy_probe:
@@ -363,9 +373,12 @@ def main():
         bytes_alg += 2 * n_docs * H * DK * DV * 4   # initial state read, final state written
     tflops = flops / sec / 1e12
     gbs = bytes_alg / sec / 1e9
-    log(f"[bench] {w.name}: {ms * 1e3:.1f} us/call, {tokens_per_s:.4g} tokens/s, "
+    log(f"[bench] {w.name}: median {ms * 1e3:.1f} us/call (mean {np.mean(per_call) * 1e3:.1f}, "
+        f"min {np.min(per_call) * 1e3:.1f}), {tokens_per_s:.4g} tokens/s, "
         f"{tflops:.1f} TFLOP/s ({100 * tflops / PEAK_BF16_TFLOPS:.1f}% bf16 MFMA), "
         f"{gbs:.0f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% HBM), wall {wall:.3f}s, status {status}")
+    if flushed is not None:
+        log(f"[bench] {w.name} flushed: median {flushed['median_ms'] * 1e3:.1f} us/call")
 
     result = {
         "metric": "KDA chunk fwd tokens/sec (H=32, K=V=128) + % bf16 MFMA peak",
@@ -375,6 +388,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "statistic": "median of per-call HIP-event times (warm caches)",
+        "mean_ms": float(np.mean(per_call)),
+        "min_ms": float(np.min(per_call)),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -404,9 +420,54 @@ def main():
         },
         "device_status": status,
     }
-    if not args.no_cpu_baseline:
+    if flushed is not None:
+        result["flushed"] = flushed
+    if not args.no_cpu_baseline and args.workload == METRIC_WORKLOAD:
         result["cpu_baseline"] = cpu_baseline(inp, w.lengths, sample_heads=list(range(0, H, 2)))
     print(json.dumps(result), flush=True)
+
+    del q, k, v, g, beta, cu, out, state_kw
+    torch.cuda.empty_cache()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--sweep", action="store_true",
+                    help="one JSON line per workload 1..5 (warm; workloads 1-2 also flushed)")
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", type=int, default=METRIC_WORKLOAD)
+    ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--with-state", action="store_true")
+    ap.add_argument("--decode", type=int, default=0, metavar="N")
+    ap.add_argument("--backward", action="store_true")
+    ap.add_argument("--peaks", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the KDA forward here is a single-GPU "
+              "operator (multi-GPU sharding is a design note, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import linear_attention_sequence_amd as kda
+
+    kda.load_library()
+    if args.decode:
+        decode_bench(args)
+        return
+    if args.backward:
+        backward_bench(args)
+        return
+    if args.peaks:
+        peaks_bench()
+        return
+    if args.sweep:
+        for idx in range(1, 6):
+            args.workload = idx
+            forward_bench(args)
+        return
+    forward_bench(args)
 
 
 if __name__ == "__main__":

@@ -28,31 +28,12 @@
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
+#include "kda_status.h"
+
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-/* Return codes of kda_chunk_fwd (0 = success). */
-enum kda_status {
-  KDA_OK = 0,
-  KDA_ERR_NULL_PTR = -1,    /* a required pointer is NULL                              */
-  KDA_ERR_BAD_SHAPE = -2,   /* T < 0, T > INT32_MAX, H < 1 or H > KDA_MAX_HEADS         */
-  KDA_ERR_UNSUPPORTED = -3, /* chunk != 64, or gate_bound not finite or outside [-5.5, 0) */
-  KDA_ERR_ALIGN = -4,       /* q, k, v, g, out not 16-byte aligned; beta, cu_seqlens not 4-byte aligned */
-  KDA_ERR_HIP = -5,         /* a HIP runtime call or kernel launch failed              */
-  KDA_ERR_ALLOC = -6        /* the stream-ordered workspace allocation failed          */
-};
-
-/* Bits of the sticky device status word (kda_device_status). */
-enum kda_device_flags {
-  KDA_DEV_BAD_CU_SEQLENS = 1, /* cu_seqlens broke its contract; out was filled with NaN  */
-  KDA_DEV_GATE_RANGE = 2      /* some g fell outside [gate_bound, 0] (or was NaN); the
-                                 result was still computed, without clamping             */
-};
-
-#define KDA_HEAD_DIM 128
-#define KDA_CHUNK 64
-#define KDA_MAX_HEADS 4096
 
 /*
  * kda_chunk_fwd -- o = KDA(q, k, v, g, beta) over a packed token stream.
@@ -84,14 +65,12 @@ enum kda_device_flags {
  *
  * Ownership: the caller owns every buffer and keeps it alive until the stream
  * has passed this call.  The library allocates one stream-ordered workspace
- * per call (hipMallocAsync / hipFreeAsync on `stream`) and never syncs the
+ * per call (hipMallocFromPoolAsync / hipFreeAsync on `stream`, from a memory
+ * pool the library creates per device; it keeps up to 8 GiB reserved between
+ * calls and leaves the device's default pool untouched) and never syncs the
  * host: a document list (8 B per token) and room for the intermediate chunk
- * images of long documents (up to about 1.2 KB per token and head, at most
- * 16 GiB; the device's default memory pool keeps it between calls).
- *
- * Environment: KDA_SPLIT=never|always overrides the automatic choice of the
- * documents whose chunks are prepared in parallel (for tests; the output is
- * the same bit for bit).
+ * images of long documents (up to about 1 KB per token and head, at most
+ * 16 GiB).
  *
  * Errors: returns KDA_OK or the negative kda_status of the FIRST violated
  * condition, checked in this order: shape (T, H), then (unless T = 0) NULL
@@ -152,7 +131,8 @@ int kda_chunk_fwd_state(const void* q, const void* k, const void* v, const float
  *
  * Arguments as for kda_chunk_fwd_state, without chunk and gate_bound (no
  * decay factorisation is used, so g only needs to be finite; g <= 0 keeps the
- * state bounded).  cu_seqlens [n_docs+1] is read exactly; n_docs * H <= 2^30.
+ * state bounded).  cu_seqlens [n_docs+1] is read exactly; n_docs * H <= 2^25
+ * (the launch runs 2 x 64 work-items per document and head, below 2^32).
  * initial_state / final_state may be NULL or the same buffer (decode updates
  * the state in place).
  *
@@ -192,9 +172,10 @@ int kda_recurrent_fwd(const void* q, const void* k, const void* v, const float* 
  * image and its transition (about 400 KiB), plus a bf16 copy of the forward
  * output.
  * Errors: as kda_chunk_fwd_state, plus KDA_ERR_NULL_PTR for d_out and the
- * gradient outputs and KDA_ERR_BAD_SHAPE when 4 * n_docs * H exceeds
- * INT32_MAX (one state-gradient chain per document, head and quarter of the
- * value columns); a cu_seqlens that breaks its contract sets
+ * gradient outputs and KDA_ERR_BAD_SHAPE when n_docs * H exceeds 2^21 (one
+ * state-gradient chain of 512 work-items per document, head and quarter of
+ * the value columns, below 2^32 work-items per launch); a cu_seqlens that
+ * breaks its contract sets
  * KDA_DEV_BAD_CU_SEQLENS and fills every gradient output with NaN.
  */
 int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
@@ -204,20 +185,35 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
                   float* dg, float* dbeta, float* d_initial_state, hipStream_t stream);
 
 /*
- * kda_last_error -- message for the last non-zero return of any entry point
- * on the calling thread ("" if none).  The string is
- * owned by the library and stays valid until the next call on the same
- * thread.
+ * kda_last_error -- the first violated condition of the last non-zero return
+ * of any entry point on the calling thread ("" if none), the counterpart of
+ * fused_kda_unsupported_reason (page "nemo_automodel.components.models.
+ * kimi_k3.kda_fused", function table: it names the first condition that keeps
+ * a call off the fused kernels).  The string is owned by the library and stays
+ * valid until the next call on the same thread.
  */
 const char* kda_last_error(void);
 
 /*
- * kda_device_status -- debug/test helper: synchronises `stream`, returns the
- * sticky kda_device_flags word of the current device accumulated by all calls
- * since the last kda_device_status, and clears it.  Returns KDA_ERR_HIP if a
- * HIP call fails.  Not for the hot path (it blocks the host).
+ * kda_device_status -- debug/test helper with no counterpart on the pages:
+ * synchronises `stream`, returns the sticky kda_device_flags word of the
+ * current device accumulated by all calls since the last kda_device_status,
+ * and clears it.  Returns KDA_ERR_HIP if a HIP call fails.  Not for the hot
+ * path (it blocks the host).
  */
 int kda_device_status(hipStream_t stream);
+
+/*
+ * kda_debug_set_split_policy -- test hook with no counterpart on the pages:
+ * forces the choice of the long documents whose chunks are prepared in
+ * parallel before their sequential chain runs ("split" documents).
+ * 0 = never split, 1 = automatic (the default), 2 = split every document the
+ * workspace allows.  All three give the same output bit for bit; only the
+ * speed differs.  Process-wide; returns the previous policy, or
+ * KDA_ERR_UNSUPPORTED for another value.  Calls already enqueued keep the
+ * policy they were enqueued with.
+ */
+int kda_debug_set_split_policy(int policy);
 
 #ifdef __cplusplus
 }

@@ -86,6 +86,8 @@ def load_library():
         lib.kda_last_error.restype = ctypes.c_char_p
         lib.kda_device_status.argtypes = [ctypes.c_void_p]
         lib.kda_device_status.restype = ctypes.c_int
+        lib.kda_debug_set_split_policy.argtypes = [ctypes.c_int]
+        lib.kda_debug_set_split_policy.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -133,6 +135,22 @@ def kda_last_error() -> str:
 
 def kda_device_status(stream=None) -> int:
     return load_library().kda_device_status(stream)
+
+
+def kda_debug_set_split_policy(policy: int) -> int:
+    return load_library().kda_debug_set_split_policy(int(policy))
+
+
+SPLIT_POLICIES = {"never": 0, "auto": 1, "always": 2}
+
+
+def set_split_policy(name: str) -> str:
+    """Force the choice of split documents (test hook): ``"never"``,
+    ``"auto"`` (the default) or ``"always"``.  Returns the previous name."""
+    prev = kda_debug_set_split_policy(SPLIT_POLICIES[name])
+    if prev < 0:
+        raise KDAError(prev, "bad split policy")
+    return {v: k for k, v in SPLIT_POLICIES.items()}[prev]
 
 
 # ---------------------------------------------------------------------------

@@ -40,9 +40,12 @@
 
 #include "kda.h"
 
+#include "kda_host_checks.h"
+
 namespace kda_host {
 int fail(int code, const std::string& msg);
 int device(int* num_cu, int** status_word);
+hipError_t alloc_async(void** p, size_t bytes, hipStream_t stream);
 int forward_with_chunk_states(const void* q, const void* k, const void* v, const float* g,
                               const float* beta, const int32_t* cu, int32_t n_docs, int64_t T,
                               int32_t H, float gate_bound, const float* h0, void* out,
@@ -1128,8 +1131,6 @@ __global__ void kda_bwd_nan_kernel(const int* __restrict__ bad, float* dq, float
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_state; i += stride) dh0[i] = nan;
 }
 
-bool aligned(const void* p, uintptr_t al) { return (reinterpret_cast<uintptr_t>(p) & (al - 1)) == 0; }
-
 }  // namespace
 
 extern "C" int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
@@ -1140,41 +1141,12 @@ extern "C" int kda_chunk_bwd(const void* q, const void* k, const void* v, const 
                              float* dg, float* dbeta, float* d_initial_state, hipStream_t stream) {
   using kda_host::fail;
   fail(KDA_OK, "");
-  if (T < 0) return fail(KDA_ERR_BAD_SHAPE, "T must be >= 0");
-  if (T > INT32_MAX) return fail(KDA_ERR_BAD_SHAPE, "T must be <= INT32_MAX");
-  if (H < 1) return fail(KDA_ERR_BAD_SHAPE, "H must be >= 1");
-  if (H > KDA_MAX_HEADS) return fail(KDA_ERR_BAD_SHAPE, "H must be <= KDA_MAX_HEADS");
-  if (n_docs < 1) return fail(KDA_ERR_BAD_SHAPE, "n_docs must be >= 1");
-  if ((int64_t)n_docs * H * (DV / CV) > INT32_MAX)
-    return fail(KDA_ERR_BAD_SHAPE, "4 * n_docs * H must be <= INT32_MAX");
-  if (!cu_seqlens && n_docs != 1) return fail(KDA_ERR_BAD_SHAPE, "n_docs must be 1 when cu_seqlens is NULL");
-  if (T == 0 && !d_initial_state) return KDA_OK;
-  if (T > 0) {
-    if (!q) return fail(KDA_ERR_NULL_PTR, "q is NULL");
-    if (!k) return fail(KDA_ERR_NULL_PTR, "k is NULL");
-    if (!v) return fail(KDA_ERR_NULL_PTR, "v is NULL");
-    if (!g) return fail(KDA_ERR_NULL_PTR, "g is NULL");
-    if (!beta) return fail(KDA_ERR_NULL_PTR, "beta is NULL");
-    if (!d_out) return fail(KDA_ERR_NULL_PTR, "d_out is NULL");
-    if (!dq || !dk || !dv || !dg || !dbeta) return fail(KDA_ERR_NULL_PTR, "a gradient output is NULL");
-  }
-  if (chunk != 64) return fail(KDA_ERR_UNSUPPORTED, "chunk must be 64");
-  if (!(gate_bound >= -5.5f && gate_bound < 0.f))
-    return fail(KDA_ERR_UNSUPPORTED, "gate_bound must be finite and in [-5.5, 0)");
-  if (T > 0) {
-    if (!aligned(q, 16)) return fail(KDA_ERR_ALIGN, "q is not 16-byte aligned");
-    if (!aligned(k, 16)) return fail(KDA_ERR_ALIGN, "k is not 16-byte aligned");
-    if (!aligned(v, 16)) return fail(KDA_ERR_ALIGN, "v is not 16-byte aligned");
-    if (!aligned(g, 16)) return fail(KDA_ERR_ALIGN, "g is not 16-byte aligned");
-    if (!aligned(beta, 4)) return fail(KDA_ERR_ALIGN, "beta is not 4-byte aligned");
-    if (!aligned(d_out, 16)) return fail(KDA_ERR_ALIGN, "d_out is not 16-byte aligned");
-    if (!aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(dg, 16) || !aligned(dbeta, 4))
-      return fail(KDA_ERR_ALIGN, "a gradient output is not aligned");
-  }
-  if (cu_seqlens && !aligned(cu_seqlens, 4)) return fail(KDA_ERR_ALIGN, "cu_seqlens is not 4-byte aligned");
-  if (initial_state && !aligned(initial_state, 16)) return fail(KDA_ERR_ALIGN, "initial_state is not 16-byte aligned");
-  if (d_final_state && !aligned(d_final_state, 16)) return fail(KDA_ERR_ALIGN, "d_final_state is not 16-byte aligned");
-  if (d_initial_state && !aligned(d_initial_state, 16)) return fail(KDA_ERR_ALIGN, "d_initial_state is not 16-byte aligned");
+  const kda_check::Result r =
+      kda_check::chunk_bwd(q, k, v, g, beta, cu_seqlens, n_docs, T, H, chunk, gate_bound,
+                           initial_state, d_out, d_final_state, dq, dk, dv, dg, dbeta,
+                           d_initial_state);
+  if (r.code != KDA_OK) return fail(r.code, r.msg);
+  if (kda_check::bwd_is_noop(T, d_initial_state)) return KDA_OK;
 
   int num_cu = 0;
   int* status_word = nullptr;
@@ -1182,23 +1154,18 @@ extern "C" int kda_chunk_bwd(const void* q, const void* k, const void* v, const 
     return fail(KDA_ERR_HIP, "device query (CU count, status word) failed");
 
   // workspace: bad | table | order | states | dstates | images | F^T | R | prep scratch | grads scratch | o
-  const size_t n_slots = (size_t)T / CH + (size_t)n_docs + 1;
-  const size_t items = n_slots * (size_t)H;
   const int grid = num_cu;
-  auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
-  size_t off = 256;
-  const size_t off_table = off; off = al(off + sizeof(ChunkDesc) * n_slots);
-  const size_t off_order = off; off = al(off + sizeof(int) * (size_t)n_docs);
-  const size_t off_states = off; off = al(off + sizeof(float) * items * DK * DV);
-  const size_t off_dstates = off; off = al(off + sizeof(float) * items * DK * DV);
-  const size_t off_img = off; off = al(off + sizeof(float) * items * IMG_FLOATS);
-  const size_t off_ft = off; off = al(off + sizeof(float) * items * DK * DK);
-  const size_t off_r = off; off = al(off + sizeof(float) * items * DK * DV);
-  const size_t off_sp = off; off = al(off + sizeof(float) * (size_t)grid * SP_FLOATS);
-  const size_t off_sc = off; off = al(off + sizeof(float) * (size_t)grid * SC_FLOATS);
-  const size_t off_o = off; off = al(off + 2 * (size_t)T * H * DV);
+  kda_check::BwdLayout lay;
+  if (!kda_check::bwd_layout(T, H, n_docs, grid, sizeof(ChunkDesc), IMG_FLOATS, SP_FLOATS, SC_FLOATS, &lay))
+    return fail(KDA_ERR_BAD_SHAPE, "workspace size overflows");
+  const size_t n_slots = lay.n_slots;
+  const size_t items = lay.items;
+  const size_t off = lay.bytes;
+  const size_t off_table = lay.off_table, off_order = lay.off_order, off_states = lay.off_states,
+               off_dstates = lay.off_dstates, off_img = lay.off_img, off_ft = lay.off_ft,
+               off_r = lay.off_r, off_sp = lay.off_sp, off_sc = lay.off_sc, off_o = lay.off_o;
   uint8_t* ws = nullptr;
-  if (hipMallocAsync(reinterpret_cast<void**>(&ws), off, stream) != hipSuccess || !ws)
+  if (kda_host::alloc_async(reinterpret_cast<void**>(&ws), off, stream) != hipSuccess || !ws)
     return fail(KDA_ERR_ALLOC, "hipMallocAsync of the backward workspace failed");
   int* bad = reinterpret_cast<int*>(ws);
   ChunkDesc* table = reinterpret_cast<ChunkDesc*>(ws + off_table);

@@ -52,6 +52,9 @@
 // overflows fp32; off-diagonal operands are all in [0, 1] and use fp16.
 
 #include "kda_kernels.h"
+#include "kda_host_checks.h"
+
+#include <atomic>
 
 // the main kernel with state input / output (kda_fwd_state.hip)
 namespace kda_state_tu {
@@ -328,9 +331,16 @@ int fail(int code, const std::string& msg) {
   return code;
 }
 
+// Workspaces come from a memory pool the library owns, one per device (the
+// device's default pool and its attributes are left alone).  The pool keeps
+// up to KDA_POOL_KEEP_BYTES reserved between calls, so that a steady stream
+// of calls does not map and unmap its workspace every time; memory beyond
+// that goes back to the device when the stream synchronises.
+constexpr uint64_t KDA_POOL_KEEP_BYTES = uint64_t(8) << 30;
+
 struct DeviceInfo {
   int num_cu = 0;
-  bool pool_ready = false;
+  hipMemPool_t pool = nullptr;
   int* status_word = nullptr;  // device address of this device's g_kda_status
 };
 std::mutex g_mu;
@@ -346,13 +356,21 @@ int device_info(int dev, DeviceInfo** out) {
       return -1;
     d.num_cu = n;
   }
-  if (!d.pool_ready) {
-    hipMemPool_t pool;
-    if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
-      uint64_t thr = UINT64_MAX;
-      (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
+  if (d.pool == nullptr) {
+    hipMemPoolProps props;
+    memset(&props, 0, sizeof(props));
+    props.allocType = hipMemAllocationTypePinned;
+    props.handleTypes = hipMemHandleTypeNone;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool = nullptr;
+    if (hipMemPoolCreate(&pool, &props) != hipSuccess || pool == nullptr) return -1;
+    uint64_t keep = KDA_POOL_KEEP_BYTES;
+    if (hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep) != hipSuccess) {
+      (void)hipMemPoolDestroy(pool);
+      return -1;
     }
-    d.pool_ready = true;
+    d.pool = pool;
   }
   if (d.status_word == nullptr) {
     void* p = nullptr;
@@ -363,20 +381,14 @@ int device_info(int dev, DeviceInfo** out) {
   return 0;
 }
 
-bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 // Upper bound of the chunk images of split documents in the workspace.
 constexpr size_t IMAGE_BUDGET_BYTES = size_t(16) << 30;
 
-// KDA_SPLIT=never|always overrides the automatic choice of split documents
-// (for tests; both settings give bit-identical results).
-int split_policy() {
-  const char* s = getenv("KDA_SPLIT");
-  if (s == nullptr) return SPLIT_AUTO;
-  if (strcmp(s, "never") == 0) return SPLIT_NEVER;
-  if (strcmp(s, "always") == 0) return SPLIT_ALWAYS;
-  return SPLIT_AUTO;
-}
+// The choice of split documents: automatic unless a test forces it through
+// kda_debug_set_split_policy (both forced settings give bit-identical results).
+std::atomic<int> g_split_policy{SPLIT_AUTO};
+int split_policy() { return g_split_policy.load(std::memory_order_relaxed); }
 
 // One call of either entry point, after its argument checks.
 struct Call {
@@ -397,26 +409,6 @@ struct Call {
   float* chunk_states = nullptr;  // S at every chunk start (the backward's forward pass)
 };
 
-// checks shared by both entry points for the token tensors (T > 0)
-int check_tokens(const Call& c, int32_t chunk) {
-  if (!c.q) return fail(KDA_ERR_NULL_PTR, "q is NULL");
-  if (!c.k) return fail(KDA_ERR_NULL_PTR, "k is NULL");
-  if (!c.v) return fail(KDA_ERR_NULL_PTR, "v is NULL");
-  if (!c.g) return fail(KDA_ERR_NULL_PTR, "g is NULL");
-  if (!c.beta) return fail(KDA_ERR_NULL_PTR, "beta is NULL");
-  if (!c.out) return fail(KDA_ERR_NULL_PTR, "out is NULL");
-  if (chunk != KDA_CHUNK) return fail(KDA_ERR_UNSUPPORTED, "chunk must be 64");
-  if (!(c.gate_bound >= -5.5f && c.gate_bound < 0.f))
-    return fail(KDA_ERR_UNSUPPORTED, "gate_bound must be finite and in [-5.5, 0)");
-  if (!aligned(c.q, 16)) return fail(KDA_ERR_ALIGN, "q is not 16-byte aligned");
-  if (!aligned(c.k, 16)) return fail(KDA_ERR_ALIGN, "k is not 16-byte aligned");
-  if (!aligned(c.v, 16)) return fail(KDA_ERR_ALIGN, "v is not 16-byte aligned");
-  if (!aligned(c.g, 16)) return fail(KDA_ERR_ALIGN, "g is not 16-byte aligned");
-  if (!aligned(c.out, 16)) return fail(KDA_ERR_ALIGN, "out is not 16-byte aligned");
-  if (!aligned(c.beta, 4)) return fail(KDA_ERR_ALIGN, "beta is not 4-byte aligned");
-  return KDA_OK;
-}
-
 int launch(const Call& c) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(KDA_ERR_HIP, "hipGetDevice failed");
@@ -428,30 +420,21 @@ int launch(const Call& c) {
   // workspace: header | docs[n_list] | doc_ids[n_list] | split[max_split] |
   // pre_chunks[cap] | images[cap][H]
   const int policy = split_policy();
-  const size_t n_list = std::max<size_t>((size_t)T, c.n_exact > 0 ? (size_t)c.n_exact : 0);
-  const size_t max_split = std::min<size_t>((size_t)T / (CH * (MIN_SPLIT_CHUNKS - 1) + 1) + 1,
-                                            MAX_SPLIT_DOCS);
-  size_t cap_chunks = 0;
-  if (policy != SPLIT_NEVER) {
-    cap_chunks = ((size_t)T + CH - 1) / CH + max_split;
-    cap_chunks = std::min(cap_chunks, IMAGE_BUDGET_BYTES / ((size_t)H * IMG_BYTES));
-    if (cap_chunks < (size_t)MIN_SPLIT_CHUNKS) cap_chunks = 0;
-  }
-  const size_t off_docs = 256;
-  const size_t off_ids = off_docs + sizeof(int2) * n_list;
-  const size_t off_split = off_ids + ((sizeof(int) * (c.n_exact >= 0 ? n_list : 0) + 7) & ~size_t(7));
-  const size_t off_pre = off_split + sizeof(int2) * max_split;
-  const size_t off_img = (off_pre + sizeof(int2) * cap_chunks + 255) & ~size_t(255);
-  const size_t ws_bytes = off_img + cap_chunks * (size_t)H * IMG_BYTES;
+  kda_check::FwdLayout lay;
+  if (!kda_check::fwd_layout(T, H, c.n_exact, policy != SPLIT_NEVER, IMG_BYTES, IMAGE_BUDGET_BYTES,
+                             MIN_SPLIT_CHUNKS, MAX_SPLIT_DOCS, &lay))
+    return fail(KDA_ERR_BAD_SHAPE, "workspace size overflows");
+  const size_t cap_chunks = lay.cap_chunks;
+  const size_t ws_bytes = lay.bytes;
   uint8_t* ws = nullptr;
-  if (hipMallocAsync(reinterpret_cast<void**>(&ws), ws_bytes, c.stream) != hipSuccess || !ws)
-    return fail(KDA_ERR_ALLOC, "hipMallocAsync of the workspace failed");
+  if (hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws), ws_bytes, di->pool, c.stream) != hipSuccess || !ws)
+    return fail(KDA_ERR_ALLOC, "stream-ordered allocation of the workspace failed");
   WorkHeader* hdr = reinterpret_cast<WorkHeader*>(ws);
-  int2* docs = reinterpret_cast<int2*>(ws + off_docs);
-  int* doc_ids = c.n_exact >= 0 ? reinterpret_cast<int*>(ws + off_ids) : nullptr;
-  int2* split = reinterpret_cast<int2*>(ws + off_split);
-  int2* pre_chunks = reinterpret_cast<int2*>(ws + off_pre);
-  uint8_t* images = ws + off_img;
+  int2* docs = reinterpret_cast<int2*>(ws + lay.off_docs);
+  int* doc_ids = c.n_exact >= 0 ? reinterpret_cast<int*>(ws + lay.off_ids) : nullptr;
+  int2* split = reinterpret_cast<int2*>(ws + lay.off_split);
+  int2* pre_chunks = reinterpret_cast<int2*>(ws + lay.off_pre);
+  uint8_t* images = ws + lay.off_img;
 
   hipLaunchKernelGGL(kda_schedule_kernel, dim3(1), dim3(SCHED_THREADS), 0, c.stream, c.cu,
                      (int)T, H, di->num_cu, (int)cap_chunks, policy, c.n_exact, c.h0, c.ht,
@@ -506,21 +489,26 @@ int device(int* num_cu, int** status_word) {
   *status_word = di->status_word;
   return 0;
 }
+// stream-ordered workspace from the library's pool of the current device
+hipError_t alloc_async(void** p, size_t bytes, hipStream_t stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  DeviceInfo* di = nullptr;
+  if (device_info(dev, &di) != 0) return hipErrorInvalidDevice;
+  return hipMallocFromPoolAsync(p, bytes, di->pool, stream);
+}
 }  // namespace kda_host
 
 extern "C" int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                              const float* beta, const int32_t* cu_seqlens, int64_t T, int32_t H,
                              int32_t chunk, float gate_bound, void* out, hipStream_t stream) {
   t_last_error.clear();
-  if (T < 0) return fail(KDA_ERR_BAD_SHAPE, "T must be >= 0");
-  if (T > INT32_MAX) return fail(KDA_ERR_BAD_SHAPE, "T must be <= INT32_MAX");
-  if (H < 1) return fail(KDA_ERR_BAD_SHAPE, "H must be >= 1");
-  if (H > KDA_MAX_HEADS) return fail(KDA_ERR_BAD_SHAPE, "H must be <= KDA_MAX_HEADS");
+  const kda_check::Result r =
+      kda_check::chunk_fwd(q, k, v, g, beta, cu_seqlens, T, H, chunk, gate_bound, out);
+  if (r.code != KDA_OK) return fail(r.code, r.msg);
   if (T == 0) return KDA_OK;
   const Call c{q, k, v, g, beta, cu_seqlens, T, H, gate_bound, out, -1, nullptr, nullptr, stream};
-  const int rc = check_tokens(c, chunk);
-  if (rc != KDA_OK) return rc;
-  if (cu_seqlens && !aligned(cu_seqlens, 4)) return fail(KDA_ERR_ALIGN, "cu_seqlens is not 4-byte aligned");
   return launch(c);
 }
 
@@ -530,31 +518,22 @@ extern "C" int kda_chunk_fwd_state(const void* q, const void* k, const void* v, 
                                    const float* initial_state, float* final_state, void* out,
                                    hipStream_t stream) {
   t_last_error.clear();
-  if (T < 0) return fail(KDA_ERR_BAD_SHAPE, "T must be >= 0");
-  if (T > INT32_MAX) return fail(KDA_ERR_BAD_SHAPE, "T must be <= INT32_MAX");
-  if (H < 1) return fail(KDA_ERR_BAD_SHAPE, "H must be >= 1");
-  if (H > KDA_MAX_HEADS) return fail(KDA_ERR_BAD_SHAPE, "H must be <= KDA_MAX_HEADS");
-  if (n_docs < 1) return fail(KDA_ERR_BAD_SHAPE, "n_docs must be >= 1");
-  if ((int64_t)n_docs * H > INT32_MAX) return fail(KDA_ERR_BAD_SHAPE, "n_docs * H must be <= INT32_MAX");
-  if (!cu_seqlens && n_docs != 1) return fail(KDA_ERR_BAD_SHAPE, "n_docs must be 1 when cu_seqlens is NULL");
-  if (T == 0 && !final_state) return KDA_OK;
+  const kda_check::Result r =
+      kda_check::chunk_fwd_state(q, k, v, g, beta, cu_seqlens, n_docs, T, H, chunk, gate_bound,
+                                 initial_state, final_state, out);
+  if (r.code != KDA_OK) return fail(r.code, r.msg);
+  if (kda_check::fwd_is_noop(T, final_state)) return KDA_OK;
   const Call c{q, k, v, g, beta, cu_seqlens, T, H, gate_bound, out, n_docs, initial_state,
                final_state, stream};
-  if (T > 0) {
-    const int rc = check_tokens(c, chunk);
-    if (rc != KDA_OK) return rc;
-  } else if (chunk != KDA_CHUNK) {
-    return fail(KDA_ERR_UNSUPPORTED, "chunk must be 64");
-  }
-  if (cu_seqlens && !aligned(cu_seqlens, 4)) return fail(KDA_ERR_ALIGN, "cu_seqlens is not 4-byte aligned");
-  if (initial_state && !aligned(initial_state, 16))
-    return fail(KDA_ERR_ALIGN, "initial_state is not 16-byte aligned");
-  if (final_state && !aligned(final_state, 16))
-    return fail(KDA_ERR_ALIGN, "final_state is not 16-byte aligned");
   return launch(c);
 }
 
 extern "C" const char* kda_last_error(void) { return t_last_error.c_str(); }
+
+extern "C" int kda_debug_set_split_policy(int policy) {
+  if (policy < SPLIT_NEVER || policy > SPLIT_ALWAYS) return KDA_ERR_UNSUPPORTED;
+  return g_split_policy.exchange(policy);
+}
 
 extern "C" int kda_device_status(hipStream_t stream) {
   if (hipStreamSynchronize(stream) != hipSuccess) return KDA_ERR_HIP;

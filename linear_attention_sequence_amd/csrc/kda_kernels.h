@@ -475,22 +475,28 @@ __device__ __forceinline__ float wave_max(float x) {
   return fmaxf(fmaxf(a, b), fmaxf(c, d));
 }
 
-// fp16 operands: the power of two e >= 0 that brings a largest magnitude m
-// below 2^14 (e = 0 for m < 2^14), as the biased-exponent bits of 2^-e and 2^e
+// fp16 operands are stored as x 2^-e for a power of two 2^e chosen from the
+// largest magnitude m of the values that share it: e = 0 when 2^-4 <= m < 2^14
+// (then fp16 holds every value to its relative precision, or to an absolute
+// 2^-25, far below m's rounding), and otherwise the e that brings m into
+// [2^13, 2^14), in both directions: large values are scaled down so that they
+// fit, small ones (v or beta near zero) up, out of the fp16 subnormal range.
+// Multiplying by a power of two is exact, so the scaled and the unscaled
+// products round the same wherever neither is subnormal.
 __device__ __forceinline__ int f16_exponent(float m) {
+  if (m >= 0.0625f && m < 16384.f) return 0;
   const int ex = (__float_as_int(m) >> 23) & 0xFF;
-  return max(0, ex - (127 + 13));
+  if (ex == 0) return 0;                          // zero: nothing to scale
+  return min(max(ex - (127 + 13), -100), 100);    // 2^+-e stays a normal float
 }
 __device__ __forceinline__ float pow2i(int e) { return __int_as_float((127 + e) << 23); }
-// the exponent for the wave's largest lane value m: 0 unless some lane has
-// m >= 2^14 (the common case costs one compare and a ballot)
+// the exponent for the wave's largest lane value m: the common case (some
+// lane at or above 2^-4, none at or above 2^14) costs two compares and two
+// ballots; otherwise the wave's maximum picks it
 __device__ __forceinline__ int wave_f16_exponent(float m) {
-  if (__builtin_amdgcn_ballot_w64(m >= 16384.f) == 0) return 0;
+  if (__builtin_amdgcn_ballot_w64(m >= 16384.f) == 0 && __builtin_amdgcn_ballot_w64(m >= 0.0625f) != 0)
+    return 0;
   return f16_exponent(wave_max(m));
-}
-
-__device__ __forceinline__ f32x4 mfma16k16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
 // Per-channel decay factors of a chunk from the sub-block totals t_w (log2
@@ -1033,8 +1039,9 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
     for (int j = 0; j < 8; ++j) {
       Uh[s][j] = (_Float16)(U[s >> 1][8 * (s & 1) + j] * udown);
     }
-  if (eu != 0) {
-    // M U is computed as M (U 2^-eu): bring Qt S to the same scale
+  if (eu > 0) {
+    // M U is computed as M (U 2^-eu) with U scaled down: bring Qt S to the
+    // same scale (S 2^-eu cannot overflow)
 #pragma unroll
     for (int s = 0; s < 8; ++s)
 #pragma unroll
@@ -1048,12 +1055,35 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
   // one accumulator per row tile
   unsigned short (*ost)[32] = sm.u2.ws[w].o;
   {
-    const float oscale = scale * pow2i(eu);
+    float oscale = scale * pow2i(eu);
     f32x16 O[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) O[mt][i] = 0.f;
+    if (eu < 0) {
+      // U was scaled up (small values): S 2^-eu could overflow, so M (U 2^-eu)
+      // is taken first and brought back to scale (exactly) before Qt S joins
+      // it in the same accumulator
+#pragma unroll
+      for (int p = 0; p < 6; ++p) {
+        const f16x8 mv = *reinterpret_cast<const f16x8*>(&sm.M[32 * PMT[p] + rowsel][16 * PS[p] + 8 * hg]);
+        O[PMT[p]] = mfma32h(mv, Uh[PS[p]], O[PMT[p]]);
+      }
+      const float up = pow2i(eu);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) O[mt][i] *= up;
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const bf16x8 qv = *reinterpret_cast<const bf16x8*>(&sm.Qt[32 * mt + rowsel][16 * s + 8 * hg]);
+          O[mt] = mfma32(qv, Sb[s], O[mt]);
+        }
+      oscale = scale;
+    } else {
     bf16x8 qa[2][2];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
@@ -1079,6 +1109,7 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
         if (p + 2 < 6)
           mh[p & 1] = *reinterpret_cast<const f16x8*>(&sm.M[32 * PMT[p + 2] + rowsel][16 * PS[p + 2] + 8 * hg]);
       }
+    }
     }
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)

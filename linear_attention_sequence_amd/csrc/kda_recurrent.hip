@@ -27,9 +27,12 @@
 
 #include "kda.h"
 
+#include "kda_host_checks.h"
+
 namespace kda_host {
 int fail(int code, const std::string& msg);
 int device(int* num_cu, int** status_word);
+hipError_t alloc_async(void** p, size_t bytes, hipStream_t stream);
 }  // namespace kda_host
 
 namespace {
@@ -168,8 +171,6 @@ __global__ __launch_bounds__(64, 2) void kda_recurrent_kernel(
   }
 }
 
-bool aligned(const void* p, uintptr_t al) { return (reinterpret_cast<uintptr_t>(p) & (al - 1)) == 0; }
-
 }  // namespace
 
 extern "C" int kda_recurrent_fwd(const void* q, const void* k, const void* v, const float* g,
@@ -178,40 +179,17 @@ extern "C" int kda_recurrent_fwd(const void* q, const void* k, const void* v, co
                                  float* final_state, void* out, hipStream_t stream) {
   using kda_host::fail;
   fail(KDA_OK, "");
-  if (T < 0) return fail(KDA_ERR_BAD_SHAPE, "T must be >= 0");
-  if (T > INT32_MAX) return fail(KDA_ERR_BAD_SHAPE, "T must be <= INT32_MAX");
-  if (H < 1) return fail(KDA_ERR_BAD_SHAPE, "H must be >= 1");
-  if (H > KDA_MAX_HEADS) return fail(KDA_ERR_BAD_SHAPE, "H must be <= KDA_MAX_HEADS");
-  if (n_docs < 1) return fail(KDA_ERR_BAD_SHAPE, "n_docs must be >= 1");
-  if ((int64_t)n_docs * H > (1 << 30)) return fail(KDA_ERR_BAD_SHAPE, "n_docs * H must be <= 2^30");
-  if (!cu_seqlens && n_docs != 1) return fail(KDA_ERR_BAD_SHAPE, "n_docs must be 1 when cu_seqlens is NULL");
-  if (T == 0 && !final_state) return KDA_OK;
-  if (T > 0) {
-    if (!q) return fail(KDA_ERR_NULL_PTR, "q is NULL");
-    if (!k) return fail(KDA_ERR_NULL_PTR, "k is NULL");
-    if (!v) return fail(KDA_ERR_NULL_PTR, "v is NULL");
-    if (!g) return fail(KDA_ERR_NULL_PTR, "g is NULL");
-    if (!beta) return fail(KDA_ERR_NULL_PTR, "beta is NULL");
-    if (!out) return fail(KDA_ERR_NULL_PTR, "out is NULL");
-    if (!aligned(q, 16)) return fail(KDA_ERR_ALIGN, "q is not 16-byte aligned");
-    if (!aligned(k, 16)) return fail(KDA_ERR_ALIGN, "k is not 16-byte aligned");
-    if (!aligned(v, 16)) return fail(KDA_ERR_ALIGN, "v is not 16-byte aligned");
-    if (!aligned(g, 16)) return fail(KDA_ERR_ALIGN, "g is not 16-byte aligned");
-    if (!aligned(out, 16)) return fail(KDA_ERR_ALIGN, "out is not 16-byte aligned");
-    if (!aligned(beta, 4)) return fail(KDA_ERR_ALIGN, "beta is not 4-byte aligned");
-  }
-  if (cu_seqlens && !aligned(cu_seqlens, 4)) return fail(KDA_ERR_ALIGN, "cu_seqlens is not 4-byte aligned");
-  if (initial_state && !aligned(initial_state, 16))
-    return fail(KDA_ERR_ALIGN, "initial_state is not 16-byte aligned");
-  if (final_state && !aligned(final_state, 16))
-    return fail(KDA_ERR_ALIGN, "final_state is not 16-byte aligned");
+  const kda_check::Result r = kda_check::recurrent_fwd(q, k, v, g, beta, cu_seqlens, n_docs, T, H,
+                                                       initial_state, final_state, out);
+  if (r.code != KDA_OK) return fail(r.code, r.msg);
+  if (kda_check::fwd_is_noop(T, final_state)) return KDA_OK;
 
   int num_cu = 0;
   int* status_word = nullptr;
   if (kda_host::device(&num_cu, &status_word) != 0)
     return fail(KDA_ERR_HIP, "device query (CU count, status word) failed");
   int* bad = nullptr;
-  if (hipMallocAsync(reinterpret_cast<void**>(&bad), 256, stream) != hipSuccess || !bad)
+  if (kda_host::alloc_async(reinterpret_cast<void**>(&bad), 256, stream) != hipSuccess || !bad)
     return fail(KDA_ERR_ALLOC, "hipMallocAsync of the workspace failed");
   hipLaunchKernelGGL(kda_recurrent_check_kernel, dim3(1), dim3(CHECK_THREADS), 0, stream,
                      cu_seqlens, (int)n_docs, (int)T, bad, status_word);

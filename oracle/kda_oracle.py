@@ -10,9 +10,10 @@ What it computes (page "nemo_automodel.components.models.kimi_k3.kda_fused",
 package docstring and the ``fused_chunk_kda`` / ``fused_kda_unsupported_reason``
 entries): the KDA delta rule, specialised to
 
-* one recurrent state ``S`` of shape K x V per (document, head), starting at
-  zero in every document ("no initial or final state"; "the recurrent state
-  resets at every document boundary" in the ``fused_chunk_kda`` docstring).
+* one recurrent state ``S`` of shape K x V per (document, head): it starts at
+  zero in each document and is not returned (the package docstring, and the
+  ``fused_chunk_kda`` entry, which resets the state at each packed-document
+  boundary).
   The state-carrying variant starts each document from a given ``S_0`` and
   also returns its last state, the convention of FLA's ``chunk_kda``
   (``initial_state``, ``output_final_state``), of which ``fused_chunk_kda`` is

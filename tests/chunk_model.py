@@ -33,14 +33,60 @@ def bf16_round(x):
     return r.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
+def f16_round(x):
+    """Round to fp16 (ties to even, subnormals kept) through fp32."""
+    return np.asarray(x, np.float64).astype(np.float32).astype(np.float16).astype(np.float64)
+
+
+def pow2_f16(x, block=None, two_way=True):
+    """fp16 rounding behind an exact power-of-two scale, as the kernels store
+    their fp16 operands: per group of ``block`` columns (all columns when None)
+    the largest magnitude m picks e = 0 when 2^-4 <= m < 2^14, and otherwise
+    e with m 2^-e in [2^13, 2^14); x 2^-e is rounded to fp16 and multiplied
+    back by 2^e.  With ``two_way`` False, e is never negative (values are only
+    ever scaled down), so small inputs fall into the fp16 subnormal range."""
+    x = np.asarray(x, np.float64)
+    out = np.empty_like(x)
+    cols = x.shape[-1]
+    block = block or cols
+    for c0 in range(0, cols, block):
+        part = x[..., c0:c0 + block]
+        m = float(np.abs(part).max()) if part.size else 0.0
+        if m == 0.0:
+            out[..., c0:c0 + block] = 0.0
+            continue
+        e = np.frexp(np.float32(m))[1] - 1 - 13
+        if 2.0 ** -4 <= m < 2.0 ** 14 or (not two_way and e < 0):
+            e = 0
+        out[..., c0:c0 + block] = f16_round(part * 2.0 ** -e) * 2.0 ** e
+    return out
+
+
+def kernel_precision_ops(two_way=True):
+    """Operand roundings of the forward kernels: Qt, Kt and the MFMA copy of S
+    in bf16; KbT and M in fp16 (both bounded by 1); Tb in fp16 with one
+    power-of-two scale per chunk; X and U in fp16 with one scale per 32 value
+    columns (one wave's columns)."""
+    return dict(Qt=bf16_round, Kt=bf16_round, S=bf16_round, Kb=f16_round, M=f16_round,
+                Tb=lambda x: pow2_f16(x, None, two_way),
+                X=lambda x: pow2_f16(x, 32, two_way),
+                U=lambda x: pow2_f16(x, 32, two_way))
+
+
 def chunk_document(q, k, v, g, beta, C: int = 64, scale=None, eps: float = 1e-6,
                    rnd=None, rnd_state=None, rnd_out=None, initial_state=None,
-                   final_state: bool = False):
+                   final_state: bool = False, ops=None):
     """One document, one head: q, k, g [L, K]; v [L, V]; beta [L]; initial_state
-    [K, V] or None (zeros).  Returns o [L, V], or (o, S_last) with final_state."""
+    [K, V] or None (zeros).  Returns o [L, V], or (o, S_last) with final_state.
+    ``ops`` (see kernel_precision_ops) rounds each named operand on its own and
+    replaces rnd / rnd_state."""
     rnd = rnd or _ident
     rnd_state = rnd_state or _ident
     rnd_out = rnd_out or _ident
+    op = {name: rnd for name in ("Qt", "Kt", "Kb", "M", "Tb", "X", "U")}
+    op["S"] = rnd_state
+    if ops is not None:
+        op.update(ops)
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -66,14 +112,14 @@ def chunk_document(q, k, v, g, beta, C: int = 64, scale=None, eps: float = 1e-6,
         A = beta[s:e, None] * np.einsum("rc,ic,ric->ri", kh[s:e], kh[s:e], E) * tri_strict
         M = np.einsum("rc,ic,ric->ri", qh[s:e], kh[s:e], E) * tri_incl
         Tb = np.linalg.solve(np.eye(c) + A, np.diag(beta[s:e]))
-        Kt = rnd(kh[s:e] * np.exp(G))
-        Qt = rnd(qh[s:e] * np.exp(G))
-        Kb = rnd(kh[s:e] * np.exp(G[-1][None, :] - G))
-        Sb = rnd_state(S)
+        Kt = op["Kt"](kh[s:e] * np.exp(G))
+        Qt = op["Qt"](qh[s:e] * np.exp(G))
+        Kb = op["Kb"](kh[s:e] * np.exp(G[-1][None, :] - G))
+        Sb = op["S"](S)
         X = v[s:e] - Kt @ Sb
-        U = rnd(Tb) @ rnd(X)
-        Ub = rnd(U)
-        o[s:e] = rnd_out(scale * (Qt @ Sb + rnd(M) @ Ub))
+        U = op["Tb"](Tb) @ op["X"](X)
+        Ub = op["U"](U)
+        o[s:e] = rnd_out(scale * (Qt @ Sb + op["M"](M) @ Ub))
         S = np.exp(G[-1])[:, None] * S + Kb.T @ Ub
     return (o, S) if final_state else o
 

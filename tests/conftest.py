@@ -11,3 +11,15 @@ if TESTS not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+
+
+import pytest  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _reset_split_policy():
+    """Tests may force the library's split-document policy; put it back."""
+    yield
+    import linear_attention_sequence_amd as kda
+    if kda._lib is not None:
+        kda.set_split_policy("auto")

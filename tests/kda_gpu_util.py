@@ -10,6 +10,13 @@ REL_L2_TOL = 5e-3
 MAX_ABS_TOL = 3e-2
 
 
+def set_split(policy):
+    """Force the split-document policy of the library ("never", "auto",
+    "always"); the conftest fixture puts it back to "auto" after each test."""
+    import linear_attention_sequence_amd as kda
+    kda.set_split_policy(policy)
+
+
 def log(msg):
     print(msg, flush=True)
     sys.stdout.flush()

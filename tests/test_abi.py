@@ -20,7 +20,8 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     assert _declared_functions() == ["kda_chunk_bwd", "kda_chunk_fwd", "kda_chunk_fwd_state",
-                                     "kda_device_status", "kda_last_error", "kda_recurrent_fwd"]
+                                     "kda_debug_set_split_policy", "kda_device_status",
+                                     "kda_last_error", "kda_recurrent_fwd"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -150,6 +151,8 @@ def _call_rec(**kw):
     (dict(n_docs=0), kda.KDA_ERR_BAD_SHAPE, "n_docs must be >= 1"),
     (dict(n_docs=2), kda.KDA_ERR_BAD_SHAPE, "n_docs must be 1 when cu_seqlens is NULL"),
     (dict(n_docs=2**29 + 1, cu=P), kda.KDA_ERR_BAD_SHAPE, "n_docs * H"),
+    # 2 x 64 work-items per (document, head): the launch stays below 2^32
+    (dict(n_docs=2**24 + 1, cu=P), kda.KDA_ERR_BAD_SHAPE, "n_docs * H must be <= 2^25"),
     (dict(g=None), kda.KDA_ERR_NULL_PTR, "g is NULL"),
     (dict(k=P + 2), kda.KDA_ERR_ALIGN, "k is not 16-byte aligned"),
     (dict(h0=P + 4), kda.KDA_ERR_ALIGN, "initial_state is not 16-byte aligned"),
@@ -178,7 +181,9 @@ def _call_bwd(**kw):
     (dict(T=-1), kda.KDA_ERR_BAD_SHAPE, "T must be >= 0"),
     (dict(n_docs=0), kda.KDA_ERR_BAD_SHAPE, "n_docs must be >= 1"),
     (dict(n_docs=3), kda.KDA_ERR_BAD_SHAPE, "n_docs must be 1 when cu_seqlens is NULL"),
-    (dict(n_docs=2**28, cu=P), kda.KDA_ERR_BAD_SHAPE, "4 * n_docs * H"),
+    (dict(n_docs=2**28, cu=P), kda.KDA_ERR_BAD_SHAPE, "n_docs * H"),
+    # 4 x 512 work-items per (document, head) in the state-gradient chain
+    (dict(n_docs=2**20 + 1, cu=P), kda.KDA_ERR_BAD_SHAPE, "n_docs * H must be <= 2^21"),
     (dict(do=None), kda.KDA_ERR_NULL_PTR, "d_out is NULL"),
     (dict(dg=None), kda.KDA_ERR_NULL_PTR, "a gradient output is NULL"),
     (dict(chunk=16), kda.KDA_ERR_UNSUPPORTED, "chunk must be 64"),
@@ -215,3 +220,13 @@ def test_unsupported_reason_on_cpu_tensors():
                                                         torch.zeros(1, 8, 2), None,
                                                         initial_state=s0)
     assert "chunk must be 64" in kda.unsupported_reason(q, q, q, q.float(), None, chunk=16)
+
+
+def test_split_policy_hook_validates_and_returns_the_previous_policy():
+    if not os.path.exists(kda.LIB_PATH):
+        pytest.skip("libkda.so not built")
+    assert kda.kda_debug_set_split_policy(3) == kda.KDA_ERR_UNSUPPORTED
+    assert kda.kda_debug_set_split_policy(-1) == kda.KDA_ERR_UNSUPPORTED
+    assert kda.set_split_policy("never") == "auto"
+    assert kda.set_split_policy("always") == "never"
+    assert kda.set_split_policy("auto") == "always"

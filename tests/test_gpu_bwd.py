@@ -9,7 +9,7 @@ bar)."""
 import numpy as np
 import pytest
 
-from kda_gpu_util import REL_L2_TOL, log, to_device
+from kda_gpu_util import REL_L2_TOL, log, to_device, set_split
 from kda_workloads import (cu_from_lengths, initial_states, make_inputs, standard_normal,
                            round_to_bf16, with_gate_scale)
 from oracle.kda_oracle_bwd import kda_backward_tasks
@@ -89,8 +89,8 @@ def test_backward_small_packed(states):
 
 
 @pytest.mark.parametrize("policy", ["never", "always"])
-def test_backward_split_and_fused_forward(monkeypatch, policy):
-    monkeypatch.setenv("KDA_SPLIT", policy)
+def test_backward_split_and_fused_forward(policy):
+    set_split(policy)
     lengths = [700, 300]
     T, H = sum(lengths), 2
     inp = make_inputs(T, H, 73, cu_from_lengths(lengths))

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
-from kda_gpu_util import check, doc_tasks, log, run_gpu, to_device
+from kda_gpu_util import check, compare_tasks, doc_tasks, log, run_gpu, set_split, to_device
 from kda_workloads import (Inputs, cu_from_lengths, make_inputs, one_hot_keys, with_gate_scale,
                            workload, workload_inputs)
 
@@ -52,21 +52,40 @@ def test_workload3_packed_lognormal_sampled_heads():
 
 
 def test_workload4_dense_batch_sampled():
+    """Every one of the 8 documents of 8192 tokens on 4 heads, the last head
+    included."""
     w, inp = workload_inputs(4)
     log(f"[case] workload 4 {w.name}")
     o = run_gpu(inp)
-    cu = inp.cu_seqlens
-    tasks = [(int(cu[i]), int(cu[i + 1]), h, h + 1) for i, h in ((0, 0), (3, 17), (7, 31))]
-    check(inp, o, tasks, w.name)
+    check(inp, o, doc_tasks(inp.cu_seqlens, w.H, heads=[0, 9, 17, 31]), w.name)
 
 
 def test_workload5_long_plus_short_sampled():
+    """The 65,536-token document on 3 heads, every short document on 2."""
     w, inp = workload_inputs(5)
     log(f"[case] workload 5 {w.name} docs={len(w.lengths)}")
     o = run_gpu(inp)
     cu = inp.cu_seqlens
-    tasks = [(0, int(cu[1]), 5, 6)] + doc_tasks(cu[1:], w.H, heads=[2, 29])
+    tasks = [(0, int(cu[1]), h, h + 1) for h in (0, 5, 31)] + doc_tasks(cu[1:], w.H, heads=[2, 29])
     check(inp, o, tasks, w.name)
+
+
+def test_long_document_slow_decay_split_and_fused():
+    """One 65,536-token document (1024 chunks) with a slow decay, so that the
+    state carries across chunks all the way (the workloads' gate forgets it
+    within a chunk): the split path (its long sequential chain) and the fused
+    path give the same bits, and both match the oracle."""
+    import torch
+    T, H = 65536, 1
+    inp = with_gate_scale(_small(T, H, 42, [T]), 42, -0.05)
+    log("[case] one 65536-token document, g = -0.05 sigmoid, split then fused")
+    set_split("always")
+    a = run_gpu(inp)
+    set_split("never")
+    b = run_gpu(inp)
+    assert bool((_bits(a) == _bits(b)).all())
+    assert bool(torch.isfinite(a.float()).all())
+    check(inp, a, doc_tasks(inp.cu_seqlens, H), "65536 tokens, gate -0.05*sigmoid")
 
 
 # ---------------------------------------------------------------- special inputs
@@ -133,32 +152,33 @@ def test_gate_at_the_bound():
 # ---------------------------------------------------------------- split documents
 # Long documents may be "split": their chunks' state-independent part runs on
 # all CUs first and only the sequential chain stays per (document, head).
-# KDA_SPLIT forces the choice; both paths must give identical bits.
+# The split policy test hook forces the choice; both paths must give
+# identical bits.
 
 def _bits(o):
     import torch
     return o.view(torch.int16)
 
 
-def test_split_path_is_bit_identical_to_fused(monkeypatch):
+def test_split_path_is_bit_identical_to_fused():
     lengths = [513, 64 * 8, 1000, 37, 700, 2000, 1, 450]
     T, H = sum(lengths), 3
     inp = _small(T, H, 31, lengths)
-    monkeypatch.setenv("KDA_SPLIT", "never")
+    set_split("never")
     a = run_gpu(inp)
-    monkeypatch.setenv("KDA_SPLIT", "always")
+    set_split("always")
     b = run_gpu(inp)
     assert bool((_bits(a) == _bits(b)).all())
     check(inp, b, doc_tasks(inp.cu_seqlens, H), "split documents")
 
 
 @pytest.mark.parametrize("cu", [True, False])
-def test_split_long_document_carries_the_state(monkeypatch, cu):
+def test_split_long_document_carries_the_state(cu):
     T, H = 2048 + 37, 4
     inp = with_gate_scale(_small(T, H, 32, [T]), 32, -0.05)
-    monkeypatch.setenv("KDA_SPLIT", "never")
+    set_split("never")
     a = run_gpu(inp, cu=cu)
-    monkeypatch.setenv("KDA_SPLIT", "always")
+    set_split("always")
     b = run_gpu(inp, cu=cu)
     assert bool((_bits(a) == _bits(b)).all())
     check(inp, b, doc_tasks(inp.cu_seqlens, H), "split, slow decay")
@@ -175,36 +195,60 @@ def _scaled_v(inp, k):
 
 
 @pytest.mark.parametrize("k", [12, 20, 40])
-def test_large_values_stay_in_range(monkeypatch, k):
+def test_large_values_stay_in_range(k):
     import torch
     T, H = 700, 2
     base = with_gate_scale(_small(T, H, 33, [300, 400]), 33, -0.05)
     for policy in ("never", "always"):
-        monkeypatch.setenv("KDA_SPLIT", policy)
+        set_split(policy)
         o = run_gpu(_scaled_v(base, k))
         assert bool(torch.isfinite(o.float()).all())
         o1 = (o.float() * 2.0 ** -k).to(torch.bfloat16)
         check(base, o1, doc_tasks(base.cu_seqlens, H), f"v * 2^{k} ({policy})")
 
 
-def test_large_beta(monkeypatch):
+@pytest.mark.parametrize("v_scale,beta_scale", [(1e-6, 1.0), (1.0, 1e-5), (1e-6, 1e-5)])
+def test_small_values_keep_their_precision(v_scale, beta_scale):
+    """X, U and Tb are fp16 operands behind a power-of-two scale that also
+    scales small values up, out of the fp16 subnormal range (v is any bf16 and
+    beta any finite value)."""
+    import dataclasses
+    T, H = 700, 2
+    base = with_gate_scale(_small(T, H, 36, [300, 400]), 36, -0.05)
+    inp = dataclasses.replace(base, v=(base.v * np.float32(v_scale)),
+                              beta=(base.beta * np.float32(beta_scale)))
+    from kda_workloads import round_to_bf16
+    inp = dataclasses.replace(inp, v=round_to_bf16(inp.v))
+    for policy in ("never", "always"):
+        set_split(policy)
+        o = run_gpu(inp)
+        rel, mx = compare_tasks(inp, o, doc_tasks(inp.cu_seqlens, H))
+        ref_scale = float(np.abs(oracle.kda_forward(inp.q, inp.k, inp.v, inp.g, inp.beta,
+                                                    inp.cu_seqlens)).max())
+        log(f"[parity] v*{v_scale} beta*{beta_scale} ({policy}): relL2={rel:.3e} "
+            f"maxabs={mx:.3e} (output scale {ref_scale:.3e})")
+        assert rel <= 5e-3, rel
+        assert mx <= 3e-2 * ref_scale, mx
+
+
+def test_large_beta():
     T, H = 640, 2
     inp = with_gate_scale(_small(T, H, 34, [T]), 34, -0.3)
     inp.beta[:] = 1.9
     for policy in ("never", "always"):
-        monkeypatch.setenv("KDA_SPLIT", policy)
+        set_split(policy)
         o = run_gpu(inp)
         check(inp, o, doc_tasks(inp.cu_seqlens, H), f"beta 1.9 ({policy})")
 
 
 @pytest.mark.parametrize("H", [1, 5, 64])
-def test_head_counts(monkeypatch, H):
+def test_head_counts(H):
     lengths = [37, 600, 64, 129]
     T = sum(lengths)
     inp = with_gate_scale(_small(T, H, 35 + H, lengths), 35 + H, -0.5)
-    monkeypatch.setenv("KDA_SPLIT", "never")
+    set_split("never")
     a = run_gpu(inp)
-    monkeypatch.setenv("KDA_SPLIT", "always")
+    set_split("always")
     b = run_gpu(inp)
     assert bool((_bits(a) == _bits(b)).all())
     heads = sorted({0, H // 2, H - 1})
@@ -225,15 +269,15 @@ def test_gate_at_the_lowest_bound():
     check(inp, o, doc_tasks(inp.cu_seqlens, H), "gate at -5.5")
 
 
-def test_more_splittable_documents_than_candidates(monkeypatch):
+def test_more_splittable_documents_than_candidates():
     # 1100 documents of 9 chunks: the scheduler examines the longest 1024 for
     # splitting, the rest stay fused; the output is the same bit for bit
     lengths = [515] * 1100
     T, H = sum(lengths), 1
     inp = _small(T, H, 41, lengths)
-    monkeypatch.setenv("KDA_SPLIT", "never")
+    set_split("never")
     a = run_gpu(inp)
-    monkeypatch.setenv("KDA_SPLIT", "always")
+    set_split("always")
     b = run_gpu(inp)
     assert bool((_bits(a) == _bits(b)).all())
     cu = inp.cu_seqlens

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import oracle
-from kda_gpu_util import MAX_ABS_TOL, REL_L2_TOL, log, to_device
+from kda_gpu_util import MAX_ABS_TOL, REL_L2_TOL, log, to_device, set_split
 from kda_workloads import (cu_from_lengths, initial_states, make_inputs, with_gate_scale,
                            workload_inputs)
 
@@ -89,9 +89,9 @@ LENGTHS = [700, 0, 1, 130, 1500, 64, 0]
 
 
 @pytest.mark.parametrize("policy", ["never", "always", "auto"])
-def test_packed_with_initial_and_final_state(monkeypatch, policy):
+def test_packed_with_initial_and_final_state(policy):
     if policy != "auto":
-        monkeypatch.setenv("KDA_SPLIT", policy)
+        set_split(policy)
     T, H = sum(LENGTHS), 4
     inp = with_gate_scale(make_inputs(T, H, 51, cu_from_lengths(LENGTHS)), 51, -0.05)
     h0 = initial_states(len(LENGTHS), H, 51)
@@ -104,19 +104,19 @@ def test_packed_with_initial_and_final_state(monkeypatch, policy):
     np.testing.assert_array_equal(ht_np[6], h0[6])
 
 
-def test_split_and_fused_states_are_bit_identical(monkeypatch):
+def test_split_and_fused_states_are_bit_identical():
     T, H = sum(LENGTHS), 2
     inp = with_gate_scale(make_inputs(T, H, 52, cu_from_lengths(LENGTHS)), 52, -0.3)
     h0 = initial_states(len(LENGTHS), H, 52)
-    monkeypatch.setenv("KDA_SPLIT", "never")
+    set_split("never")
     o1, s1 = _run(inp, h0)
-    monkeypatch.setenv("KDA_SPLIT", "always")
+    set_split("always")
     o2, s2 = _run(inp, h0)
     assert bool((o1 == o2).all())
     assert bool((s1 == s2).all())
 
 
-def test_no_decay_with_states(monkeypatch):
+def test_no_decay_with_states():
     """g = 0 (the initial state never decays and every token stays in the
     state) over a 2048-token and a 300-token document: the slowest-decaying
     case of the chunked state path, fused and split, which agree bit for bit."""
@@ -124,9 +124,9 @@ def test_no_decay_with_states(monkeypatch):
     T, H = sum(lengths), 2
     inp = with_gate_scale(make_inputs(T, H, 91, cu_from_lengths(lengths)), 91, 0.0)
     h0 = initial_states(len(lengths), H, 91)
-    monkeypatch.setenv("KDA_SPLIT", "never")
+    set_split("never")
     o1, s1 = _run(inp, h0)
-    monkeypatch.setenv("KDA_SPLIT", "always")
+    set_split("always")
     o2, s2 = _run(inp, h0)
     assert bool((o1 == o2).all()) and bool((s1 == s2).all())
     _check(inp, o2, s2, h0, "state, no decay")

@@ -77,6 +77,17 @@ def test_l2norm_epsilon_reading():
     assert abs(qh0 - 2 ** -0.5) < 1e-15
 
 
+def test_l2norm_epsilon_is_immaterial_at_workload_norms():
+    """The pages give no epsilon for the in-kernel l2 norm.  At the workloads'
+    norms (|x|^2 ~ 128 for N(0,1) rows) the reading eps = 1e-6 and eps = 0 give
+    the same output to 1e-7 relative: the choice cannot move a parity result."""
+    q, k, v, g, beta = _rand(40, 2, 128, 128, seed=12)
+    o_eps = oracle.kda_document(q, k, v, g, beta, eps=1e-6)
+    o_0 = oracle.kda_document(q, k, v, g, beta, eps=0.0)
+    rel = np.linalg.norm(o_eps - o_0) / np.linalg.norm(o_0)
+    assert 0.0 < rel < 1e-7, rel
+
+
 # --------------------------------------------------------------------------
 # beta = 0: nothing is ever written, the state stays zero (no initial state)
 # --------------------------------------------------------------------------
