@@ -83,6 +83,24 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                   int32_t chunk, float gate_bound, void* out, hipStream_t stream);
 
 /*
+ * kda_chunk_fwd_noalloc -- kda_chunk_fwd for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, layouts, errors and output (bit for
+ * bit); it calls no hipMalloc, hipFree or allocating routine.  Its workspace
+ * is a fixed 64 MiB array per device that the library holds until the process
+ * ends, so T is limited to what fits there: 8 bytes per token plus a few KiB
+ * (about 8.3 million tokens); a larger T returns KDA_ERR_BAD_SHAPE before
+ * anything is enqueued.  The images of long documents get only what the array
+ * has left, so long documents may run slower than with kda_chunk_fwd.
+ * Every call on a device shares that device's array: calls that overlap on
+ * one device (on different streams, or from different threads without
+ * ordering) race and must not be issued.
+ */
+int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* g,
+                          const float* beta, const int32_t* cu_seqlens, int64_t T, int32_t H,
+                          int32_t chunk, float gate_bound, void* out, hipStream_t stream);
+
+/*
  * kda_chunk_fwd_state -- kda_chunk_fwd with a state carried into and out of
  * every document: document d starts from S = initial_state[d] (instead of
  * zero) and its last state is written to final_state[d].  This is the

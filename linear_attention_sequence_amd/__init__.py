@@ -64,6 +64,8 @@ def load_library():
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
             ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
         lib.kda_chunk_fwd.restype = ctypes.c_int
+        lib.kda_chunk_fwd_noalloc.argtypes = lib.kda_chunk_fwd.argtypes
+        lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
         lib.kda_chunk_fwd_state.argtypes = [
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
@@ -101,6 +103,14 @@ def kda_chunk_fwd(q, k, v, g, beta, cu_seqlens, T, H, chunk, gate_bound, out, st
     lib = load_library()
     return lib.kda_chunk_fwd(q, k, v, g, beta, cu_seqlens, int(T), int(H), int(chunk),
                              float(gate_bound), out, stream)
+
+
+def kda_chunk_fwd_noalloc(q, k, v, g, beta, cu_seqlens, T, H, chunk, gate_bound, out,
+                          stream) -> int:
+    """Call the C entry point with raw addresses (ints or None); returns its status."""
+    lib = load_library()
+    return lib.kda_chunk_fwd_noalloc(q, k, v, g, beta, cu_seqlens, int(T), int(H), int(chunk),
+                                     float(gate_bound), out, stream)
 
 
 def kda_chunk_fwd_state(q, k, v, g, beta, cu_seqlens, n_docs, T, H, chunk, gate_bound,

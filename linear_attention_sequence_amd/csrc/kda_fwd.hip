@@ -338,15 +338,29 @@ int fail(int code, const std::string& msg) {
 // that goes back to the device when the stream synchronises.
 constexpr uint64_t KDA_POOL_KEEP_BYTES = uint64_t(8) << 30;
 
+// The workspace of kda_chunk_fwd_noalloc, for callers that cannot allocate:
+// one fixed array per device, kept until the process ends.  Host code never
+// passes this name to a kernel (on the host it is only a stand-in for the
+// symbol): it looks up each device's own address with hipGetSymbolAddress,
+// once per device, and passes that.  Every call on a device shares that
+// device's array, so calls that overlap on one device race; the array keeps
+// the last call's contents, and the scheduler rewrites every field a call
+// reads before any kernel of the call reads it.
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+
 struct DeviceInfo {
   int num_cu = 0;
   hipMemPool_t pool = nullptr;
   int* status_word = nullptr;  // device address of this device's g_kda_status
+  uint8_t* scratch = nullptr;  // device address of this device's scratch array
 };
 std::mutex g_mu;
 std::vector<DeviceInfo> g_devices;
 
-int device_info(int dev, DeviceInfo** out) {
+// CU count, status word and scratch address of device dev (the current
+// device); with_pool also creates the library's memory pool of the device.
+int device_info(int dev, DeviceInfo** out, bool with_pool = true) {
   std::lock_guard<std::mutex> lock(g_mu);
   if ((int)g_devices.size() <= dev) g_devices.resize(dev + 1);
   DeviceInfo& d = g_devices[dev];
@@ -356,7 +370,12 @@ int device_info(int dev, DeviceInfo** out) {
       return -1;
     d.num_cu = n;
   }
-  if (d.pool == nullptr) {
+  if (d.scratch == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return -1;
+    d.scratch = static_cast<uint8_t*>(p);
+  }
+  if (with_pool && d.pool == nullptr) {
     hipMemPoolProps props;
     memset(&props, 0, sizeof(props));
     props.allocType = hipMemAllocationTypePinned;
@@ -407,13 +426,15 @@ struct Call {
   float* ht;
   hipStream_t stream;
   float* chunk_states = nullptr;  // S at every chunk start (the backward's forward pass)
+  bool no_alloc = false;          // use the device's scratch array, allocate nothing
 };
 
 int launch(const Call& c) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(KDA_ERR_HIP, "hipGetDevice failed");
   DeviceInfo* di = nullptr;
-  if (device_info(dev, &di) != 0) return fail(KDA_ERR_HIP, "device query (CU count, status word) failed");
+  if (device_info(dev, &di, !c.no_alloc) != 0)
+    return fail(KDA_ERR_HIP, "device query (CU count, status word, scratch) failed");
   const int64_t T = c.T;
   const int H = c.H;
 
@@ -424,11 +445,29 @@ int launch(const Call& c) {
   if (!kda_check::fwd_layout(T, H, c.n_exact, policy != SPLIT_NEVER, IMG_BYTES, IMAGE_BUDGET_BYTES,
                              MIN_SPLIT_CHUNKS, MAX_SPLIT_DOCS, &lay))
     return fail(KDA_ERR_BAD_SHAPE, "workspace size overflows");
+  if (c.no_alloc && lay.bytes > NOALLOC_SCRATCH_BYTES) {
+    // the images of split documents get what the scratch has left
+    kda_check::FwdLayout base;
+    if (!kda_check::fwd_layout(T, H, c.n_exact, false, IMG_BYTES, 0, MIN_SPLIT_CHUNKS,
+                               MAX_SPLIT_DOCS, &base))
+      return fail(KDA_ERR_BAD_SHAPE, "workspace size overflows");
+    const size_t room = base.bytes <= NOALLOC_SCRATCH_BYTES ? NOALLOC_SCRATCH_BYTES - base.bytes : 0;
+    if (base.bytes > NOALLOC_SCRATCH_BYTES ||
+        !kda_check::fwd_layout(T, H, c.n_exact, policy != SPLIT_NEVER, IMG_BYTES, room,
+                               MIN_SPLIT_CHUNKS, MAX_SPLIT_DOCS, &lay) ||
+        lay.bytes > NOALLOC_SCRATCH_BYTES)
+      return fail(KDA_ERR_BAD_SHAPE, "T is too large for the 64 MiB scratch of kda_chunk_fwd_noalloc "
+                                     "(it needs 8 bytes per token and a few KiB)");
+  }
   const size_t cap_chunks = lay.cap_chunks;
   const size_t ws_bytes = lay.bytes;
   uint8_t* ws = nullptr;
-  if (hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws), ws_bytes, di->pool, c.stream) != hipSuccess || !ws)
+  if (c.no_alloc) {
+    ws = di->scratch;
+  } else if (hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws), ws_bytes, di->pool, c.stream) != hipSuccess ||
+             !ws) {
     return fail(KDA_ERR_ALLOC, "stream-ordered allocation of the workspace failed");
+  }
   WorkHeader* hdr = reinterpret_cast<WorkHeader*>(ws);
   int2* docs = reinterpret_cast<int2*>(ws + lay.off_docs);
   int* doc_ids = c.n_exact >= 0 ? reinterpret_cast<int*>(ws + lay.off_ids) : nullptr;
@@ -458,7 +497,7 @@ int launch(const Call& c) {
       e = hipGetLastError();
     }
   }
-  const hipError_t ef = hipFreeAsync(ws, c.stream);
+  const hipError_t ef = c.no_alloc ? hipSuccess : hipFreeAsync(ws, c.stream);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
   if (ef != hipSuccess) return fail(KDA_ERR_HIP, "hipFreeAsync of the workspace failed");
   return KDA_OK;
@@ -509,6 +548,20 @@ extern "C" int kda_chunk_fwd(const void* q, const void* k, const void* v, const 
   if (r.code != KDA_OK) return fail(r.code, r.msg);
   if (T == 0) return KDA_OK;
   const Call c{q, k, v, g, beta, cu_seqlens, T, H, gate_bound, out, -1, nullptr, nullptr, stream};
+  return launch(c);
+}
+
+extern "C" int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* g,
+                                     const float* beta, const int32_t* cu_seqlens, int64_t T,
+                                     int32_t H, int32_t chunk, float gate_bound, void* out,
+                                     hipStream_t stream) {
+  t_last_error.clear();
+  const kda_check::Result r =
+      kda_check::chunk_fwd(q, k, v, g, beta, cu_seqlens, T, H, chunk, gate_bound, out);
+  if (r.code != KDA_OK) return fail(r.code, r.msg);
+  if (T == 0) return KDA_OK;
+  Call c{q, k, v, g, beta, cu_seqlens, T, H, gate_bound, out, -1, nullptr, nullptr, stream};
+  c.no_alloc = true;
   return launch(c);
 }
 

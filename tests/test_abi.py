@@ -19,9 +19,9 @@ def _declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert _declared_functions() == ["kda_chunk_bwd", "kda_chunk_fwd", "kda_chunk_fwd_state",
-                                     "kda_debug_set_split_policy", "kda_device_status",
-                                     "kda_last_error", "kda_recurrent_fwd"]
+    assert _declared_functions() == ["kda_chunk_bwd", "kda_chunk_fwd", "kda_chunk_fwd_noalloc",
+                                     "kda_chunk_fwd_state", "kda_debug_set_split_policy",
+                                     "kda_device_status", "kda_last_error", "kda_recurrent_fwd"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -230,3 +230,21 @@ def test_split_policy_hook_validates_and_returns_the_previous_policy():
     assert kda.set_split_policy("never") == "auto"
     assert kda.set_split_policy("always") == "never"
     assert kda.set_split_policy("auto") == "always"
+
+
+def test_no_alloc_entry_point_validates_like_kda_chunk_fwd():
+    if not os.path.exists(kda.LIB_PATH):
+        pytest.skip("libkda.so not built")
+    for kw, code, msg in [(dict(T=-1), kda.KDA_ERR_BAD_SHAPE, "T must be >= 0"),
+                          (dict(q=None), kda.KDA_ERR_NULL_PTR, "q is NULL"),
+                          (dict(chunk=32), kda.KDA_ERR_UNSUPPORTED, "chunk must be 64"),
+                          (dict(out=P + 2), kda.KDA_ERR_ALIGN, "out is not 16-byte aligned")]:
+        args = dict(q=P, k=P, v=P, g=P, beta=P, cu=None, T=128, H=2, chunk=64, gate_bound=-5.0,
+                    out=P, stream=None)
+        args.update(kw)
+        rc = kda.kda_chunk_fwd_noalloc(*(args[x] for x in ("q", "k", "v", "g", "beta", "cu", "T",
+                                                           "H", "chunk", "gate_bound", "out",
+                                                           "stream")))
+        assert rc == code and msg in kda.kda_last_error()
+    assert kda.kda_chunk_fwd_noalloc(None, None, None, None, None, None, 0, 1, 64, -5.0, None,
+                                     None) == kda.KDA_OK
