@@ -490,7 +490,7 @@ int launch(const Call& c) {
       e = kda_state_tu::launch_main_state(dim3(di->num_cu), c.stream, c.q, c.k, c.v, c.g, c.beta,
                                           c.out, hdr, docs, split, images, T, H, c.gate_bound);
     } else {
-      hipLaunchKernelGGL(kda_chunk_fwd_kernel<false>, dim3(di->num_cu), dim3(NTHR), 0, c.stream,
+      hipLaunchKernelGGL(kda_pc_kernel<false>, dim3(di->num_cu), dim3(NPC), 0, c.stream,
                          static_cast<const bf16*>(c.q), static_cast<const bf16*>(c.k),
                          static_cast<const bf16*>(c.v), c.g, c.beta, static_cast<bf16*>(c.out),
                          hdr, docs, split, images, T, H, c.gate_bound);

@@ -10,7 +10,7 @@ hipError_t launch_main_state(dim3 grid, hipStream_t stream, const void* q, const
                              const void* v, const float* g, const float* beta, void* out,
                              void* hdr, const void* docs, const void* split, const void* images,
                              int64_t T, int H, float gate_bound) {
-  hipLaunchKernelGGL(kda_chunk_fwd_kernel<true>, grid, dim3(NTHR), 0, stream,
+  hipLaunchKernelGGL(kda_pc_kernel<true>, grid, dim3(NPC), 0, stream,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                      static_cast<const bf16*>(v), g, beta, static_cast<bf16*>(out),
                      static_cast<WorkHeader*>(hdr), static_cast<const int2*>(docs),

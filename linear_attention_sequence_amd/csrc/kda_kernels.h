@@ -281,12 +281,17 @@ __device__ __forceinline__ void bstore(u32x4 x, Rsrc r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b128(x, r, (int)off, 0, 0);
 }
 
+// Sixteen 16-byte pieces per lane: either the raw inputs of a chunk
+// (q: p[0..3], k: p[4..7], g: p[8..15]; element 8 s + j of q or k is channel
+// 32 s + 8 cg + j, and g holds the same 32 channels as fp32 bits) with beta,
+// or this lane's share of a precomputed chunk image (piece tid + NTHR i in
+// p[i]).  One register buffer serves both, so that the producer of the main
+// kernel never holds two.
 struct RawChunk {
-  u32x4 q[4];    // 32 bf16 channels of one token (element 8 s + j = channel 32 s + 8 cg + j)
-  u32x4 k[4];
-  u32x4 g[8];    // the same 32 channels, fp32 bits
+  u32x4 p[16];
   float beta;
 };
+constexpr int RAW_Q = 0, RAW_K = 4, RAW_G = 8;
 
 // per-lane byte offsets, fixed for the whole kernel
 struct Offsets {
@@ -332,20 +337,20 @@ __device__ __forceinline__ void load_raw_part(RawChunk& rc, const RawSrc& src, c
   if (part == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      rc.q[i] = bload(src.q, of.qk + 64u * i);
-      rc.k[i] = bload(src.k, of.qk + 64u * i);
+      rc.p[RAW_Q + i] = bload(src.q, of.qk + 64u * i);
+      rc.p[RAW_K + i] = bload(src.k, of.qk + 64u * i);
     }
   } else if (part == 1) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      rc.g[2 * i] = bload(src.g, 2u * of.qk + 128u * i);
-      rc.g[2 * i + 1] = bload(src.g, 2u * of.qk + 128u * i + 16u);
+      rc.p[RAW_G + 2 * i] = bload(src.g, 2u * of.qk + 128u * i);
+      rc.p[RAW_G + 2 * i + 1] = bload(src.g, 2u * of.qk + 128u * i + 16u);
     }
   } else {
 #pragma unroll
     for (int i = 2; i < 4; ++i) {
-      rc.g[2 * i] = bload(src.g, 2u * of.qk + 128u * i);
-      rc.g[2 * i + 1] = bload(src.g, 2u * of.qk + 128u * i + 16u);
+      rc.p[RAW_G + 2 * i] = bload(src.g, 2u * of.qk + 128u * i);
+      rc.p[RAW_G + 2 * i + 1] = bload(src.g, 2u * of.qk + 128u * i + 16u);
     }
     rc.beta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(src.b, (int)of.b, 0, 0));
   }
@@ -372,31 +377,35 @@ __device__ __forceinline__ VChunk load_v(const bf16* __restrict__ v, int64_t c0,
   return vc;
 }
 
-// a chunk image in registers: thread tid holds pieces tid + NTHR i
-struct Image {
-  u32x4 p[IMG_PER_THREAD];
-};
-
-// pieces [i0, i1) of an image (the last round only covers the first waves)
-__device__ __forceinline__ void load_image_part(Image& im, Rsrc r, int tid, int i0, int i1) {
+// a chunk image into registers: thread tid loads pieces tid + NTHR i (the last
+// round only covers the first waves).  kPhase selects the rounds image_to_lds
+// writes in that phase (-1: all).
+static_assert(IMG_PER_THREAD == 16, "an image fills the sixteen pieces of RawChunk");
+// phase 0: the Kt rows and rows 32..63 of Tb (read by the chain's first part
+// only); phase 1: the rest (Qt, KbT, M, rows 0..31 of Tb, the paddings)
+__device__ __forceinline__ constexpr int image_round_phase(int i) {
+  return ((NTHR * i >= IMG_QK / 2 && NTHR * i < GP_KB) || (NTHR * i >= GP_TLONG && NTHR * i < GP_PAD)) ? 0 : 1;
+}
+template <int kPhase = -1>
+__device__ __forceinline__ void load_image(RawChunk& im, const uint8_t* __restrict__ src, int tid) {
+  const Rsrc r = make_rsrc(src, IMG_BYTES);
 #pragma unroll
   for (int i = 0; i < IMG_PER_THREAD; ++i)
-    if (i >= i0 && i < i1 && tid + NTHR * i < IMG_VEC)
+    if ((kPhase < 0 || image_round_phase(i) == kPhase) && tid + NTHR * i < IMG_VEC)
       im.p[i] = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * tid, 16 * NTHR * i, 0);
 }
 
-__device__ __forceinline__ void load_image(Image& im, const uint8_t* __restrict__ src, int tid) {
-  load_image_part(im, make_rsrc(src, IMG_BYTES), tid, 0, IMG_PER_THREAD);
-}
-
 // each round of NTHR pieces lies in one part of the image: the part of round
-// i is known at compile time
-__device__ __forceinline__ void image_to_lds(Smem& sm, const Image& im, int tid) {
+// i is known at compile time.  kPhase selects the rounds of one phase
+// (image_round_phase); -1 writes everything.
+template <int kPhase = -1>
+__device__ __forceinline__ void image_to_lds(Smem& sm, const RawChunk& im, int tid) {
   uint8_t* dst = reinterpret_cast<uint8_t*>(&sm);
 #pragma unroll
   for (int i = 0; i < IMG_PER_THREAD; ++i) {
     const int p = tid + NTHR * i;
     const int r0 = NTHR * i;  // first piece of the round
+    if (kPhase >= 0 && image_round_phase(i) != kPhase) continue;
     int off;
     if (r0 < GP_KB) {
       off = OFF_QT + (p >> 4) * ROW_QK + (p & 15) * 16;
@@ -615,9 +624,9 @@ struct Lane {
   int tok;  // prologue: token of this lane inside the chunk
 };
 
-__device__ __forceinline__ Lane make_lane() {
+__device__ __forceinline__ Lane make_lane(int tid = threadIdx.x) {
   Lane ln;
-  ln.tid = threadIdx.x;
+  ln.tid = tid;
   ln.w = __builtin_amdgcn_readfirstlane(ln.tid >> 6);
   ln.l = ln.tid & 63;
   ln.r = ln.l & 15;
@@ -632,7 +641,13 @@ __device__ __forceinline__ Lane make_lane() {
 // inputs `cur` (n valid tokens) to the image in LDS (Qt, Kt, KbT, M, Tb, D).
 // hook(0..2) run at fixed points once `cur` has been consumed (they may
 // refill it); the scheduling barriers keep the loads they issue spread out.
-// Ends with a workgroup barrier after which the image is complete.
+// hook(3) runs right after the fourth workgroup barrier (B3), hook(4) between
+// B4 and B5, hook(5) between B5 and B6.
+// Seven workgroup barriers, B0 .. B6, the last of which ends the function;
+// after it the image is complete.  Until B1 the function writes to LDS only
+// tot, beta and gate_bad (so that another workgroup role may still read the
+// previous image and use the staging slices until then); until B2 not Qt,
+// Kt or KbT; until B5 not Tb or its scale.
 template <class Sm, class Sink, class Hook>
 __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const RawChunk& cur, int n,
                                               float gate_bound, const Lane& ln, Hook hook) {
@@ -649,8 +664,9 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
     float qh[32], kh[32], lg[32];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t qa[4] = {cur.q[i][0], cur.q[i][1], cur.q[i][2], cur.q[i][3]};
-      const uint32_t ka[4] = {cur.k[i][0], cur.k[i][1], cur.k[i][2], cur.k[i][3]};
+      const u32x4 qi = cur.p[RAW_Q + i], ki = cur.p[RAW_K + i];
+      const uint32_t qa[4] = {qi[0], qi[1], qi[2], qi[3]};
+      const uint32_t ka[4] = {ki[0], ki[1], ki[2], ki[3]};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         qh[8 * i + 2 * j] = bf16_lo_to_f32(qa[j]);
@@ -662,8 +678,9 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
     float gmin = 0.f, gmax = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float ga[4] = {__uint_as_float(cur.g[i][0]), __uint_as_float(cur.g[i][1]),
-                           __uint_as_float(cur.g[i][2]), __uint_as_float(cur.g[i][3])};
+      const u32x4 gi = cur.p[RAW_G + i];
+      const float ga[4] = {__uint_as_float(gi[0]), __uint_as_float(gi[1]), __uint_as_float(gi[2]),
+                           __uint_as_float(gi[3])};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         gmin = fminf(gmin, ga[j]);
@@ -711,9 +728,11 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
       kr[j] = kn * ert;
     }
   }
+  __syncthreads();  // B0
 
   // diagonal block (w, w) of M and A on fp32 MFMA: k-step s takes element s
   // from every lane (the same channel on both operands)
+  f32x4 dM, dA;
   {
     f32x4 accM[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     f32x4 accA[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -725,7 +744,12 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
     __builtin_amdgcn_sched_barrier(0);
     hook(1);
     __builtin_amdgcn_sched_barrier(0);
-    store_block(sm, accM[0] + accM[1], accA[0] + accA[1], w, w, l, true, beta_mine);
+    dM = accM[0] + accM[1];
+    dA = accA[0] + accA[1];
+  }
+  __syncthreads();  // B1: the previous image's Qt, M, KbT and D may still be read until here
+  {
+    store_block(sm, dM, dA, w, w, l, true, beta_mine);
     // the chain's MFMAs read the upper blocks (0, 1) and (2, 3) (inside the two
     // diagonal 32x32 tiles): zero them; the other upper blocks are never read
     if (w == 0 || w == 2) {
@@ -743,9 +767,8 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
       }
     }
   }
-  __syncthreads();  // B1: tot, beta, R, diagonal A / M visible
   fill_tables(sm, sink, tid);
-  __syncthreads();  // B2: decay tables visible
+  __syncthreads();  // B2: decay tables, R and the diagonal A / M blocks visible
 
   // ---- operand tiles of the chain: Qt = lq e^{G_end(w)}, Kt = -lk e^{G_end(w)},
   //      KbT = kr e^{G_c - G_end(w)}
@@ -802,7 +825,7 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
   __builtin_amdgcn_sched_barrier(0);
   // ---- off-diagonal blocks (w, b), b < w, on fp16 MFMA (fully unrolled per
   // wave).  Wave 0, which has none, meanwhile inverts the four diagonal
-  // blocks of I + A (complete since B1): T = (I + A)^-1 by 16x16 blocks, by
+  // blocks of I + A (complete since B2): T = (I + A)^-1 by 16x16 blocks, by
   // forward substitution, lane l owning column l % 16 of diagonal block
   // l / 16.  tmax tracks the largest |Tb| = |T_ij beta_j| a wave produces.
   // T shares its space with R, which waves 1-3 still read: until B3 the
@@ -845,6 +868,9 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
   }
 
   __syncthreads();  // B3: A and M complete, R dead (T, which shares its space, may be written)
+  __builtin_amdgcn_sched_barrier(0);
+  hook(3);
+  __builtin_amdgcn_sched_barrier(0);
   if (w == 0) {
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) sm.u2.T[16 * da + rr][16 * da + dj] = sm.u.A[16 * pr + rr][16 * pc + dj];
@@ -861,6 +887,9 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
   else if (w == 2) tmax = levels_column<2>(sm, l, tmax);
   tmax = wave_max(tmax);
   if (l == 0) sm.tbmax[w] = tmax;
+  __builtin_amdgcn_sched_barrier(0);
+  hook(4);
+  __builtin_amdgcn_sched_barrier(0);
   __syncthreads();  // B5: T complete
   // Tb = T Diag(beta) 2^-e in fp16 (in LDS it overwrites A), e chosen so
   // that |Tb 2^-e| < 2^14 (e = 0 unless Tb is huge): thread tid converts row
@@ -885,18 +914,31 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
       sink.tb(rr, cc, th);
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
+  hook(5);
+  __builtin_amdgcn_sched_barrier(0);
   __syncthreads();  // B6: the image is complete, T dead (its space stages O)
 }
 
 // The state-dependent part of a chunk of n tokens starting at token c0, from
 // the image in LDS and this chunk's V (wave w owns value columns 32 w ..):
-//   X = V - Kt S,  U = Tb X,  O = scale (Qt S + M U),  S <- D S + KbT U.
-// hook(0..3) run at fixed points after V has been consumed (they may refill
-// vcur): after the V staging, after X, after U and after O.
+//   X = V - Kt S,  U = Tb X,  O = scale (Qt S + M U),  S <- D S + KbT U,
+// in three parts.  chain_a computes X and U: it reads V, Kt, Tb and Tb's
+// scale and stages V in the wave's slice; chain_o computes and stores O: it
+// reads Qt and M and stages O in the slice; chain_b updates S: it reads only
+// KbT and D.  ChainMid carries U (fp16, 2^-eu) from chain_a to the others.
+// hook(0..2) run at fixed points of chain_a after V has been consumed (they
+// may refill vcur): after the V staging, after X and after U.
+struct ChainMid {
+  f16x8 Uh[4];
+  int eu;
+};
+
 template <class Hook>
-__device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChunk& vcur, int n,
-                                            int64_t c0, int H, int h, bf16* __restrict__ out,
-                                            const Lane& ln, const Offsets& of, Hook hook) {
+__device__ __forceinline__ void chain_a(Smem& sm, const f32x16 (&S)[4], const VChunk& vcur, int n,
+                                        int64_t c0, int H, int h, bf16* __restrict__ out,
+                                        const Lane& ln, const Offsets& of, Hook hook,
+                                        ChainMid& mid) {
   const int w = ln.w, l = ln.l, m = ln.m, hg = ln.hg;
   const float scale = 0.08838834764831845f;  // 128^-1/2
 
@@ -1039,6 +1081,35 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
     for (int j = 0; j < 8; ++j) {
       Uh[s][j] = (_Float16)(U[s >> 1][8 * (s & 1) + j] * udown);
     }
+  __builtin_amdgcn_sched_barrier(0);
+  hook(2);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) mid.Uh[s] = Uh[s];
+  mid.eu = eu;
+}
+
+// O = scale (Qt S + M U) of the chunk, from S and the U that chain_a left in
+// mid, staged through the wave's slice for 16-byte row stores.  Reads Qt and
+// M.
+__device__ __forceinline__ void chain_o(Smem& sm, const f32x16 (&S)[4], const ChainMid& mid, int n,
+                                        int64_t c0, int H, int h, bf16* __restrict__ out,
+                                        const Lane& ln, const Offsets& of) {
+  const int w = ln.w, l = ln.l, m = ln.m, hg = ln.hg;
+  const float scale = 0.08838834764831845f;  // 128^-1/2
+  const int rowsel = swap23(m);
+  constexpr int PMT[6] = {0, 0, 1, 1, 1, 1};
+  constexpr int PS[6] = {0, 1, 0, 1, 2, 3};
+  const int eu = mid.eu;
+  const float udown = pow2i(-eu);
+  f16x8 Uh[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) Uh[s] = mid.Uh[s];
+  bf16x8 Sb[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) Sb[s][j] = (bf16)S[s >> 1][8 * (s & 1) + j];
   if (eu > 0) {
     // M U is computed as M (U 2^-eu) with U scaled down: bring Qt S to the
     // same scale (S 2^-eu cannot overflow)
@@ -1047,9 +1118,6 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
 #pragma unroll
       for (int j = 0; j < 8; ++j) Sb[s][j] = (bf16)(S[s >> 1][8 * (s & 1) + j] * udown);
   }
-  __builtin_amdgcn_sched_barrier(0);
-  hook(2);
-  __builtin_amdgcn_sched_barrier(0);
 
   // O = scale (qh e^G S + M U), staged through LDS for 16-byte stores;
   // one accumulator per row tile
@@ -1120,13 +1188,26 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
         ost[t][m] = __builtin_bit_cast(unsigned short, ob);
       }
   }
+  // O rows: lane l writes 16 bytes of row 16 it + l / 4 (rows past the end
+  // are dropped by the descriptor's range)
+  wave_sync_lds();
+  {
+    const Rsrc ro = make_rsrc(out + ((size_t)c0 * H + h) * DV, chunk_bytes(n, H, 256u));
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int t = 16 * it + (l >> 2);
+      bstore(*reinterpret_cast<const u32x4*>(&ost[t][8 * (l & 3)]), ro, of.v[it]);
+    }
+  }
+}
 
-  __builtin_amdgcn_sched_barrier(0);
-  hook(3);
-  __builtin_amdgcn_sched_barrier(0);
-  // S <- e^{G_c} S + (kh e^{G_c - G})^T U: the product accumulates from zero
-  // (the four row tiles interleaved) and S takes it with one fma per element,
-  // so S itself is only ever touched by vector ALU code
+// S <- e^{G_c} S + (kh e^{G_c - G})^T U: the product accumulates from zero
+// (the four row tiles interleaved) and S takes it with one fma per element,
+// so S itself is only ever touched by vector ALU code
+__device__ __forceinline__ void chain_b(Smem& sm, f32x16 (&S)[4], const ChainMid& mid, const Lane& ln) {
+  const int hg = ln.hg;
+  const int rowsel = swap23(ln.m);
+  const int eu = mid.eu;
   {
     f32x16 dS[4];
 #pragma unroll
@@ -1143,7 +1224,7 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
       for (int kt = 0; kt < 4; ++kt) {
         if (s + 1 < 4)
           kb[(s + 1) & 1][kt] = *reinterpret_cast<const f16x8*>(&sm.KbT[32 * kt + rowsel][16 * (s + 1) + 8 * hg]);
-        dS[kt] = mfma32h(kb[s & 1][kt], Uh[s], dS[kt]);
+        dS[kt] = mfma32h(kb[s & 1][kt], mid.Uh[s], dS[kt]);
       }
     }
     if (eu != 0) {  // the product took U 2^-eu (exact power of two)
@@ -1164,16 +1245,6 @@ __device__ __forceinline__ void chain_chunk(Smem& sm, f32x16 (&S)[4], const VChu
 #pragma unroll
         for (int j = 0; j < 8; ++j) S[kt][i0 + j] = fmaf(d[j], S[kt][i0 + j], dS[kt][i0 + j]);
       }
-  }
-
-  // O rows: lane l writes 16 bytes of row 16 it + l / 4 (rows past the end
-  // are dropped by the descriptor's range)
-  wave_sync_lds();
-  const Rsrc ro = make_rsrc(out + ((size_t)c0 * H + h) * DV, chunk_bytes(n, H, 256u));
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int t = 16 * it + (l >> 2);
-    bstore(*reinterpret_cast<const u32x4*>(&ost[t][8 * (l & 3)]), ro, of.v[it]);
   }
 }
 
@@ -1209,55 +1280,300 @@ __device__ __forceinline__ void store_state(const f32x16 (&S)[4], float* dst, co
 }
 
 // ---------------------------------------------------------------------------
-// main kernel: one (document, head) unit at a time; fused documents prepare
-// and chain each chunk, split documents chain precomputed images.  With
-// h0 / ht (then doc_ids maps a unit's list entry to its document index), a
-// unit starts from h0[doc][h] instead of zero and stores its last state to
-// ht[doc][h]; each unit touches only its own slot, so ht may equal h0.
+// main kernel: producer / consumer.  One workgroup of 8 waves per CU.  Waves
+// 0-3 (the producer) build the image of chunk i (prepare_chunk, or a copy of
+// a split chunk's image from the workspace) while waves 4-7 (the consumer)
+// chain chunk i - 1 on the image in LDS: two waves per SIMD, one of each role.
+//
+// Both roles pass the same seven workgroup barriers per iteration (B0..B6,
+// those of prepare_chunk).  The image is single-buffered; the barriers order
+// the consumer's reads of image i - 1 before the producer's writes of image i:
+//   before B0:  producer: prologue (registers, its own tot / beta);
+//               consumer: chain_a, X and U (reads Kt, Tb and Tb's scale;
+//               stages V in its slice);
+//   B0 .. B1:   producer: diagonal A / M products (registers);
+//               consumer: chain_o and chain_b, O and the state update (reads
+//               Qt, M, KbT and D; stages O in its slice);
+//   B1 .. B6:   producer: the rest of the image (the slices take R and T);
+//               consumer: idle.
+// The producer hands each chunk to the consumer through an item descriptor in
+// LDS (two slots, by iteration parity), written between B5 and B6.
 // ---------------------------------------------------------------------------
+constexpr int NPC = 2 * NTHR;  // threads of the producer / consumer kernel
+
+enum ItemFlags { ITEM_VALID = 1, ITEM_FIRST = 2, ITEM_LAST = 4 };
+
+struct Item {
+  int64_t c0;     // first token of the chunk
+  int64_t first;  // first token of the unit's document
+  int n;          // tokens in the chunk (0 for an empty document)
+  int h;          // head
+  int unit;       // work-list entry: list index * H + h
+  int flags;      // ItemFlags
+};
+
+// a unit as the producer walks it (uniform values)
+struct PUnit {
+  int u;          // work-list entry (>= n_units: none)
+  int h;
+  int64_t bos;    // first token
+  int len;        // tokens
+  int nch;        // chunks (at least 1: an empty document is one item of 0 tokens)
+  int img0;       // split document: index of its first chunk image; -1: fused
+};
+
+struct alignas(16) PCSmem {
+  Smem s;
+  Item items[2];
+  int fetch;      // a unit index fetched from the counter
+  int nu[5];      // the next unit: index, doc.x, doc.y, split.x, split.y
+};
+
+__device__ __forceinline__ PUnit make_punit(int u, int n_units, int H, int dx, int dy, int sx, int sy) {
+  PUnit p;
+  p.u = u;
+  p.h = 0;
+  p.bos = 0;
+  p.len = 0;
+  p.nch = 0;
+  p.img0 = -1;
+  if (u < n_units) {
+    p.h = u % H;
+    p.len = dy;
+    if (dx < 0) {
+      p.bos = sx;
+      p.img0 = sy;
+    } else {
+      p.bos = dx;
+    }
+    p.nch = max(1, (dy + CH - 1) / CH);
+  }
+  return p;
+}
+
+// wave-uniform copies of values read from LDS (all lanes read the same word),
+// so that the compiler keeps them, and what is derived from them (buffer
+// descriptors among others), in scalar registers
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uni64(int64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ Item read_item(const Item& src) {
+  Item it;
+  it.c0 = uni64(src.c0);
+  it.first = uni64(src.first);
+  it.n = uni(src.n);
+  it.h = uni(src.h);
+  it.unit = uni(src.unit);
+  it.flags = uni(src.flags);
+  return it;
+}
+
+__device__ __forceinline__ Item make_item(const PUnit& p, int c) {
+  Item it;
+  it.first = p.bos;
+  it.c0 = p.bos + (int64_t)CH * c;
+  it.n = (int)min<int64_t>(CH, (int64_t)p.len - (int64_t)CH * c);
+  if (it.n < 0) it.n = 0;
+  it.h = p.h;
+  it.unit = p.u;
+  it.flags = ITEM_VALID | (c == 0 ? ITEM_FIRST : 0) | (c == p.nch - 1 ? ITEM_LAST : 0);
+  return it;
+}
+
 template <bool kState>
-__global__ __launch_bounds__(NTHR, 1) void kda_chunk_fwd_kernel(
+__global__ __launch_bounds__(NPC, 1) void kda_pc_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, bf16* __restrict__ out,
     WorkHeader* __restrict__ hdr, const int2* __restrict__ docs, const int2* __restrict__ split,
     const uint8_t* __restrict__ images, int64_t T, int H, float gate_bound) {
-  __shared__ Smem sm;
-  const Lane ln = make_lane();
+  __shared__ PCSmem ps;
+  Smem& sm = ps.s;
+  const Lane ln = make_lane(threadIdx.x & (NTHR - 1));
   const int tid = ln.tid, w = ln.w, l = ln.l;
 
   if (hdr->status != 0) {
     // cu_seqlens was rejected on the device: make the failure visible
     const size_t total = (size_t)T * H * DV;
-    const size_t stride = (size_t)gridDim.x * NTHR;
+    const size_t stride = (size_t)gridDim.x * NPC;
     unsigned short* o16 = reinterpret_cast<unsigned short*>(out);
-    for (size_t i = (size_t)blockIdx.x * NTHR + tid; i < total; i += stride) o16[i] = 0x7FC0;
+    for (size_t i = (size_t)blockIdx.x * NPC + threadIdx.x; i < total; i += stride) o16[i] = 0x7FC0;
     if (kState && hdr->ht != nullptr) {
       float* ht = hdr->ht;
       const size_t nst = (size_t)hdr->n_state_docs * H * DK * DV;
-      for (size_t i = (size_t)blockIdx.x * NTHR + tid; i < nst; i += stride) ht[i] = __builtin_nanf("");
+      for (size_t i = (size_t)blockIdx.x * NPC + threadIdx.x; i < nst; i += stride) ht[i] = __builtin_nanf("");
     }
     return;
   }
   const int n_units = hdr->n_units;
   const Offsets of = make_offsets(H, ln.tok, ln.cg, w, l);
-  if (tid == 0) sm.gate_bad = 0;
 
-  for (;;) {
-    __syncthreads();
-    if (tid == 0) sm.unit = atomicAdd(&hdr->counter, 1);
-    __syncthreads();
-    const int unit = __builtin_amdgcn_readfirstlane(sm.unit);
-    if (unit >= n_units) break;
-    const int di = unit / H;
-    const int h = unit - di * H;
-    const int2 doc = docs[di];
+  // the first unit
+  if (threadIdx.x == 0) {
+    sm.gate_bad = 0;
+    ps.fetch = atomicAdd(&hdr->counter, 1);
+  }
+  __syncthreads();
 
-    // S starts at zero or at h0[doc][h]; with states, the last S goes to
-    // ht[doc][h].  Each branch below keeps its own S (its own registers).
-    auto state_in = [&](f32x16 (&S)[4]) {
+  if (threadIdx.x < NTHR) {
+    // ======================== producer (waves 0-3) ========================
+    // a unit's description from the work list (uniform scalar loads)
+    auto unit_of = [&](int u) -> PUnit {
+      int dx = 0, dy = 0, sx = 0, sy = 0;
+      if (u < n_units) {
+        const int2 d = docs[u / H];
+        dx = d.x;
+        dy = d.y;
+        if (dx < 0) {
+          const int2 sp = split[-dx - 1];
+          sx = sp.x;
+          sy = sp.y;
+        }
+      }
+      return make_punit(u, n_units, H, dx, dy, sx, sy);
+    };
+    auto raw_of = [&](const PUnit& p, int c) {
+      const int64_t c0 = p.bos + (int64_t)CH * c;
+      return raw_src(q, k, g, beta, c0, (int)min<int64_t>(CH, (int64_t)p.len - (int64_t)CH * c), H, p.h);
+    };
+    auto image_of = [&](const PUnit& p, int c) {
+      return images + ((size_t)(p.img0 + c) * H + p.h) * IMG_BYTES;
+    };
+    // the inputs of item (p, c): raw q, k, g, beta (fused unit) or the
+    // precomputed image (split unit)
+    auto load_inputs = [&](RawChunk& b, const PUnit& p, int c, const Offsets& o, int t) {
+      if (p.img0 >= 0) load_image(b, image_of(p, c), t);
+      else load_raw(b, raw_of(p, c), o);
+    };
+    PUnit pu = unit_of(uni(ps.fetch));  // the unit of the current item
+    int pc = 0;                         // the chunk of the current item in pu
+    RawChunk buf;                       // inputs of the current item
+    if (tid == 0) {
+      Item none{};
+      ps.items[0] = pu.u < n_units ? make_item(pu, 0) : none;
+      ps.items[1] = none;
+    }
+    if (pu.u < n_units) load_inputs(buf, pu, 0, of, tid);
+    __syncthreads();  // item 0 published
+
+    for (int iter = 0;; ++iter) {
+      // this iteration prepares `pi`; the consumer chains the previous item
+      const Item pi = read_item(ps.items[iter & 1]);
+      const Item ci = read_item(ps.items[(iter + 1) & 1]);
+      const bool pv = (pi.flags & ITEM_VALID) != 0;
+      if (!pv && !(ci.flags & ITEM_VALID)) break;
+      // the lane coordinates again, from a value the compiler cannot see
+      // through: what it derives from them (LDS addresses and the like) is
+      // computed inside the iteration instead of being hoisted out of the
+      // loop, where it would hold registers for the whole kernel
+      int t = tid;
+      asm volatile("" : "+v"(t));
+      const Lane lnI = make_lane(t);
+      const Offsets ofI = make_offsets(H, lnI.tok, lnI.cg, lnI.w, lnI.l);
+      const bool last_of_unit = pc + 1 >= pu.nch;
+      const bool next_same = pv && !last_of_unit;  // the next item is this unit's next chunk
+      PUnit nu = pu;  // the next item: (nu, nc)
+      int nc = pc + 1;
+      // between B0 and B1: after the last chunk of a unit, wave 3 fetches the
+      // next unit from the counter
+      auto fetch_next = [&]() {
+        if (pv && last_of_unit && lnI.w == 3 && lnI.l == 0) {
+          const int u = atomicAdd(&hdr->counter, 1);
+          int dx = 0, dy = 0, sx = 0, sy = 0;
+          if (u < n_units) {
+            const int2 d = docs[u / H];
+            dx = d.x;
+            dy = d.y;
+            if (dx < 0) {
+              const int2 sp = split[-dx - 1];
+              sx = sp.x;
+              sy = sp.y;
+            }
+          }
+          ps.nu[0] = u;
+          ps.nu[1] = dx;
+          ps.nu[2] = dy;
+          ps.nu[3] = sx;
+          ps.nu[4] = sy;
+        }
+      };
+      // after B1, once this item's inputs are consumed: the next item, if it
+      // starts a new unit, and its inputs into buf (zeros when there is none,
+      // so that buf is redefined on every path and nothing keeps it alive
+      // across the prologue of prepare_chunk).  The next chunk of the same
+      // unit is loaded earlier, as soon as buf is free (prefetch_same).
+      auto prefetch_same = [&]() {
+        if (next_same && pu.img0 < 0) load_raw(buf, raw_of(pu, pc + 1), ofI);
+      };
+      auto prefetch_next = [&]() {
+        if (next_same) return;
+        if (!pv) {
+          nu.u = n_units;
+        } else if (last_of_unit) {
+          nu = make_punit(uni(ps.nu[0]), n_units, H, uni(ps.nu[1]), uni(ps.nu[2]), uni(ps.nu[3]),
+                          uni(ps.nu[4]));
+          nc = 0;
+        }
+        if (nu.u < n_units) {
+          load_inputs(buf, nu, nc, ofI, lnI.tid);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) buf.p[i] = u32x4{0u, 0u, 0u, 0u};
+          buf.beta = 0.f;
+        }
+      };
+      // between B5 and B6: hand the next item to the consumer
+      auto publish_next = [&]() {
+        if (lnI.tid == 0) {
+          Item none{};
+          ps.items[(iter + 1) & 1] = nu.u < n_units ? make_item(nu, nc) : none;
+        }
+        pu = nu;
+        pc = nc;
+      };
+      if (pv && pi.n > 0 && pu.img0 < 0) {
+        // fused unit: build the image
+        prepare_chunk(sm, LdsSink{&sm}, buf, pi.n, gate_bound, lnI, [&](int part) {
+          if (part == 1) {
+            fetch_next();
+            prefetch_same();
+          } else if (part == 3) {
+            prefetch_next();
+          } else if (part == 5) {
+            publish_next();
+          }
+        });
+      } else {
+        // split unit: write the precomputed image (in two phases); or
+        // nothing to prepare
+        const bool copy = pv && pi.n > 0;
+        const uint8_t* nimg = image_of(pu, next_same ? pc + 1 : pc);
+        __syncthreads();  // B0: the consumer has read Kt and Tb of the previous image
+        if (copy) image_to_lds<0>(sm, buf, lnI.tid);
+        if (copy && next_same) load_image<0>(buf, nimg, lnI.tid);  // the next chunk, as its rounds free up
+        fetch_next();
+        __syncthreads();  // B1: ... and Qt, M, KbT and D
+        if (copy) image_to_lds<1>(sm, buf, lnI.tid);
+        if (copy && next_same) load_image<1>(buf, nimg, lnI.tid);
+        prefetch_next();
+        __syncthreads();  // B2
+        __syncthreads();  // B3
+        __syncthreads();  // B4
+        __syncthreads();  // B5
+        publish_next();
+        __syncthreads();  // B6
+      }
+    }
+  } else {
+    // ======================== consumer (waves 4-7) ========================
+    VChunk vcur;  // V of the current item
+    f32x16 S[4];  // the state
+    auto state_in = [&](const Item& it) {
       const float* h0 = kState ? hdr->h0 : nullptr;
       if (h0 != nullptr) {
-        load_state(S, h0 + ((size_t)hdr->doc_ids[di] * H + h) * (DK * DV), ln);
+        load_state(S, h0 + ((size_t)hdr->doc_ids[it.unit / H] * H + it.h) * (DK * DV), ln);
       } else {
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
@@ -1265,96 +1581,60 @@ __global__ __launch_bounds__(NTHR, 1) void kda_chunk_fwd_kernel(
           for (int i = 0; i < 16; ++i) S[kt][i] = 0.f;
       }
     };
-    // S at the start of the chunk that begins at token c0 (states only)
-    auto save_chunk = [&](const f32x16 (&S)[4], int64_t c0) {
+    auto save_chunk = [&](const Item& it) {
       if constexpr (kState) {
         float* cs = hdr->chunk_states;
         if (cs != nullptr) {
-          const int u = __builtin_amdgcn_readfirstlane(sm.unit);
-          const int d = u / H;
-          const int2 dd = docs[d];
-          const int64_t first = dd.x < 0 ? (int64_t)split[-dd.x - 1].x : (int64_t)dd.x;
-          const int64_t slot = first / CH + hdr->doc_ids[d] + (c0 - first) / CH;
-          store_state(S, cs + ((size_t)slot * H + (u - d * H)) * (DK * DV), ln);
+          const int64_t slot = it.first / CH + hdr->doc_ids[it.unit / H] + (it.c0 - it.first) / CH;
+          store_state(S, cs + ((size_t)slot * H + it.h) * (DK * DV), ln);
         }
       }
     };
-    auto state_out = [&](const f32x16 (&S)[4]) {
+    auto state_out = [&](const Item& it) {
       if constexpr (kState) {
-        // the unit's indices again, from LDS (nothing kept live across the chain)
-        const int u = __builtin_amdgcn_readfirstlane(sm.unit);
-        const int d = u / H;
         float* ht = hdr->ht;
-        if (ht != nullptr) store_state(S, ht + ((size_t)hdr->doc_ids[d] * H + (u - d * H)) * (DK * DV), ln);
+        if (ht != nullptr) store_state(S, ht + ((size_t)hdr->doc_ids[it.unit / H] * H + it.h) * (DK * DV), ln);
       }
     };
-
-    if (doc.x < 0) {
-      // ---- split document: chain over precomputed images
-      const int2 sp = split[-doc.x - 1];
-      const int64_t bos = sp.x, eos = (int64_t)sp.x + doc.y;
-      const uint8_t* img = images + ((size_t)sp.y * H + h) * IMG_BYTES;
-      const size_t img_stride = (size_t)H * IMG_BYTES;
-      Image im;
-      load_image(im, img, tid);
-      VChunk vcur = load_v(v, bos, (int)min<int64_t>(CH, eos - bos), H, h, of);
-      f32x16 S[4];
-      state_in(S);
-      for (int64_t c0 = bos; c0 < eos; c0 += CH) {
-        const int n = (int)min<int64_t>(CH, eos - c0);
-        save_chunk(S, c0);
-        image_to_lds(sm, im, tid);
-        __syncthreads();  // the image is in LDS
-        img += img_stride;
-        const int64_t c1 = c0 + CH;
-        const int n1 = (int)min<int64_t>(CH, eos - c1);
-        const Rsrc rimg = make_rsrc(img, c1 < eos ? IMG_BYTES : 0);
-        chain_chunk(sm, S, vcur, n, c0, H, h, out, ln, of, [&](int stage) {
-          static_assert(IMG_PER_THREAD == 16, "the four load parts cover the image");
-          if (stage == 0) {
-            vcur = load_v(v, c1, n1, H, h, of);
-            load_image_part(im, rimg, tid, 0, 4);
-          } else if (stage == 1) {
-            load_image_part(im, rimg, tid, 4, 8);
-          } else if (stage == 2) {
-            load_image_part(im, rimg, tid, 8, 12);
-          } else {
-            load_image_part(im, rimg, tid, 12, IMG_PER_THREAD);
-          }
-        });
-        __syncthreads();  // the next chunk overwrites the image
+    __syncthreads();  // item 0 published
+    {
+      const Item nx = read_item(ps.items[0]);
+      if (nx.flags & ITEM_VALID) vcur = load_v(v, nx.c0, nx.n, H, nx.h, of);
+    }
+    for (int iter = 0;; ++iter) {
+      // this iteration chains `ci`; the producer prepares `pi`
+      const Item pi = read_item(ps.items[iter & 1]);
+      const Item ci = read_item(ps.items[(iter + 1) & 1]);
+      const bool pv = (pi.flags & ITEM_VALID) != 0;
+      const bool cv = (ci.flags & ITEM_VALID) != 0;
+      if (!pv && !cv) break;
+      const bool active = cv && ci.n > 0;
+      ChainMid mid;
+      if (cv && (ci.flags & ITEM_FIRST)) state_in(ci);
+      if (active) {
+        save_chunk(ci);
+        chain_a(sm, S, vcur, ci.n, ci.c0, H, ci.h, out, ln, of, [&](int stage) {
+          if (stage == 0 && pv) vcur = load_v(v, pi.c0, pi.n, H, pi.h, of);
+        }, mid);
+      } else if (pv) {
+        vcur = load_v(v, pi.c0, pi.n, H, pi.h, of);
       }
-      state_out(S);
-    } else {
-      // ---- fused document: prepare and chain each chunk here
-      const int64_t bos = doc.x, eos = (int64_t)doc.x + doc.y;
-      RawChunk cur;
-      VChunk vcur;
-      {
-        const int n0 = (int)min<int64_t>(CH, eos - bos);
-        load_raw(cur, raw_src(q, k, g, beta, bos, n0, H, h), of);
-        vcur = load_v(v, bos, n0, H, h, of);
+      __syncthreads();  // B0
+      if (active) {
+        chain_o(sm, S, mid, ci.n, ci.c0, H, ci.h, out, ln, of);
+        chain_b(sm, S, mid, ln);
       }
-      f32x16 S[4];
-      state_in(S);
-      for (int64_t c0 = bos; c0 < eos; c0 += CH) {
-        const int n = (int)min<int64_t>(CH, eos - c0);
-        const int64_t c1 = c0 + CH;
-        const int n1 = (int)min<int64_t>(CH, eos - c1);
-        const RawSrc src = raw_src(q, k, g, beta, c1, n1, H, h);
-        save_chunk(S, c0);
-        prepare_chunk(sm, LdsSink{&sm}, cur, n, gate_bound, ln,
-                      [&](int part) { load_raw_part(cur, src, of, part); });
-        chain_chunk(sm, S, vcur, n, c0, H, h, out, ln, of, [&](int stage) {
-          if (stage == 0) vcur = load_v(v, c1, n1, H, h, of);
-        });
-        __syncthreads();  // the next chunk overwrites every LDS tile
-      }
-      state_out(S);
+      if (cv && (ci.flags & ITEM_LAST)) state_out(ci);
+      __syncthreads();  // B1
+      __syncthreads();  // B2
+      __syncthreads();  // B3
+      __syncthreads();  // B4
+      __syncthreads();  // B5
+      __syncthreads();  // B6
     }
   }
   __syncthreads();
-  if (tid == 0 && sm.gate_bad) atomicOr(kState ? hdr->status_word : &g_kda_status, KDA_DEV_GATE_RANGE);
+  if (threadIdx.x == 0 && sm.gate_bad) atomicOr(kState ? hdr->status_word : &g_kda_status, KDA_DEV_GATE_RANGE);
 }
 
 }  // namespace
