@@ -415,7 +415,7 @@ def forward_bench(args):
             "frac": gbs / PEAK_HBM_GBS,
             "traffic": None if args.with_state else measured_traffic(w.name),
             "algorithmic_bytes": bytes_alg,
-            "kernel": "kda_chunk_fwd call (kda_schedule_kernel + kda_pre_kernel + kda_chunk_fwd_kernel)",
+            "kernel": "kda_chunk_fwd call (kda_schedule_kernel + kda_pre_kernel + kda_pc_kernel)",
             "timing": "HIP events on the launch stream around each call",
         },
         "device_status": status,

@@ -27,10 +27,12 @@
 //   kda_pre_kernel       builds the images of every chunk of the split
 //                        documents in parallel (two workgroups per CU) and
 //                        writes them to the workspace;
-//   kda_chunk_fwd_kernel one workgroup of 4 waves per CU pulls units from a
-//                        counter: a fused unit prepares and chains each chunk
-//                        itself, a split unit only chains precomputed images,
-//                        so a long document's sequential chain is short.
+//   kda_pc_kernel        one workgroup of 8 waves per CU pulls units from a
+//                        counter: waves 0-3 build (fused unit) or copy in
+//                        (split unit) the image of chunk i while waves 4-7
+//                        chain chunk i - 1, so a long document's sequential
+//                        chain is short and a fused chunk's image is built
+//                        beside the chain rather than before it.
 //
 // Precision: Qt, Kt and the state's MFMA copy are bf16; S stays fp32 in
 // registers.  M (|M| <= 1), KbT (<= 1) and Tb are fp16, and so are X and U
@@ -295,23 +297,30 @@ __global__ __launch_bounds__(NTHR, 2) void kda_pre_kernel(
   for (int unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
     const int2 ch = pre_chunks[unit / H];
     const int h = unit % H;
+    // the lane coordinates from a value the compiler cannot see through, so
+    // that what it derives from them is not hoisted out of the loop (where it
+    // would hold registers for the whole kernel)
+    int t = ln.tid;
+    asm volatile("" : "+v"(t));
+    const Lane lnI = make_lane(t);
+    const Offsets ofI = make_offsets(H, lnI.tok, lnI.cg, lnI.w, lnI.l);
     RawChunk cur;
-    load_raw(cur, raw_src(q, k, g, beta, ch.x, ch.y, H, h), of);
+    load_raw(cur, raw_src(q, k, g, beta, ch.x, ch.y, H, h), ofI);
     uint8_t* img = images + ((size_t)(unit / H) * H + h) * IMG_BYTES;
     const GlobalSink sink{make_rsrc(img, IMG_BYTES)};
-    prepare_chunk(sm, sink, cur, ch.y, gate_bound, ln, [&](int) {});
+    prepare_chunk(sm, sink, cur, ch.y, gate_bound, lnI, [&](int) {});
     // KbT and M: padded LDS staging rows -> image pieces
     const uint8_t* st = reinterpret_cast<const uint8_t*>(&sm.KbT[0][0]);
 #pragma unroll
     for (int i = 0; i < IMG_KB / NTHR; ++i) {
-      const int pc = ln.tid + NTHR * i;
+      const int pc = lnI.tid + NTHR * i;
       bstore(*reinterpret_cast<const u32x4*>(st + (pc >> 3) * ROW_CC + (pc & 7) * 16), sink.r,
              16 * (GP_KB + pc));
     }
     const uint8_t* sm_m = st + DK * ROW_CC;
 #pragma unroll
     for (int i = 0; i < (CH * (CH / 8) + NTHR - 1) / NTHR; ++i) {
-      const int pc = ln.tid + NTHR * i, row = pc >> 3, cp = pc & 7;
+      const int pc = lnI.tid + NTHR * i, row = pc >> 3, cp = pc & 7;
       const int gp = img_mt_piece(0, row, cp);
       if (gp >= 0) bstore(*reinterpret_cast<const u32x4*>(sm_m + row * ROW_CC + cp * 16), sink.r, 16 * gp);
     }

@@ -514,9 +514,10 @@ __device__ __forceinline__ int wave_f16_exponent(float m) {
 //   rows 4..6:  e^{G_c - G_end(w)}    = 2^{t_{w+1} + .. + t_3}, w = 0..2
 //   rows 7..12: e^{G_end(w) - G_end(b)} = 2^{t_{b+1} + .. + t_w}, pair (w, b), b < w,
 //               at row 7 + w (w - 1) / 2 + b
-// D is also written to the image (sink.dv).
-template <class Sm, class Sink>
-__device__ __forceinline__ void fill_tables(Sm& sm, const Sink& sink, int tid) {
+// Thread tid < DK writes row 3 of channel tid (D, which the caller hands on
+// to the image).
+template <class Sm>
+__device__ __forceinline__ void fill_tables(Sm& sm, int tid) {
   // thread pair (c, half): channel c reads its four totals once; half 0 writes
   // rows 0..6, half 1 rows 7..12
   const int c = tid & (DK - 1);
@@ -529,7 +530,6 @@ __device__ __forceinline__ void fill_tables(Sm& sm, const Sink& sink, int tid) {
     sm.etab[1][c] = __builtin_amdgcn_exp2f(t01);
     sm.etab[2][c] = __builtin_amdgcn_exp2f(t012);
     sm.etab[3][c] = d;
-    sink.dv(c, d);
     sm.etab[4][c] = __builtin_amdgcn_exp2f(t123);
     sm.etab[5][c] = __builtin_amdgcn_exp2f(t23);
     sm.etab[6][c] = __builtin_amdgcn_exp2f(t3);
@@ -645,9 +645,9 @@ __device__ __forceinline__ Lane make_lane(int tid = threadIdx.x) {
 // B4 and B5, hook(5) between B5 and B6.
 // Seven workgroup barriers, B0 .. B6, the last of which ends the function;
 // after it the image is complete.  Until B1 the function writes to LDS only
-// tot, beta and gate_bad (so that another workgroup role may still read the
-// previous image and use the staging slices until then); until B2 not Qt,
-// Kt or KbT; until B5 not Tb or its scale.
+// tot, beta, gate_bad and the decay tables (so that another workgroup role
+// may still read the previous image and use the staging slices until then);
+// until B2 not Qt, Kt or KbT; until B5 not Tb or its scale.
 template <class Sm, class Sink, class Hook>
 __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const RawChunk& cur, int n,
                                               float gate_bound, const Lane& ln, Hook hook) {
@@ -729,10 +729,17 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
     }
   }
   __syncthreads();  // B0
+  // the decay tables (its own LDS space) meanwhile; D, which belongs to the
+  // image, is handed on after B1
+  fill_tables(sm, tid);
+  __builtin_amdgcn_sched_barrier(0);
+  hook(1);
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();  // B1: the previous image's Qt, M, KbT and D may still be read until here
 
-  // diagonal block (w, w) of M and A on fp32 MFMA: k-step s takes element s
-  // from every lane (the same channel on both operands)
-  f32x4 dM, dA;
+  // diagonal block (w, w) of M and A on fp32 MFMA (the factors
+  // e^{+-(G - G_end(w))} inside a sub-block need fp32's range): k-step s
+  // takes element s from every lane (the same channel on both operands)
   {
     f32x4 accM[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     f32x4 accA[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -741,15 +748,7 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
       accM[s & 1] = mfma16f(lq[s], kr[s], accM[s & 1]);
       accA[s & 1] = mfma16f(lk[s], kr[s], accA[s & 1]);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    hook(1);
-    __builtin_amdgcn_sched_barrier(0);
-    dM = accM[0] + accM[1];
-    dA = accA[0] + accA[1];
-  }
-  __syncthreads();  // B1: the previous image's Qt, M, KbT and D may still be read until here
-  {
-    store_block(sm, dM, dA, w, w, l, true, beta_mine);
+    store_block(sm, accM[0] + accM[1], accA[0] + accA[1], w, w, l, true, beta_mine);
     // the chain's MFMAs read the upper blocks (0, 1) and (2, 3) (inside the two
     // diagonal 32x32 tiles): zero them; the other upper blocks are never read
     if (w == 0 || w == 2) {
@@ -766,8 +765,8 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
         sm.u2.R[w][s][l] = rv;
       }
     }
+    if (tid < DK) sink.dv(tid, sm.etab[3][tid]);  // written by this thread before B1
   }
-  fill_tables(sm, sink, tid);
   __syncthreads();  // B2: decay tables, R and the diagonal A / M blocks visible
 
   // ---- operand tiles of the chain: Qt = lq e^{G_end(w)}, Kt = -lk e^{G_end(w)},
@@ -1291,7 +1290,7 @@ __device__ __forceinline__ void store_state(const f32x16 (&S)[4], float* dst, co
 //   before B0:  producer: prologue (registers, its own tot / beta);
 //               consumer: chain_a, X and U (reads Kt, Tb and Tb's scale;
 //               stages V in its slice);
-//   B0 .. B1:   producer: diagonal A / M products (registers);
+//   B0 .. B1:   producer: decay tables (its own LDS space);
 //               consumer: chain_o and chain_b, O and the state update (reads
 //               Qt, M, KbT and D; stages O in its slice);
 //   B1 .. B6:   producer: the rest of the image (the slices take R and T);
@@ -1568,6 +1567,11 @@ __global__ __launch_bounds__(NPC, 1) void kda_pc_kernel(
     }
   } else {
     // ======================== consumer (waves 4-7) ========================
+    // The chain holds up the producer at B0 and B1 and is idle after them:
+    // its waves take precedence over the producer's in instruction issue
+    // (otherwise the older producer waves win it, and the chain's MFMAs wait
+    // behind the producer's long runs of them).
+    __builtin_amdgcn_s_setprio(2);
     VChunk vcur;  // V of the current item
     f32x16 S[4];  // the state
     auto state_in = [&](const Item& it) {
