@@ -78,9 +78,9 @@ __device__ __forceinline__ f32x16 mfma32h(const f16x8& a, const f16x8& b, const 
 //
 // The leading part, Qt .. u.tb, is the chunk's "image": everything the chain
 // reads that does not depend on the state.  For a split document the pre
-// kernel builds it and copies it to global memory byte for byte; the main
-// kernel copies it back instead of building it.  The per-channel state decay
-// e^{G_c} travels in the row padding of Kt (see dvec).
+// kernel builds it and writes it to global memory; the main kernel copies it
+// back instead of building it.  The per-channel state decay e^{G_c} travels in
+// the row padding of KbT (see dvec), Tb's scale in that of Kt row 32.
 // ---------------------------------------------------------------------------
 struct alignas(16) Smem {
   bf16 Qt[CH][DK + 8];       // qh * e^G                      (A operand of Qt S)
@@ -96,12 +96,10 @@ struct alignas(16) Smem {
     f16x8 R[3][4][64];       // right operands of off-diagonal sub-blocks (fp16), lane order
     float T[CH][CH + 4];     // (I + A)^-1 (fp32)
     struct {
-      union {
-        unsigned short vt[32][CH + 8];  // this chunk's V, transposed (its 32 columns)
-        unsigned short o[CH][32];       // then the bf16 O rows of those columns
-      };
+      unsigned short o[CH][32];  // the bf16 O rows of the wave's 32 columns
     } ws[4];                 // per-wave staging slices
   } u2;
+  unsigned short vt[4][32][CH + 8];  // per wave: V of the chunk chained next, transposed (its 32 columns)
   float etab[13][DK];        // per-channel decay factors of the chunk (see fill_tables)
   float tot[4][DK];          // per sub-block total decay (log2 domain)
   float beta[CH];
@@ -111,9 +109,9 @@ struct alignas(16) Smem {
 };
 
 
-// e^{G_c} of channels c .. c + 3 (c a multiple of 4): the padding of Kt row c / 4
+// e^{G_c} of channels c .. c + 3 (c a multiple of 4): the padding of KbT row c / 4
 __device__ __forceinline__ float* dvec(Smem& sm, int c) {
-  return reinterpret_cast<float*>(&sm.Kt[c >> 2][DK]);
+  return reinterpret_cast<float*>(&sm.KbT[c >> 2][CH]);
 }
 // the power of two Tb was divided by: the padding of Kt row 32
 __device__ __forceinline__ float* tbscale(Smem& sm) {
@@ -132,37 +130,39 @@ static_assert(OFF_TB == (int)offsetof(Smem, M) + CH * ROW_CC, "Tb follows M");
 static_assert(OFF_KT == OFF_QT + CH * ROW_QK, "Kt follows Qt");
 
 // The image in global memory holds the tiles the chain reads, without the LDS
-// row padding, in 16-byte pieces:
-//   the Qt and Kt rows (16 pieces each);
-//   the KbT rows (8 each);
-//   the first 32 columns of rows 0..31 of M, then of Tb (4 each: the chain's
-//   first row tile reads only those);
-//   rows 32..63 of M, then of Tb (8 each);
-//   one piece per Kt row padding for D (rows 0..31) and Tb's scale (row 32).
-// Every part but the last fills whole rounds of NTHR pieces, so image_to_lds
-// knows the part of each round at compile time.
-constexpr int IMG_QK = 2 * CH * (DK / 8);          // Qt, Kt pieces
+// row padding, in 16-byte pieces, in two groups: first what the chain's
+// second part (O and the state update) reads, then what its first part (X and
+// U) reads:
+//   the Qt rows (16 pieces each), the KbT rows (8 each), rows 32..63 of M (8
+//   each), the first 32 columns of rows 0..31 of M (4 each: the chain's first
+//   row tile reads only those), D (channels 4 r .. 4 r + 3 in piece r,
+//   r = 0..31);
+//   the Kt rows (16 each), rows 32..63 of Tb, the first 32 columns of rows
+//   0..31 of Tb, Tb's scale.
+// The parts of each group fill rounds of NTHR pieces that lie in one group
+// (the last round of each is partial), so that the copy into LDS moves whole
+// rounds per group.
+constexpr int IMG_ROW16 = CH * (DK / 8);           // Qt (or Kt) pieces
 constexpr int IMG_KB = DK * (CH / 8);              // KbT pieces
-constexpr int IMG_SHORT = 2 * 32 * 4;              // rows 0..31 of M and Tb, columns 0..31
-constexpr int IMG_LONG = 32 * (CH / 8);            // rows 32..63 of M (or of Tb)
-constexpr int IMG_PAD = DK / 4 + 1;                // Kt row paddings in use
-constexpr int IMG_VEC = IMG_QK + IMG_KB + IMG_SHORT + 2 * IMG_LONG + IMG_PAD;
+constexpr int IMG_SHORT = 32 * 4;                  // rows 0..31 of M (or Tb), columns 0..31
+constexpr int IMG_LONG = 32 * (CH / 8);            // rows 32..63 of M (or Tb)
+constexpr int GP_QT = 0;                           // global piece indices of the parts
+constexpr int GP_KB = GP_QT + IMG_ROW16;
+constexpr int GP_MLONG = GP_KB + IMG_KB;
+constexpr int GP_MSHORT = GP_MLONG + IMG_LONG;
+constexpr int GP_D = GP_MSHORT + IMG_SHORT;
+constexpr int GP_KT = GP_D + DK / 4;               // the second group
+constexpr int GP_TLONG = GP_KT + IMG_ROW16;
+constexpr int GP_TSHORT = GP_TLONG + IMG_LONG;
+constexpr int GP_TBS = GP_TSHORT + IMG_SHORT;
+constexpr int IMG_VEC = GP_TBS + 1;
 constexpr int IMG_BYTES = 16 * IMG_VEC;            // one image in global memory
-constexpr int IMG_PER_THREAD = (IMG_VEC + NTHR - 1) / NTHR;  // pieces per thread (the last partial)
 static_assert(ROW_QK == 17 * 16 && ROW_CC == 9 * 16, "rows are whole pieces plus one of padding");
-static_assert(IMG_QK % NTHR == 0 && IMG_KB % NTHR == 0 && IMG_SHORT == NTHR && IMG_LONG == NTHR,
-              "every part but the last fills whole rounds");
 constexpr int OFF_M = OFF_KBT + DK * ROW_CC;       // LDS rows of M, then Tb
-// global piece indices of the parts the pre kernel writes
-constexpr int GP_KB = IMG_QK;
-constexpr int GP_SHORT = GP_KB + IMG_KB;
-constexpr int GP_MLONG = GP_SHORT + IMG_SHORT;
-constexpr int GP_TLONG = GP_MLONG + IMG_LONG;
-constexpr int GP_PAD = GP_TLONG + IMG_LONG;
 // global piece of (row, 8-column piece cp) of M (t = 0) or Tb (t = 1); -1 for
 // the pieces the chain never reads (rows 0..31, columns 32..63)
 __device__ __forceinline__ int img_mt_piece(int t, int row, int cp) {
-  if (row < 32) return cp < 4 ? GP_SHORT + 128 * t + 4 * row + cp : -1;
+  if (row < 32) return cp < 4 ? (t ? GP_TSHORT : GP_MSHORT) + 4 * row + cp : -1;
   return (t ? GP_TLONG : GP_MLONG) + 8 * (row - 32) + cp;
 }
 
@@ -266,6 +266,17 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 
+// wave-uniform copies of values every lane holds alike (read from LDS, or
+// derived from such values where the compiler cannot see it), so that it
+// keeps them, and what is derived from them (buffer descriptors among
+// others), in scalar registers
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uni64(int64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
@@ -281,12 +292,9 @@ __device__ __forceinline__ void bstore(u32x4 x, Rsrc r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b128(x, r, (int)off, 0, 0);
 }
 
-// Sixteen 16-byte pieces per lane: either the raw inputs of a chunk
-// (q: p[0..3], k: p[4..7], g: p[8..15]; element 8 s + j of q or k is channel
-// 32 s + 8 cg + j, and g holds the same 32 channels as fp32 bits) with beta,
-// or this lane's share of a precomputed chunk image (piece tid + NTHR i in
-// p[i]).  One register buffer serves both, so that the producer of the main
-// kernel never holds two.
+// The raw inputs of a chunk, sixteen 16-byte pieces per lane (q: p[0..3],
+// k: p[4..7], g: p[8..15]; element 8 s + j of q or k is channel 32 s + 8 cg + j,
+// and g holds the same 32 channels as fp32 bits) with beta.
 struct RawChunk {
   u32x4 p[16];
   float beta;
@@ -322,7 +330,9 @@ struct RawSrc {
 __device__ __forceinline__ RawSrc raw_src(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                           const float* __restrict__ g, const float* __restrict__ beta,
                                           int64_t c0, int n, int H, int h) {
-  const size_t row = (size_t)c0 * H + h;
+  // (every lane asks for the same chunk)
+  const size_t row = (size_t)uni64(c0 * H + h);
+  n = uni(n);
   const uint32_t nb = chunk_bytes(n, H, 256u);
   RawSrc src;
   src.q = make_rsrc(q + row * DK, nb);
@@ -377,51 +387,67 @@ __device__ __forceinline__ VChunk load_v(const bf16* __restrict__ v, int64_t c0,
   return vc;
 }
 
-// a chunk image into registers: thread tid loads pieces tid + NTHR i (the last
-// round only covers the first waves).  kPhase selects the rounds image_to_lds
-// writes in that phase (-1: all).
-static_assert(IMG_PER_THREAD == 16, "an image fills the sixteen pieces of RawChunk");
-// phase 0: the Kt rows and rows 32..63 of Tb (read by the chain's first part
-// only); phase 1: the rest (Qt, KbT, M, rows 0..31 of Tb, the paddings)
-__device__ __forceinline__ constexpr int image_round_phase(int i) {
-  return ((NTHR * i >= IMG_QK / 2 && NTHR * i < GP_KB) || (NTHR * i >= GP_TLONG && NTHR * i < GP_PAD)) ? 0 : 1;
+// ---- a precomputed image back into LDS, through registers.  Round i (0..15)
+// of thread tid is piece img_round_base(i) + tid of the image, held in p[i];
+// rounds 0..9 are the first group (Qt, KbT, M, D: phase 1, what the chain's
+// second part reads), rounds 10..15 the second (Kt, Tb, Tb's scale: phase 0,
+// what its first part reads).
+constexpr int IMG_ROUNDS = 16;
+constexpr int IMG_ROUNDS_P1 = 10;
+__device__ __forceinline__ constexpr int img_round_base(int i) {
+  return i < 4 ? GP_QT + NTHR * i : i < 8 ? GP_KB + NTHR * (i - 4) : i == 8 ? GP_MLONG : i == 9 ? GP_MSHORT
+         : i < 14 ? GP_KT + NTHR * (i - 10) : i == 14 ? GP_TLONG : GP_TSHORT;
 }
+__device__ __forceinline__ constexpr int img_round_count(int i) {
+  return i == 9 ? IMG_SHORT + DK / 4 : i == 15 ? IMG_SHORT + 1 : NTHR;
+}
+static_assert(IMG_ROW16 == 4 * NTHR && IMG_KB == 4 * NTHR && IMG_LONG == NTHR &&
+                  img_round_base(9) + img_round_count(9) == GP_KT &&
+                  img_round_base(15) + img_round_count(15) == IMG_VEC,
+              "the rounds cover the image, each group in whole rounds");
+__device__ __forceinline__ constexpr int image_round_phase(int i) { return i < IMG_ROUNDS_P1 ? 1 : 0; }
+// the rounds of phase kPhase (-1: all) into registers.  n_bytes is the
+// image's size, or 0 to load zeros (a descriptor of size 0 reads nothing);
+// lanes past a round's count read past the end, zeros as well.  Every load is
+// unconditional, so that each round's registers are simply replaced.
 template <int kPhase = -1>
-__device__ __forceinline__ void load_image(RawChunk& im, const uint8_t* __restrict__ src, int tid) {
-  const Rsrc r = make_rsrc(src, IMG_BYTES);
+__device__ __forceinline__ void load_image(RawChunk& im, const uint8_t* __restrict__ src, uint32_t n_bytes,
+                                           int tid) {
+  // (every lane asks for the same image)
+  const Rsrc r = make_rsrc(reinterpret_cast<const uint8_t*>(uni64((int64_t)src)), (uint32_t)uni((int)n_bytes));
 #pragma unroll
-  for (int i = 0; i < IMG_PER_THREAD; ++i)
-    if ((kPhase < 0 || image_round_phase(i) == kPhase) && tid + NTHR * i < IMG_VEC)
-      im.p[i] = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * tid, 16 * NTHR * i, 0);
+  for (int i = 0; i < IMG_ROUNDS; ++i)
+    if (kPhase < 0 || image_round_phase(i) == kPhase)
+      im.p[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          r, tid < img_round_count(i) ? 16 * (img_round_base(i) + tid) : IMG_BYTES, 0, 0);
 }
-
-// each round of NTHR pieces lies in one part of the image: the part of round
-// i is known at compile time.  kPhase selects the rounds of one phase
-// (image_round_phase); -1 writes everything.
+// the rounds of phase kPhase (-1: all) from registers into the LDS image
 template <int kPhase = -1>
 __device__ __forceinline__ void image_to_lds(Smem& sm, const RawChunk& im, int tid) {
   uint8_t* dst = reinterpret_cast<uint8_t*>(&sm);
 #pragma unroll
-  for (int i = 0; i < IMG_PER_THREAD; ++i) {
-    const int p = tid + NTHR * i;
-    const int r0 = NTHR * i;  // first piece of the round
+  for (int i = 0; i < IMG_ROUNDS; ++i) {
     if (kPhase >= 0 && image_round_phase(i) != kPhase) continue;
     int off;
-    if (r0 < GP_KB) {
-      off = OFF_QT + (p >> 4) * ROW_QK + (p & 15) * 16;
-    } else if (r0 < GP_SHORT) {
-      const int q = p - GP_KB;
+    if (i < 4) {         // Qt rows
+      const int q = NTHR * i + tid;
+      off = OFF_QT + (q >> 4) * ROW_QK + (q & 15) * 16;
+    } else if (i < 8) {  // KbT rows
+      const int q = NTHR * (i - 4) + tid;
       off = OFF_KBT + (q >> 3) * ROW_CC + (q & 7) * 16;
-    } else if (r0 < GP_MLONG) {
-      const int q = p - GP_SHORT;  // Tb rows follow M rows in LDS: row (q >> 2) + 64 (q >> 7)
-      off = OFF_M + ((q & 127) >> 2) * ROW_CC + CH * ROW_CC * (q >> 7) + (q & 3) * 16;
-    } else if (r0 < GP_PAD) {
-      const int q = p - GP_MLONG;  // M rows 32..63, then Tb rows 32..63
-      off = OFF_M + (32 + ((q & 255) >> 3)) * ROW_CC + CH * ROW_CC * (q >> 8) + (q & 7) * 16;
-    } else {
-      off = OFF_KT + (p - GP_PAD) * ROW_QK + 2 * DK;
+    } else if (i == 8 || i == 14) {  // rows 32..63 of M, of Tb
+      off = (i == 8 ? OFF_M : OFF_TB) + (32 + (tid >> 3)) * ROW_CC + (tid & 7) * 16;
+    } else if (i >= 10 && i < 14) {  // Kt rows
+      const int q = NTHR * (i - 10) + tid;
+      off = OFF_KT + (q >> 4) * ROW_QK + (q & 15) * 16;
+    } else if (tid < IMG_SHORT) {  // columns 0..31 of rows 0..31 of M (round 9), of Tb (round 15)
+      off = (i == 9 ? OFF_M : OFF_TB) + (tid >> 2) * ROW_CC + (tid & 3) * 16;
+    } else if (i == 9) { // D: the padding of KbT row tid - IMG_SHORT
+      off = OFF_KBT + (tid - IMG_SHORT) * ROW_CC + 2 * CH;
+    } else {             // Tb's scale: the padding of Kt row 32
+      off = OFF_KT + 32 * ROW_QK + 2 * DK;
     }
-    if (p < IMG_VEC) *reinterpret_cast<u32x4*>(dst + off) = im.p[i];
+    if (tid < img_round_count(i)) *reinterpret_cast<u32x4*>(dst + off) = im.p[i];
   }
 }
 
@@ -443,19 +469,19 @@ struct LdsSink {
 struct GlobalSink {
   Rsrc r;  // one image, IMG_BYTES (the layout above)
   __device__ __forceinline__ void qk(int tok, int col, const bf16x8& qt, const bf16x8& kt) const {
-    const uint32_t o = (uint32_t)(tok * 2 * DK + 2 * col);
-    bstore(__builtin_bit_cast(u32x4, qt), r, o);
-    bstore(__builtin_bit_cast(u32x4, kt), r, 16 * CH * (DK / 8) + o);
+    const uint32_t o = (uint32_t)(tok * 2 * DK + 2 * col);  // 16 * (16 tok + col / 8)
+    bstore(__builtin_bit_cast(u32x4, qt), r, 16 * GP_QT + o);
+    bstore(__builtin_bit_cast(u32x4, kt), r, 16 * GP_KT + o);
   }
   __device__ __forceinline__ void dv(int c, float f) const {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f), r, 16 * (GP_PAD + (c >> 2)) + 4 * (c & 3), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f), r, 16 * (GP_D + (c >> 2)) + 4 * (c & 3), 0, 0);
   }
   __device__ __forceinline__ void tb(int row, int col, const f16x8& x) const {
     const int pc = img_mt_piece(1, row, col >> 3);
     if (pc >= 0) bstore(__builtin_bit_cast(u32x4, x), r, 16 * pc);
   }
   __device__ __forceinline__ void tbs(float f) const {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f), r, 16 * (GP_PAD + DK / 4), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f), r, 16 * GP_TBS, 0, 0);
   }
 };
 
@@ -922,32 +948,26 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
 // The state-dependent part of a chunk of n tokens starting at token c0, from
 // the image in LDS and this chunk's V (wave w owns value columns 32 w ..):
 //   X = V - Kt S,  U = Tb X,  O = scale (Qt S + M U),  S <- D S + KbT U,
-// in three parts.  chain_a computes X and U: it reads V, Kt, Tb and Tb's
-// scale and stages V in the wave's slice; chain_o computes and stores O: it
+// in three parts.  chain_a computes X and U: it reads V (staged by stage_v),
+// Kt, Tb and Tb's scale; chain_o computes and stores O: it
 // reads Qt and M and stages O in the slice; chain_b updates S: it reads only
 // KbT and D.  ChainMid carries U (fp16, 2^-eu) from chain_a to the others.
-// hook(0..2) run at fixed points of chain_a after V has been consumed (they
-// may refill vcur): after the V staging, after X and after U.
+// Scheduling fences in chain_a (after the V staging, after X and after U)
+// keep its stages in order.
 struct ChainMid {
   f16x8 Uh[4];
   int eu;
 };
 
-template <class Hook>
-__device__ __forceinline__ void chain_a(Smem& sm, const f32x16 (&S)[4], const VChunk& vcur, int n,
-                                        int64_t c0, int H, int h, bf16* __restrict__ out,
-                                        const Lane& ln, const Offsets& of, Hook hook,
-                                        ChainMid& mid) {
-  const int w = ln.w, l = ln.l, m = ln.m, hg = ln.hg;
-  const float scale = 0.08838834764831845f;  // 128^-1/2
-
-  // this chunk's V, transposed into the wave's staging slice (rows past
-  // the end were read as zero)
-  unsigned short (*vt)[CH + 8] = sm.u2.ws[w].vt;
+// V of the chunk chained next (rows past its end were read as zero),
+// transposed into the wave's part of vt, where chain_a reads it
+__device__ __forceinline__ void stage_v(Smem& sm, const VChunk& vn, const Lane& ln) {
+  const int l = ln.l;
+  unsigned short (*vt)[CH + 8] = sm.vt[ln.w];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int t = 16 * i + (l >> 2);
-    const u32x4 u = vcur.r[i];
+    const u32x4 u = vn.r[i];
     const uint32_t uu[4] = {u[0], u[1], u[2], u[3]};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -957,7 +977,16 @@ __device__ __forceinline__ void chain_a(Smem& sm, const f32x16 (&S)[4], const VC
       vt[8 * (l & 3) + 2 * j + 1][t ^ (8 * (l & 3))] = (unsigned short)(uu[j] >> 16);
     }
   }
-  wave_sync_lds();
+}
+
+__device__ __forceinline__ void chain_a(Smem& sm, const f32x16 (&S)[4], int n, int64_t c0, int H, int h,
+                                        bf16* __restrict__ out, const Lane& ln, const Offsets& of,
+                                        ChainMid& mid) {
+  const int w = ln.w, l = ln.l, m = ln.m, hg = ln.hg;
+  const float scale = 0.08838834764831845f;  // 128^-1/2
+
+  // this chunk's V, staged transposed by stage_v
+  const unsigned short (*vt)[CH + 8] = sm.vt[w];
   const int rowsel = swap23(m);
   // V in the C layout of the X tiles (packed bf16; added after the product)
   u32x4 vx[2][2];
@@ -966,9 +995,6 @@ __device__ __forceinline__ void chain_a(Smem& sm, const f32x16 (&S)[4], const VC
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
       vx[mt][hh] = *reinterpret_cast<const u32x4*>(&vt[m][(32 * mt + 16 * hh + 8 * hg) ^ (8 * (m >> 3))]);
-  wave_sync_lds();  // V read out before the slice stages O
-  __builtin_amdgcn_sched_barrier(0);
-  hook(0);
   __builtin_amdgcn_sched_barrier(0);
 
   bf16x8 Sb[8];
@@ -1024,8 +1050,6 @@ __device__ __forceinline__ void chain_a(Smem& sm, const f32x16 (&S)[4], const VC
 #pragma unroll
     for (int j = 0; j < 8; ++j) Xh[s][j] = (_Float16)xv[8 * s + j];
   __builtin_amdgcn_sched_barrier(0);
-  hook(1);
-  __builtin_amdgcn_sched_barrier(0);
 
   // U = Tb X: the six lower-triangular (row tile, k-step) pairs, fp16 operands
   constexpr int PMT[6] = {0, 0, 1, 1, 1, 1};
@@ -1080,8 +1104,6 @@ __device__ __forceinline__ void chain_a(Smem& sm, const f32x16 (&S)[4], const VC
     for (int j = 0; j < 8; ++j) {
       Uh[s][j] = (_Float16)(U[s >> 1][8 * (s & 1) + j] * udown);
     }
-  __builtin_amdgcn_sched_barrier(0);
-  hook(2);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int s = 0; s < 4; ++s) mid.Uh[s] = Uh[s];
@@ -1284,9 +1306,10 @@ __device__ __forceinline__ void store_state(const f32x16 (&S)[4], float* dst, co
 // a split chunk's image from the workspace) while waves 4-7 (the consumer)
 // chain chunk i - 1 on the image in LDS: two waves per SIMD, one of each role.
 //
-// Both roles pass the same seven workgroup barriers per iteration (B0..B6,
-// those of prepare_chunk).  The image is single-buffered; the barriers order
-// the consumer's reads of image i - 1 before the producer's writes of image i:
+// The image is single-buffered; workgroup barriers order the consumer's reads
+// of image i - 1 before the producer's writes of image i.  An iteration in
+// which the producer builds an image from raw inputs has seven barriers, B0 ..
+// B6 (those of prepare_chunk):
 //   before B0:  producer: prologue (registers, its own tot / beta);
 //               consumer: chain_a, X and U (reads Kt, Tb and Tb's scale;
 //               stages V in its slice);
@@ -1295,12 +1318,19 @@ __device__ __forceinline__ void store_state(const f32x16 (&S)[4], float* dst, co
 //               Qt, M, KbT and D; stages O in its slice);
 //   B1 .. B6:   producer: the rest of the image (the slices take R and T);
 //               consumer: idle.
+// An iteration that copies a precomputed image (or prepares nothing) has two:
+//   B0 .. B1:   producer: Kt, Tb and Tb's scale of image i;
+//   after B1:   producer: Qt, KbT, M and D of image i;
+//               consumer: chain_a of image i (the next iteration), which reads
+//               only what was written before B1.
 // The producer hands each chunk to the consumer through an item descriptor in
-// LDS (two slots, by iteration parity), written between B5 and B6.
+// LDS (two slots, by iteration parity), published before the iteration that
+// prepares it; the consumer reads it after that iteration's B0 and from it
+// knows the iteration's barrier count.
 // ---------------------------------------------------------------------------
 constexpr int NPC = 2 * NTHR;  // threads of the producer / consumer kernel
 
-enum ItemFlags { ITEM_VALID = 1, ITEM_FIRST = 2, ITEM_LAST = 4 };
+enum ItemFlags { ITEM_VALID = 1, ITEM_FIRST = 2, ITEM_LAST = 4, ITEM_SPLIT = 8 };
 
 struct Item {
   int64_t c0;     // first token of the chunk
@@ -1308,8 +1338,11 @@ struct Item {
   int n;          // tokens in the chunk (0 for an empty document)
   int h;          // head
   int unit;       // work-list entry: list index * H + h
-  int flags;      // ItemFlags
+  int flags;      // ItemFlags (ITEM_SPLIT: the image is precomputed)
 };
+
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt at their maxima: not waited for)
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // a unit as the producer walks it (uniform values)
 struct PUnit {
@@ -1350,15 +1383,6 @@ __device__ __forceinline__ PUnit make_punit(int u, int n_units, int H, int dx, i
   return p;
 }
 
-// wave-uniform copies of values read from LDS (all lanes read the same word),
-// so that the compiler keeps them, and what is derived from them (buffer
-// descriptors among others), in scalar registers
-__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
-__device__ __forceinline__ int64_t uni64(int64_t x) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)x >> 32));
-  return (int64_t)(((uint64_t)hi << 32) | lo);
-}
 __device__ __forceinline__ Item read_item(const Item& src) {
   Item it;
   it.c0 = uni64(src.c0);
@@ -1378,7 +1402,8 @@ __device__ __forceinline__ Item make_item(const PUnit& p, int c) {
   if (it.n < 0) it.n = 0;
   it.h = p.h;
   it.unit = p.u;
-  it.flags = ITEM_VALID | (c == 0 ? ITEM_FIRST : 0) | (c == p.nch - 1 ? ITEM_LAST : 0);
+  it.flags = ITEM_VALID | (c == 0 ? ITEM_FIRST : 0) | (c == p.nch - 1 ? ITEM_LAST : 0) |
+             (p.img0 >= 0 ? ITEM_SPLIT : 0);
   return it;
 }
 
@@ -1441,10 +1466,18 @@ __global__ __launch_bounds__(NPC, 1) void kda_pc_kernel(
       return images + ((size_t)(p.img0 + c) * H + p.h) * IMG_BYTES;
     };
     // the inputs of item (p, c): raw q, k, g, beta (fused unit) or the
-    // precomputed image (split unit)
+    // precomputed image (split unit); zeros when there is no item, so that
+    // buf is redefined on every path
     auto load_inputs = [&](RawChunk& b, const PUnit& p, int c, const Offsets& o, int t) {
-      if (p.img0 >= 0) load_image(b, image_of(p, c), t);
-      else load_raw(b, raw_of(p, c), o);
+      if (p.u < n_units && p.img0 >= 0) {
+        load_image(b, image_of(p, c), IMG_BYTES, t);
+      } else if (p.u < n_units) {
+        load_raw(b, raw_of(p, c), o);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) b.p[i] = u32x4{0u, 0u, 0u, 0u};
+        b.beta = 0.f;
+      }
     };
     PUnit pu = unit_of(uni(ps.fetch));  // the unit of the current item
     int pc = 0;                         // the chunk of the current item in pu
@@ -1454,15 +1487,16 @@ __global__ __launch_bounds__(NPC, 1) void kda_pc_kernel(
       ps.items[0] = pu.u < n_units ? make_item(pu, 0) : none;
       ps.items[1] = none;
     }
-    if (pu.u < n_units) load_inputs(buf, pu, 0, of, tid);
+    load_inputs(buf, pu, 0, of, tid);
     __syncthreads();  // item 0 published
 
+    bool cv = false;  // the consumer chains an item in this iteration
     for (int iter = 0;; ++iter) {
-      // this iteration prepares `pi`; the consumer chains the previous item
-      const Item pi = read_item(ps.items[iter & 1]);
-      const Item ci = read_item(ps.items[(iter + 1) & 1]);
-      const bool pv = (pi.flags & ITEM_VALID) != 0;
-      if (!pv && !(ci.flags & ITEM_VALID)) break;
+      // this iteration prepares chunk pc of pu; the consumer chains the
+      // previous item
+      const bool pv = pu.u < n_units;
+      if (!pv && !cv) break;
+      const int pn = pv ? (int)max<int64_t>(0, min<int64_t>(CH, (int64_t)pu.len - (int64_t)CH * pc)) : 0;
       // the lane coordinates again, from a value the compiler cannot see
       // through: what it derives from them (LDS addresses and the like) is
       // computed inside the iteration instead of being hoisted out of the
@@ -1471,14 +1505,10 @@ __global__ __launch_bounds__(NPC, 1) void kda_pc_kernel(
       asm volatile("" : "+v"(t));
       const Lane lnI = make_lane(t);
       const Offsets ofI = make_offsets(H, lnI.tok, lnI.cg, lnI.w, lnI.l);
-      const bool last_of_unit = pc + 1 >= pu.nch;
-      const bool next_same = pv && !last_of_unit;  // the next item is this unit's next chunk
-      PUnit nu = pu;  // the next item: (nu, nc)
-      int nc = pc + 1;
-      // between B0 and B1: after the last chunk of a unit, wave 3 fetches the
-      // next unit from the counter
+      // between B0 and B1 of a unit's last chunk: wave 3 fetches the next
+      // unit from the counter
       auto fetch_next = [&]() {
-        if (pv && last_of_unit && lnI.w == 3 && lnI.l == 0) {
+        if (lnI.w == 3 && lnI.l == 0) {
           const int u = atomicAdd(&hdr->counter, 1);
           int dx = 0, dy = 0, sx = 0, sy = 0;
           if (u < n_units) {
@@ -1498,72 +1528,90 @@ __global__ __launch_bounds__(NPC, 1) void kda_pc_kernel(
           ps.nu[4] = sy;
         }
       };
-      // after B1, once this item's inputs are consumed: the next item, if it
-      // starts a new unit, and its inputs into buf (zeros when there is none,
-      // so that buf is redefined on every path and nothing keeps it alive
-      // across the prologue of prepare_chunk).  The next chunk of the same
-      // unit is loaded earlier, as soon as buf is free (prefetch_same).
-      auto prefetch_same = [&]() {
-        if (next_same && pu.img0 < 0) load_raw(buf, raw_of(pu, pc + 1), ofI);
+      // after B1: the unit fetched between B0 and B1
+      auto fetched = [&]() {
+        return make_punit(uni(ps.nu[0]), n_units, H, uni(ps.nu[1]), uni(ps.nu[2]), uni(ps.nu[3]), uni(ps.nu[4]));
       };
-      auto prefetch_next = [&]() {
-        if (next_same) return;
-        if (!pv) {
-          nu.u = n_units;
-        } else if (last_of_unit) {
-          nu = make_punit(uni(ps.nu[0]), n_units, H, uni(ps.nu[1]), uni(ps.nu[2]), uni(ps.nu[3]),
-                          uni(ps.nu[4]));
-          nc = 0;
-        }
-        if (nu.u < n_units) {
-          load_inputs(buf, nu, nc, ofI, lnI.tid);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) buf.p[i] = u32x4{0u, 0u, 0u, 0u};
-          buf.beta = 0.f;
-        }
-      };
-      // between B5 and B6: hand the next item to the consumer
-      auto publish_next = [&]() {
+      // hand item (p, c) to the consumer, which reads it after the next B0 of
+      // iteration it + 1 (the slot it replaces was read before the B0 of
+      // iteration it)
+      auto publish = [&](int it, const PUnit& p, int c) {
         if (lnI.tid == 0) {
           Item none{};
-          ps.items[(iter + 1) & 1] = nu.u < n_units ? make_item(nu, nc) : none;
+          ps.items[(it + 1) & 1] = p.u < n_units ? make_item(p, c) : none;
         }
-        pu = nu;
-        pc = nc;
       };
-      if (pv && pi.n > 0 && pu.img0 < 0) {
-        // fused unit: build the image
-        prepare_chunk(sm, LdsSink{&sm}, buf, pi.n, gate_bound, lnI, [&](int part) {
+      PUnit nu = pu;  // the next item: (nu, nc)
+      int nc = pc + 1;
+      if (pv && pn > 0 && pu.img0 < 0) {
+        // fused unit: build the image (seven barriers; the consumer, told by
+        // the item, passes B2 .. B6 with it).  The next chunk's inputs go
+        // into buf as soon as it is free: the same unit's after B1, a new
+        // unit's (zeros if none) once it is known, after B3, so that buf is
+        // redefined on every path and nothing keeps it alive across the
+        // prologue.
+        const bool last = pc + 1 >= pu.nch;
+        prepare_chunk(sm, LdsSink{&sm}, buf, pn, gate_bound, lnI, [&](int part) {
           if (part == 1) {
-            fetch_next();
-            prefetch_same();
+            if (last) fetch_next();
+            else load_raw(buf, raw_of(pu, pc + 1), ofI);
           } else if (part == 3) {
-            prefetch_next();
+            if (last) {
+              nu = fetched();
+              nc = 0;
+              load_inputs(buf, nu, 0, ofI, lnI.tid);
+            }
           } else if (part == 5) {
-            publish_next();
+            publish(iter, nu, nc);
           }
         });
+      } else if (pv && pn > 0) {
+        // split unit: all its remaining chunks here, an iteration each with
+        // two barriers (the consumer starts on an image right after its B1).
+        // A chunk's image goes from registers into LDS, what the chain's
+        // first part reads after B0 and the rest after B1 (the next B0 orders
+        // it before the chain's second part), each phase's registers then
+        // taking the next chunk's.  The image registers are this loop's own,
+        // so that nothing is copied between iterations.
+        RawChunk im = buf;
+        for (;; ++iter, ++pc) {
+          const bool last = pc + 1 >= pu.nch;
+          const uint8_t* nimg = image_of(pu, pc + 1);
+          const uint32_t nbytes = last ? 0u : IMG_BYTES;  // the next chunk, or zeros
+          __syncthreads();  // B0: the consumer has read Kt, Tb and Tb's scale of the previous image
+          image_to_lds<0>(sm, im, lnI.tid);
+          load_image<0>(im, nimg, nbytes, lnI.tid);
+          if (last) fetch_next();
+          __syncthreads();  // B1: ... and Qt, M, KbT and D
+          image_to_lds<1>(sm, im, lnI.tid);
+          load_image<1>(im, nimg, nbytes, lnI.tid);
+          if (last) {
+            nu = fetched();
+            nc = 0;
+            load_inputs(buf, nu, 0, ofI, lnI.tid);
+            publish(iter, nu, nc);
+            break;
+          }
+          publish(iter, pu, pc + 1);
+        }
       } else {
-        // split unit: write the precomputed image (in two phases); or
-        // nothing to prepare
-        const bool copy = pv && pi.n > 0;
-        const uint8_t* nimg = image_of(pu, next_same ? pc + 1 : pc);
-        __syncthreads();  // B0: the consumer has read Kt and Tb of the previous image
-        if (copy) image_to_lds<0>(sm, buf, lnI.tid);
-        if (copy && next_same) load_image<0>(buf, nimg, lnI.tid);  // the next chunk, as its rounds free up
-        fetch_next();
-        __syncthreads();  // B1: ... and Qt, M, KbT and D
-        if (copy) image_to_lds<1>(sm, buf, lnI.tid);
-        if (copy && next_same) load_image<1>(buf, nimg, lnI.tid);
-        prefetch_next();
-        __syncthreads();  // B2
-        __syncthreads();  // B3
-        __syncthreads();  // B4
-        __syncthreads();  // B5
-        publish_next();
-        __syncthreads();  // B6
+        // nothing to prepare (no item, or an empty document): two barriers
+        const bool last = pv;  // an empty document is its unit's only chunk
+        __syncthreads();  // B0
+        if (last) fetch_next();
+        __syncthreads();  // B1
+        if (last) {
+          nu = fetched();
+          nc = 0;
+        } else {
+          nu.u = n_units;
+        }
+        load_inputs(buf, nu, nc, ofI, lnI.tid);
+        publish(iter, nu, nc);
       }
+      pu = nu;
+      pc = nc;
+      cv = pv;
     }
   } else {
     // ======================== consumer (waves 4-7) ========================
@@ -1572,7 +1620,7 @@ __global__ __launch_bounds__(NPC, 1) void kda_pc_kernel(
     // (otherwise the older producer waves win it, and the chain's MFMAs wait
     // behind the producer's long runs of them).
     __builtin_amdgcn_s_setprio(2);
-    VChunk vcur;  // V of the current item
+    VChunk vcur;  // V of the item chained next
     f32x16 S[4];  // the state
     auto state_in = [&](const Item& it) {
       const float* h0 = kState ? hdr->h0 : nullptr;
@@ -1601,40 +1649,51 @@ __global__ __launch_bounds__(NPC, 1) void kda_pc_kernel(
       }
     };
     __syncthreads();  // item 0 published
-    {
-      const Item nx = read_item(ps.items[0]);
-      if (nx.flags & ITEM_VALID) vcur = load_v(v, nx.c0, nx.n, H, nx.h, of);
-    }
+    const bool any = (uni(ps.items[0].flags) & ITEM_VALID) != 0;
     for (int iter = 0;; ++iter) {
-      // this iteration chains `ci`; the producer prepares `pi`
-      const Item pi = read_item(ps.items[iter & 1]);
+      // this iteration chains `ci`, the item the producer prepared in the
+      // previous one; once the producer has none, the next iteration has
+      // none to prepare either and both roles stop
       const Item ci = read_item(ps.items[(iter + 1) & 1]);
-      const bool pv = (pi.flags & ITEM_VALID) != 0;
       const bool cv = (ci.flags & ITEM_VALID) != 0;
-      if (!pv && !cv) break;
+      if (!cv && (iter > 0 || !any)) break;
       const bool active = cv && ci.n > 0;
       ChainMid mid;
       if (cv && (ci.flags & ITEM_FIRST)) state_in(ci);
       if (active) {
         save_chunk(ci);
-        chain_a(sm, S, vcur, ci.n, ci.c0, H, ci.h, out, ln, of, [&](int stage) {
-          if (stage == 0 && pv) vcur = load_v(v, pi.c0, pi.n, H, pi.h, of);
-        }, mid);
-      } else if (pv) {
-        vcur = load_v(v, pi.c0, pi.n, H, pi.h, of);
+        chain_a(sm, S, ci.n, ci.c0, H, ci.h, out, ln, of, mid);
       }
       __syncthreads();  // B0
+      // the item the producer prepares in this iteration (published before
+      // its B0): its V, one load site for every path, so that the wait for
+      // it, in the next iteration, counts only what was issued after it
+      const Item pi = read_item(ps.items[iter & 1]);
+      const bool pv = (pi.flags & ITEM_VALID) != 0;
+      if (pv) vcur = load_v(v, pi.c0, pi.n, H, pi.h, of);
       if (active) {
         chain_o(sm, S, mid, ci.n, ci.c0, H, ci.h, out, ln, of);
         chain_b(sm, S, mid, ln);
+      } else {
+        // only V is in flight here: wait for it on this (rare) path, so that
+        // where the paths join, the wait for V is the active path's, which
+        // lets the O stores drain
+        wait_vmem();
       }
       if (cv && (ci.flags & ITEM_LAST)) state_out(ci);
+      // V of the next chunk into place while the O stores drain: in the next
+      // iteration chain_a finds it staged and waits for nothing
+      if (pv) stage_v(sm, vcur, ln);
       __syncthreads();  // B1
-      __syncthreads();  // B2
-      __syncthreads();  // B3
-      __syncthreads();  // B4
-      __syncthreads();  // B5
-      __syncthreads();  // B6
+      if (pv && pi.n > 0 && !(pi.flags & ITEM_SPLIT)) {
+        // the producer builds this image from raw inputs (and uses the
+        // staging slices) until B6
+        __syncthreads();  // B2
+        __syncthreads();  // B3
+        __syncthreads();  // B4
+        __syncthreads();  // B5
+        __syncthreads();  // B6
+      }
     }
   }
   __syncthreads();
