@@ -188,7 +188,11 @@ int kda_recurrent_fwd(const void* q, const void* k, const void* v, const float* 
  * Ownership: as kda_chunk_fwd; the stream-ordered workspace holds, per chunk
  * and head, the state and its gradient at the chunk boundary, the fp32 chunk
  * image and its transition (about 400 KiB), plus a bf16 copy of the forward
- * output.
+ * output.  A call whose workspace would exceed a ceiling (16 GiB by default,
+ * kda_debug_set_bwd_workspace_limit) reads cu_seqlens back to the host (the
+ * call then waits for `stream`) and runs over consecutive groups of whole
+ * documents, each group's workspace within the ceiling; a single document
+ * larger than the ceiling is one group of its own.  Same result bit for bit.
  * Errors: as kda_chunk_fwd_state, plus KDA_ERR_NULL_PTR for d_out and the
  * gradient outputs and KDA_ERR_BAD_SHAPE when n_docs * H exceeds 2^21 (one
  * state-gradient chain of 512 work-items per document, head and quarter of
@@ -232,6 +236,14 @@ int kda_device_status(hipStream_t stream);
  * policy they were enqueued with.
  */
 int kda_debug_set_split_policy(int policy);
+
+/*
+ * kda_debug_set_bwd_workspace_limit -- test hook with no counterpart on the
+ * pages: sets the ceiling of one backward pass's workspace in bytes (0
+ * restores the default, 16 GiB), above which kda_chunk_bwd runs over groups of
+ * documents.  Process-wide; returns the previous ceiling.
+ */
+uint64_t kda_debug_set_bwd_workspace_limit(uint64_t bytes);
 
 #ifdef __cplusplus
 }

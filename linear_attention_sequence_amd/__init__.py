@@ -90,6 +90,8 @@ def load_library():
         lib.kda_device_status.restype = ctypes.c_int
         lib.kda_debug_set_split_policy.argtypes = [ctypes.c_int]
         lib.kda_debug_set_split_policy.restype = ctypes.c_int
+        lib.kda_debug_set_bwd_workspace_limit.argtypes = [ctypes.c_uint64]
+        lib.kda_debug_set_bwd_workspace_limit.restype = ctypes.c_uint64
         _lib = lib
     return _lib
 
@@ -149,6 +151,10 @@ def kda_device_status(stream=None) -> int:
 
 def kda_debug_set_split_policy(policy: int) -> int:
     return load_library().kda_debug_set_split_policy(int(policy))
+
+
+def kda_debug_set_bwd_workspace_limit(n_bytes: int) -> int:
+    return int(load_library().kda_debug_set_bwd_workspace_limit(int(n_bytes)))
 
 
 SPLIT_POLICIES = {"never": 0, "auto": 1, "always": 2}

@@ -37,6 +37,8 @@
 #include <stdint.h>
 #include <string>
 #include <type_traits>
+#include <vector>
+#include <atomic>
 
 #include "kda.h"
 
@@ -1131,59 +1133,72 @@ __global__ void kda_bwd_nan_kernel(const int* __restrict__ bad, float* dq, float
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_state; i += stride) dh0[i] = nan;
 }
 
+// cu_seqlens of documents b0 .. b0 + n - 1, rebased to start at token 0
+__global__ void kda_cu_rebase_kernel(const int32_t* __restrict__ cu, int b0, int n,
+                                     int32_t* __restrict__ out) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i <= n; i += gridDim.x * blockDim.x)
+    out[i] = cu[b0 + i] - cu[b0];
+}
+
 }  // namespace
 
-extern "C" int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
-                             const float* beta, const int32_t* cu_seqlens, int32_t n_docs,
-                             int64_t T, int32_t H, int32_t chunk, float gate_bound,
-                             const float* initial_state, const void* d_out,
-                             const float* d_final_state, float* dq, float* dk, float* dv,
-                             float* dg, float* dbeta, float* d_initial_state, hipStream_t stream) {
+namespace {
+
+// Ceiling of one pass's workspace: a call whose workspace would exceed it runs
+// over consecutive groups of whole documents (documents are independent),
+// each group's workspace within it.
+constexpr size_t BWD_WS_LIMIT_DEFAULT = (size_t)16 << 30;
+std::atomic<size_t> g_bwd_ws_limit{BWD_WS_LIMIT_DEFAULT};
+
+// One backward pass over n_docs documents: the caller's cu_seqlens as given
+// (cu_b0 < 0), or documents cu_b0 .. cu_b0 + n_docs - 1 of it, whose token
+// tensors and states the caller has offset (their cu_seqlens entries are
+// rebased into the workspace).
+int bwd_run(const void* q, const void* k, const void* v, const float* g, const float* beta,
+            const int32_t* cu_seqlens, int cu_b0, int32_t n_docs, int64_t T, int32_t H,
+            float gate_bound, const float* initial_state, const void* d_out,
+            const float* d_final_state, float* dq, float* dk, float* dv, float* dg, float* dbeta,
+            float* d_initial_state, int num_cu, int* status_word, hipStream_t stream) {
   using kda_host::fail;
-  fail(KDA_OK, "");
-  const kda_check::Result r =
-      kda_check::chunk_bwd(q, k, v, g, beta, cu_seqlens, n_docs, T, H, chunk, gate_bound,
-                           initial_state, d_out, d_final_state, dq, dk, dv, dg, dbeta,
-                           d_initial_state);
-  if (r.code != KDA_OK) return fail(r.code, r.msg);
-  if (kda_check::bwd_is_noop(T, d_initial_state)) return KDA_OK;
-
-  int num_cu = 0;
-  int* status_word = nullptr;
-  if (kda_host::device(&num_cu, &status_word) != 0)
-    return fail(KDA_ERR_HIP, "device query (CU count, status word) failed");
-
-  // workspace: bad | table | order | states | dstates | images | F^T | R | prep scratch | grads scratch | o
+  // workspace: bad | table | order | states | dstates | images | F^T | R | prep scratch |
+  //            grads scratch | o [| rebased cu_seqlens]
   const int grid = num_cu;
   kda_check::BwdLayout lay;
   if (!kda_check::bwd_layout(T, H, n_docs, grid, sizeof(ChunkDesc), IMG_FLOATS, SP_FLOATS, SC_FLOATS, &lay))
     return fail(KDA_ERR_BAD_SHAPE, "workspace size overflows");
   const size_t n_slots = lay.n_slots;
   const size_t items = lay.items;
-  const size_t off = lay.bytes;
-  const size_t off_table = lay.off_table, off_order = lay.off_order, off_states = lay.off_states,
-               off_dstates = lay.off_dstates, off_img = lay.off_img, off_ft = lay.off_ft,
-               off_r = lay.off_r, off_sp = lay.off_sp, off_sc = lay.off_sc, off_o = lay.off_o;
+  const size_t off_cu = (lay.bytes + 255) & ~(size_t)255;
+  const size_t off = cu_b0 >= 0 ? off_cu + 4 * ((size_t)n_docs + 1) : lay.bytes;
   uint8_t* ws = nullptr;
   if (kda_host::alloc_async(reinterpret_cast<void**>(&ws), off, stream) != hipSuccess || !ws)
     return fail(KDA_ERR_ALLOC, "hipMallocAsync of the backward workspace failed");
   int* bad = reinterpret_cast<int*>(ws);
-  ChunkDesc* table = reinterpret_cast<ChunkDesc*>(ws + off_table);
-  int* order = reinterpret_cast<int*>(ws + off_order);
-  float* states = reinterpret_cast<float*>(ws + off_states);
-  float* dstates = reinterpret_cast<float*>(ws + off_dstates);
-  float* imgs = reinterpret_cast<float*>(ws + off_img);
-  float* fts = reinterpret_cast<float*>(ws + off_ft);
-  float* rs = reinterpret_cast<float*>(ws + off_r);
-  float* sp = reinterpret_cast<float*>(ws + off_sp);
-  float* sc = reinterpret_cast<float*>(ws + off_sc);
-  void* o_scratch = ws + off_o;
+  ChunkDesc* table = reinterpret_cast<ChunkDesc*>(ws + lay.off_table);
+  int* order = reinterpret_cast<int*>(ws + lay.off_order);
+  float* states = reinterpret_cast<float*>(ws + lay.off_states);
+  float* dstates = reinterpret_cast<float*>(ws + lay.off_dstates);
+  float* imgs = reinterpret_cast<float*>(ws + lay.off_img);
+  float* fts = reinterpret_cast<float*>(ws + lay.off_ft);
+  float* rs = reinterpret_cast<float*>(ws + lay.off_r);
+  float* sp = reinterpret_cast<float*>(ws + lay.off_sp);
+  float* sc = reinterpret_cast<float*>(ws + lay.off_sc);
+  void* o_scratch = ws + lay.off_o;
 
   int rc = KDA_OK;
   hipError_t e = hipSuccess;
-  hipLaunchKernelGGL(kda_bwd_setup_kernel, dim3(1), dim3(1024), 0, stream, cu_seqlens, (int)n_docs,
-                     (int)T, (int)n_slots, table, order, bad, status_word);
-  e = hipGetLastError();
+  if (cu_b0 >= 0) {
+    int32_t* cu_b = reinterpret_cast<int32_t*>(ws + off_cu);
+    hipLaunchKernelGGL(kda_cu_rebase_kernel, dim3((n_docs + 256) / 256), dim3(256), 0, stream,
+                       cu_seqlens, cu_b0, (int)n_docs, cu_b);
+    e = hipGetLastError();
+    cu_seqlens = cu_b;
+  }
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(kda_bwd_setup_kernel, dim3(1), dim3(1024), 0, stream, cu_seqlens, (int)n_docs,
+                       (int)T, (int)n_slots, table, order, bad, status_word);
+    e = hipGetLastError();
+  }
   if (e == hipSuccess && T > 0) {
     rc = kda_host::forward_with_chunk_states(q, k, v, g, beta, cu_seqlens, n_docs, T, H,
                                              gate_bound, initial_state, o_scratch, states, stream);
@@ -1218,4 +1233,103 @@ extern "C" int kda_chunk_bwd(const void* q, const void* k, const void* v, const 
   if (e != hipSuccess) return fail(KDA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
   if (ef != hipSuccess) return fail(KDA_ERR_HIP, "hipFreeAsync of the backward workspace failed");
   return KDA_OK;
+}
+
+// A cu_seqlens the host found broken: the setup kernel flags it on the device
+// (as a single pass would) and the NaN kernel fills every gradient output.
+int bwd_reject(const int32_t* cu_seqlens, int32_t n_docs, int64_t T, int32_t H, float* dq,
+               float* dk, float* dv, float* dg, float* dbeta, float* d_initial_state, int num_cu,
+               int* status_word, hipStream_t stream) {
+  using kda_host::fail;
+  const size_t n_slots = (size_t)T / KDA_CHUNK + (size_t)n_docs + 1;
+  const size_t off_table = 256, off_order = off_table + n_slots * sizeof(ChunkDesc);
+  const size_t bytes = off_order + 4 * (size_t)n_docs;
+  uint8_t* ws = nullptr;
+  if (kda_host::alloc_async(reinterpret_cast<void**>(&ws), bytes, stream) != hipSuccess || !ws)
+    return fail(KDA_ERR_ALLOC, "hipMallocAsync of the backward workspace failed");
+  int* bad = reinterpret_cast<int*>(ws);
+  hipLaunchKernelGGL(kda_bwd_setup_kernel, dim3(1), dim3(1024), 0, stream, cu_seqlens, (int)n_docs,
+                     (int)T, (int)n_slots, reinterpret_cast<ChunkDesc*>(ws + off_table),
+                     reinterpret_cast<int*>(ws + off_order), bad, status_word);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(kda_bwd_nan_kernel, dim3(num_cu), dim3(NT), 0, stream, bad, dq, dk, dv, dg,
+                       dbeta, d_initial_state, (size_t)T * H * DK, (size_t)T * H,
+                       (size_t)n_docs * H * DK * DV);
+    e = hipGetLastError();
+  }
+  const hipError_t ef = hipFreeAsync(ws, stream);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  if (ef != hipSuccess) return fail(KDA_ERR_HIP, "hipFreeAsync of the backward workspace failed");
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
+                             const float* beta, const int32_t* cu_seqlens, int32_t n_docs,
+                             int64_t T, int32_t H, int32_t chunk, float gate_bound,
+                             const float* initial_state, const void* d_out,
+                             const float* d_final_state, float* dq, float* dk, float* dv,
+                             float* dg, float* dbeta, float* d_initial_state, hipStream_t stream) {
+  using kda_host::fail;
+  fail(KDA_OK, "");
+  const kda_check::Result r =
+      kda_check::chunk_bwd(q, k, v, g, beta, cu_seqlens, n_docs, T, H, chunk, gate_bound,
+                           initial_state, d_out, d_final_state, dq, dk, dv, dg, dbeta,
+                           d_initial_state);
+  if (r.code != KDA_OK) return fail(r.code, r.msg);
+  if (kda_check::bwd_is_noop(T, d_initial_state)) return KDA_OK;
+
+  int num_cu = 0;
+  int* status_word = nullptr;
+  if (kda_host::device(&num_cu, &status_word) != 0)
+    return fail(KDA_ERR_HIP, "device query (CU count, status word) failed");
+
+  kda_check::BwdLayout lay;
+  if (!kda_check::bwd_layout(T, H, n_docs, num_cu, sizeof(ChunkDesc), IMG_FLOATS, SP_FLOATS, SC_FLOATS, &lay))
+    return fail(KDA_ERR_BAD_SHAPE, "workspace size overflows");
+  const size_t limit = g_bwd_ws_limit.load(std::memory_order_relaxed);
+  if (lay.bytes <= limit || cu_seqlens == nullptr || n_docs == 1)
+    return bwd_run(q, k, v, g, beta, cu_seqlens, -1, n_docs, T, H, gate_bound, initial_state, d_out,
+                   d_final_state, dq, dk, dv, dg, dbeta, d_initial_state, num_cu, status_word, stream);
+
+  // Too large for one pass: the document boundaries on the host (this waits
+  // for the stream), then consecutive groups of documents.
+  std::vector<int32_t> cu((size_t)n_docs + 1);
+  if (hipMemcpyAsync(cu.data(), cu_seqlens, sizeof(int32_t) * cu.size(), hipMemcpyDeviceToHost, stream) !=
+          hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return fail(KDA_ERR_HIP, "reading cu_seqlens for the batched backward failed");
+  bool ok = cu[0] == 0 && cu[n_docs] == T;
+  for (int32_t i = 1; ok && i <= n_docs; ++i) ok = cu[i] >= cu[i - 1] && cu[i] <= T;
+  if (!ok)
+    return bwd_reject(cu_seqlens, n_docs, T, H, dq, dk, dv, dg, dbeta, d_initial_state, num_cu,
+                      status_word, stream);
+  const size_t tok = (size_t)H * DK, st = (size_t)H * DK * DV;
+  for (int32_t b0 = 0; b0 < n_docs;) {
+    int32_t b1 = b0 + 1;  // at least one document per pass
+    for (; b1 < n_docs; ++b1) {
+      kda_check::BwdLayout l2;
+      if (!kda_check::bwd_layout((int64_t)cu[b1 + 1] - cu[b0], H, b1 + 1 - b0, num_cu, sizeof(ChunkDesc),
+                                 IMG_FLOATS, SP_FLOATS, SC_FLOATS, &l2) ||
+          l2.bytes > limit)
+        break;
+    }
+    const size_t t0 = (size_t)cu[b0];
+    const int rc = bwd_run(
+        static_cast<const bf16*>(q) + t0 * tok, static_cast<const bf16*>(k) + t0 * tok,
+        static_cast<const bf16*>(v) + t0 * tok, g + t0 * tok, beta + t0 * H, cu_seqlens, b0, b1 - b0,
+        (int64_t)cu[b1] - cu[b0], H, gate_bound, initial_state ? initial_state + b0 * st : nullptr,
+        static_cast<const bf16*>(d_out) + t0 * tok, d_final_state ? d_final_state + b0 * st : nullptr,
+        dq + t0 * tok, dk + t0 * tok, dv + t0 * tok, dg + t0 * tok, dbeta + t0 * H,
+        d_initial_state ? d_initial_state + b0 * st : nullptr, num_cu, status_word, stream);
+    if (rc != KDA_OK) return rc;
+    b0 = b1;
+  }
+  return KDA_OK;
+}
+
+extern "C" uint64_t kda_debug_set_bwd_workspace_limit(uint64_t bytes) {
+  return g_bwd_ws_limit.exchange(bytes == 0 ? BWD_WS_LIMIT_DEFAULT : (size_t)bytes);
 }

@@ -20,9 +20,9 @@ entries): the KDA delta rule, specialised to
   the drop-in with the final state switched off (same page, ``fused_chunk_kda``
   entry).  ``S_0 = 0`` gives back the plain forward;
 * q and k l2-normalised inside the operator (``use_qk_l2norm_in_kernel``);
-* a log decay ``g`` per token, head and key channel (the "bounded log gate";
-  the K3 model page's ``KimiKDAFp32Params`` returns an fp32 ``[b, s, h, d]``
-  decay);
+* a log decay ``g`` per token, head and key channel, bounded below (the
+  package docstring; the K3 model page's ``KimiKDAFp32Params`` returns an fp32
+  ``[b, s, h, d]`` decay);
 * packed documents delimited by int32 ``cu_seqlens``.
 
 The pages print no formula for the recurrence.  The oracle takes the KDA

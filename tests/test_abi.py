@@ -20,8 +20,9 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     assert _declared_functions() == ["kda_chunk_bwd", "kda_chunk_fwd", "kda_chunk_fwd_noalloc",
-                                     "kda_chunk_fwd_state", "kda_debug_set_split_policy",
-                                     "kda_device_status", "kda_last_error", "kda_recurrent_fwd"]
+                                     "kda_chunk_fwd_state", "kda_debug_set_bwd_workspace_limit",
+                                     "kda_debug_set_split_policy", "kda_device_status",
+                                     "kda_last_error", "kda_recurrent_fwd"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -230,6 +231,15 @@ def test_split_policy_hook_validates_and_returns_the_previous_policy():
     assert kda.set_split_policy("never") == "auto"
     assert kda.set_split_policy("always") == "never"
     assert kda.set_split_policy("auto") == "always"
+
+
+def test_bwd_workspace_limit_hook_returns_the_previous_ceiling():
+    if not os.path.exists(kda.LIB_PATH):
+        pytest.skip("libkda.so not built")
+    default = 16 << 30
+    assert kda.kda_debug_set_bwd_workspace_limit(1 << 20) == default
+    assert kda.kda_debug_set_bwd_workspace_limit(0) == 1 << 20
+    assert kda.kda_debug_set_bwd_workspace_limit(0) == default
 
 
 def test_no_alloc_entry_point_validates_like_kda_chunk_fwd():

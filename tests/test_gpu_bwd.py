@@ -256,6 +256,62 @@ def test_backward_many_tiny_documents():
     _check(inp, do, got, h0, dht, "bwd tiny documents")
 
 
+def test_backward_thousands_of_one_token_documents():
+    """4096 documents of one token at H = 32: a workspace slot per document
+    and head would take ~54 GB in one pass, so the call runs over groups of
+    documents, each within the default 16 GiB ceiling."""
+    T, H = 4096, 32
+    inp = make_inputs(T, H, 91, cu_from_lengths([1] * T))
+    do = _dout(T, H, 91)
+    log(f"[case] bwd {T} one-token documents, H={H}")
+    got = _run(inp, do)
+    _check(inp, do, got, None, None, "bwd 4096 one-token documents", heads=[0, 17, 31])
+
+
+def test_backward_in_groups_matches_one_pass():
+    """A ceiling of one byte forces one document per pass: the gradients are
+    the single pass's bit for bit (documents are independent), with states,
+    empty documents and both ends of the stream."""
+    import linear_attention_sequence_amd as kda
+    lengths = [0, 130, 0, 37, 200, 64, 1, 300, 5, 0]
+    T, H = sum(lengths), 2
+    inp = with_gate_scale(make_inputs(T, H, 92, cu_from_lengths(lengths)), 92, -0.05)
+    do = _dout(T, H, 92)
+    h0 = initial_states(len(lengths), H, 92)
+    dht = np.ascontiguousarray(initial_states(len(lengths), H, 93))
+    log("[case] bwd in groups of one document vs one pass")
+    one = _run(inp, do, h0, dht)
+    prev = kda.kda_debug_set_bwd_workspace_limit(1)
+    try:
+        grouped = _run(inp, do, h0, dht)
+    finally:
+        kda.kda_debug_set_bwd_workspace_limit(prev)
+    for name, a, b in zip(NAMES + ("dh0",), one, grouped):
+        assert np.array_equal(a, b), name
+    _check(inp, do, grouped, h0, dht, "bwd in groups")
+
+
+def test_backward_in_groups_rejects_bad_cu_seqlens():
+    """The grouped path reads cu_seqlens on the host; a broken one still sets
+    the device flag and fills every gradient with NaN."""
+    import torch
+    import linear_attention_sequence_amd as kda
+    H = 2
+    inp = make_inputs(100, H, 94, cu_from_lengths([50, 30, 20]))
+    d = to_device(inp)
+    kda.device_status()
+    bad = torch.tensor([0, 60, 40, 100], dtype=torch.int32, device="cuda")
+    prev = kda.kda_debug_set_bwd_workspace_limit(1)
+    try:
+        r = kda.chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["v"].clone(), bad)
+        torch.cuda.synchronize()
+    finally:
+        kda.kda_debug_set_bwd_workspace_limit(prev)
+    assert kda.device_status() & kda.KDA_DEV_BAD_CU_SEQLENS
+    for x in r[:5]:
+        assert bool(torch.isnan(x).all())
+
+
 def test_backward_more_documents_than_ranked():
     """1100 documents, more than the setup kernel ranks by length (their
     state-gradient chains then run in cu_seqlens order): 1 to 5 tokens each,
