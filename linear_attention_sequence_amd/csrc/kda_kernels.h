@@ -1575,7 +1575,10 @@ __global__ __launch_bounds__(NPC, 1) void kda_pc_kernel(
         // so that nothing is copied between iterations.
         RawChunk im = buf;
         for (;; ++iter, ++pc) {
-          const bool last = pc + 1 >= pu.nch;
+          // wave-uniform, so that the last chunk's extra work is a scalar
+          // branch: a lane-mask branch would merge its loads' registers
+          // with this path and make every chunk wait for its own prefetch
+          const bool last = uni(pc + 1 >= pu.nch ? 1 : 0) != 0;
           const uint8_t* nimg = image_of(pu, pc + 1);
           const uint32_t nbytes = last ? 0u : IMG_BYTES;  // the next chunk, or zeros
           __syncthreads();  // B0: the consumer has read Kt, Tb and Tb's scale of the previous image
