@@ -93,12 +93,13 @@ struct alignas(16) Smem {
   } u;
   // ---- end of the image
   union {
-    f16x8 R[3][4][64];       // right operands of off-diagonal sub-blocks (fp16), lane order
     float T[CH][CH + 4];     // (I + A)^-1 (fp32)
-    struct {
-      unsigned short o[CH][32];  // the bf16 O rows of the wave's 32 columns
-    } ws[4];                 // per-wave staging slices
+    uint8_t o[4][CH][64];    // per wave: the bf16 O rows of its 32 columns (see chain_o)
   } u2;
+  f16x8 R[3][4][64];         // right operands of off-diagonal sub-blocks (fp16), lane order
+  // R has a space of its own, so that the diagonal blocks of T are written
+  // where they belong while R is still read (one barrier fewer than PreSmem)
+  static constexpr bool kOwnR = true;
   unsigned short vt[4][32][CH + 8];  // per wave: V of the chunk chained next, transposed (its 32 columns)
   float etab[13][DK];        // per-channel decay factors of the chunk (see fill_tables)
   float tot[4][DK];          // per sub-block total decay (log2 domain)
@@ -184,7 +185,17 @@ struct alignas(16) PreSmem {
   float beta[CH];
   float tbmax[8];
   int gate_bad;
+  // R shares its space with T (two workgroups per CU need the room): the
+  // diagonal blocks of T wait elsewhere until R is dead
+  static constexpr bool kOwnR = false;
 };
+
+// the right operands of the off-diagonal sub-blocks in either layout
+template <class Sm>
+__device__ __forceinline__ auto r_ops(Sm& sm) -> f16x8 (&)[3][4][64] {
+  if constexpr (Sm::kOwnR) return sm.R;
+  else return sm.u2.R;
+}
 // KbT and M rows staged in PreSmem (padded like Smem) go to the image piece by
 // piece: KbT (whole rounds), then the M pieces the chain reads
 static_assert(offsetof(PreSmem, M) == sizeof(((PreSmem*)nullptr)->KbT) && ROW_CC * DK == sizeof(((PreSmem*)nullptr)->KbT),
@@ -582,7 +593,7 @@ __device__ __forceinline__ void offdiag_row(Sm& sm, const float (&lq)[32], const
     f32x4 accA[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const f16x8 rv = sm.u2.R[b][s][l];
+      const f16x8 rv = r_ops(sm)[b][s][l];
       const float4 fa = *reinterpret_cast<const float4*>(&fr[32 * s + 8 * cg]);
       const float4 fb = *reinterpret_cast<const float4*>(&fr[32 * s + 8 * cg + 4]);
       const float f[8] = {fa.x, fa.y, fa.z, fa.w, fb.x, fb.y, fb.z, fb.w};
@@ -667,12 +678,14 @@ __device__ __forceinline__ Lane make_lane(int tid = threadIdx.x) {
 // inputs `cur` (n valid tokens) to the image in LDS (Qt, Kt, KbT, M, Tb, D).
 // hook(0..2) run at fixed points once `cur` has been consumed (they may
 // refill it); the scheduling barriers keep the loads they issue spread out.
-// hook(3) runs right after the fourth workgroup barrier (B3), hook(4) between
-// B4 and B5, hook(5) between B5 and B6.
-// Seven workgroup barriers, B0 .. B6, the last of which ends the function;
-// after it the image is complete.  Until B1 the function writes to LDS only
-// tot, beta, gate_bad and the decay tables (so that another workgroup role
-// may still read the previous image and use the staging slices until then);
+// hook(3) runs right after the fourth workgroup barrier (B3), hook(4) just
+// before B5, hook(5) between B5 and B6.
+// Seven workgroup barriers, B0 .. B6, the last of which ends the function
+// (six where R has a space of its own, Sm::kOwnR: there is no B4); after it
+// the image is complete.  Until B1 the function writes to LDS only
+// tot, beta, gate_bad and the decay tables, and computes the diagonal blocks
+// of A and M in registers (so that another workgroup role
+// may still read the previous image until then);
 // until B2 not Qt, Kt or KbT; until B5 not Tb or its scale.
 template <class Sm, class Sink, class Hook>
 __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const RawChunk& cur, int n,
@@ -761,19 +774,21 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
   __builtin_amdgcn_sched_barrier(0);
   hook(1);
   __builtin_amdgcn_sched_barrier(0);
-  __syncthreads();  // B1: the previous image's Qt, M, KbT and D may still be read until here
-
   // diagonal block (w, w) of M and A on fp32 MFMA (the factors
   // e^{+-(G - G_end(w))} inside a sub-block need fp32's range): k-step s
-  // takes element s from every lane (the same channel on both operands)
-  {
-    f32x4 accM[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    f32x4 accA[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  // takes element s from every lane (the same channel on both operands).
+  // The products stay in registers until B1, so that they run while another
+  // workgroup role still reads the previous image.
+  f32x4 accM[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  f32x4 accA[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int s = 0; s < 32; ++s) {
-      accM[s & 1] = mfma16f(lq[s], kr[s], accM[s & 1]);
-      accA[s & 1] = mfma16f(lk[s], kr[s], accA[s & 1]);
-    }
+  for (int s = 0; s < 32; ++s) {
+    accM[s & 1] = mfma16f(lq[s], kr[s], accM[s & 1]);
+    accA[s & 1] = mfma16f(lk[s], kr[s], accA[s & 1]);
+  }
+  __syncthreads();  // B1: the previous image's Qt, M, KbT and D may still be read until here
+
+  {
     store_block(sm, accM[0] + accM[1], accA[0] + accA[1], w, w, l, true, beta_mine);
     // the chain's MFMAs read the upper blocks (0, 1) and (2, 3) (inside the two
     // diagonal 32x32 tiles): zero them; the other upper blocks are never read
@@ -788,7 +803,7 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
         f16x8 rv;
 #pragma unroll
         for (int j = 0; j < 8; ++j) rv[j] = (_Float16)kr[8 * s + j];
-        sm.u2.R[w][s][l] = rv;
+        r_ops(sm)[w][s][l] = rv;
       }
     }
     if (tid < DK) sink.dv(tid, sm.etab[3][tid]);  // written by this thread before B1
@@ -853,9 +868,9 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
   // blocks of I + A (complete since B2): T = (I + A)^-1 by 16x16 blocks, by
   // forward substitution, lane l owning column l % 16 of diagonal block
   // l / 16.  tmax tracks the largest |Tb| = |T_ij beta_j| a wave produces.
-  // T shares its space with R, which waves 1-3 still read: until B3 the
-  // columns wait in an upper block of A (A is strictly lower; its upper
-  // blocks are never written or read): block da in block (pr, pc).
+  // Where T shares its space with R, which waves 1-3 still read, the
+  // columns wait in an upper block of A until B3 (A is strictly lower; its
+  // upper blocks are never written or read): block da in block (pr, pc).
   const int da = l >> 4, dj = l & 15;
   const int pr = da == 3 ? 1 : da, pc = da == 3 ? 3 : da + 1;
   float tmax = 0.f;
@@ -887,8 +902,15 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
     const float bj = fabsf(sm.beta[16 * da + dj]);
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-      sm.u.A[16 * pr + rr][16 * pc + dj] = x[rr];
+      if constexpr (Sm::kOwnR) sm.u2.T[16 * da + rr][16 * da + dj] = x[rr];
+      else sm.u.A[16 * pr + rr][16 * pc + dj] = x[rr];
       tmax = fmaxf(tmax, fabsf(x[rr]) * bj);
+    }
+    if constexpr (Sm::kOwnR) {
+      if (da == 0 || da == 2) {  // upper blocks (0, 1) and (2, 3): read by U = Tb X
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) sm.u2.T[16 * da + rr][16 * (da + 1) + dj] = 0.f;
+      }
     }
   }
 
@@ -896,15 +918,17 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
   __builtin_amdgcn_sched_barrier(0);
   hook(3);
   __builtin_amdgcn_sched_barrier(0);
-  if (w == 0) {
+  if constexpr (!Sm::kOwnR) {
+    if (w == 0) {
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) sm.u2.T[16 * da + rr][16 * da + dj] = sm.u.A[16 * pr + rr][16 * pc + dj];
-    if (da == 0 || da == 2) {  // upper blocks (0, 1) and (2, 3): read by U = Tb X
+      for (int rr = 0; rr < 16; ++rr) sm.u2.T[16 * da + rr][16 * da + dj] = sm.u.A[16 * pr + rr][16 * pc + dj];
+      if (da == 0 || da == 2) {  // upper blocks (0, 1) and (2, 3): read by U = Tb X
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) sm.u2.T[16 * da + rr][16 * (da + 1) + dj] = 0.f;
+        for (int rr = 0; rr < 16; ++rr) sm.u2.T[16 * da + rr][16 * (da + 1) + dj] = 0.f;
+      }
     }
+    __syncthreads();  // B4: diagonal blocks of T visible
   }
-  __syncthreads();  // B4: diagonal blocks of T visible
   // off-diagonal blocks: wave b walks column block b downwards,
   // T_ab = -T_aa sum_{k=b}^{a-1} A_ak T_kb, on fp32 MFMA
   if (w == 0) tmax = levels_column<0>(sm, l, tmax);
@@ -950,7 +974,7 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
 //   X = V - Kt S,  U = Tb X,  O = scale (Qt S + M U),  S <- D S + KbT U,
 // in three parts.  chain_a computes X and U: it reads V (staged by stage_v),
 // Kt, Tb and Tb's scale; chain_o computes and stores O: it
-// reads Qt and M and stages O in the slice; chain_b updates S: it reads only
+// reads Qt and M; chain_b updates S: it reads only
 // KbT and D.  ChainMid carries U (fp16, 2^-eu) from chain_a to the others.
 // Scheduling fences in chain_a (after the V staging, after X and after U)
 // keep its stages in order.
@@ -1111,14 +1135,22 @@ __device__ __forceinline__ void chain_a(Smem& sm, const f32x16 (&S)[4], int n, i
 }
 
 // O = scale (Qt S + M U) of the chunk, from S and the U that chain_a left in
-// mid, staged through the wave's slice for 16-byte row stores.  Reads Qt and
-// M.
+// mid, computed transposed: O^T = S^T Qt^T + U^T M^T, with the fragments of S
+// and U as left operands (in their C layout a lane holds one value column
+// and eight consecutive key channels or tokens per k-step, which is the left
+// operand layout of S^T and U^T) and rows of Qt and M as right operands.  In
+// the C layout of O^T lane (n, hg) then holds token 32 mt + n and value
+// columns 8 q + 4 hg + 0..3 (q = 0..3): four 8-byte pieces of that token's
+// row.  They go through the wave's slice of u2 (one 64-byte row per token,
+// 16-byte piece q at q ^ (row / 4 % 4), so that neither the 8-byte writes nor
+// the 16-byte reads of 16 lanes share a bank) and leave as 16-byte row
+// pieces, four lanes to a row.  Reads Qt and M.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void chain_o(Smem& sm, const f32x16 (&S)[4], const ChainMid& mid, int n,
                                         int64_t c0, int H, int h, bf16* __restrict__ out,
                                         const Lane& ln, const Offsets& of) {
-  const int w = ln.w, l = ln.l, m = ln.m, hg = ln.hg;
+  const int w = ln.w, m = ln.m, hg = ln.hg;
   const float scale = 0.08838834764831845f;  // 128^-1/2
-  const int rowsel = swap23(m);
   constexpr int PMT[6] = {0, 0, 1, 1, 1, 1};
   constexpr int PS[6] = {0, 1, 0, 1, 2, 3};
   const int eu = mid.eu;
@@ -1140,84 +1172,94 @@ __device__ __forceinline__ void chain_o(Smem& sm, const f32x16 (&S)[4], const Ch
       for (int j = 0; j < 8; ++j) Sb[s][j] = (bf16)(S[s >> 1][8 * (s & 1) + j] * udown);
   }
 
-  // O = scale (qh e^G S + M U), staged through LDS for 16-byte stores;
-  // one accumulator per row tile
-  unsigned short (*ost)[32] = sm.u2.ws[w].o;
-  {
-    float oscale = scale * pow2i(eu);
-    f32x16 O[2];
+  // one accumulator per token tile mt (tokens 32 mt .. 32 mt + 31)
+  float oscale = scale * pow2i(eu);
+  f32x16 O[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) O[mt][i] = 0.f;
+  if (eu < 0) {
+    // U was scaled up (small values): S 2^-eu could overflow, so (U 2^-eu)^T
+    // M^T is taken first and brought back to scale (exactly) before S^T Qt^T
+    // joins it in the same accumulator
+#pragma unroll
+    for (int p = 0; p < 6; ++p) {
+      const f16x8 mv = *reinterpret_cast<const f16x8*>(&sm.M[32 * PMT[p] + m][16 * PS[p] + 8 * hg]);
+      O[PMT[p]] = mfma32h(Uh[PS[p]], mv, O[PMT[p]]);
+    }
+    const float up = pow2i(eu);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) O[mt][i] = 0.f;
-    if (eu < 0) {
-      // U was scaled up (small values): S 2^-eu could overflow, so M (U 2^-eu)
-      // is taken first and brought back to scale (exactly) before Qt S joins
-      // it in the same accumulator
+      for (int i = 0; i < 16; ++i) O[mt][i] *= up;
 #pragma unroll
-      for (int p = 0; p < 6; ++p) {
-        const f16x8 mv = *reinterpret_cast<const f16x8*>(&sm.M[32 * PMT[p] + rowsel][16 * PS[p] + 8 * hg]);
-        O[PMT[p]] = mfma32h(mv, Uh[PS[p]], O[PMT[p]]);
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const bf16x8 qv = *reinterpret_cast<const bf16x8*>(&sm.Qt[32 * mt + m][16 * s + 8 * hg]);
+        O[mt] = mfma32(Sb[s], qv, O[mt]);
       }
-      const float up = pow2i(eu);
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) O[mt][i] *= up;
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const bf16x8 qv = *reinterpret_cast<const bf16x8*>(&sm.Qt[32 * mt + rowsel][16 * s + 8 * hg]);
-          O[mt] = mfma32(qv, Sb[s], O[mt]);
-        }
-      oscale = scale;
-    } else {
+    oscale = scale;
+  } else {
     bf16x8 qa[2][2];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
-        qa[mt][s] = *reinterpret_cast<const bf16x8*>(&sm.Qt[32 * mt + rowsel][16 * s + 8 * hg]);
+        qa[mt][s] = *reinterpret_cast<const bf16x8*>(&sm.Qt[32 * mt + m][16 * s + 8 * hg]);
     // M operands loaded two pairs ahead
     f16x8 mh[2];
 #pragma unroll
     for (int p = 0; p < 2; ++p)
-      mh[p] = *reinterpret_cast<const f16x8*>(&sm.M[32 * PMT[p] + rowsel][16 * PS[p] + 8 * hg]);
+      mh[p] = *reinterpret_cast<const f16x8*>(&sm.M[32 * PMT[p] + m][16 * PS[p] + 8 * hg]);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        O[mt] = mfma32(qa[mt][s & 1], Sb[s], O[mt]);
+        O[mt] = mfma32(Sb[s], qa[mt][s & 1], O[mt]);
         if (s + 2 < 8)
-          qa[mt][s & 1] = *reinterpret_cast<const bf16x8*>(&sm.Qt[32 * mt + rowsel][16 * (s + 2) + 8 * hg]);
+          qa[mt][s & 1] = *reinterpret_cast<const bf16x8*>(&sm.Qt[32 * mt + m][16 * (s + 2) + 8 * hg]);
       }
       if (s < 6) {
         const int p = s;
-        O[PMT[p]] = mfma32h(mh[p & 1], Uh[PS[p]], O[PMT[p]]);
+        O[PMT[p]] = mfma32h(Uh[PS[p]], mh[p & 1], O[PMT[p]]);
         if (p + 2 < 6)
-          mh[p & 1] = *reinterpret_cast<const f16x8*>(&sm.M[32 * PMT[p + 2] + rowsel][16 * PS[p + 2] + 8 * hg]);
+          mh[p & 1] = *reinterpret_cast<const f16x8*>(&sm.M[32 * PMT[p + 2] + m][16 * PS[p + 2] + 8 * hg]);
       }
     }
-    }
+  }
+  // token 32 mt + m, value columns 8 q + 4 hg + 0..3 of the wave's 32 from
+  // O[mt][4 q ..], into the slice
+  uint8_t* ost = &sm.u2.o[w][0][0];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < 2; ++mt) {
+    const int row = 32 * mt + m;
+    uint8_t* dst = ost + 64 * row + 8 * hg;
+    const int sw = (row >> 2) & 3;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int t = 32 * mt + 16 * (i >> 3) + 8 * hg + (i & 7);
-        const bf16 ob = (bf16)(O[mt][i] * oscale);
-        ost[t][m] = __builtin_bit_cast(unsigned short, ob);
+    for (int q = 0; q < 4; ++q) {
+      u32x2 pk;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const bf16 lo = (bf16)(O[mt][4 * q + 2 * e] * oscale);
+        const bf16 hi = (bf16)(O[mt][4 * q + 2 * e + 1] * oscale);
+        pk[e] = (uint32_t)__builtin_bit_cast(unsigned short, lo) |
+                ((uint32_t)__builtin_bit_cast(unsigned short, hi) << 16);
       }
+      *reinterpret_cast<u32x2*>(dst + 16 * (q ^ sw)) = pk;
+    }
   }
   // O rows: lane l writes 16 bytes of row 16 it + l / 4 (rows past the end
   // are dropped by the descriptor's range)
   wave_sync_lds();
   {
+    const int l = ln.l;
     const Rsrc ro = make_rsrc(out + ((size_t)c0 * H + h) * DV, chunk_bytes(n, H, 256u));
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int t = 16 * it + (l >> 2);
-      bstore(*reinterpret_cast<const u32x4*>(&ost[t][8 * (l & 3)]), ro, of.v[it]);
+      bstore(*reinterpret_cast<const u32x4*>(ost + 64 * t + 16 * ((l & 3) ^ ((t >> 2) & 3))), ro, of.v[it]);
     }
   }
 }
@@ -1308,16 +1350,18 @@ __device__ __forceinline__ void store_state(const f32x16 (&S)[4], float* dst, co
 //
 // The image is single-buffered; workgroup barriers order the consumer's reads
 // of image i - 1 before the producer's writes of image i.  An iteration in
-// which the producer builds an image from raw inputs has seven barriers, B0 ..
-// B6 (those of prepare_chunk):
+// which the producer builds an image from raw inputs has the six barriers of
+// prepare_chunk, B0 .. B3, B5, B6:
 //   before B0:  producer: prologue (registers, its own tot / beta);
 //               consumer: chain_a, X and U (reads Kt, Tb and Tb's scale;
 //               stages V in its slice);
-//   B0 .. B1:   producer: decay tables (its own LDS space);
+//   B0 .. B1:   producer: decay tables (its own LDS space), the diagonal
+//               blocks of A and M (registers);
 //               consumer: chain_o and chain_b, O and the state update (reads
-//               Qt, M, KbT and D; stages O in its slice);
-//   B1 .. B6:   producer: the rest of the image (the slices take R and T);
-//               consumer: idle.
+//               Qt, M, KbT and D);
+//   B1 .. B6:   producer: the rest of the image;
+//               consumer: loads and stages the V of the chunk it chains
+//               next, then waits.
 // An iteration that copies a precomputed image (or prepares nothing) has two:
 //   B0 .. B1:   producer: Kt, Tb and Tb's scale of image i;
 //   after B1:   producer: Qt, KbT, M and D of image i;
@@ -1340,9 +1384,6 @@ struct Item {
   int unit;       // work-list entry: list index * H + h
   int flags;      // ItemFlags (ITEM_SPLIT: the image is precomputed)
 };
-
-// s_waitcnt vmcnt(0) (expcnt and lgkmcnt at their maxima: not waited for)
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // a unit as the producer walks it (uniform values)
 struct PUnit {
@@ -1544,22 +1585,30 @@ __global__ __launch_bounds__(NPC, 1) void kda_pc_kernel(
       PUnit nu = pu;  // the next item: (nu, nc)
       int nc = pc + 1;
       if (pv && pn > 0 && pu.img0 < 0) {
-        // fused unit: build the image (seven barriers; the consumer, told by
-        // the item, passes B2 .. B6 with it).  The next chunk's inputs go
+        // fused unit: build the image (six barriers; the consumer, told by
+        // the item, passes B2, B3, B5 and B6 with it).  The next chunk's inputs go
         // into buf as soon as it is free: the same unit's after B1, a new
         // unit's (zeros if none) once it is known, after B3, so that buf is
         // redefined on every path and nothing keeps it alive across the
         // prologue.
         const bool last = pc + 1 >= pu.nch;
         prepare_chunk(sm, LdsSink{&sm}, buf, pn, gate_bound, lnI, [&](int part) {
+          // the next chunk of the same unit arrives in three parts (q and k
+          // after B0, g's two halves and beta after the tiles and after B3),
+          // so that its loads do not all share the window in which the
+          // consumer loads V and stores O
           if (part == 1) {
             if (last) fetch_next();
-            else load_raw(buf, raw_of(pu, pc + 1), ofI);
+            else load_raw_part(buf, raw_of(pu, pc + 1), ofI, 0);
+          } else if (part == 2) {
+            if (!last) load_raw_part(buf, raw_of(pu, pc + 1), ofI, 1);
           } else if (part == 3) {
             if (last) {
               nu = fetched();
               nc = 0;
               load_inputs(buf, nu, 0, ofI, lnI.tid);
+            } else {
+              load_raw_part(buf, raw_of(pu, pc + 1), ofI, 2);
             }
           } else if (part == 5) {
             publish(iter, nu, nc);
@@ -1581,10 +1630,16 @@ __global__ __launch_bounds__(NPC, 1) void kda_pc_kernel(
           const bool last = uni(pc + 1 >= pu.nch ? 1 : 0) != 0;
           const uint8_t* nimg = image_of(pu, pc + 1);
           const uint32_t nbytes = last ? 0u : IMG_BYTES;  // the next chunk, or zeros
-          __syncthreads();  // B0: the consumer has read Kt, Tb and Tb's scale of the previous image
+          // this chunk's V (the consumer's columns of wave w), in flight
+          // while this role waits at B0; staged after it, where the
+          // consumer's chain_a no longer reads the previous chunk's
+          const int64_t vc0 = pu.bos + (int64_t)CH * pc;
+          const VChunk vn = load_v(v, vc0, (int)min<int64_t>(CH, (int64_t)pu.len - (int64_t)CH * pc), H, pu.h, ofI);
+          __syncthreads();  // B0: the consumer has read Kt, Tb and Tb's scale of the previous image, and V
           image_to_lds<0>(sm, im, lnI.tid);
           load_image<0>(im, nimg, nbytes, lnI.tid);
           if (last) fetch_next();
+          stage_v(sm, vn, lnI);
           __syncthreads();  // B1: ... and Qt, M, KbT and D
           image_to_lds<1>(sm, im, lnI.tid);
           load_image<1>(im, nimg, nbytes, lnI.tid);
@@ -1623,7 +1678,6 @@ __global__ __launch_bounds__(NPC, 1) void kda_pc_kernel(
     // (otherwise the older producer waves win it, and the chain's MFMAs wait
     // behind the producer's long runs of them).
     __builtin_amdgcn_s_setprio(2);
-    VChunk vcur;  // V of the item chained next
     f32x16 S[4];  // the state
     auto state_in = [&](const Item& it) {
       const float* h0 = kState ? hdr->h0 : nullptr;
@@ -1673,27 +1727,26 @@ __global__ __launch_bounds__(NPC, 1) void kda_pc_kernel(
       // it, in the next iteration, counts only what was issued after it
       const Item pi = read_item(ps.items[iter & 1]);
       const bool pv = (pi.flags & ITEM_VALID) != 0;
-      if (pv) vcur = load_v(v, pi.c0, pi.n, H, pi.h, of);
+      // the producer builds this item's image from raw inputs until B6; the
+      // V of a precomputed (split) item it stages itself before B1, and an
+      // empty item needs none
+      const bool pfused = pv && pi.n > 0 && !(pi.flags & ITEM_SPLIT);
       if (active) {
         chain_o(sm, S, mid, ci.n, ci.c0, H, ci.h, out, ln, of);
         chain_b(sm, S, mid, ln);
-      } else {
-        // only V is in flight here: wait for it on this (rare) path, so that
-        // where the paths join, the wait for V is the active path's, which
-        // lets the O stores drain
-        wait_vmem();
       }
       if (cv && (ci.flags & ITEM_LAST)) state_out(ci);
-      // V of the next chunk into place while the O stores drain: in the next
-      // iteration chain_a finds it staged and waits for nothing
-      if (pv) stage_v(sm, vcur, ln);
       __syncthreads();  // B1
-      if (pv && pi.n > 0 && !(pi.flags & ITEM_SPLIT)) {
-        // the producer builds this image from raw inputs (and uses the
-        // staging slices) until B6
+      if (pfused) {
+        // V of a fused item is loaded and staged while the producer builds
+        // the image (this role has nothing else to do until B6), away from
+        // the window between B0 and B1 in which the O stores and the
+        // producer's loads go out
+        const VChunk vcur = load_v(v, pi.c0, pi.n, H, pi.h, of);
+        stage_v(sm, vcur, ln);
+        static_assert(Smem::kOwnR, "prepare_chunk has no B4 on this layout");
         __syncthreads();  // B2
         __syncthreads();  // B3
-        __syncthreads();  // B4
         __syncthreads();  // B5
         __syncthreads();  // B6
       }
