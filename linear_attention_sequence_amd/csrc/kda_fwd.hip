@@ -294,9 +294,19 @@ __global__ __launch_bounds__(NTHR, 2) void kda_pre_kernel(
   const Offsets of = make_offsets(H, ln.tok, ln.cg, ln.w, ln.l);
   if (ln.tid == 0) sm.gate_bad = 0;
   // every unit costs the same: workgroup b takes units b, b + grid, ...
+  // The next unit's raw inputs arrive during the current one's prepare, in
+  // three parts (after B0, after the tiles, after B3), into the registers the
+  // prologue has consumed by then.
+  auto src_of = [&](int u) {
+    const int2 ch = pre_chunks[u / H];
+    return raw_src(q, k, g, beta, ch.x, ch.y, H, u % H);
+  };
+  RawChunk cur;
+  if ((int)blockIdx.x < n_units) load_raw(cur, src_of(blockIdx.x), of);
   for (int unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
     const int2 ch = pre_chunks[unit / H];
     const int h = unit % H;
+    const int next = unit + (int)gridDim.x;
     // the lane coordinates from a value the compiler cannot see through, so
     // that what it derives from them is not hoisted out of the loop (where it
     // would hold registers for the whole kernel)
@@ -304,11 +314,11 @@ __global__ __launch_bounds__(NTHR, 2) void kda_pre_kernel(
     asm volatile("" : "+v"(t));
     const Lane lnI = make_lane(t);
     const Offsets ofI = make_offsets(H, lnI.tok, lnI.cg, lnI.w, lnI.l);
-    RawChunk cur;
-    load_raw(cur, raw_src(q, k, g, beta, ch.x, ch.y, H, h), ofI);
     uint8_t* img = images + ((size_t)(unit / H) * H + h) * IMG_BYTES;
     const GlobalSink sink{make_rsrc(img, IMG_BYTES)};
-    prepare_chunk(sm, sink, cur, ch.y, gate_bound, lnI, [&](int) {});
+    prepare_chunk(sm, sink, cur, ch.y, gate_bound, lnI, [&](int part) {
+      if (part >= 1 && part <= 3 && next < n_units) load_raw_part(cur, src_of(next), ofI, part - 1);
+    });
     // KbT and M: padded LDS staging rows -> image pieces
     const uint8_t* st = reinterpret_cast<const uint8_t*>(&sm.KbT[0][0]);
 #pragma unroll

@@ -97,9 +97,6 @@ struct alignas(16) Smem {
     uint8_t o[4][CH][64];    // per wave: the bf16 O rows of its 32 columns (see chain_o)
   } u2;
   f16x8 R[3][4][64];         // right operands of off-diagonal sub-blocks (fp16), lane order
-  // R has a space of its own, so that the diagonal blocks of T are written
-  // where they belong while R is still read (one barrier fewer than PreSmem)
-  static constexpr bool kOwnR = true;
   unsigned short vt[4][32][CH + 8];  // per wave: V of the chunk chained next, transposed (its 32 columns)
   float etab[13][DK];        // per-channel decay factors of the chunk (see fill_tables)
   float tot[4][DK];          // per sub-block total decay (log2 domain)
@@ -176,26 +173,20 @@ struct alignas(16) PreSmem {
   struct {
     float A[CH][CH + 4];
   } u;
-  union {
-    f16x8 R[3][4][64];
+  struct {
     float T[CH][CH + 4];
   } u2;
+  // the sub-block totals are read (fill_tables) before R is written: two
+  // workgroups per CU need the room
+  union {
+    f16x8 R[3][4][64];
+    float tot[4][DK];
+  };
   float etab[13][DK];
-  float tot[4][DK];
   float beta[CH];
   float tbmax[8];
   int gate_bad;
-  // R shares its space with T (two workgroups per CU need the room): the
-  // diagonal blocks of T wait elsewhere until R is dead
-  static constexpr bool kOwnR = false;
 };
-
-// the right operands of the off-diagonal sub-blocks in either layout
-template <class Sm>
-__device__ __forceinline__ auto r_ops(Sm& sm) -> f16x8 (&)[3][4][64] {
-  if constexpr (Sm::kOwnR) return sm.R;
-  else return sm.u2.R;
-}
 // KbT and M rows staged in PreSmem (padded like Smem) go to the image piece by
 // piece: KbT (whole rounds), then the M pieces the chain reads
 static_assert(offsetof(PreSmem, M) == sizeof(((PreSmem*)nullptr)->KbT) && ROW_CC * DK == sizeof(((PreSmem*)nullptr)->KbT),
@@ -593,7 +584,7 @@ __device__ __forceinline__ void offdiag_row(Sm& sm, const float (&lq)[32], const
     f32x4 accA[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const f16x8 rv = r_ops(sm)[b][s][l];
+      const f16x8 rv = sm.R[b][s][l];
       const float4 fa = *reinterpret_cast<const float4*>(&fr[32 * s + 8 * cg]);
       const float4 fb = *reinterpret_cast<const float4*>(&fr[32 * s + 8 * cg + 4]);
       const float f[8] = {fa.x, fa.y, fa.z, fa.w, fb.x, fb.y, fb.z, fb.w};
@@ -680,11 +671,11 @@ __device__ __forceinline__ Lane make_lane(int tid = threadIdx.x) {
 // refill it); the scheduling barriers keep the loads they issue spread out.
 // hook(3) runs right after the fourth workgroup barrier (B3), hook(4) just
 // before B5, hook(5) between B5 and B6.
-// Seven workgroup barriers, B0 .. B6, the last of which ends the function
-// (six where R has a space of its own, Sm::kOwnR: there is no B4); after it
-// the image is complete.  Until B1 the function writes to LDS only
-// tot, beta, gate_bad and the decay tables, and computes the diagonal blocks
-// of A and M in registers (so that another workgroup role
+// Six workgroup barriers, B0 .. B3, B5 and B6 (there is no B4), the last of
+// which ends the function; after it the image is complete.  Until B1 the
+// function writes to LDS only tot, beta, gate_bad and the decay tables, and
+// computes the diagonal blocks of A and M in registers (so that another
+// workgroup role
 // may still read the previous image until then);
 // until B2 not Qt, Kt or KbT; until B5 not Tb or its scale.
 template <class Sm, class Sink, class Hook>
@@ -803,7 +794,7 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
         f16x8 rv;
 #pragma unroll
         for (int j = 0; j < 8; ++j) rv[j] = (_Float16)kr[8 * s + j];
-        r_ops(sm)[w][s][l] = rv;
+        sm.R[w][s][l] = rv;
       }
     }
     if (tid < DK) sink.dv(tid, sm.etab[3][tid]);  // written by this thread before B1
@@ -868,11 +859,7 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
   // blocks of I + A (complete since B2): T = (I + A)^-1 by 16x16 blocks, by
   // forward substitution, lane l owning column l % 16 of diagonal block
   // l / 16.  tmax tracks the largest |Tb| = |T_ij beta_j| a wave produces.
-  // Where T shares its space with R, which waves 1-3 still read, the
-  // columns wait in an upper block of A until B3 (A is strictly lower; its
-  // upper blocks are never written or read): block da in block (pr, pc).
   const int da = l >> 4, dj = l & 15;
-  const int pr = da == 3 ? 1 : da, pc = da == 3 ? 3 : da + 1;
   float tmax = 0.f;
   if (w == 1) offdiag_row<1>(sm, lq, lk, l, cg, beta_mine);
   else if (w == 2) offdiag_row<2>(sm, lq, lk, l, cg, beta_mine);
@@ -902,33 +889,19 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
     const float bj = fabsf(sm.beta[16 * da + dj]);
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-      if constexpr (Sm::kOwnR) sm.u2.T[16 * da + rr][16 * da + dj] = x[rr];
-      else sm.u.A[16 * pr + rr][16 * pc + dj] = x[rr];
+      sm.u2.T[16 * da + rr][16 * da + dj] = x[rr];
       tmax = fmaxf(tmax, fabsf(x[rr]) * bj);
     }
-    if constexpr (Sm::kOwnR) {
-      if (da == 0 || da == 2) {  // upper blocks (0, 1) and (2, 3): read by U = Tb X
+    if (da == 0 || da == 2) {  // upper blocks (0, 1) and (2, 3): read by U = Tb X
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) sm.u2.T[16 * da + rr][16 * (da + 1) + dj] = 0.f;
-      }
+      for (int rr = 0; rr < 16; ++rr) sm.u2.T[16 * da + rr][16 * (da + 1) + dj] = 0.f;
     }
   }
 
-  __syncthreads();  // B3: A and M complete, R dead (T, which shares its space, may be written)
+  __syncthreads();  // B3: A and M complete, R dead, diagonal blocks of T visible
   __builtin_amdgcn_sched_barrier(0);
   hook(3);
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (!Sm::kOwnR) {
-    if (w == 0) {
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) sm.u2.T[16 * da + rr][16 * da + dj] = sm.u.A[16 * pr + rr][16 * pc + dj];
-      if (da == 0 || da == 2) {  // upper blocks (0, 1) and (2, 3): read by U = Tb X
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) sm.u2.T[16 * da + rr][16 * (da + 1) + dj] = 0.f;
-      }
-    }
-    __syncthreads();  // B4: diagonal blocks of T visible
-  }
   // off-diagonal blocks: wave b walks column block b downwards,
   // T_ab = -T_aa sum_{k=b}^{a-1} A_ak T_kb, on fp32 MFMA
   if (w == 0) tmax = levels_column<0>(sm, l, tmax);
@@ -1744,7 +1717,6 @@ __global__ __launch_bounds__(NPC, 1) void kda_pc_kernel(
         // producer's loads go out
         const VChunk vcur = load_v(v, pi.c0, pi.n, H, pi.h, of);
         stage_v(sm, vcur, ln);
-        static_assert(Smem::kOwnR, "prepare_chunk has no B4 on this layout");
         __syncthreads();  // B2
         __syncthreads();  // B3
         __syncthreads();  // B5
