@@ -54,9 +54,9 @@ COPY_PROBE_BYTES = 1 << 30
 # kda_fwd.hip, kda_fwd_state.hip in that order); otherwise null.
 TRAFFIC = {
     "workload": "packed_lognormal_T32768_H32",
-    "kernel_sha256": "2dafeb81f6b6348aa276900497c6417deca90900b29a8d4cadf93bb42bec73a9",
-    "fetch_kib": {"kda_schedule_kernel": 8.5, "kda_pre_kernel": 267247.8, "kda_pc_kernel": 647062.7},
-    "write_kib": {"kda_schedule_kernel": 2.3, "kda_pre_kernel": 500705.8, "kda_pc_kernel": 262174.0},
+    "kernel_sha256": "69524b03b4fc44fee81821512af297b7ec8fa2e01d49a6275895f158a63921bc",
+    "fetch_kib": {"kda_schedule_kernel": 8.4, "kda_pre_kernel": 266809.6, "kda_pc_kernel": 647184.4},
+    "write_kib": {"kda_schedule_kernel": 2.3, "kda_pre_kernel": 497122.8, "kda_pc_kernel": 262174.0},
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }
