@@ -97,6 +97,10 @@ struct alignas(16) Smem {
     uint8_t o[4][CH][64];    // per wave: the bf16 O rows of its 32 columns (see chain_o)
   } u2;
   f16x8 R[3][4][64];         // right operands of off-diagonal sub-blocks (fp16), lane order
+  // Qt of every other chunk (chunks alternate between Qt and Qt1, so that a
+  // copied image can write its Qt while the chain still reads the previous
+  // chunk's)
+  bf16 Qt1[CH][DK + 8];
   unsigned short vt[4][32][CH + 8];  // per wave: V of the chunk chained next, transposed (its 32 columns)
   float etab[13][DK];        // per-channel decay factors of the chunk (see fill_tables)
   float tot[4][DK];          // per sub-block total decay (log2 domain)
@@ -111,6 +115,8 @@ struct alignas(16) Smem {
 __device__ __forceinline__ float* dvec(Smem& sm, int c) {
   return reinterpret_cast<float*>(&sm.KbT[c >> 2][CH]);
 }
+// the Qt buffer of parity qb (0: Qt, 1: Qt1)
+__device__ __forceinline__ bf16 (*qt_buf(Smem& sm, int qb))[DK + 8] { return qb ? sm.Qt1 : sm.Qt; }
 // the power of two Tb was divided by: the padding of Kt row 32
 __device__ __forceinline__ float* tbscale(Smem& sm) {
   return reinterpret_cast<float*>(&sm.Kt[32][DK]);
@@ -118,6 +124,7 @@ __device__ __forceinline__ float* tbscale(Smem& sm) {
 
 // byte offsets of the image parts
 constexpr int OFF_QT = (int)offsetof(Smem, Qt);
+constexpr int OFF_QT1 = (int)offsetof(Smem, Qt1);
 constexpr int OFF_KT = (int)offsetof(Smem, Kt);
 constexpr int OFF_KBT = (int)offsetof(Smem, KbT);
 constexpr int OFF_TB = (int)offsetof(Smem, u);
@@ -391,9 +398,11 @@ __device__ __forceinline__ VChunk load_v(const bf16* __restrict__ v, int64_t c0,
 
 // ---- a precomputed image back into LDS, through registers.  Round i (0..15)
 // of thread tid is piece img_round_base(i) + tid of the image, held in p[i];
-// rounds 0..9 are the first group (Qt, KbT, M, D: phase 1, what the chain's
-// second part reads), rounds 10..15 the second (Kt, Tb, Tb's scale: phase 0,
-// what its first part reads).
+// rounds 0..9 are the first group (Qt, KbT, M, D), rounds 10..15 the second
+// (Kt, Tb, Tb's scale).  Phase 0, copied while the chain reads the previous
+// image's Qt (in the other Qt buffer), KbT, M and D, is what the chain's
+// first part reads and Qt: rounds 0..3 and 10..15; phase 1, copied once the
+// chain is done with the previous image, is KbT, M and D: rounds 4..9.
 constexpr int IMG_ROUNDS = 16;
 constexpr int IMG_ROUNDS_P1 = 10;
 __device__ __forceinline__ constexpr int img_round_base(int i) {
@@ -407,7 +416,7 @@ static_assert(IMG_ROW16 == 4 * NTHR && IMG_KB == 4 * NTHR && IMG_LONG == NTHR &&
                   img_round_base(9) + img_round_count(9) == GP_KT &&
                   img_round_base(15) + img_round_count(15) == IMG_VEC,
               "the rounds cover the image, each group in whole rounds");
-__device__ __forceinline__ constexpr int image_round_phase(int i) { return i < IMG_ROUNDS_P1 ? 1 : 0; }
+__device__ __forceinline__ constexpr int image_round_phase(int i) { return i >= 4 && i < IMG_ROUNDS_P1 ? 1 : 0; }
 // the rounds of phase kPhase (-1: all) into registers.  n_bytes is the
 // image's size, or 0 to load zeros (a descriptor of size 0 reads nothing);
 // lanes past a round's count read past the end, zeros as well.  Every load is
@@ -423,9 +432,10 @@ __device__ __forceinline__ void load_image(RawChunk& im, const uint8_t* __restri
       im.p[i] = __builtin_amdgcn_raw_buffer_load_b128(
           r, tid < img_round_count(i) ? 16 * (img_round_base(i) + tid) : IMG_BYTES, 0, 0);
 }
-// the rounds of phase kPhase (-1: all) from registers into the LDS image
+// the rounds of phase kPhase (-1: all) from registers into the LDS image, Qt
+// into the Qt buffer qb
 template <int kPhase = -1>
-__device__ __forceinline__ void image_to_lds(Smem& sm, const RawChunk& im, int tid) {
+__device__ __forceinline__ void image_to_lds(Smem& sm, const RawChunk& im, int tid, int qb) {
   uint8_t* dst = reinterpret_cast<uint8_t*>(&sm);
 #pragma unroll
   for (int i = 0; i < IMG_ROUNDS; ++i) {
@@ -433,7 +443,7 @@ __device__ __forceinline__ void image_to_lds(Smem& sm, const RawChunk& im, int t
     int off;
     if (i < 4) {         // Qt rows
       const int q = NTHR * i + tid;
-      off = OFF_QT + (q >> 4) * ROW_QK + (q & 15) * 16;
+      off = (qb ? OFF_QT1 : OFF_QT) + (q >> 4) * ROW_QK + (q & 15) * 16;
     } else if (i < 8) {  // KbT rows
       const int q = NTHR * (i - 4) + tid;
       off = OFF_KBT + (q >> 3) * ROW_CC + (q & 7) * 16;
@@ -457,8 +467,9 @@ __device__ __forceinline__ void image_to_lds(Smem& sm, const RawChunk& im, int t
 // and D): the LDS image of the main kernel, or the global image.
 struct LdsSink {
   Smem* sm;
+  int qb;  // the Qt buffer
   __device__ __forceinline__ void qk(int tok, int col, const bf16x8& qt, const bf16x8& kt) const {
-    *reinterpret_cast<bf16x8*>(&sm->Qt[tok][col]) = qt;
+    *reinterpret_cast<bf16x8*>(&qt_buf(*sm, qb)[tok][col]) = qt;
     *reinterpret_cast<bf16x8*>(&sm->Kt[tok][col]) = kt;
   }
   __device__ __forceinline__ void dv(int c, float f) const { dvec(*sm, c)[c & 3] = f; }
@@ -1121,8 +1132,9 @@ __device__ __forceinline__ void chain_a(Smem& sm, const f32x16 (&S)[4], int n, i
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void chain_o(Smem& sm, const f32x16 (&S)[4], const ChainMid& mid, int n,
                                         int64_t c0, int H, int h, bf16* __restrict__ out,
-                                        const Lane& ln, const Offsets& of) {
+                                        const Lane& ln, const Offsets& of, int qb) {
   const int w = ln.w, m = ln.m, hg = ln.hg;
+  const bf16 (*Qt)[DK + 8] = qt_buf(sm, qb);
   const float scale = 0.08838834764831845f;  // 128^-1/2
   constexpr int PMT[6] = {0, 0, 1, 1, 1, 1};
   constexpr int PS[6] = {0, 1, 0, 1, 2, 3};
@@ -1170,7 +1182,7 @@ __device__ __forceinline__ void chain_o(Smem& sm, const f32x16 (&S)[4], const Ch
     for (int s = 0; s < 8; ++s)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        const bf16x8 qv = *reinterpret_cast<const bf16x8*>(&sm.Qt[32 * mt + m][16 * s + 8 * hg]);
+        const bf16x8 qv = *reinterpret_cast<const bf16x8*>(&Qt[32 * mt + m][16 * s + 8 * hg]);
         O[mt] = mfma32(Sb[s], qv, O[mt]);
       }
     oscale = scale;
@@ -1180,7 +1192,7 @@ __device__ __forceinline__ void chain_o(Smem& sm, const f32x16 (&S)[4], const Ch
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
-        qa[mt][s] = *reinterpret_cast<const bf16x8*>(&sm.Qt[32 * mt + m][16 * s + 8 * hg]);
+        qa[mt][s] = *reinterpret_cast<const bf16x8*>(&Qt[32 * mt + m][16 * s + 8 * hg]);
     // M operands loaded two pairs ahead
     f16x8 mh[2];
 #pragma unroll
@@ -1192,7 +1204,7 @@ __device__ __forceinline__ void chain_o(Smem& sm, const f32x16 (&S)[4], const Ch
       for (int mt = 0; mt < 2; ++mt) {
         O[mt] = mfma32(Sb[s], qa[mt][s & 1], O[mt]);
         if (s + 2 < 8)
-          qa[mt][s & 1] = *reinterpret_cast<const bf16x8*>(&sm.Qt[32 * mt + m][16 * (s + 2) + 8 * hg]);
+          qa[mt][s & 1] = *reinterpret_cast<const bf16x8*>(&Qt[32 * mt + m][16 * (s + 2) + 8 * hg]);
       }
       if (s < 6) {
         const int p = s;
@@ -1321,7 +1333,8 @@ __device__ __forceinline__ void store_state(const f32x16 (&S)[4], float* dst, co
 // a split chunk's image from the workspace) while waves 4-7 (the consumer)
 // chain chunk i - 1 on the image in LDS: two waves per SIMD, one of each role.
 //
-// The image is single-buffered; workgroup barriers order the consumer's reads
+// The image is single-buffered (all but Qt, which alternates between two
+// buffers); workgroup barriers order the consumer's reads
 // of image i - 1 before the producer's writes of image i.  An iteration in
 // which the producer builds an image from raw inputs has the six barriers of
 // prepare_chunk, B0 .. B3, B5, B6:
@@ -1336,8 +1349,10 @@ __device__ __forceinline__ void store_state(const f32x16 (&S)[4], float* dst, co
 //               consumer: loads and stages the V of the chunk it chains
 //               next, then waits.
 // An iteration that copies a precomputed image (or prepares nothing) has two:
-//   B0 .. B1:   producer: Kt, Tb and Tb's scale of image i;
-//   after B1:   producer: Qt, KbT, M and D of image i;
+//   B0 .. B1:   producer: Kt, Tb and Tb's scale of image i, and its Qt (into
+//               the Qt buffer of parity i; the chain reads image i - 1's in
+//               the other);
+//   after B1:   producer: KbT, M and D of image i;
 //               consumer: chain_a of image i (the next iteration), which reads
 //               only what was written before B1.
 // The producer hands each chunk to the consumer through an item descriptor in
@@ -1565,7 +1580,7 @@ __global__ __launch_bounds__(NPC, 1) void kda_pc_kernel(
         // redefined on every path and nothing keeps it alive across the
         // prologue.
         const bool last = pc + 1 >= pu.nch;
-        prepare_chunk(sm, LdsSink{&sm}, buf, pn, gate_bound, lnI, [&](int part) {
+        prepare_chunk(sm, LdsSink{&sm, iter & 1}, buf, pn, gate_bound, lnI, [&](int part) {
           // the next chunk of the same unit arrives in three parts (q and k
           // after B0, g's two halves and beta after the tiles and after B3),
           // so that its loads do not all share the window in which the
@@ -1609,12 +1624,12 @@ __global__ __launch_bounds__(NPC, 1) void kda_pc_kernel(
           const int64_t vc0 = pu.bos + (int64_t)CH * pc;
           const VChunk vn = load_v(v, vc0, (int)min<int64_t>(CH, (int64_t)pu.len - (int64_t)CH * pc), H, pu.h, ofI);
           __syncthreads();  // B0: the consumer has read Kt, Tb and Tb's scale of the previous image, and V
-          image_to_lds<0>(sm, im, lnI.tid);
+          image_to_lds<0>(sm, im, lnI.tid, iter & 1);
           load_image<0>(im, nimg, nbytes, lnI.tid);
           if (last) fetch_next();
           stage_v(sm, vn, lnI);
-          __syncthreads();  // B1: ... and Qt, M, KbT and D
-          image_to_lds<1>(sm, im, lnI.tid);
+          __syncthreads();  // B1: ... and M, KbT and D (its Qt is in the other buffer)
+          image_to_lds<1>(sm, im, lnI.tid, iter & 1);
           load_image<1>(im, nimg, nbytes, lnI.tid);
           if (last) {
             nu = fetched();
@@ -1705,7 +1720,7 @@ __global__ __launch_bounds__(NPC, 1) void kda_pc_kernel(
       // empty item needs none
       const bool pfused = pv && pi.n > 0 && !(pi.flags & ITEM_SPLIT);
       if (active) {
-        chain_o(sm, S, mid, ci.n, ci.c0, H, ci.h, out, ln, of);
+        chain_o(sm, S, mid, ci.n, ci.c0, H, ci.h, out, ln, of, (iter + 1) & 1);
         chain_b(sm, S, mid, ln);
       }
       if (cv && (ci.flags & ITEM_LAST)) state_out(ci);
