@@ -54,9 +54,9 @@ COPY_PROBE_BYTES = 1 << 30
 # kda_fwd.hip, kda_fwd_state.hip in that order); otherwise null.
 TRAFFIC = {
     "workload": "packed_lognormal_T32768_H32",
-    "kernel_sha256": "0e171b8fa345d816845731d6473d29c0cb316e8da7aba2ec8b36fa5bfd90739a",
-    "fetch_kib": {"kda_schedule_kernel": 8.4, "kda_pre_kernel": 266821.9, "kda_pc_kernel": 647224.0},
-    "write_kib": {"kda_schedule_kernel": 2.3, "kda_pre_kernel": 497753.2, "kda_pc_kernel": 262177.8},
+    "kernel_sha256": "d2d716f968d183fa1d63a0dcf03364bc84b6e96933f36c12a3fd82dcfe42c8dd",
+    "fetch_kib": {"kda_schedule_kernel": 8.4, "kda_pre_kernel": 266851.9, "kda_pc_kernel": 647295.1},
+    "write_kib": {"kda_schedule_kernel": 2.3, "kda_pre_kernel": 497252.9, "kda_pc_kernel": 262175.8},
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }

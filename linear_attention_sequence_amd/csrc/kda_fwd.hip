@@ -243,8 +243,13 @@ __global__ __launch_bounds__(SCHED_THREADS) void kda_schedule_kernel(
         // longest fused document (beyond the candidates: at most the last one's length)
         const float rest = (s < nd) ? (float)nch_of(min(s, n_cand - 1)) * COST_FUSED : 0.f;
         const float avg = ((float)sum * COST_CHAIN + (total - (float)sum) * COST_FUSED) * per_cu;
-        const float est = pre + fmaxf(fmaxf((float)longest_split * COST_CHAIN, rest), avg);
+        const float bound = fmaxf((float)longest_split * COST_CHAIN, avg);
+        const float est = pre + fmaxf(bound, rest);
         if (policy == SPLIT_ALWAYS || est < best) { best = est; best_s = s; best_sum = sum; }
+        // once the longest document left fused is no longer the bound, more
+        // splits only add prepare work (COST_PRE exceeds what a split saves,
+        // COST_FUSED - COST_CHAIN): stop
+        if (policy != SPLIT_ALWAYS && rest <= bound) break;
       }
     }
     // first chunk of each split document in pre_chunks (exclusive prefix sum)

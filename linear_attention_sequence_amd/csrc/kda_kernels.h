@@ -228,7 +228,7 @@ __device__ __forceinline__ void store_block(Sm& sm, const f32x4& accM, const f32
 // ---------------------------------------------------------------------------
 constexpr int SCHED_THREADS = 1024;
 constexpr int NBUCKET = 1024;
-constexpr int MIN_SPLIT_CHUNKS = 8;   // shorter documents are never split
+constexpr int MIN_SPLIT_CHUNKS = 2;   // a document of one chunk is never split
 constexpr int MAX_SPLIT_DOCS = 1024;  // split candidates examined (the longest documents)
 // relative cost of one chunk of one head: fused (prepare + chain on one
 // workgroup), prepare only (pre kernel), chain only (main kernel)
