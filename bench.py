@@ -55,8 +55,8 @@ COPY_PROBE_BYTES = 1 << 30
 TRAFFIC = {
     "workload": "packed_lognormal_T32768_H32",
     "kernel_sha256": "d2d716f968d183fa1d63a0dcf03364bc84b6e96933f36c12a3fd82dcfe42c8dd",
-    "fetch_kib": {"kda_schedule_kernel": 8.4, "kda_pre_kernel": 266851.9, "kda_pc_kernel": 647295.1},
-    "write_kib": {"kda_schedule_kernel": 2.3, "kda_pre_kernel": 497252.9, "kda_pc_kernel": 262175.8},
+    "fetch_kib": {"kda_schedule_kernel": 8.4, "kda_pre_kernel": 266842.2, "kda_pc_kernel": 647130.4},
+    "write_kib": {"kda_schedule_kernel": 2.3, "kda_pre_kernel": 497448.5, "kda_pc_kernel": 262178.5},
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }
