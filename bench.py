@@ -54,9 +54,9 @@ COPY_PROBE_BYTES = 1 << 30
 # kda_fwd.hip, kda_fwd_state.hip in that order); otherwise null.
 TRAFFIC = {
     "workload": "packed_lognormal_T32768_H32",
-    "kernel_sha256": "d2d716f968d183fa1d63a0dcf03364bc84b6e96933f36c12a3fd82dcfe42c8dd",
-    "fetch_kib": {"kda_schedule_kernel": 8.4, "kda_pre_kernel": 266842.2, "kda_pc_kernel": 647130.4},
-    "write_kib": {"kda_schedule_kernel": 2.3, "kda_pre_kernel": 497448.5, "kda_pc_kernel": 262178.5},
+    "kernel_sha256": "2ee6c3cac4e2b61888ce82b06284dd1c9d77067181db0bc2e7c3c9c0bd88880f",
+    "fetch_kib": {"kda_schedule_kernel": 8.6, "kda_pre_kernel": 266885.0, "kda_pc_kernel": 646953.3},
+    "write_kib": {"kda_schedule_kernel": 2.3, "kda_pre_kernel": 497827.0, "kda_pc_kernel": 262178.9},
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }

@@ -676,6 +676,32 @@ __device__ __forceinline__ Lane make_lane(int tid = threadIdx.x) {
   return ln;
 }
 
+// Tb = T Diag(beta) 2^-e in fp16 (in LDS it overwrites A), e chosen so that
+// |Tb 2^-e| < 2^14 (e = 0 unless Tb is huge): thread tid (0 .. 255) converts
+// row tid / 4, columns 16 (tid % 4) + 8 half .. + 7 for half in [H0, H1).
+// Reads T, beta and the blocks' largest |Tb| (complete at B5).
+template <int H0, int H1, class Sm, class Sink>
+__device__ __forceinline__ void convert_tb(Sm& sm, const Sink& sink, int tid) {
+  const int e = f16_exponent(fmaxf(fmaxf(sm.tbmax[0], sm.tbmax[1]), fmaxf(sm.tbmax[2], sm.tbmax[3])));
+  const float down = pow2i(-e);
+  if (H0 == 0 && tid == 0) sink.tbs(pow2i(e));
+  const int rr = tid >> 2;
+#pragma unroll
+  for (int half = H0; half < H1; ++half) {
+    const int cc = 16 * (tid & 3) + 8 * half;
+    const float4 t0 = *reinterpret_cast<const float4*>(&sm.u2.T[rr][cc]);
+    const float4 t1 = *reinterpret_cast<const float4*>(&sm.u2.T[rr][cc + 4]);
+    const float4 b0 = *reinterpret_cast<const float4*>(&sm.beta[cc]);
+    const float4 b1 = *reinterpret_cast<const float4*>(&sm.beta[cc + 4]);
+    const float x[8] = {t0.x * b0.x, t0.y * b0.y, t0.z * b0.z, t0.w * b0.w,
+                        t1.x * b1.x, t1.y * b1.y, t1.z * b1.z, t1.w * b1.w};
+    f16x8 th;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) th[j] = (_Float16)(x[j] * down);
+    sink.tb(rr, cc, th);
+  }
+}
+
 // Everything of a chunk that does not depend on the state: from the raw
 // inputs `cur` (n valid tokens) to the image in LDS (Qt, Kt, KbT, M, Tb, D).
 // hook(0..2) run at fixed points once `cur` has been consumed (they may
@@ -683,13 +709,14 @@ __device__ __forceinline__ Lane make_lane(int tid = threadIdx.x) {
 // hook(3) runs right after the fourth workgroup barrier (B3), hook(4) just
 // before B5, hook(5) between B5 and B6.
 // Six workgroup barriers, B0 .. B3, B5 and B6 (there is no B4), the last of
-// which ends the function; after it the image is complete.  Until B1 the
-// function writes to LDS only tot, beta, gate_bad and the decay tables, and
-// computes the diagonal blocks of A and M in registers (so that another
-// workgroup role
-// may still read the previous image until then);
-// until B2 not Qt, Kt or KbT; until B5 not Tb or its scale.
-template <class Sm, class Sink, class Hook>
+// which ends the function; after it the image is complete (with kTbShared,
+// once the other role has converted the second column half of Tb between B5
+// and B6, convert_tb<1, 2>).  Until B1 the function writes to LDS only tot,
+// beta, gate_bad and the decay tables, and computes the diagonal blocks of A
+// and M in registers (so that another workgroup role may still read the
+// previous image until then); until B2 not Qt, Kt or KbT; until B5 not Tb or
+// its scale.
+template <bool kTbShared = false, class Sm, class Sink, class Hook>
 __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const RawChunk& cur, int n,
                                               float gate_bound, const Lane& ln, Hook hook) {
   const int tid = ln.tid, w = ln.w, l = ln.l, r = ln.r, cg = ln.cg, tok = ln.tok;
@@ -924,29 +951,10 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
   hook(4);
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();  // B5: T complete
-  // Tb = T Diag(beta) 2^-e in fp16 (in LDS it overwrites A), e chosen so
-  // that |Tb 2^-e| < 2^14 (e = 0 unless Tb is huge): thread tid converts row
-  // tid / 4, columns 16 (tid % 4) .. + 15
-  {
-    const int e = f16_exponent(fmaxf(fmaxf(sm.tbmax[0], sm.tbmax[1]), fmaxf(sm.tbmax[2], sm.tbmax[3])));
-    const float down = pow2i(-e);
-    if (tid == 0) sink.tbs(pow2i(e));
-    const int rr = tid >> 2;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int cc = 16 * (tid & 3) + 8 * half;
-      const float4 t0 = *reinterpret_cast<const float4*>(&sm.u2.T[rr][cc]);
-      const float4 t1 = *reinterpret_cast<const float4*>(&sm.u2.T[rr][cc + 4]);
-      const float4 b0 = *reinterpret_cast<const float4*>(&sm.beta[cc]);
-      const float4 b1 = *reinterpret_cast<const float4*>(&sm.beta[cc + 4]);
-      const float x[8] = {t0.x * b0.x, t0.y * b0.y, t0.z * b0.z, t0.w * b0.w,
-                          t1.x * b1.x, t1.y * b1.y, t1.z * b1.z, t1.w * b1.w};
-      f16x8 th;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) th[j] = (_Float16)(x[j] * down);
-      sink.tb(rr, cc, th);
-    }
-  }
+  // Tb: both column halves here, or only the first when the caller's other
+  // role (the main kernel's consumer waves, idle until B6) converts the second
+  if constexpr (kTbShared) convert_tb<0, 1>(sm, sink, tid);
+  else convert_tb<0, 2>(sm, sink, tid);
   __builtin_amdgcn_sched_barrier(0);
   hook(5);
   __builtin_amdgcn_sched_barrier(0);
@@ -1580,7 +1588,7 @@ __global__ __launch_bounds__(NPC, 1) void kda_pc_kernel(
         // redefined on every path and nothing keeps it alive across the
         // prologue.
         const bool last = pc + 1 >= pu.nch;
-        prepare_chunk(sm, LdsSink{&sm, iter & 1}, buf, pn, gate_bound, lnI, [&](int part) {
+        prepare_chunk<true>(sm, LdsSink{&sm, iter & 1}, buf, pn, gate_bound, lnI, [&](int part) {
           // the next chunk of the same unit arrives in three parts (q and k
           // after B0, g's two halves and beta after the tiles and after B3),
           // so that its loads do not all share the window in which the
@@ -1727,7 +1735,7 @@ __global__ __launch_bounds__(NPC, 1) void kda_pc_kernel(
       __syncthreads();  // B1
       if (pfused) {
         // V of a fused item is loaded and staged while the producer builds
-        // the image (this role has nothing else to do until B6), away from
+        // the image (this role has nothing else to do until B5), away from
         // the window between B0 and B1 in which the O stores and the
         // producer's loads go out
         const VChunk vcur = load_v(v, pi.c0, pi.n, H, pi.h, of);
@@ -1735,6 +1743,7 @@ __global__ __launch_bounds__(NPC, 1) void kda_pc_kernel(
         __syncthreads();  // B2
         __syncthreads();  // B3
         __syncthreads();  // B5
+        convert_tb<1, 2>(sm, LdsSink{&sm, 0}, ln.tid);  // the second column half of Tb
         __syncthreads();  // B6
       }
     }
