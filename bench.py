@@ -54,9 +54,9 @@ COPY_PROBE_BYTES = 1 << 30
 # kda_fwd.hip, kda_fwd_state.hip in that order); otherwise null.
 TRAFFIC = {
     "workload": "packed_lognormal_T32768_H32",
-    "kernel_sha256": "2ee6c3cac4e2b61888ce82b06284dd1c9d77067181db0bc2e7c3c9c0bd88880f",
-    "fetch_kib": {"kda_schedule_kernel": 8.6, "kda_pre_kernel": 266885.0, "kda_pc_kernel": 646953.3},
-    "write_kib": {"kda_schedule_kernel": 2.3, "kda_pre_kernel": 497827.0, "kda_pc_kernel": 262178.9},
+    "kernel_sha256": "a78c47199cfe2a636382eb70c2f8258f1d32497dc67fca2e98f5db0e1ff9d0e6",
+    "fetch_kib": {"kda_schedule_kernel": 8.4, "kda_pre_kernel": 266835.0, "kda_pc_kernel": 646775.5},
+    "write_kib": {"kda_schedule_kernel": 2.3, "kda_pre_kernel": 497732.2, "kda_pc_kernel": 262173.5},
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }

@@ -706,8 +706,9 @@ __device__ __forceinline__ void convert_tb(Sm& sm, const Sink& sink, int tid) {
 // inputs `cur` (n valid tokens) to the image in LDS (Qt, Kt, KbT, M, Tb, D).
 // hook(0..2) run at fixed points once `cur` has been consumed (they may
 // refill it); the scheduling barriers keep the loads they issue spread out.
-// hook(3) runs right after the fourth workgroup barrier (B3), hook(4) just
-// before B5, hook(5) between B5 and B6.
+// hook(6) runs between B1 and B2, after this role's stores there; hook(3)
+// runs right after the fourth workgroup barrier (B3), hook(4) just before
+// B5, hook(5) between B5 and B6.
 // Six workgroup barriers, B0 .. B3, B5 and B6 (there is no B4), the last of
 // which ends the function; after it the image is complete (with kTbShared,
 // once the other role has converted the second column half of Tb between B5
@@ -837,6 +838,9 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
     }
     if (tid < DK) sink.dv(tid, sm.etab[3][tid]);  // written by this thread before B1
   }
+  __builtin_amdgcn_sched_barrier(0);
+  hook(6);
+  __builtin_amdgcn_sched_barrier(0);
   __syncthreads();  // B2: decay tables, R and the diagonal A / M blocks visible
 
   // ---- operand tiles of the chain: Qt = lq e^{G_end(w)}, Kt = -lk e^{G_end(w)},
@@ -965,9 +969,9 @@ __device__ __forceinline__ void prepare_chunk(Sm& sm, const Sink& sink, const Ra
 // the image in LDS and this chunk's V (wave w owns value columns 32 w ..):
 //   X = V - Kt S,  U = Tb X,  O = scale (Qt S + M U),  S <- D S + KbT U,
 // in three parts.  chain_a computes X and U: it reads V (staged by stage_v),
-// Kt, Tb and Tb's scale; chain_o computes and stores O: it
-// reads Qt and M; chain_b updates S: it reads only
-// KbT and D.  ChainMid carries U (fp16, 2^-eu) from chain_a to the others.
+// Kt, Tb and Tb's scale; chain_o computes O and stages it in LDS (write_o
+// stores it, on the other role, after the next workgroup barrier): it reads
+// Qt and M; chain_b updates S: it reads only KbT and D.  ChainMid carries U (fp16, 2^-eu) from chain_a to the others.
 // Scheduling fences in chain_a (after the V staging, after X and after U)
 // keep its stages in order.
 struct ChainMid {
@@ -1138,9 +1142,8 @@ __device__ __forceinline__ void chain_a(Smem& sm, const f32x16 (&S)[4], int n, i
 // the 16-byte reads of 16 lanes share a bank) and leave as 16-byte row
 // pieces, four lanes to a row.  Reads Qt and M.
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ void chain_o(Smem& sm, const f32x16 (&S)[4], const ChainMid& mid, int n,
-                                        int64_t c0, int H, int h, bf16* __restrict__ out,
-                                        const Lane& ln, const Offsets& of, int qb) {
+__device__ __forceinline__ void chain_o(Smem& sm, const f32x16 (&S)[4], const ChainMid& mid,
+                                        const Lane& ln, int qb) {
   const int w = ln.w, m = ln.m, hg = ln.hg;
   const bf16 (*Qt)[DK + 8] = qt_buf(sm, qb);
   const float scale = 0.08838834764831845f;  // 128^-1/2
@@ -1243,17 +1246,22 @@ __device__ __forceinline__ void chain_o(Smem& sm, const f32x16 (&S)[4], const Ch
       *reinterpret_cast<u32x2*>(dst + 16 * (q ^ sw)) = pk;
     }
   }
-  // O rows: lane l writes 16 bytes of row 16 it + l / 4 (rows past the end
-  // are dropped by the descriptor's range)
-  wave_sync_lds();
-  {
-    const int l = ln.l;
-    const Rsrc ro = make_rsrc(out + ((size_t)c0 * H + h) * DV, chunk_bytes(n, H, 256u));
+}
+
+// The O rows that chain_o staged (wave w's slice, 32 columns) out to memory,
+// for the chunk of n tokens at token c0: lane l writes 16 bytes of row
+// 16 it + l / 4 (rows past the end are dropped by the descriptor's range).
+// Run by the producer wave of the same index, once a workgroup barrier has
+// followed chain_o.
+__device__ __forceinline__ void write_o(const Smem& sm, int n, int64_t c0, int H, int h, bf16* __restrict__ out,
+                                        const Lane& ln, const Offsets& of) {
+  const uint8_t* ost = &sm.u2.o[ln.w][0][0];
+  const int l = ln.l;
+  const Rsrc ro = make_rsrc(out + ((size_t)c0 * H + h) * DV, chunk_bytes(n, H, 256u));
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int t = 16 * it + (l >> 2);
-      bstore(*reinterpret_cast<const u32x4*>(ost + 64 * t + 16 * ((l & 3) ^ ((t >> 2) & 3))), ro, of.v[it]);
-    }
+  for (int it = 0; it < 4; ++it) {
+    const int t = 16 * it + (l >> 2);
+    bstore(*reinterpret_cast<const u32x4*>(ost + 64 * t + 16 * ((l & 3) ^ ((t >> 2) & 3))), ro, of.v[it]);
   }
 }
 
@@ -1578,6 +1586,13 @@ __global__ __launch_bounds__(NPC, 1) void kda_pc_kernel(
           ps.items[(it + 1) & 1] = p.u < n_units ? make_item(p, c) : none;
         }
       };
+      // O of the item the consumer chains in this iteration, which its
+      // chain_o staged in LDS before B1: out to memory after B1, before
+      // publish() reuses that item's slot
+      auto store_o = [&]() {
+        const Item it = read_item(ps.items[(iter + 1) & 1]);
+        if ((it.flags & ITEM_VALID) && it.n > 0) write_o(sm, it.n, it.c0, H, it.h, out, lnI, ofI);
+      };
       PUnit nu = pu;  // the next item: (nu, nc)
       int nc = pc + 1;
       if (pv && pn > 0 && pu.img0 < 0) {
@@ -1591,8 +1606,8 @@ __global__ __launch_bounds__(NPC, 1) void kda_pc_kernel(
         prepare_chunk<true>(sm, LdsSink{&sm, iter & 1}, buf, pn, gate_bound, lnI, [&](int part) {
           // the next chunk of the same unit arrives in three parts (q and k
           // after B0, g's two halves and beta after the tiles and after B3),
-          // so that its loads do not all share the window in which the
-          // consumer loads V and stores O
+          // so that its loads do not all share the window in which V is
+          // loaded and O stored (between B1 and B2, part 6)
           if (part == 1) {
             if (last) fetch_next();
             else load_raw_part(buf, raw_of(pu, pc + 1), ofI, 0);
@@ -1608,6 +1623,8 @@ __global__ __launch_bounds__(NPC, 1) void kda_pc_kernel(
             }
           } else if (part == 5) {
             publish(iter, nu, nc);
+          } else if (part == 6) {
+            store_o();
           }
         });
       } else if (pv && pn > 0) {
@@ -1637,6 +1654,7 @@ __global__ __launch_bounds__(NPC, 1) void kda_pc_kernel(
           if (last) fetch_next();
           stage_v(sm, vn, lnI);
           __syncthreads();  // B1: ... and M, KbT and D (its Qt is in the other buffer)
+          store_o();
           image_to_lds<1>(sm, im, lnI.tid, iter & 1);
           load_image<1>(im, nimg, nbytes, lnI.tid);
           if (last) {
@@ -1654,6 +1672,7 @@ __global__ __launch_bounds__(NPC, 1) void kda_pc_kernel(
         __syncthreads();  // B0
         if (last) fetch_next();
         __syncthreads();  // B1
+        store_o();
         if (last) {
           nu = fetched();
           nc = 0;
@@ -1728,7 +1747,7 @@ __global__ __launch_bounds__(NPC, 1) void kda_pc_kernel(
       // empty item needs none
       const bool pfused = pv && pi.n > 0 && !(pi.flags & ITEM_SPLIT);
       if (active) {
-        chain_o(sm, S, mid, ci.n, ci.c0, H, ci.h, out, ln, of, (iter + 1) & 1);
+        chain_o(sm, S, mid, ln, (iter + 1) & 1);
         chain_b(sm, S, mid, ln);
       }
       if (cv && (ci.flags & ITEM_LAST)) state_out(ci);
