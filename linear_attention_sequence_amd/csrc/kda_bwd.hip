@@ -27,7 +27,8 @@
 //   1. the stateful forward with S stored at every chunk start (kda_fwd.hip);
 //   2. kda_bwd_setup_kernel: cu_seqlens check and the chunk table;
 //   3. kda_bwd_prep_kernel (parallel over chunks): qh, kh, G, T, Kk, M and
-//      F^T, R of every chunk;
+//      F^T, R of every chunk (through Z = Kt^T Tb^T: F^T = D - Z Kbar,
+//      R = scale (Qt^T - Z M^T) dO);
 //   4. kda_bwd_chain_kernel (per document, head and quarter of the value
 //      columns, last chunk first): dS <- F^T dS + R, storing dS at every
 //      chunk end;
@@ -86,19 +87,14 @@ constexpr int IMG_RQ = IMG_M + CH * CH;      // [64] 1/||q||
 constexpr int IMG_RK = IMG_RQ + CH;          // [64] 1/||k||
 constexpr int IMG_FLOATS = IMG_RK + CH;
 
-// per-workgroup scratch of the gradient pass, fp32
+// per-workgroup scratch of the gradient pass, fp32 (the [64][64] tiles dM,
+// dTb and Z live in LDS the products have finished with)
 constexpr int SC_DQK = 0;                    // [128][128]: rows 0..63 dQt, 64..127 dKt
 constexpr int SC_DKB = SC_DQK + 2 * CH * DK;  // [64][128] dKbar
-constexpr int SC_DM = SC_DKB + CH * DK;       // [64][64]
-constexpr int SC_DTB = SC_DM + CH * CH;
-constexpr int SC_Z = SC_DTB + CH * CH;
-constexpr int SC_FLOATS = SC_Z + CH * CH;
+constexpr int SC_FLOATS = SC_DKB + CH * DK;
 
-// per-workgroup scratch of the prep pass (Y1 = Tb^T Kbar, P1 = scale M^T dO, Y2 = Tb^T P1)
-constexpr int SP_Y1 = 0;
-constexpr int SP_P1 = SP_Y1 + CH * DK;
-constexpr int SP_Y2 = SP_P1 + CH * DV;
-constexpr int SP_FLOATS = SP_Y2 + CH * DV;
+// per-workgroup scratch of the prep pass: none (its products stay in LDS)
+constexpr int SP_FLOATS = 0;
 
 struct ChunkDesc {
   int start;  // first token
@@ -420,10 +416,9 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_prep_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, const bf16* __restrict__ dout, const ChunkDesc* __restrict__ table,
     const int* __restrict__ bad, int n_items, int H, float* __restrict__ imgs, float* __restrict__ fts,
-    float* __restrict__ rs, float* __restrict__ wscratch) {
+    float* __restrict__ rs) {
   __shared__ PrepSmem sm;
   if (*bad) return;
-  float* sp = wscratch + (size_t)blockIdx.x * SP_FLOATS;
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int slot = item / H, h = item - slot * H;
     const ChunkDesc cd = table[slot];
@@ -560,38 +555,41 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_prep_kernel(
       const float x = bf16_to_f32(dout[(drow0 + (size_t)min(r, len - 1) * H) * DV + v]);
       return r < len ? x : 0.f;
     };
-    // Y1 = Tb^T Kbar  [t][c]
-    wg_gemm<CH, DK, CH, false, false>(
-        [&](int t, int r) { return sm.t[r][t] * sm.beta[t]; },
-        [&](int r, int c) { return sm.kh[r][c] * __expf(Gl[c] - sm.G[r][c]); },
-        [&](int t, int c, float x, float) { sp[SP_Y1 + t * DK + c] = x; }, sm.stage, tid);
-    // P1 = scale M^T dO  [t][v]
-    wg_gemm<CH, DV, CH, false, false>(
-        [&](int t, int r) { return SCALE * sm.m[r][t]; }, [&](int r, int v) { return dO(r, v); },
-        [&](int t, int v, float x, float) { sp[SP_P1 + t * DV + v] = x; }, sm.stage, tid);
-    // Y2 = Tb^T P1
-    wg_gemm<CH, DV, CH, false, false>(
-        [&](int t, int r) { return sm.t[r][t] * sm.beta[t]; },
-        [&](int r, int v) { return sp[SP_P1 + r * DV + v]; },
-        [&](int t, int v, float x, float) { sp[SP_Y2 + t * DV + v] = x; }, sm.stage, tid);
-    // F^T = D - Kt^T Y1  [c][c']
-    float* ft = fts + (size_t)item * DK * DK;
-    wg_gemm<DK, DK, CH, false, false>(
+    // Z = Kt^T Tb^T  [c][r] (Z_cr = sum_t Kt_tc T_rt beta_t), over M and T,
+    // which the image holds from here on: M and T are contiguous, 128 rows of
+    // LDC floats
+    static_assert(offsetof(PrepSmem, t) == offsetof(PrepSmem, m) + sizeof(PrepSmem::m),
+                  "M and T contiguous");
+    float (*const zb)[LDC] = reinterpret_cast<float (*)[LDC]>(&sm.m[0][0]);
+    wg_gemm<DK, CH, CH, false, true>(
         [&](int c, int t) { return sm.kh[t][c] * __expf(sm.G[t][c]); },
-        [&](int t, int c2) { return sp[SP_Y1 + t * DK + c2]; },
+        [&](int t, int r) { return sm.t[r][t] * sm.beta[t]; },
+        [&](int c, int r, float x, float) { zb[c][r] = x; }, sm.stage, tid);
+    // F^T = D - Z Kbar  [c][c']
+    float* ft = fts + (size_t)item * DK * DK;
+    wg_gemm<DK, DK, CH, true, false>(
+        [&](int c, int r) { return zb[c][r]; },
+        [&](int r, int c2) { return sm.kh[r][c2] * __expf(Gl[c2] - sm.G[r][c2]); },
         [&](int c, int c2, float x, float) { ft[c * DK + c2] = (c == c2 ? __expf(Gl[c]) : 0.f) - x; },
         sm.stage, tid);
-    // R = scale Qt^T dO - Kt^T Y2  [c][v]
+    // W = scale (Qt^T - Z M^T)  [c][s], over kh (read last by F^T); M from
+    // the image, which this workgroup wrote above
+    float (*const wb)[LDC] = reinterpret_cast<float (*)[LDC]>(&sm.kh[0][0]);
+    static_assert(DK * LDC <= CH * LD, "W fits over kh");
+    const float* im = img + IMG_M;
+    wg_gemm<DK, CH, CH, true, true>(
+        [&](int c, int r) { return zb[c][r]; },
+        [&](int r, int s2) { return im[s2 * CH + r]; },
+        [&](int c, int s2, float x, float) {
+          wb[c][s2] = SCALE * (sm.qh[s2][c] * __expf(sm.G[s2][c]) - x);
+        },
+        sm.stage, tid);
+    // R = W dO  [c][v]
     float* rr = rs + (size_t)item * DK * DV;
-    wg_gemm<DK, DV, CH, false, false>(
-        [&](int c, int t) { return SCALE * sm.qh[t][c] * __expf(sm.G[t][c]); },
-        [&](int t, int v) { return dO(t, v); },
+    wg_gemm<DK, DV, CH, true, false>(
+        [&](int c, int s2) { return wb[c][s2]; },
+        [&](int s2, int v) { return dO(s2, v); },
         [&](int c, int v, float x, float) { rr[c * DV + v] = x; }, sm.stage, tid);
-    wg_gemm<DK, DV, CH, false, false>(
-        [&](int c, int t) { return -sm.kh[t][c] * __expf(sm.G[t][c]); },
-        [&](int t, int v) { return sp[SP_Y2 + t * DV + v]; },
-        [&](int c, int v, float x, float prev) { rr[c * DV + v] = prev + x; }, sm.stage, tid,
-        [&](int c, int v) { return rr[c * DV + v]; });
   }
 }
 
@@ -778,17 +776,22 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
         [&](int t, int vv) { return sm.a.u[t][vv]; },
         [&](int vv, int c) { return dSc[c * DV + vv]; },
         [&](int t, int c, float x, float) { sc[SC_DKB + t * DK + c] = x; }, sm.stage, tid);
-    // dM = scale tril(dO U^T)
+    // dM = scale tril(dO U^T), straight into its phase-B place (over dX, which
+    // no product reads any more)
     wg_gemm<CH, CH, DV, true, true>(
         [&](int r, int vv) { return SCALE * dO(r, vv); },
         [&](int vv, int i) { return sm.a.u[i][vv]; },
-        [&](int r, int i, float x, float) { sc[SC_DM + r * CH + i] = i <= r ? x : 0.f; }, sm.stage, tid);
-    // dTb = tril(dU X^T)
+        [&](int r, int i, float x, float) { sm.b.dm[r][i] = i <= r ? x : 0.f; }, sm.stage, tid);
+    // dTb = tril(dU X^T), over U (read last by the product above); Z below goes
+    // over X.  Both are read before phase B writes qh and kh over them.
+    float (*const dtb)[LDM] = reinterpret_cast<float (*)[LDM]>(&sm.a.u[0][0]);
+    float (*const zb)[LDM] = reinterpret_cast<float (*)[LDM]>(&sm.a.x[0][0]);
+    static_assert(CH * LDM <= CH * LD, "a [64][64] tile fits in a [64][128] one");
     wg_gemm<CH, CH, DV, true, true>(
         [&](int r, int vv) { return sm.a.du[r][vv]; },
         [&](int vv, int i) { return sm.a.x[i][vv]; },
-        [&](int r, int i, float x, float) { sc[SC_DTB + r * CH + i] = i <= r ? x : 0.f; }, sm.stage, tid);
-    // ---- phase A's LDS is free from here
+        [&](int r, int i, float x, float) { dtb[r][i] = i <= r ? x : 0.f; }, sm.stage, tid);
+    // ---- phase A's products are done: X, dU, dX are free, U holds dTb
     // dD[c] = sum_v dSc[c][v] S0[c][v] (32 threads per row, 16-byte loads);
     // dbeta_i = sum_r dTb_ri T_ri (both lower: the sum runs over all rows, in 8
     // row groups of 8 combined through LDS)
@@ -805,7 +808,7 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         tv[j] = T[(8 * part + j) * CH + i];
-        dv8[j] = sc[SC_DTB + (8 * part + j) * CH + i];
+        dv8[j] = dtb[8 * part + j][i];
       }
 #pragma unroll
       for (int j = 0; j < P; ++j) {
@@ -828,15 +831,15 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
     }
     // Z = (dTb Diag(beta)) T^T;  dA = -T^T Z (strictly lower)
     wg_gemm<CH, CH, CH, true, true>(
-        [&](int r, int m) { return sc[SC_DTB + r * CH + m] * sm.beta[m]; },
+        [&](int r, int m) { return dtb[r][m] * sm.beta[m]; },
         [&](int m, int i) { return T[i * CH + m]; },
-        [&](int r, int i, float x, float) { sc[SC_Z + r * CH + i] = x; }, sm.stage, tid);
+        [&](int r, int i, float x, float) { zb[r][i] = x; }, sm.stage, tid);
     wg_gemm<CH, CH, CH, false, false>(
         [&](int r, int m) { return -T[m * CH + r]; },
-        [&](int m, int i) { return sc[SC_Z + m * CH + i]; },
+        [&](int m, int i) { return zb[m][i]; },
         [&](int r, int i, float x, float) { sm.b.dkk[r][i] = i < r ? x : 0.f; }, sm.stage, tid);
-    // ---- phase B: qh, kh, G of the image and dM into LDS (16-byte vectors,
-    // all loads first)
+    // ---- phase B: qh, kh, G of the image into LDS (16-byte vectors, all
+    // loads first; dM is in place already)
     {
       constexpr int PV = CH * DK / 4 / NT;  // float4 per thread per tile
       float4 vq[PV], vk[PV], vg[PV];
@@ -847,10 +850,6 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
         vk[j] = *reinterpret_cast<const float4*>(img + IMG_KH + e);
         vg[j] = *reinterpret_cast<const float4*>(img + IMG_G + e);
       }
-      constexpr int PM = CH * CH / NT;
-      float vm[PM];
-#pragma unroll
-      for (int j = 0; j < PM; ++j) vm[j] = sc[SC_DM + tid + NT * j];
 #pragma unroll
       for (int j = 0; j < PV; ++j) {
         const int e = 4 * (tid + NT * j), r = e >> 7, c = e & 127;
@@ -863,11 +862,6 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
           sm.b.kh[r][c + u] = k4[u];
           sm.b.G[r][c + u] = g4[u];
         }
-      }
-#pragma unroll
-      for (int j = 0; j < PM; ++j) {
-        const int e = tid + NT * j;
-        sm.b.dm[e >> 6][e & 63] = vm[j];
       }
     }
     // dbeta_r += sum_i dA_ri Kk_ri (both strictly lower: all i, 8 threads per row)
@@ -1181,7 +1175,6 @@ int bwd_run(const void* q, const void* k, const void* v, const float* g, const f
   float* imgs = reinterpret_cast<float*>(ws + lay.off_img);
   float* fts = reinterpret_cast<float*>(ws + lay.off_ft);
   float* rs = reinterpret_cast<float*>(ws + lay.off_r);
-  float* sp = reinterpret_cast<float*>(ws + lay.off_sp);
   float* sc = reinterpret_cast<float*>(ws + lay.off_sc);
   void* o_scratch = ws + lay.off_o;
 
@@ -1206,7 +1199,7 @@ int bwd_run(const void* q, const void* k, const void* v, const float* g, const f
       hipLaunchKernelGGL(kda_bwd_prep_kernel, dim3(grid), dim3(NT), 0, stream,
                          static_cast<const bf16*>(q), static_cast<const bf16*>(k), g, beta,
                          static_cast<const bf16*>(d_out), table, bad, (int)items, (int)H, imgs, fts,
-                         rs, sp);
+                         rs);
       e = hipGetLastError();
     }
   }
