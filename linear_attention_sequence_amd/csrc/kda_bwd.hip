@@ -137,7 +137,10 @@ struct NoOld {
   __device__ float operator()(int, int) const { return 0.f; }
 };
 
-template <int M, int N, int K, bool AK, bool BK, class LA, class LB, class OUT, class OLD = NoOld>
+// PFMAX: k-tiles in flight (at most); EARLY_OLD: old() is fetched before the
+// first k-tile instead of after the last, so its loads overlap the product.
+template <int M, int N, int K, bool AK, bool BK, int PFMAX = 3, bool EARLY_OLD = false, class LA,
+          class LB, class OUT, class OLD = NoOld>
 __device__ __forceinline__ void wg_gemm(LA la, LB lb, OUT out, float* stage, int tid,
                                         OLD old = OLD()) {
   static_assert(M % 16 == 0 && N % 16 == 0 && K % 16 == 0 && M <= 128 && N <= 128, "shape");
@@ -164,7 +167,7 @@ __device__ __forceinline__ void wg_gemm(LA la, LB lb, OUT out, float* stage, int
   // up to PF k-tiles in flight: tile k is multiplied while tiles k+1 .. k+PF-1
   // are on their way (a load round trip is several tiles' worth of MFMA time)
   constexpr int KT = K / 16;
-  constexpr int PF = KT < 3 ? KT : 3;
+  constexpr int PF = KT < PFMAX ? KT : PFMAX;
   float ra[PF][NA], rb[PF][NB];
   auto fetch = [&](int set, int k0) {
 #pragma unroll
@@ -183,6 +186,18 @@ __device__ __forceinline__ void wg_gemm(LA la, LB lb, OUT out, float* stage, int
   f32x4 acc[PER];
 #pragma unroll
   for (int p = 0; p < PER; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // old(m, n): values out() adds to, all fetched before the first out() so
+  // that the loads are not ordered behind its stores
+  f32x4 prev[PER];
+  auto fetch_old = [&]() {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int t = w + NW * p, tm = t / TN, tn = t - tm * TN;
+      if (TILES % NW != 0 && t >= TILES) break;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) prev[p][i] = old(16 * tm + 4 * (l >> 4) + i, 16 * tn + (l & 15));
+    }
+  };
   auto tile = [&](int set, int kt) {
     __syncthreads();
 #pragma unroll
@@ -225,6 +240,7 @@ __device__ __forceinline__ void wg_gemm(LA la, LB lb, OUT out, float* stage, int
   };
 #pragma unroll
   for (int set = 0; set < PF; ++set) fetch(set, 16 * set);
+  if (EARLY_OLD) fetch_old();
 #pragma unroll 1
   for (int kt = 0; kt < KT; kt += PF) {
 #pragma unroll
@@ -232,16 +248,7 @@ __device__ __forceinline__ void wg_gemm(LA la, LB lb, OUT out, float* stage, int
       if (kt + set < KT) tile(set, kt + set);
   }
   __syncthreads();
-  // old(m, n): values out() adds to, all fetched before the first out() so
-  // that the loads are not ordered behind its stores
-  f32x4 prev[PER];
-#pragma unroll
-  for (int p = 0; p < PER; ++p) {
-    const int t = w + NW * p, tm = t / TN, tn = t - tm * TN;
-    if (TILES % NW != 0 && t >= TILES) break;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) prev[p][i] = old(16 * tm + 4 * (l >> 4) + i, 16 * tn + (l & 15));
-  }
+  if (!EARLY_OLD) fetch_old();
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
     const int t = w + NW * p, tm = t / TN, tn = t - tm * TN;
@@ -603,6 +610,8 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_prep_kernel(
 // ---------------------------------------------------------------------------
 constexpr int CV = DV / 4;  // value columns per chain workgroup
 
+constexpr int CHAIN_PF = 8;  // k-tiles of F^T in flight in a chain step
+
 struct ChainSmem {
   float ds[DK][CV + 1];
   alignas(16) float stage[STAGE_FLOATS];
@@ -637,10 +646,12 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_chain_kernel(
     }
     const float* ft = fts + item * DK * DK;
     const float* rr = rs + item * DK * DV + v0;
-    wg_gemm<DK, CV, DK, true, false>([&](int c, int c2) { return ft[c * DK + c2]; },
-                                     [&](int c2, int v) { return sm.ds[c2][v]; },
-                                     [&](int c, int v, float x, float) { sm.ds[c][v] = x + rr[c * DV + v]; },
-                                     sm.stage, tid);
+    // all of F^T's k-tiles in flight at once and R fetched with them: one
+    // memory round trip per step of the chain
+    wg_gemm<DK, CV, DK, true, false, CHAIN_PF, true>(
+        [&](int c, int c2) { return ft[c * DK + c2]; }, [&](int c2, int v) { return sm.ds[c2][v]; },
+        [&](int c, int v, float x, float r) { sm.ds[c][v] = x + r; }, sm.stage, tid,
+        [&](int c, int v) { return rr[c * DV + v]; });
   }
   __syncthreads();
   if (dh0 != nullptr)
