@@ -568,13 +568,13 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_prep_kernel(
     static_assert(offsetof(PrepSmem, t) == offsetof(PrepSmem, m) + sizeof(PrepSmem::m),
                   "M and T contiguous");
     float (*const zb)[LDC] = reinterpret_cast<float (*)[LDC]>(&sm.m[0][0]);
-    wg_gemm<DK, CH, CH, false, true>(
+    wg_gemm<DK, CH, CH, false, true, 4>(
         [&](int c, int t) { return sm.kh[t][c] * __expf(sm.G[t][c]); },
         [&](int t, int r) { return sm.t[r][t] * sm.beta[t]; },
         [&](int c, int r, float x, float) { zb[c][r] = x; }, sm.stage, tid);
     // F^T = D - Z Kbar  [c][c']
     float* ft = fts + (size_t)item * DK * DK;
-    wg_gemm<DK, DK, CH, true, false>(
+    wg_gemm<DK, DK, CH, true, false, 4>(
         [&](int c, int r) { return zb[c][r]; },
         [&](int r, int c2) { return sm.kh[r][c2] * __expf(Gl[c2] - sm.G[r][c2]); },
         [&](int c, int c2, float x, float) { ft[c * DK + c2] = (c == c2 ? __expf(Gl[c]) : 0.f) - x; },
@@ -584,7 +584,7 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_prep_kernel(
     float (*const wb)[LDC] = reinterpret_cast<float (*)[LDC]>(&sm.kh[0][0]);
     static_assert(DK * LDC <= CH * LD, "W fits over kh");
     const float* im = img + IMG_M;
-    wg_gemm<DK, CH, CH, true, true>(
+    wg_gemm<DK, CH, CH, true, true, 4>(
         [&](int c, int r) { return zb[c][r]; },
         [&](int r, int s2) { return im[s2 * CH + r]; },
         [&](int c, int s2, float x, float) {
@@ -593,7 +593,7 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_prep_kernel(
         sm.stage, tid);
     // R = W dO  [c][v]
     float* rr = rs + (size_t)item * DK * DV;
-    wg_gemm<DK, DV, CH, true, false>(
+    wg_gemm<DK, DV, CH, true, false, 4>(
         [&](int c, int s2) { return wb[c][s2]; },
         [&](int s2, int v) { return dO(s2, v); },
         [&](int c, int v, float x, float) { rr[c * DV + v] = x; }, sm.stage, tid);
@@ -744,18 +744,18 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
     };
     // ---- phase A: the products, X, U, dU, dX in LDS
     // X = V - Kt S0
-    wg_gemm<CH, DV, DK, true, false>(
+    wg_gemm<CH, DV, DK, true, false, 3, true>(
         [&](int t, int c) { return ikh[t * DK + c] * __expf(iG[t * DK + c]); },
         [&](int c, int vv) { return S0[c * DV + vv]; },
         [&](int t, int vv, float x, float vt) { sm.a.x[t][vv] = vt - x; }, sm.stage, tid,
         [&](int t, int vv) { return Vv(t, vv); });
     // U = Tb X
-    wg_gemm<CH, DV, CH, true, false>(
+    wg_gemm<CH, DV, CH, true, false, 4>(
         [&](int t, int i) { return T[t * CH + i] * sm.beta[i]; },
         [&](int i, int vv) { return sm.a.x[i][vv]; },
         [&](int t, int vv, float x, float) { sm.a.u[t][vv] = x; }, sm.stage, tid);
     // dU = scale M^T dO + Kbar dSc
-    wg_gemm<CH, DV, CH, false, false>(
+    wg_gemm<CH, DV, CH, false, false, 4>(
         [&](int t, int r) { return SCALE * Mm[r * CH + t]; },
         [&](int r, int vv) { return dO(r, vv); },
         [&](int t, int vv, float x, float) { sm.a.du[t][vv] = x; }, sm.stage, tid);
@@ -765,7 +765,7 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
         [&](int t, int vv, float x, float prev) { sm.a.du[t][vv] = prev + x; }, sm.stage, tid,
         [&](int t, int vv) { return sm.a.du[t][vv]; });
     // dX = Tb^T dU  (= dV)
-    wg_gemm<CH, DV, CH, false, false>(
+    wg_gemm<CH, DV, CH, false, false, 4>(
         [&](int t, int r) { return T[r * CH + t] * sm.beta[t]; },
         [&](int r, int vv) { return sm.a.du[r][vv]; },
         [&](int t, int vv, float x, float) {
@@ -841,11 +841,11 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
       }
     }
     // Z = (dTb Diag(beta)) T^T;  dA = -T^T Z (strictly lower)
-    wg_gemm<CH, CH, CH, true, true>(
+    wg_gemm<CH, CH, CH, true, true, 4>(
         [&](int r, int m) { return dtb[r][m] * sm.beta[m]; },
         [&](int m, int i) { return T[i * CH + m]; },
         [&](int r, int i, float x, float) { zb[r][i] = x; }, sm.stage, tid);
-    wg_gemm<CH, CH, CH, false, false>(
+    wg_gemm<CH, CH, CH, false, false, 4>(
         [&](int r, int m) { return -T[m * CH + r]; },
         [&](int m, int i) { return zb[m][i]; },
         [&](int r, int i, float x, float) { sm.b.dkk[r][i] = i < r ? x : 0.f; }, sm.stage, tid);
