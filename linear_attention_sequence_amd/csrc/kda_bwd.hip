@@ -744,7 +744,7 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
     };
     // ---- phase A: the products, X, U, dU, dX in LDS
     // X = V - Kt S0
-    wg_gemm<CH, DV, DK, true, false, 3, true>(
+    wg_gemm<CH, DV, DK, true, false, 4, true>(
         [&](int t, int c) { return ikh[t * DK + c] * __expf(iG[t * DK + c]); },
         [&](int c, int vv) { return S0[c * DV + vv]; },
         [&](int t, int vv, float x, float vt) { sm.a.x[t][vv] = vt - x; }, sm.stage, tid,
@@ -759,7 +759,7 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
         [&](int t, int r) { return SCALE * Mm[r * CH + t]; },
         [&](int r, int vv) { return dO(r, vv); },
         [&](int t, int vv, float x, float) { sm.a.du[t][vv] = x; }, sm.stage, tid);
-    wg_gemm<CH, DV, DK, true, false>(
+    wg_gemm<CH, DV, DK, true, false, 4>(
         [&](int t, int c) { return ikh[t * DK + c] * __expf(sm.gl[c] - iG[t * DK + c]); },
         [&](int c, int vv) { return dSc[c * DV + vv]; },
         [&](int t, int vv, float x, float prev) { sm.a.du[t][vv] = prev + x; }, sm.stage, tid,
@@ -775,7 +775,7 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
         sm.stage, tid);
     // dQt = scale dO S0^T (rows 0..63 of SC_DQK) and dKt = -dX S0^T (rows
     // 64..127) as one product: S0 is streamed once for both
-    wg_gemm<2 * CH, DK, DV, true, true>(
+    wg_gemm<2 * CH, DK, DV, true, true, 4>(
         [&](int t, int vv) {
           const float a = SCALE * dO(min(t, CH - 1), vv), b = -sm.a.dx[t & (CH - 1)][vv];
           return t < CH ? a : b;
@@ -783,13 +783,13 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
         [&](int vv, int c) { return S0[c * DV + vv]; },
         [&](int t, int c, float x, float) { sc[SC_DQK + t * DK + c] = x; }, sm.stage, tid);
     // dKbar = U dSc^T
-    wg_gemm<CH, DK, DV, true, true>(
+    wg_gemm<CH, DK, DV, true, true, 4>(
         [&](int t, int vv) { return sm.a.u[t][vv]; },
         [&](int vv, int c) { return dSc[c * DV + vv]; },
         [&](int t, int c, float x, float) { sc[SC_DKB + t * DK + c] = x; }, sm.stage, tid);
     // dM = scale tril(dO U^T), straight into its phase-B place (over dX, which
     // no product reads any more)
-    wg_gemm<CH, CH, DV, true, true>(
+    wg_gemm<CH, CH, DV, true, true, 4>(
         [&](int r, int vv) { return SCALE * dO(r, vv); },
         [&](int vv, int i) { return sm.a.u[i][vv]; },
         [&](int r, int i, float x, float) { sm.b.dm[r][i] = i <= r ? x : 0.f; }, sm.stage, tid);
@@ -798,7 +798,7 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_grads_kernel(
     float (*const dtb)[LDM] = reinterpret_cast<float (*)[LDM]>(&sm.a.u[0][0]);
     float (*const zb)[LDM] = reinterpret_cast<float (*)[LDM]>(&sm.a.x[0][0]);
     static_assert(CH * LDM <= CH * LD, "a [64][64] tile fits in a [64][128] one");
-    wg_gemm<CH, CH, DV, true, true>(
+    wg_gemm<CH, CH, DV, true, true, 4>(
         [&](int r, int vv) { return sm.a.du[r][vv]; },
         [&](int vv, int i) { return sm.a.x[i][vv]; },
         [&](int r, int i, float x, float) { dtb[r][i] = i <= r ? x : 0.f; }, sm.stage, tid);
